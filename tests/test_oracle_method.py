@@ -1,0 +1,358 @@
+"""Pins of the oracle's method functions against closed forms, invariants, brute force and
+library routines (scipy softmax, torch scaled_dot_product_attention).
+
+Each test names the property it pins; together they are chosen so that a dropped term, a wrong
+sign, an off-by-one window or a transposed operand in the oracle fails at least one of them.
+"""
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle as O
+from long_context_attention_03_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+F32, BF16 = O.DT_F32, O.DT_BF16
+
+
+# ----------------------------------------------------------------------------- kv_compress
+def _rand(shape, seed, std=1.0):
+    return (np.random.default_rng(seed).normal(size=shape) * std).astype(np.float32)
+
+
+def test_entry_counts_match_page():
+    """Group counts at one million tokens: ~250k (m=4) and ~7.8k (m=128), as printed."""
+    with open(os.path.join(GOLD, "page_entry_counts.txt")) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    for T, m, printed, tol in rows:
+        T, m, printed, tol = int(T), int(m), int(printed), float(tol)
+        Tm = T - T % m  # only complete groups are passed
+        x = np.zeros((1, Tm, 32), np.float32)
+        r = O.kv_compress(x, F32, m, np.zeros(32, np.float32), np.zeros(m, np.float32),
+                          O.FMT_ROW_F32)
+        n = r["rows"].shape[1]
+        assert n == Tm // m
+        assert abs(n - printed) <= tol * printed
+
+
+def test_m1_is_identity_bitwise():
+    x = _rand((2, 16, 512), 1)
+    w, b = _rand(512, 2, 0.02), _rand(1, 3, 0.1)
+    for fmt in (O.FMT_ROW_F32, O.FMT_ROW_E4M3_BF16):
+        r = O.kv_compress(x, F32, 1, w, b, fmt)
+        ref, _ = O.encode_rows(x.astype(np.float64), fmt)
+        assert np.array_equal(r["rows"], ref)
+        assert np.array_equal(r["pre"], x.astype(np.float64))
+    r = O.kv_compress(x[:, :, :128], F32, 1, w[:128], b, O.FMT_FP4_E8M0)
+    ref, sc = O.encode_rows(x[:, :, :128].astype(np.float64), O.FMT_FP4_E8M0)
+    assert np.array_equal(r["rows"], ref) and np.array_equal(r["scales"], sc)
+
+
+@pytest.mark.parametrize("m", [4, 128])
+def test_group_weights_sum_to_one_and_positive(m):
+    x = _rand((1, 4 * m, 64), 4)
+    r = O.kv_compress(x, F32, m, _rand(64, 5, 0.3), _rand(m, 6, 2.0), O.FMT_ROW_F32)
+    pi = r["pi"]
+    assert np.allclose(pi.sum(-1), 1.0, rtol=0, atol=1e-14)
+    assert (pi > 0).all()
+
+
+def test_zero_gate_gives_arithmetic_mean():
+    x = _rand((2, 64, 96), 7)
+    r = O.kv_compress(x, F32, 4, np.zeros(96, np.float32), np.zeros(4, np.float32), O.FMT_ROW_F32)
+    mean = x.astype(np.float64).reshape(2, 16, 4, 96).mean(axis=2)
+    assert np.allclose(r["pre"], mean, rtol=0, atol=1e-14)
+
+
+def test_bias_only_gate_is_softmax_of_biases_in_group_order():
+    """w = 0: pi = softmax(beta), with beta indexed by the position inside the group."""
+    m = 8
+    x = _rand((1, 3 * m, 32), 8)
+    beta = np.arange(m, dtype=np.float32) * 0.37 - 1.0  # asymmetric: a reversed index fails
+    r = O.kv_compress(x, F32, m, np.zeros(32, np.float32), beta, O.FMT_ROW_F32)
+    ref_pi = scipy.special.softmax(beta.astype(np.float64))
+    assert np.allclose(r["pi"][0], ref_pi[None, :], rtol=0, atol=1e-15)
+    ref = np.einsum("t,gtd->gd", ref_pi, x[0].astype(np.float64).reshape(3, m, 32))
+    assert np.allclose(r["pre"][0], ref, rtol=0, atol=1e-14)
+
+
+def test_unit_gate_selects_one_channel_logit():
+    """w = e_c, beta = 0: z_t = x_{t,c}, so pi = softmax over the group of channel c."""
+    m, D, c = 4, 48, 17
+    x = _rand((1, 5 * m, D), 9)
+    w = np.zeros(D, np.float32)
+    w[c] = 1.0
+    r = O.kv_compress(x, F32, m, w, np.zeros(m, np.float32), O.FMT_ROW_F32)
+    z = x[0, :, c].astype(np.float64).reshape(5, m)
+    assert np.allclose(r["pi"][0], scipy.special.softmax(z, axis=1), rtol=0, atol=1e-15)
+
+
+def test_constant_group_and_convex_hull():
+    m = 4
+    x = _rand((1, 8 * m, 40), 10)
+    x[0, :m] = x[0, 0]  # first group constant
+    r = O.kv_compress(x, F32, m, _rand(40, 11, 0.5), _rand(m, 12, 1.0), O.FMT_ROW_F32)
+    assert np.allclose(r["pre"][0, 0], x[0, 0], rtol=0, atol=1e-15)
+    g = x[0].astype(np.float64).reshape(8, m, 40)
+    assert (r["pre"][0] <= g.max(1) + 1e-15).all() and (r["pre"][0] >= g.min(1) - 1e-15).all()
+
+
+def test_bf16_raw_input_is_decoded():
+    x = torch.from_numpy(_rand((1, 8, 64), 13)).to(torch.bfloat16)
+    bits = x.view(torch.int16).numpy().astype(np.uint16)
+    r16 = O.kv_compress(bits, BF16, 4, _rand(64, 14, 0.1), _rand(4, 15, 0.1), O.FMT_ROW_F32)
+    r32 = O.kv_compress(x.float().numpy(), F32, 4, _rand(64, 14, 0.1), _rand(4, 15, 0.1),
+                        O.FMT_ROW_F32)
+    assert np.array_equal(r16["pre"], r32["pre"])
+
+
+# ----------------------------------------------------------------------------- indexer
+def _fp4(x):
+    return O.encode_rows(np.asarray(x, np.float64), O.FMT_FP4_E8M0)
+
+
+def test_index_scores_vs_decoded_float_matmul():
+    """Exact integer scores == fp64 matmul of the decoded FP4 values (exact: dyadic, few bits)."""
+    rng = np.random.default_rng(20)
+    HI, dI, n = 4, 128, 3000
+    qc, qs = _fp4(rng.normal(size=(HI, dI)))
+    kc, ks = _fp4(rng.normal(size=(n, dI)))
+    s, ok = O.index_scores(qc, qs, kc, ks)
+    qd = O.decode_rows(qc, dI, O.FMT_FP4_E8M0, qs)
+    kd = O.decode_rows(kc, dI, O.FMT_FP4_E8M0, ks)
+    ref = (kd @ qd.T).sum(axis=1)
+    assert ok.all()
+    assert np.array_equal(s, ref)
+
+
+def test_index_score_closed_forms():
+    HI, dI = 4, 64
+    qc = np.full((HI, dI // 2), 0x22, np.uint8)  # every element 1.0
+    qs = np.full((HI, dI // 32), 127, np.uint8)
+    kc = np.full((3, dI // 2), 0x22, np.uint8)
+    ks = np.full((3, dI // 32), 127, np.uint8)
+    ks[1, 0] = 128  # first block of key 1 doubled
+    kc[2, :] = 0xAA  # key 2: every element -1.0
+    s, ok = O.index_scores(qc, qs, kc, ks)
+    assert list(s) == [HI * dI, HI * (dI + 32), -HI * dI]
+    qs2 = qs.copy()
+    qs2[2, 1] = 125  # head 2, block 1 scaled by 1/4
+    s2, _ = O.index_scores(qc, qs2, kc[:1], ks[:1])
+    assert s2[0] == HI * dI - 32 + 8
+
+
+def test_topk_matches_brute_force_sort_with_ties():
+    rng = np.random.default_rng(21)
+    B, Q, HI, dI, N, m, k = 2, 3, 4, 64, 500, 4, 37
+    # coarse values so that many scores tie
+    kc, ks = _fp4(np.round(rng.normal(size=(B, N, dI))))
+    qc, qs = _fp4(np.round(rng.normal(size=(B, Q, HI, dI))))
+    pos = np.array([N * m - 1, 4 * 173 + 2], np.int64)
+    idx, sc, ex = O.index_topk(qc, qs, kc, ks, pos, m, k)
+    assert ex.all()
+    for b in range(B):
+        for i in range(Q):
+            nv = min((pos[b] + i + 1) // m, N)
+            s, _ = O.index_scores(qc[b, i], qs[b, i], kc[b, :nv], ks[b, :nv])
+            order = sorted(range(nv), key=lambda g: (-s[g], g))
+            exp = order[:k] + [-1] * max(0, k - nv)
+            assert list(idx[b, i]) == exp
+            assert np.array_equal(sc[b, i, :min(k, nv)], s[order[:k]])
+    # the ties were real: some equal scores inside the top-k
+    assert any(len(np.unique(sc[b, 0])) < k for b in range(B))
+
+
+def test_topk_k_ge_valid_returns_all_in_order_then_pad():
+    rng = np.random.default_rng(22)
+    kc, ks = _fp4(rng.normal(size=(1, 40, 32)))
+    qc, qs = _fp4(rng.normal(size=(1, 1, 2, 32)))
+    pos = np.array([4 * 30 + 1], np.int64)  # 30 complete groups visible
+    idx, sc, _ = O.index_topk(qc, qs, kc, ks, pos, 4, 64)
+    assert sorted(idx[0, 0, :30]) == list(range(30))
+    assert (idx[0, 0, 30:] == -1).all() and np.isneginf(sc[0, 0, 30:]).all()
+    assert (np.diff(sc[0, 0, :30]) <= 0).all()
+
+
+def test_topk_causality_incomplete_group_not_visible():
+    rng = np.random.default_rng(23)
+    kc, ks = _fp4(rng.normal(size=(1, 8, 32)))
+    qc, qs = _fp4(rng.normal(size=(1, 4, 1, 32)))
+    pos = np.array([2], np.int64)  # queries at positions 2,3,4,5 with m=4
+    idx, _, _ = O.index_topk(qc, qs, kc, ks, pos, 4, 3)
+    assert (idx[0, 0] == -1).all()                      # position 2: no complete group
+    assert list(idx[0, 1]) == [0, -1, -1]               # position 3: group 0 complete
+    assert list(idx[0, 3]) == [0, -1, -1]               # position 5: still one group
+
+
+# ----------------------------------------------------------------------------- attention
+def _f32_rows(x):
+    return O.encode_rows(np.asarray(x, np.float64), O.FMT_ROW_F32)[0]
+
+
+def _sdpa(q, K, V, mask=None, scale=1.0):
+    """torch SDPA in fp64 on the CPU: q [H, D], K/V [n, D], mask [n] bool."""
+    qt = torch.from_numpy(q)[None, :, None, :]               # [1, H, 1, D]
+    Kt = torch.from_numpy(K)[None, None].expand(1, q.shape[0], -1, -1)
+    Vt = torch.from_numpy(V)[None, None].expand(1, q.shape[0], -1, -1)
+    am = None if mask is None else torch.from_numpy(mask)[None, None, None, :]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=am, scale=scale)
+    return o[0, :, 0, :].numpy()
+
+
+def _case(seed, B=1, Q=1, H=4, D=64, N=40, w=16, k=8):
+    rng = np.random.default_rng(seed)
+    q = rng.normal(size=(B, Q, H, D)).astype(np.float32)
+    cache_v = rng.normal(size=(B, N, D))
+    win_v = rng.normal(size=(B, w - 1 + Q, D))
+    return q, cache_v, win_v
+
+
+@pytest.mark.parametrize("pos0", [100, 5])
+def test_window_only_equals_masked_sdpa(pos0):
+    """No compressed rows, no sink: naive sliding-window attention over [p-w+1, p], p >= 0."""
+    q, cv, wv = _case(30, Q=3, w=16)
+    w, scale = 16, 0.125
+    idx = np.full((1, 3, 4), -1, np.int32)
+    out, lse = O.csa_attend(q, _f32_rows(cv), O.FMT_ROW_F32, idx, _f32_rows(wv), w,
+                            np.array([pos0]), None, scale)
+    wd = wv[0].astype(np.float32).astype(np.float64)
+    for i in range(3):
+        rows_pos = pos0 - (w - 1) + np.arange(w - 1 + 3)
+        p = pos0 + i
+        mask = (rows_pos >= p - w + 1) & (rows_pos <= p) & (rows_pos >= 0)
+        ref = _sdpa(q[0, i].astype(np.float64), wd, wd, mask, scale)
+        assert np.allclose(out[0, i], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_sink_equals_extra_zero_value_key():
+    q, cv, wv = _case(31, H=3, D=32, N=20, w=8)
+    sink = np.array([0.5, -2.0, 3.0], np.float32)
+    scale = 0.2
+    idx = np.array([[[3, 7, 11, 19, -1]]], np.int32)
+    out, lse = O.csa_attend(q, _f32_rows(cv), O.FMT_ROW_F32, idx, _f32_rows(wv), 8,
+                            np.array([50]), sink, scale)
+    cd = cv[0].astype(np.float32).astype(np.float64)
+    wd = wv[0].astype(np.float32).astype(np.float64)
+    Y = np.concatenate([cd[[3, 7, 11, 19]], wd])
+    for h in range(3):
+        qh = q[0, 0, h].astype(np.float64)
+        k_extra = qh * (float(sink[h]) / (scale * qh @ qh))  # scale * q.k_extra = sigma
+        K = np.concatenate([Y, k_extra[None]])
+        V = np.concatenate([Y, np.zeros((1, 32))])
+        ref = _sdpa(qh[None], K, V, None, scale)[0]
+        assert np.allclose(out[0, 0, h], ref, rtol=1e-10, atol=1e-12)
+        # weights of the rows plus the sink weight sum to one (sink lowers the row total)
+        s = scale * Y @ qh
+        tot = np.exp(s - lse[0, 0, h]).sum()
+        assert tot < 1.0 and abs(tot + np.exp(sink[h] - lse[0, 0, h]) - 1.0) < 1e-12
+
+
+def test_no_sink_equals_plain_softmax_and_lse():
+    q, cv, wv = _case(32, H=2, D=16, N=10, w=4)
+    idx = np.array([[[0, 1, 2, 3, 4, 5, 6, 7, 8, 9]]], np.int32)
+    out, lse = O.csa_attend(q, _f32_rows(cv), O.FMT_ROW_F32, idx, _f32_rows(wv), 4,
+                            np.array([40]), None, 0.3)
+    Y = np.concatenate([cv[0], wv[0]]).astype(np.float32).astype(np.float64)
+    for h in range(2):
+        s = 0.3 * Y @ q[0, 0, h].astype(np.float64)
+        assert abs(lse[0, 0, h] - scipy.special.logsumexp(s)) < 1e-12
+        assert np.allclose(out[0, 0, h], scipy.special.softmax(s) @ Y, rtol=1e-12, atol=1e-13)
+
+
+def test_csa_with_all_entries_equals_hca():
+    """k >= N: CSA over every visible entry is dense attention over the same cache."""
+    q, cv, wv = _case(33, B=2, H=4, D=64, N=25, w=16)
+    rows, win = _f32_rows(cv), _f32_rows(wv)
+    pos = np.array([4 * 25 - 1, 4 * 25 + 2], np.int64)
+    sink = np.array([0.1, 0.2, -0.3, 1.0], np.float32)
+    idx = np.tile(np.arange(25, dtype=np.int32)[::-1], (2, 1, 1))
+    o1, l1 = O.csa_attend(q, rows, O.FMT_ROW_F32, idx, win, 16, pos, sink, 0.125)
+    o2, l2 = O.hca_attend(q, rows, O.FMT_ROW_F32, 4, win, 16, pos, sink, 0.125)
+    assert np.allclose(o1, o2, rtol=1e-13, atol=1e-14) and np.allclose(l1, l2, rtol=0, atol=1e-13)
+
+
+def test_idx_permutation_and_empty_slots():
+    q, cv, wv = _case(34, N=30)
+    rows, win = _f32_rows(cv), _f32_rows(wv)
+    a = np.array([[[4, 9, 1, 22, 17]]], np.int32)
+    b = np.array([[[17, -1, 1, 22, -1, 9, 4]]], np.int32)
+    o1, l1 = O.csa_attend(q, rows, O.FMT_ROW_F32, a, win, 16, np.array([90]), None, 0.1)
+    o2, l2 = O.csa_attend(q, rows, O.FMT_ROW_F32, b, win, 16, np.array([90]), None, 0.1)
+    assert np.allclose(o1, o2, rtol=1e-13, atol=1e-14)
+
+
+def test_hca_causality_future_rows_do_not_matter():
+    q, cv, wv = _case(35, Q=3, N=12, w=8)
+    pos = np.array([4 * 6 + 1], np.int64)  # positions 25..27 -> 6 or 7 visible groups (m=4)
+    rows, win = _f32_rows(cv), _f32_rows(wv)
+    o1, _ = O.hca_attend(q, rows, O.FMT_ROW_F32, 4, win, 8, pos, None, 0.1)
+    cv2 = cv.copy()
+    cv2[0, 7:] += 100.0  # groups 7.. are never visible to positions <= 27
+    wv2 = wv.copy()
+    o2, _ = O.hca_attend(q, _f32_rows(cv2), O.FMT_ROW_F32, 4, win, 8, pos, None, 0.1)
+    assert np.array_equal(o1, o2)
+    wv2[0, -1] += 100.0  # last window row = position 27: only query 2 sees it
+    o3, _ = O.hca_attend(q, rows, O.FMT_ROW_F32, 4, _f32_rows(wv2), 8, pos, None, 0.1)
+    assert np.array_equal(o1[0, :2], o3[0, :2]) and not np.allclose(o1[0, 2], o3[0, 2])
+    cv3 = cv.copy()
+    cv3[0, 6] += 100.0  # group 6 completes at position 27: visible to query 2 only
+    o4, _ = O.hca_attend(q, _f32_rows(cv3), O.FMT_ROW_F32, 4, win, 8, pos, None, 0.1)
+    assert np.array_equal(o1[0, :2], o4[0, :2]) and not np.allclose(o1[0, 2], o4[0, 2])
+
+
+def test_partition_plus_lse_merge_equals_one_pass():
+    """Split the rows in two, merge by log-sum-exp: equals the single pass (sink-free)."""
+    q, cv, wv = _case(36, H=2, D=32, N=20, w=4)
+    rows, win = _f32_rows(cv), _f32_rows(wv)
+    pos = np.array([2], np.int64)  # window rows mostly before position 0 -> only 3 rows valid
+    all_idx = np.arange(20, dtype=np.int32)[None, None]
+    o, l = O.csa_attend(q, rows, O.FMT_ROW_F32, all_idx, win, 4, pos, None, 0.2)
+    oa, la = O.csa_attend(q, rows, O.FMT_ROW_F32, all_idx[..., :9], win, 0, pos, None, 0.2)
+    ob, lb = O.csa_attend(q, rows, O.FMT_ROW_F32, all_idx[..., 9:], win, 4, pos, None, 0.2)
+    L = np.logaddexp(la, lb)
+    merged = oa * np.exp(la - L)[..., None] + ob * np.exp(lb - L)[..., None]
+    assert np.allclose(o, merged, rtol=1e-12, atol=1e-13) and np.allclose(l, L, atol=1e-12)
+
+
+def test_e4m3_rows_and_bf16_queries_decode():
+    rng = np.random.default_rng(37)
+    D = 512
+    qf = torch.from_numpy(rng.normal(size=(1, 1, 2, D)).astype(np.float32)).to(torch.bfloat16)
+    qbits = qf.view(torch.int16).numpy().astype(np.uint16)
+    cache, _ = O.encode_rows(rng.normal(size=(1, 6, D)), O.FMT_ROW_E4M3_BF16)
+    win, _ = O.encode_rows(rng.normal(size=(1, 4, D)), O.FMT_ROW_E4M3_BF16)
+    idx = np.array([[[5, 0, 2]]], np.int32)
+    out, lse = O.csa_attend(qbits, cache, O.FMT_ROW_E4M3_BF16, idx, win, 4, np.array([30]), None,
+                            D ** -0.5)
+    Y = np.concatenate([O.decode_rows(cache[0, [5, 0, 2]], D, O.FMT_ROW_E4M3_BF16),
+                        O.decode_rows(win[0], D, O.FMT_ROW_E4M3_BF16)])
+    for h in range(2):
+        qh = qf[0, 0, h].double().numpy()
+        ref = _sdpa(qh[None], Y, Y, None, D ** -0.5)[0]
+        assert np.allclose(out[0, 0, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_tiny_workload_end_to_end_is_self_consistent():
+    """The tiny workload through kv_compress -> index_topk -> csa/hca attend (CPU only)."""
+    wl = synth.WORKLOADS["tiny"]
+    raw = synth.raw_tokens(wl, wl.L)
+    x = raw["x"].numpy()
+    csa = O.kv_compress(x, F32, 4, raw["w_csa"].numpy(), raw["b_csa"].numpy(), O.FMT_ROW_F32)
+    hca = O.kv_compress(x, F32, 128, raw["w_hca"].numpy(), raw["b_hca"].numpy(), O.FMT_ROW_F32)
+    ik = O.kv_compress(raw["xi"].numpy(), F32, 4, raw["w_idx"].numpy(), raw["b_idx"].numpy(),
+                       O.FMT_FP4_E8M0)
+    assert csa["rows"].shape[1] == 1024 and hca["rows"].shape[1] == 32
+    d = synth.Draws(wl.seed + 1000)
+    iq, iqs = O.encode_rows(d.normal((1, 1, wl.HI, wl.dI)).double().numpy(), O.FMT_FP4_E8M0)
+    pos = np.array([wl.L - 1], np.int64)
+    idx, sc, ex = O.index_topk(iq, iqs, ik["rows"], ik["scales"], pos, 4, wl.k)
+    assert ex.all() and (idx >= 0).all() and len(set(idx[0, 0])) == wl.k
+    q = d.normal((1, 1, wl.H, wl.D)).numpy()
+    win, _ = O.encode_rows(x[:, -wl.w:].astype(np.float64), O.FMT_ROW_F32)
+    sink = d.normal((wl.H,)).numpy()
+    o, l = O.csa_attend(q, csa["rows"], O.FMT_ROW_F32, idx, win, wl.w, pos, sink, wl.scale)
+    oh, lh = O.hca_attend(q, hca["rows"], O.FMT_ROW_F32, 128, win, wl.w, pos, sink, wl.scale)
+    assert np.isfinite(o).all() and np.isfinite(oh).all()
