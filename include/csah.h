@@ -1,0 +1,173 @@
+/*
+ * csah.h -- C ABI of a compress-then-sparsify attention library for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the attention hot path of DeepSeek-V4's hybrid attention as described by
+ *   [EXPL]  "DeepSeek V4 Architecture Explained: CSA, HCA, mHC and Muon", section
+ *           "How compress-then-sparsify attention works" and the "Key numbers" table;
+ *   [LLMB]  "Inside DeepSeek-V4: How Hybrid Sparse Attention Slashes 1M Context Overhead by 90%",
+ *           sections "1. Compressed Sparse Attention (CSA)" and "2. Heavily Compressed
+ *           Attention (HCA)";
+ *   [BSWEN] "How DeepSeek V4 Handles 1M Token Context with Hybrid Attention", sections
+ *           "Component 2: Multi-Level KV Compression" and "Component 3: DeepSeek Sparse
+ *           Attention (DSA)".
+ *
+ * Conventions shared by every entry point
+ *  - Every array argument is a DEVICE pointer to memory owned by the caller. The library never
+ *    allocates, frees or synchronises; it keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). A call only enqueues
+ *    kernels on it and returns.
+ *  - Arguments are validated on the host before anything is enqueued. On a nonzero status nothing
+ *    was enqueued. Device buffers smaller than the shapes imply, or device-side values outside
+ *    their documented ranges, are not detectable on the host: kernels clamp every index they
+ *    derive from device data so that they stay inside the shapes passed, and the results are then
+ *    unspecified.
+ *  - Strides are counted in rows (tokens or entries) of the buffer's own row format.
+ *  - Calls are reentrant; concurrent calls must use distinct workspaces.
+ *
+ * Row formats of one token's / one compressed entry's shared K=V vector (D values):
+ *   CSAH_FMT_ROW_F32        D little-endian binary32 values (4*D bytes).
+ *   CSAH_FMT_ROW_E4M3_BF16  D-64 OCP E4M3 bytes (unit scale) followed by 64 bf16 values
+ *                           (D+64 bytes; 576 bytes at D=512). [EXPL] "Key numbers": rotary
+ *                           dimensions are stored in BF16 and the others in FP8.
+ *   CSAH_FMT_FP4_E8M0       indexer keys / queries: D/2 bytes of OCP MX E2M1 codes (element 2j in
+ *                           the low nibble of byte j) in the row array, and D/32 E8M0 scale bytes
+ *                           per row in a separate scale array indexed by the same rows.
+ */
+#ifndef CSAH_H
+#define CSAH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSAH_ABI_VERSION 1
+
+/* status codes */
+#define CSAH_OK 0
+#define CSAH_ERR_INVALID_ARGUMENT (-1) /* null pointer, bad shape or stride                   */
+#define CSAH_ERR_UNSUPPORTED (-2)      /* shape/format combination not built, or no gfx950    */
+#define CSAH_ERR_WORKSPACE_TOO_SMALL (-3)
+#define CSAH_ERR_LAUNCH (-4)           /* the HIP runtime refused a launch                     */
+
+/* element types of raw rows and queries */
+#define CSAH_DT_F32 0
+#define CSAH_DT_BF16 1
+
+/* row formats */
+#define CSAH_FMT_ROW_F32 0
+#define CSAH_FMT_ROW_E4M3_BF16 1
+#define CSAH_FMT_FP4_E8M0 2
+
+/* ABI version of the loaded library (CSAH_ABI_VERSION at build time). */
+int csah_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char* csah_status_string(int status);
+
+/* Bytes per row of `fmt` at width D (the row array only for FP4_E8M0); -1 if not a format. */
+int64_t csah_row_bytes(int fmt, int D);
+
+/*
+ * csah_kv_compress -- softmax-gated pooling of each group of m consecutive tokens' shared K=V row
+ * into one compressed entry, with a learned bias per position inside the group.
+ *   [EXPL]: m consecutive tokens fold into one KV entry through trainable compression weights, a
+ *   softmax over the group and learnable positional biases. [LLMB] "1. CSA": factor 4;
+ *   "2. HCA": factor 128. For group g (tokens gm .. gm+m-1):
+ *     z_t = sum_c w[c] * x_t[c] + beta[t - g*m],   pi = softmax_t(z),   c_g = sum_t pi_t * x_t,
+ *   then c_g is encoded in out_fmt (E4M3 and E2M1 round to nearest even and saturate; MX blocks
+ *   use the shared exponent floor(log2 amax) - 2, and an all-zero block gets scale byte 127).
+ *   m = 1 returns the rows themselves, encoded: it is also the library's quantiser.
+ * raw       [B][raw_seq_stride][D] tokens, raw_dtype CSAH_DT_F32 or CSAH_DT_BF16; only the first T
+ *           rows of each sequence are read.
+ * T         tokens per sequence; must be a multiple of m (complete groups only).
+ * w, beta   fp32 gate weights [D] and positional biases [m].
+ * out_rows  [B][out_seq_stride] rows of out_fmt; entry g of sequence b is written to row
+ *           b*out_seq_stride + g (point it at the cache's append position). out_seq_stride >= T/m.
+ * out_scales FP4_E8M0 only: [B][out_seq_stride][D/32] scale bytes (NULL otherwise).
+ * Supported: D % 64 == 0, 64 <= D <= 1024; D == 512 for ROW_E4M3_BF16; 1 <= m <= 65536.
+ */
+int csah_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B, int64_t T,
+                     int D, int m, const float* w, const float* beta, void* out_rows, int out_fmt,
+                     int64_t out_seq_stride, uint8_t* out_scales, void* stream);
+
+/*
+ * csah_index_topk -- the lightning indexer: score every visible compressed entry against the
+ * query's FP4 indexer heads and keep the top k.
+ *   [EXPL]: low-rank indexer queries are scored against compressed indexer keys and each query
+ *   keeps its top-k entries; [LLMB] "1. CSA": the indexer runs in FP4 and keeps the top 1,024;
+ *   [BSWEN] "Component 3": score all compressed entries, then select the top k.
+ *   score_g = sum_h sum_blocks 2^(Eq+Ek-254) * sum_{i in block} e2m1(q_h,i) * e2m1(k_g,i)
+ *   (a plain sum over heads). Scores are dyadic and computed exactly whenever the sum of the
+ *   absolute products over the finest power-of-two granularity stays below 2^24 and all scales
+ *   keep the products inside the binary32 normal range.
+ *   Query i of sequence b sees entries g < min(floor((pos[b]+i+1)/m), N): a group is visible once
+ *   it is complete. The output lists the first min(k, visible) entries ordered by (score
+ *   descending, index ascending); remaining slots are -1 (score -inf).
+ * q_codes   [B][Q][HI][dI/2] E2M1 codes, q_scales [B][Q][HI][dI/32] E8M0.
+ * k_codes   [B][k_seq_stride][dI/2], k_scales [B][k_seq_stride][dI/32]; N <= k_seq_stride.
+ * pos       [B] int64 device array, position of query 0 of each sequence.
+ * idx_out   [B][Q][k] int32; score_out [B][Q][k] fp32 or NULL.
+ * ws        device workspace of at least csah_index_topk_workspace(B, Q, N, k, dI) bytes,
+ *           256-byte aligned; its contents need no initialisation and are clobbered.
+ * Supported: 1 <= HI <= 16, dI in {32, 64, 128}, 1 <= k <= 4096, N < 2^31, m >= 1.
+ */
+size_t csah_index_topk_workspace(int B, int Q, int64_t N, int k, int dI);
+int csah_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int dI,
+                    const uint8_t* k_codes, const uint8_t* k_scales, int64_t k_seq_stride,
+                    int64_t N, const int64_t* pos, int m, int B, int Q, int k, int32_t* idx_out,
+                    float* score_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csah_csa_attend -- sparse attention of every query head over its selected compressed entries,
+ * the sliding window of recent uncompressed tokens and a per-head sink, in one softmax.
+ *   [EXPL]: each query attends to its top-k compressed entries plus a small window of recent
+ *   uncompressed tokens, and an attention-sink term lets a head's weights total less than one;
+ *   K and V share one row per entry (shared-KV multi-query layout). [LLMB] "1. CSA": the window
+ *   covers the nearest 128 tokens, uncompressed.
+ *     s_j = scale * q_h . y_j over rows j in S = {cache row idx[..]} U {window rows},
+ *     M = max(sigma_h, max s), den = e^(sigma_h - M) + sum e^(s_j - M),
+ *     out_h = sum e^(s_j - M) y_j / den,   lse_h = M + ln(den).
+ *   Window rows of query i are rows i .. i+w-1 of the window buffer whose position
+ *   pos[b] - (w-1) + r is >= 0 (the w tokens ending at the query's own position).
+ *   With sink == NULL the sigma term is absent; an empty row set then gives out = 0, lse = -inf.
+ * q         [B][Q][H][D] of q_dtype (CSAH_DT_BF16 or CSAH_DT_F32).
+ * cache     [B][cache_seq_stride] rows of fmt (ROW_E4M3_BF16 or ROW_F32), N rows valid.
+ * idx       [B][Q][k] int32 entry ids, -1 = empty slot (ids outside [0, N) are skipped too).
+ * win       [B][win_seq_stride] rows of fmt; win_seq_stride >= w-1+Q. w may be 0 (win unused).
+ * pos       [B] int64 device array, position of query 0.
+ * sink      [H] fp32 logits or NULL. scale: softmax temperature applied to q.y.
+ * out       [B][Q][H][D] fp32; lse [B][Q][H] fp32 or NULL.
+ * ws        at least csah_attend_workspace(B, Q, H, D, k + w) bytes, 256-byte aligned.
+ * Supported: H % 16 == 0; (fmt, D) = (ROW_E4M3_BF16, 512) or (ROW_F32, 128); k + w < 2^31.
+ */
+size_t csah_attend_workspace(int B, int Q, int H, int D, int64_t max_rows);
+int csah_csa_attend(const void* q, int q_dtype, int H, int D, const void* cache, int fmt,
+                    int64_t cache_seq_stride, int64_t N, const int32_t* idx, int k,
+                    const void* win, int64_t win_seq_stride, int w, const int64_t* pos,
+                    const float* sink, float scale, int B, int Q, float* out, float* lse,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csah_hca_attend -- dense attention over every visible compressed entry plus the same window and
+ * sink as csah_csa_attend.
+ *   [EXPL]: HCA is the same design with a much larger group and no sparse selection stage, with
+ *   the same sliding window and shared-KV layout; [LLMB] "2. HCA": dense attention over the
+ *   128x-compressed entries. Query i of sequence b attends to entries g < min(floor((pos[b]+i+1)/m),
+ *   N), then to its window rows and the sink exactly as in csah_csa_attend.
+ * ws        at least csah_attend_workspace(B, Q, H, D, N + w) bytes, 256-byte aligned.
+ * Supported: as csah_csa_attend; m >= 1; N + w < 2^31.
+ */
+int csah_hca_attend(const void* q, int q_dtype, int H, int D, const void* cache, int fmt,
+                    int64_t cache_seq_stride, int64_t N, int m, const void* win,
+                    int64_t win_seq_stride, int w, const int64_t* pos, const float* sink,
+                    float scale, int B, int Q, float* out, float* lse, void* ws, size_t ws_bytes,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSAH_H */

@@ -1,0 +1,212 @@
+"""Python binding of libcsah (include/csah.h): compress-then-sparsify attention on MI355X.
+
+Argument marshalling only. Every step runs in the library's HIP kernels; torch is used to hold
+device memory and to name the current stream. If the library is missing, every call raises.
+
+Tensor conventions (device tensors, C-contiguous unless a stride argument says otherwise):
+  raw        [B, T, D] float32 or bfloat16 tokens
+  rows       [B, S, row_bytes(fmt, D)] uint8 cache rows; scales [B, S, D/32] uint8 (FP4 only)
+  q          [B, Q, H, D] bfloat16 or float32
+  idx        [B, Q, k] int32;  pos [B] int64 (position of query 0)
+  window     [B, w-1+Q, row_bytes] uint8
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsah.so")
+
+OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, LAUNCH = 0, -1, -2, -3, -4
+DT_F32, DT_BF16 = 0, 1
+FMT_ROW_F32, FMT_ROW_E4M3_BF16, FMT_FP4_E8M0 = 0, 1, 2
+
+EXPORTS = ("csah_abi_version", "csah_status_string", "csah_row_bytes", "csah_kv_compress",
+           "csah_index_topk_workspace", "csah_index_topk", "csah_attend_workspace",
+           "csah_csa_attend", "csah_hca_attend")
+
+_lib = None
+
+
+class CsahError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+def lib():
+    """Load libcsah.so (built by build.py); raise if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python long_context_attention_03_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, F, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                            ctypes.c_size_t)
+        sig = {
+            "csah_abi_version": (I, []),
+            "csah_status_string": (ctypes.c_char_p, [I]),
+            "csah_row_bytes": (I64, [I, I]),
+            "csah_kv_compress": (I, [P, I, I64, I, I64, I, I, P, P, P, I, I64, P, P]),
+            "csah_index_topk_workspace": (SZ, [I, I, I64, I, I]),
+            "csah_index_topk": (I, [P, P, I, I, P, P, I64, I64, P, I, I, I, I, P, P, P, SZ, P]),
+            "csah_attend_workspace": (SZ, [I, I, I, I, I64]),
+            "csah_csa_attend": (I, [P, I, I, I, P, I, I64, I64, P, I, P, I64, I, P, P, F, I, I,
+                                    P, P, P, SZ, P]),
+            "csah_hca_attend": (I, [P, I, I, I, P, I, I64, I64, I, P, I64, I, P, P, F, I, I, P,
+                                    P, P, SZ, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().csah_status_string(int(status)).decode()
+
+
+def row_bytes(fmt: int, D: int) -> int:
+    return int(lib().csah_row_bytes(fmt, D))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, st):
+    if st != OK:
+        raise CsahError(fn, st)
+
+
+def _dt(t):
+    if t.dtype == torch.float32:
+        return DT_F32
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _workspace(nbytes: int, device, ws=None):
+    if nbytes == 0:
+        return None
+    if ws is not None and ws.numel() >= nbytes:
+        return ws
+    # 256-byte alignment: torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------- kv_compress
+def kv_compress(raw, m: int, w, beta, out_fmt: int, out_rows=None, out_scales=None, stream=None):
+    """Pool every m tokens of raw [B, T, D] into one encoded entry.
+
+    Returns (rows [B, T/m, row_bytes], scales [B, T/m, D/32] or None). When ``out_rows`` is
+    given it may be a slice of a larger cache (its sequence stride is taken from dim 0).
+    """
+    B, T, D = raw.shape
+    G = T // m
+    if out_rows is None:
+        out_rows = torch.empty((B, G, row_bytes(out_fmt, D)), dtype=torch.uint8, device=raw.device)
+        if out_fmt == FMT_FP4_E8M0:
+            out_scales = torch.empty((B, G, D // 32), dtype=torch.uint8, device=raw.device)
+    out_stride = out_rows.stride(0) // out_rows.stride(1)
+    st = lib().csah_kv_compress(_ptr(raw), _dt(raw), raw.stride(0) // raw.stride(1), B, T, D, m,
+                                _ptr(w), _ptr(beta), _ptr(out_rows), out_fmt, out_stride,
+                                _ptr(out_scales), _stream(stream))
+    _check("csah_kv_compress", st)
+    return out_rows, out_scales
+
+
+# ----------------------------------------------------------------------------- index_topk
+def index_topk_workspace(B: int, Q: int, N: int, k: int, dI: int) -> int:
+    return int(lib().csah_index_topk_workspace(B, Q, N, k, dI))
+
+
+def index_topk(q_codes, q_scales, k_codes, k_scales, pos, m: int, k: int, N: int | None = None,
+               want_scores: bool = True, ws=None, idx_out=None, score_out=None, stream=None):
+    """Top-k entries per query -> (idx int32 [B, Q, k], scores fp32 [B, Q, k] or None)."""
+    B, Q, HI, half = q_codes.shape
+    dI = 2 * half
+    kstride = k_codes.stride(0) // k_codes.stride(1)
+    N = k_codes.shape[1] if N is None else N
+    dev = q_codes.device
+    if idx_out is None:
+        idx_out = torch.empty((B, Q, k), dtype=torch.int32, device=dev)
+    if want_scores and score_out is None:
+        score_out = torch.empty((B, Q, k), dtype=torch.float32, device=dev)
+    need = index_topk_workspace(B, Q, N, k, dI)
+    ws = _workspace(need, dev, ws)
+    st = lib().csah_index_topk(_ptr(q_codes), _ptr(q_scales), HI, dI, _ptr(k_codes),
+                               _ptr(k_scales), kstride, N, _ptr(pos), m, B, Q, k, _ptr(idx_out),
+                               _ptr(score_out), _ptr(ws), need, _stream(stream))
+    _check("csah_index_topk", st)
+    return idx_out, score_out
+
+
+# ----------------------------------------------------------------------------- attention
+def attend_workspace(B: int, Q: int, H: int, D: int, max_rows: int) -> int:
+    return int(lib().csah_attend_workspace(B, Q, H, D, max_rows))
+
+
+def _fmt_of(rows, D):
+    rb = rows.shape[-1]
+    if rb == row_bytes(FMT_ROW_E4M3_BF16, D):
+        return FMT_ROW_E4M3_BF16
+    if rb == row_bytes(FMT_ROW_F32, D):
+        return FMT_ROW_F32
+    raise ValueError(f"row width {rb} matches no row format at D={D}")
+
+
+def csa_attend(q, cache, idx, window, w: int, pos, sink, scale: float, N: int | None = None,
+               ws=None, out=None, lse=None, stream=None):
+    """Sparse attention over cache rows idx + window + sink -> (out fp32 [B,Q,H,D], lse [B,Q,H])."""
+    B, Q, H, D = q.shape
+    fmt = _fmt_of(cache, D)
+    N = cache.shape[1] if N is None else N
+    k = idx.shape[-1]
+    dev = q.device
+    out = torch.empty((B, Q, H, D), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev) if lse is None else lse
+    need = attend_workspace(B, Q, H, D, k + w)
+    ws = _workspace(need, dev, ws)
+    wstride = window.stride(0) // window.stride(1) if w > 0 else 0
+    st = lib().csah_csa_attend(_ptr(q), _dt(q), H, D, _ptr(cache), fmt,
+                               cache.stride(0) // cache.stride(1), N, _ptr(idx), k,
+                               _ptr(window) if w > 0 else None, wstride, w, _ptr(pos), _ptr(sink),
+                               float(scale), B, Q, _ptr(out), _ptr(lse), _ptr(ws), need,
+                               _stream(stream))
+    _check("csah_csa_attend", st)
+    return out, lse
+
+
+def hca_attend(q, cache, m: int, window, w: int, pos, sink, scale: float, N: int | None = None,
+               ws=None, out=None, lse=None, stream=None):
+    """Dense attention over every visible entry + window + sink -> (out, lse)."""
+    B, Q, H, D = q.shape
+    fmt = _fmt_of(cache, D)
+    N = cache.shape[1] if N is None else N
+    dev = q.device
+    out = torch.empty((B, Q, H, D), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev) if lse is None else lse
+    need = attend_workspace(B, Q, H, D, N + w)
+    ws = _workspace(need, dev, ws)
+    wstride = window.stride(0) // window.stride(1) if w > 0 else 0
+    st = lib().csah_hca_attend(_ptr(q), _dt(q), H, D, _ptr(cache), fmt,
+                               cache.stride(0) // cache.stride(1), N, m,
+                               _ptr(window) if w > 0 else None, wstride, w, _ptr(pos), _ptr(sink),
+                               float(scale), B, Q, _ptr(out), _ptr(lse), _ptr(ws), need,
+                               _stream(stream))
+    _check("csah_hca_attend", st)
+    return out, lse

@@ -1,0 +1,162 @@
+// api.hip -- the C ABI declared in include/csah.h: argument validation, workspace sizing, device
+// check and kernel launches. Nothing here allocates device memory or synchronises.
+#include <string.h>
+
+#include <mutex>
+
+#include "csah_internal.h"
+
+using namespace csah;
+
+namespace {
+
+// Validation never touches the HIP runtime; the device check runs only for valid arguments.
+int check_device() {
+  static std::mutex mu;
+  static int cached[64];
+  static bool init[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return CSAH_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!init[dev]) {
+    hipDeviceProp_t prop;
+    int ok = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+             strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    cached[dev] = ok ? CSAH_OK : CSAH_ERR_UNSUPPORTED;
+    init[dev] = true;
+  }
+  return cached[dev];
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? CSAH_OK : CSAH_ERR_LAUNCH; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int row_bytes(int fmt, int D) {
+  if (fmt == CSAH_FMT_ROW_F32) return 4 * D;
+  if (fmt == CSAH_FMT_ROW_E4M3_BF16) return D >= 64 ? D + 64 : -1;
+  if (fmt == CSAH_FMT_FP4_E8M0) return D % 2 == 0 ? D / 2 : -1;
+  return -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csah_abi_version(void) { return CSAH_ABI_VERSION; }
+
+const char* csah_status_string(int status) {
+  switch (status) {
+    case CSAH_OK: return "ok";
+    case CSAH_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case CSAH_ERR_UNSUPPORTED: return "unsupported shape, format or device";
+    case CSAH_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case CSAH_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int64_t csah_row_bytes(int fmt, int D) { return D > 0 ? row_bytes(fmt, D) : -1; }
+
+int csah_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B, int64_t T,
+                     int D, int m, const float* w, const float* beta, void* out_rows, int out_fmt,
+                     int64_t out_seq_stride, uint8_t* out_scales, void* stream) {
+  if (!raw || !w || !beta || !out_rows || B < 0 || T < 0 || D <= 0 || m <= 0)
+    return CSAH_ERR_INVALID_ARGUMENT;
+  if (raw_dtype != CSAH_DT_F32 && raw_dtype != CSAH_DT_BF16) return CSAH_ERR_INVALID_ARGUMENT;
+  if (out_fmt != CSAH_FMT_ROW_F32 && out_fmt != CSAH_FMT_ROW_E4M3_BF16 &&
+      out_fmt != CSAH_FMT_FP4_E8M0)
+    return CSAH_ERR_INVALID_ARGUMENT;
+  if (T % m != 0 || raw_seq_stride < T || out_seq_stride < T / m) return CSAH_ERR_INVALID_ARGUMENT;
+  if ((out_fmt == CSAH_FMT_FP4_E8M0) != (out_scales != nullptr)) return CSAH_ERR_INVALID_ARGUMENT;
+  if (!aligned(raw, 16) || !aligned(out_rows, 16)) return CSAH_ERR_INVALID_ARGUMENT;
+  if (D != 64 && D != 128 && D != 256 && D != 512 && D != 1024) return CSAH_ERR_UNSUPPORTED;
+  if (out_fmt == CSAH_FMT_ROW_E4M3_BF16 && D != 512) return CSAH_ERR_UNSUPPORTED;
+  if (m > 65536) return CSAH_ERR_UNSUPPORTED;
+  int st = check_device();
+  if (st) return st;
+  KvCompressArgs a{raw, raw_dtype, raw_seq_stride, B, T / m, D, m, w, beta, out_rows, out_fmt,
+                   out_seq_stride, out_scales, stream};
+  return launch_status(launch_kv_compress(a));
+}
+
+size_t csah_index_topk_workspace(int B, int Q, int64_t N, int k, int dI) {
+  if (B <= 0 || Q <= 0 || N < 0 || k <= 0) return 0;
+  return index_workspace_bytes(B, Q, N, k, dI);
+}
+
+int csah_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int dI,
+                    const uint8_t* k_codes, const uint8_t* k_scales, int64_t k_seq_stride,
+                    int64_t N, const int64_t* pos, int m, int B, int Q, int k, int32_t* idx_out,
+                    float* score_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!q_codes || !q_scales || !k_codes || !k_scales || !pos || !idx_out || !ws)
+    return CSAH_ERR_INVALID_ARGUMENT;
+  if (HI <= 0 || dI <= 0 || m <= 0 || B <= 0 || Q <= 0 || k <= 0 || N < 0 || k_seq_stride < N)
+    return CSAH_ERR_INVALID_ARGUMENT;
+  if (!aligned(k_codes, 16) || !aligned(ws, 256)) return CSAH_ERR_INVALID_ARGUMENT;
+  if (HI > 16 || (dI != 32 && dI != 64 && dI != 128) || k > 4096 || N >= ((int64_t)1 << 31) ||
+      (int64_t)B * Q >= 65536)
+    return CSAH_ERR_UNSUPPORTED;
+  int st = check_device();
+  if (st) return st;
+  if (ws_bytes < index_workspace_bytes(B, Q, N, k, dI)) return CSAH_ERR_WORKSPACE_TOO_SMALL;
+  IndexArgs a{q_codes, q_scales, HI, dI, k_codes, k_scales, k_seq_stride, N, pos, m, B, Q, k,
+              idx_out, score_out, ws, ws_bytes, stream};
+  return launch_status(launch_index_topk(a));
+}
+
+size_t csah_attend_workspace(int B, int Q, int H, int D, int64_t max_rows) {
+  if (B <= 0 || Q <= 0 || H <= 0 || D <= 0 || max_rows < 0) return 0;
+  return attend_workspace_bytes(B, Q, H, D, max_rows);
+}
+
+static int attend_common(const void* q, int q_dtype, int H, int D, const void* cache, int fmt,
+                         int64_t cache_seq_stride, int64_t N, const int32_t* idx, int k, int m,
+                         const void* win, int64_t win_seq_stride, int w, const int64_t* pos,
+                         const float* sink, float scale, int B, int Q, float* out, float* lse,
+                         void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !cache || !pos || !out || H <= 0 || D <= 0 || B <= 0 || Q <= 0 || N < 0 || w < 0)
+    return CSAH_ERR_INVALID_ARGUMENT;
+  if (q_dtype != CSAH_DT_F32 && q_dtype != CSAH_DT_BF16) return CSAH_ERR_INVALID_ARGUMENT;
+  if (fmt != CSAH_FMT_ROW_F32 && fmt != CSAH_FMT_ROW_E4M3_BF16) return CSAH_ERR_INVALID_ARGUMENT;
+  if (cache_seq_stride < N) return CSAH_ERR_INVALID_ARGUMENT;
+  if (w > 0 && (!win || win_seq_stride < (int64_t)w - 1 + Q)) return CSAH_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(cache, 16) || (w > 0 && !aligned(win, 16)))
+    return CSAH_ERR_INVALID_ARGUMENT;
+  if (!((fmt == CSAH_FMT_ROW_E4M3_BF16 && D == 512) || (fmt == CSAH_FMT_ROW_F32 && D == 128)))
+    return CSAH_ERR_UNSUPPORTED;
+  const int64_t max_rows = (idx ? (int64_t)k : N) + w;
+  if (max_rows >= ((int64_t)1 << 31) || (int64_t)B * Q >= 65536) return CSAH_ERR_UNSUPPORTED;
+  int st = check_device();
+  if (st) return st;
+  const size_t need = attend_workspace_bytes(B, Q, H, D, max_rows);
+  if (need > 0 && (!ws || !aligned(ws, 256))) return need > ws_bytes ? CSAH_ERR_WORKSPACE_TOO_SMALL
+                                                                       : CSAH_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < need) return CSAH_ERR_WORKSPACE_TOO_SMALL;
+  AttendArgs a{q,   q_dtype, H,     D,     cache, fmt, cache_seq_stride, N,        idx,   k,
+               m,   win,     win_seq_stride, w, pos, sink, scale,   B,  Q, out, lse, ws, ws_bytes,
+               stream, max_rows};
+  return launch_status(launch_attend(a));
+}
+
+int csah_csa_attend(const void* q, int q_dtype, int H, int D, const void* cache, int fmt,
+                    int64_t cache_seq_stride, int64_t N, const int32_t* idx, int k,
+                    const void* win, int64_t win_seq_stride, int w, const int64_t* pos,
+                    const float* sink, float scale, int B, int Q, float* out, float* lse,
+                    void* ws, size_t ws_bytes, void* stream) {
+  if (!idx || k < 0) return CSAH_ERR_INVALID_ARGUMENT;
+  return attend_common(q, q_dtype, H, D, cache, fmt, cache_seq_stride, N, idx, k, 1, win,
+                       win_seq_stride, w, pos, sink, scale, B, Q, out, lse, ws, ws_bytes, stream);
+}
+
+int csah_hca_attend(const void* q, int q_dtype, int H, int D, const void* cache, int fmt,
+                    int64_t cache_seq_stride, int64_t N, int m, const void* win,
+                    int64_t win_seq_stride, int w, const int64_t* pos, const float* sink,
+                    float scale, int B, int Q, float* out, float* lse, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (m <= 0) return CSAH_ERR_INVALID_ARGUMENT;
+  return attend_common(q, q_dtype, H, D, cache, fmt, cache_seq_stride, N, nullptr, 0, m, win,
+                       win_seq_stride, w, pos, sink, scale, B, Q, out, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

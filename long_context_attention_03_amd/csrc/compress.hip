@@ -1,0 +1,199 @@
+// compress.hip -- kv_compress: softmax-gated pooling of m consecutive tokens into one entry.
+//
+// [EXPL] "DeepSeek V4 Architecture Explained: CSA, HCA, mHC and Muon", section "How
+// compress-then-sparsify attention works": a group of m consecutive tokens' keys and values is
+// folded into one entry using trainable compression weights, a softmax over the group and
+// learnable positional biases. [LLMB] "Inside DeepSeek-V4 ...", sections "1. Compressed Sparse
+// Attention (CSA)" (factor 4) and "2. Heavily Compressed Attention (HCA)" (factor 128).
+//
+//   z_t = w . x_t + beta[t - g m],  pi = softmax(z),  c_g = sum_t pi_t x_t.
+//
+// One wavefront owns one group. Lane l owns DPL = D/64 consecutive dimensions, so every token
+// row is read with one coalesced vector load per lane. The softmax is evaluated online in one pass
+// over the group (running max, running denominator, running weighted sum), which keeps a group of
+// any size in registers. The gate dot product is a wavefront reduction per token. The pooled row
+// is then encoded in the output format by the same wavefront and written with vector stores.
+// HBM traffic is one read of the raw rows and one write of the compressed rows.
+#include "csah_internal.h"
+#include "device_common.h"
+
+namespace csah {
+
+template <int DPL, bool RAW_BF16>
+__device__ __forceinline__ void load_token(const void* raw, int64_t row, int lane, float* x) {
+  constexpr int D = DPL * 64;
+  if constexpr (RAW_BF16) {
+    const uint16_t* p = (const uint16_t*)raw + row * D + lane * DPL;
+    if constexpr (DPL >= 8) {
+#pragma unroll
+      for (int v = 0; v < DPL / 8; v++) {
+        u32x4 w = *(const u32x4*)(p + 8 * v);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          x[8 * v + 2 * e] = u2f(w[e] << 16);
+          x[8 * v + 2 * e + 1] = u2f(w[e] & 0xFFFF0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL; e++) x[e] = u2f((uint32_t)p[e] << 16);
+    }
+  } else {
+    const float* p = (const float*)raw + row * D + lane * DPL;
+    if constexpr (DPL >= 4) {
+#pragma unroll
+      for (int v = 0; v < DPL / 4; v++) {
+        f32x4 w = *(const f32x4*)(p + 4 * v);
+#pragma unroll
+        for (int e = 0; e < 4; e++) x[4 * v + e] = w[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL; e++) x[e] = p[e];
+    }
+  }
+}
+
+template <int DPL, bool RAW_BF16, int OUT_FMT>
+__global__ __launch_bounds__(256) void kv_compress_kernel(
+    const void* __restrict__ raw, int64_t raw_seq_stride, int B, int64_t G, int m,
+    const float* __restrict__ w, const float* __restrict__ beta, uint8_t* __restrict__ out_rows,
+    int64_t out_seq_stride, uint8_t* __restrict__ out_scales) {
+  constexpr int D = DPL * 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t gid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gid >= (int64_t)B * G) return;
+  const int64_t b = gid / G, g = gid - b * G;
+
+  float wv[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; e++) wv[e] = w[lane * DPL + e];
+
+  float acc[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; e++) acc[e] = 0.0f;
+  float M = -INFINITY, L = 0.0f;
+  const int64_t row0 = b * raw_seq_stride + g * m;
+  for (int t = 0; t < m; t++) {
+    float x[DPL];
+    load_token<DPL, RAW_BF16>(raw, row0 + t, lane, x);
+    float z = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL; e++) z = fmaf(wv[e], x[e], z);
+    z = wave_sum(z) + beta[t];
+    const float Mn = fmaxf(M, z);
+    const float sc = expf(M - Mn);  // 0 on the first token (M = -inf)
+    const float p = expf(z - Mn);
+#pragma unroll
+    for (int e = 0; e < DPL; e++) acc[e] = fmaf(acc[e], sc, p * x[e]);
+    L = fmaf(L, sc, p);
+    M = Mn;
+  }
+  float c[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; e++) c[e] = acc[e] / L;
+
+  const int64_t orow = b * out_seq_stride + g;
+  if constexpr (OUT_FMT == CSAH_FMT_ROW_F32) {
+    float* o = (float*)out_rows + orow * D + lane * DPL;
+#pragma unroll
+    for (int e = 0; e < DPL; e++) o[e] = c[e];
+  } else if constexpr (OUT_FMT == CSAH_FMT_ROW_E4M3_BF16) {
+    // D = 512: lanes 0..55 hold dims 0..447 (E4M3), lanes 56..63 dims 448..511 (bf16).
+    static_assert(DPL == 8, "E4M3+bf16 rows are 512 wide");
+    uint8_t* o = out_rows + orow * (int64_t)(D + 64);
+    if (lane < 56) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 4; e++) lo |= f32_to_e4m3(c[e]) << (8 * e);
+#pragma unroll
+      for (int e = 0; e < 4; e++) hi |= f32_to_e4m3(c[4 + e]) << (8 * e);
+      *(u32x2*)(o + 8 * lane) = u32x2{lo, hi};
+    } else {
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        bf16x2 p2 = {(__bf16)c[2 * e], (__bf16)c[2 * e + 1]};
+        v[e] = __builtin_bit_cast(uint32_t, p2);
+      }
+      *(u32x4*)(o + 448 + 16 * (lane - 56)) = v;
+    }
+  } else {
+    // MX block of 32 dims = 32/DPL lanes; shared exponent floor(log2 amax) - 2.
+    constexpr int LPB = 32 / DPL;
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL; e++) amax = fmaxf(amax, fabsf(c[e]));
+#pragma unroll
+    for (int o = 1; o < LPB; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    int sexp;
+    if (amax == 0.0f) sexp = 0;
+    else {
+      int ef = (int)((f2u(amax) >> 23) & 255u);  // biased exponent (0 for subnormals)
+      sexp = ef - 127 - 2;
+      sexp = sexp < -127 ? -127 : (sexp > 127 ? 127 : sexp);
+    }
+    uint8_t* o = out_rows + orow * (int64_t)(D / 2) + lane * (DPL / 2);
+    uint32_t packed[DPL / 2 > 0 ? DPL / 2 : 1];
+    uint32_t nib[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; e++) nib[e] = f32_to_e2m1(ldexpf(c[e], -sexp));
+    if constexpr (DPL == 1) {
+      // two lanes share a byte: the even lane writes (own | neighbour << 4)
+      uint32_t other = (uint32_t)__shfl_xor((int)nib[0], 1, 64);
+      if ((lane & 1) == 0) out_rows[orow * (int64_t)(D / 2) + lane / 2] = (uint8_t)(nib[0] | (other << 4));
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPL / 2; e++) packed[e] = nib[2 * e] | (nib[2 * e + 1] << 4);
+#pragma unroll
+      for (int e = 0; e < DPL / 2; e++) o[e] = (uint8_t)packed[e];
+    }
+    if (lane % LPB == 0) out_scales[orow * (int64_t)(D / 32) + lane / LPB] = (uint8_t)(sexp + 127);
+  }
+}
+
+template <int DPL, bool RAW_BF16>
+static hipError_t launch_dpl(const KvCompressArgs& a) {
+  const int64_t groups = (int64_t)a.B * a.G;
+  dim3 grid((unsigned)((groups + 3) / 4)), block(256);
+  hipStream_t s = (hipStream_t)a.stream;
+  switch (a.out_fmt) {
+    case CSAH_FMT_ROW_F32:
+      kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_F32><<<grid, block, 0, s>>>(
+          a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.w, a.beta, (uint8_t*)a.out_rows,
+          a.out_seq_stride, a.out_scales);
+      break;
+    case CSAH_FMT_ROW_E4M3_BF16:
+      if constexpr (DPL == 8)
+        kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_E4M3_BF16><<<grid, block, 0, s>>>(
+            a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.w, a.beta, (uint8_t*)a.out_rows,
+            a.out_seq_stride, a.out_scales);
+      else
+        return hipErrorInvalidValue;
+      break;
+    default:
+      kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_FP4_E8M0><<<grid, block, 0, s>>>(
+          a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.w, a.beta, (uint8_t*)a.out_rows,
+          a.out_seq_stride, a.out_scales);
+  }
+  return hipGetLastError();
+}
+
+template <bool RAW_BF16>
+static hipError_t launch_raw(const KvCompressArgs& a) {
+  switch (a.D) {
+    case 64: return launch_dpl<1, RAW_BF16>(a);
+    case 128: return launch_dpl<2, RAW_BF16>(a);
+    case 256: return launch_dpl<4, RAW_BF16>(a);
+    case 512: return launch_dpl<8, RAW_BF16>(a);
+    case 1024: return launch_dpl<16, RAW_BF16>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_kv_compress(const KvCompressArgs& a) {
+  if (a.B == 0 || a.G == 0) return hipSuccess;
+  return a.raw_dtype == CSAH_DT_BF16 ? launch_raw<true>(a) : launch_raw<false>(a);
+}
+
+}  // namespace csah

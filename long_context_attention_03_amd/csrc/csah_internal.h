@@ -1,0 +1,81 @@
+// csah_internal.h -- launch descriptors shared between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "csah.h"
+
+namespace csah {
+
+struct KvCompressArgs {
+  const void* raw;
+  int raw_dtype;
+  int64_t raw_seq_stride;
+  int B;
+  int64_t G;  // groups per sequence = T / m
+  int D, m;
+  const float* w;
+  const float* beta;
+  void* out_rows;
+  int out_fmt;
+  int64_t out_seq_stride;
+  uint8_t* out_scales;
+  void* stream;
+};
+hipError_t launch_kv_compress(const KvCompressArgs& a);
+
+// ---- index_topk --------------------------------------------------------------------------------
+struct IndexArgs {
+  const uint8_t* q_codes;
+  const uint8_t* q_scales;
+  int HI, dI;
+  const uint8_t* k_codes;
+  const uint8_t* k_scales;
+  int64_t k_seq_stride, N;
+  const int64_t* pos;
+  int m, B, Q, k;
+  int32_t* idx_out;
+  float* score_out;
+  void* ws;
+  size_t ws_bytes;
+  void* stream;
+};
+size_t index_workspace_bytes(int B, int Q, int64_t N, int k, int dI);
+hipError_t launch_index_topk(const IndexArgs& a);
+
+// ---- attention ---------------------------------------------------------------------------------
+struct AttendPlan {
+  int splits;          // row splits per (sequence, query, head group)
+  int rows_per_split;  // multiple of the 32-row tile
+  int head_groups;     // ceil(H / 16)
+};
+AttendPlan attend_plan(int B, int Q, int H, int D, int64_t max_rows);
+size_t attend_workspace_bytes(int B, int Q, int H, int D, int64_t max_rows);
+
+struct AttendArgs {
+  const void* q;
+  int q_dtype, H, D;
+  const void* cache;
+  int fmt;
+  int64_t cache_seq_stride, N;
+  const int32_t* idx;  // NULL: dense (HCA) over g < floor((pos+i+1)/m)
+  int k, m;
+  const void* win;
+  int64_t win_seq_stride;
+  int w;
+  const int64_t* pos;
+  const float* sink;
+  float scale;
+  int B, Q;
+  float* out;
+  float* lse;
+  void* ws;
+  size_t ws_bytes;
+  void* stream;
+  int64_t max_rows;
+};
+hipError_t launch_attend(const AttendArgs& a);
+
+}  // namespace csah

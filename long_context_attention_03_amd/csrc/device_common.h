@@ -1,0 +1,108 @@
+// device_common.h -- gfx950 device helpers shared by the library's kernels (not by the oracle).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csah {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float u2f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t f2u(float f) { return __float_as_uint(f); }
+
+// 2^(e-127) for an E8M0 byte, as binary32 (e = 0 is the subnormal 2^-127, 255 is NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  e &= 255u;
+  uint32_t bits = e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : (e << 23));
+  return u2f(bits);
+}
+
+// Two E2M1 elements of byte `sel` (low nibble first) as fp32, unscaled.
+template <int SEL>
+__device__ __forceinline__ f32x2 fp4x2_to_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
+}
+
+// Monotone map of binary32 onto uint32 (larger float -> larger key); -0 must be folded first.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = f2u(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return u2f((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+// Butterfly add across lanes lane ^ 1 and lane ^ 2 (DPP quad permutes).
+__device__ __forceinline__ float quad_xor1_add(float v) {
+  int t = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  return v + __int_as_float(t);
+}
+__device__ __forceinline__ float quad_xor2_add(float v) {
+  int t = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  return v + __int_as_float(t);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int o) { return __shfl_xor(v, o, 64); }
+
+// 64-bit lane mask of lanes whose predicate holds.
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  uint32_t lo = __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u);
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), lo);
+}
+
+// ---- encoders used by the compressor (independent of any host code) ------------------------
+
+// binary32 -> OCP E4M3 (bias 7, max 448), round to nearest even, saturating; NaN -> 0x7F.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+  uint32_t u = f2u(f);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = fabsf(f);
+  if (!(a == a)) return 0x7Fu;
+  if (a >= 464.0f) return sign | 0x7Eu;        // at or above the midpoint to 512: saturate
+  if (a < 0.015625f) {                         // below 2^-6: subnormal grid of step 2^-9
+    uint32_t q = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8; 8 is the smallest normal
+    return sign | q;
+  }
+  uint32_t ua = f2u(a);
+  uint32_t r = (ua + 0x7FFFFu + ((ua >> 20) & 1u)) >> 20;  // keep 3 mantissa bits, ties to even
+  uint32_t code = r - ((127u - 7u) << 3);
+  if (code > 0x7Eu) code = 0x7Eu;
+  return sign | code;
+}
+
+// E2M1 code of a value already divided by its block scale; ties to even, saturating at 6.
+__device__ __forceinline__ uint32_t f32_to_e2m1(float r) {
+  uint32_t sign = (f2u(r) >> 28) & 0x8u;
+  float a = fabsf(r);
+  uint32_t code;
+  if (a < 2.0f) {
+    code = (uint32_t)__builtin_rintf(a * 2.0f);           // 0,0.5,1,1.5,2 -> codes 0..4
+  } else if (a < 4.0f) {
+    code = (uint32_t)__builtin_rintf(a) + 2u;              // 2,3,4 -> codes 4,5,6
+  } else {
+    float q = __builtin_rintf(a * 0.5f);                   // 4,6,8 -> 2,3,4
+    code = q >= 3.0f ? 7u : 6u;                            // 8 saturates to 6
+  }
+  return sign | code;
+}
+
+}  // namespace csah

@@ -1,0 +1,411 @@
+// index_topk.hip -- FP4 lightning-indexer scan and exact top-k selection.
+//
+// [EXPL] "DeepSeek V4 Architecture Explained: CSA, HCA, mHC and Muon", section "How
+// compress-then-sparsify attention works": indexer queries are scored against compressed indexer
+// keys and each query keeps its top-k entries. [LLMB] "Inside DeepSeek-V4 ...", section
+// "1. Compressed Sparse Attention (CSA)": an FP4 indexer computes coarse relevance scores and keeps
+// the top 1,024 compressed blocks. [BSWEN] "How DeepSeek V4 Handles 1M Token Context with Hybrid
+// Attention", section "Component 3: DeepSeek Sparse Attention (DSA)": score every compressed entry,
+// select the top k, attend only to those.
+//
+// Score of entry g:  sum_h sum_b 2^(Eq_hb+Ek_gb-254) sum_{i in b} e2m1(q_hi) e2m1(k_gi).
+// Because the heads are combined by a plain sum, the score is one dot product of the key with the
+// head-summed query qt_i = sum_h 2^(Eq_h,b(i)-127) e2m1(q_hi), scaled per key block:
+//   score_g = sum_b 2^(Ek_gb-127) sum_{i in b} qt_i e2m1(k_gi).
+// Every term is a partial sum of the exact products, so when the products' absolute sum spans
+// fewer than 24 bits of the finest granularity each fp32 operation is exact: the result is the
+// exact score in any order, and the selection below is bit-exact.
+//
+// Pipeline per (sequence, query) "slot":
+//   prep      qt (fp32, dI values) + clear the histogram / counters        (1 WG per slot)
+//   scan      stream the FP4 keys (coalesced 16-byte loads, one 32-element block per lane,
+//             dI/32 lanes per entry), write fp32 scores, build a 2048-bin histogram of the top
+//             11 bits of each score's order key in LDS, flush it with global atomics
+//   collect   find the bin holding the k-th largest score; entries above it ("sure") and in it
+//             ("tie") are appended with one atomic per wavefront, as 64-bit keys
+//             (order_key(score) << 32 | ~g), unique per entry
+//   finalize  one WG per slot: bitonic sort of the candidates in LDS (descending key = score
+//             descending, index ascending); a radix select over the tie list first when the
+//             candidates exceed LDS (massive ties)
+#include "csah_internal.h"
+#include "device_common.h"
+
+namespace csah {
+
+constexpr int kBins = 2048;
+constexpr int kBinShift = 21;  // top 11 bits of the order key
+constexpr int kSortCap = 4096;
+
+struct IdxWs {
+  char* base;
+  size_t slot_bytes, off_hist, off_ctr, off_scores, off_sure, off_tie;
+  __device__ char* slot(int s) const { return base + (size_t)s * slot_bytes; }
+  __device__ float* qt(int s) const { return (float*)slot(s); }
+  __device__ uint32_t* hist(int s) const { return (uint32_t*)(slot(s) + off_hist); }
+  __device__ uint32_t* ctr(int s) const { return (uint32_t*)(slot(s) + off_ctr); }
+  __device__ float* scores(int s) const { return (float*)(slot(s) + off_scores); }
+  __device__ uint64_t* sure(int s) const { return (uint64_t*)(slot(s) + off_sure); }
+  __device__ uint64_t* tie(int s) const { return (uint64_t*)(slot(s) + off_tie); }
+};
+
+static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static IdxWs make_ws(void* base, int64_t N, int k) {
+  IdxWs w;
+  w.base = (char*)base;
+  w.off_hist = al256(128 * sizeof(float));
+  w.off_ctr = w.off_hist + al256(kBins * sizeof(uint32_t));
+  w.off_scores = w.off_ctr + 256;
+  w.off_sure = w.off_scores + al256((size_t)N * sizeof(float));
+  w.off_tie = w.off_sure + al256((size_t)k * sizeof(uint64_t));
+  w.slot_bytes = w.off_tie + al256((size_t)N * sizeof(uint64_t));
+  return w;
+}
+
+size_t index_workspace_bytes(int B, int Q, int64_t N, int k, int dI) {
+  (void)dI;
+  IdxWs w = make_ws(nullptr, N, k);
+  return (size_t)B * (size_t)Q * w.slot_bytes;
+}
+
+__device__ __forceinline__ int64_t visible_entries(const int64_t* pos, int b, int i, int m,
+                                                   int64_t N) {
+  int64_t nv = (pos[b] + i + 1) / m;
+  return nv < 0 ? 0 : (nv > N ? N : nv);
+}
+
+// ---- prep: head-summed query and cleared counters ---------------------------------------------
+__global__ __launch_bounds__(256) void index_prep_kernel(const uint8_t* __restrict__ q_codes,
+                                                          const uint8_t* __restrict__ q_scales,
+                                                          int HI, int dI, IdxWs ws) {
+  const int slot = blockIdx.x, t = threadIdx.x;
+  if (t < dI) {
+    float acc = 0.0f;
+    for (int h = 0; h < HI; h++) {
+      const uint32_t byte = q_codes[((int64_t)slot * HI + h) * (dI / 2) + t / 2];
+      const f32x2 v = fp4x2_to_f32<0>(byte);
+      const float s = e8m0_to_f32(q_scales[((int64_t)slot * HI + h) * (dI / 32) + t / 32]);
+      acc += ((t & 1) ? v[1] : v[0]) * s;
+    }
+    ws.qt(slot)[t] = acc;
+  }
+  uint32_t* h = ws.hist(slot);
+  for (int j = t; j < kBins; j += 256) h[j] = 0u;
+  if (t < 64) ws.ctr(slot)[t] = 0u;
+}
+
+// ---- scan --------------------------------------------------------------------------------------
+template <int NB>
+__device__ __forceinline__ float block_dot(const u32x4 c, const float* qv) {
+  float t = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    f32x2 v0 = fp4x2_to_f32<0>(c[j]);
+    f32x2 v1 = fp4x2_to_f32<1>(c[j]);
+    f32x2 v2 = fp4x2_to_f32<2>(c[j]);
+    f32x2 v3 = fp4x2_to_f32<3>(c[j]);
+    t = fmaf(v0[0], qv[8 * j + 0], t);
+    t = fmaf(v0[1], qv[8 * j + 1], t);
+    t = fmaf(v1[0], qv[8 * j + 2], t);
+    t = fmaf(v1[1], qv[8 * j + 3], t);
+    t = fmaf(v2[0], qv[8 * j + 4], t);
+    t = fmaf(v2[1], qv[8 * j + 5], t);
+    t = fmaf(v3[0], qv[8 * j + 6], t);
+    t = fmaf(v3[1], qv[8 * j + 7], t);
+  }
+  return t;
+}
+
+template <int NB, int U>
+__global__ __launch_bounds__(256) void index_scan_kernel(
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
+    int64_t k_seq_stride, int64_t N, const int64_t* __restrict__ pos, int m, int Q, int chunk,
+    IdxWs ws) {
+  constexpr int EPR = 256 / NB;  // entries per WG row of lanes
+  const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
+  const int tid = threadIdx.x, sub = tid % NB, ent = tid / NB;
+  __shared__ uint32_t hist[kBins];
+  for (int j = tid; j < kBins; j += 256) hist[j] = 0u;
+  __syncthreads();
+
+  const int64_t nv = visible_entries(pos, b, i, m, N);
+  const int64_t g0 = (int64_t)blockIdx.x * chunk;
+  const int64_t g1 = g0 + chunk < nv ? g0 + chunk : nv;
+  if (g0 < nv) {
+    float qv[32];
+    const float* qt = ws.qt(slot) + 32 * sub;
+#pragma unroll
+    for (int j = 0; j < 32; j++) qv[j] = qt[j];
+    const uint8_t* kc = k_codes + (int64_t)b * k_seq_stride * (16 * NB) + 16 * sub;
+    const uint8_t* ks = k_scales + (int64_t)b * k_seq_stride * NB + sub;
+    float* sc = ws.scores(slot);
+    for (int64_t gb = g0 + ent; gb < g1; gb += (int64_t)EPR * U) {
+      u32x4 c[U];
+      uint32_t e[U];
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int64_t g = gb + (int64_t)u * EPR;
+        if (g < g1) {
+          c[u] = __builtin_nontemporal_load((const u32x4*)(kc + g * (16 * NB)));
+          e[u] = ks[g * NB];
+        } else {
+          c[u] = u32x4{0, 0, 0, 0};
+          e[u] = 127;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int64_t g = gb + (int64_t)u * EPR;
+        float s = block_dot<NB>(c[u], qv) * e8m0_to_f32(e[u]);
+        if constexpr (NB >= 2) s = quad_xor1_add(s);
+        if constexpr (NB >= 4) s = quad_xor2_add(s);
+        s = s + 0.0f;  // fold -0 into +0: equal scores must get equal keys
+        if (sub == 0 && g < g1) {
+          sc[g] = s;
+          atomicAdd(&hist[order_key(s) >> kBinShift], 1u);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = ws.hist(slot);
+  for (int j = tid; j < kBins; j += 256) {
+    const uint32_t c = hist[j];
+    if (c) atomicAdd(&gh[j], c);
+  }
+}
+
+// ---- threshold + candidate collection ----------------------------------------------------------
+__device__ void find_threshold_bin(const uint32_t* __restrict__ gh, int64_t kk, uint32_t* h,
+                                   uint32_t* suf, int* out_bin, uint32_t* out_above) {
+  // h: kBins counts, suf: 256 partial sums (8 bins per thread), both in LDS.
+  const int t = threadIdx.x;
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < kBins / 256; j++) {
+    const uint32_t c = gh[t * (kBins / 256) + j];
+    h[t * (kBins / 256) + j] = c;
+    local += c;
+  }
+  suf[t] = local;
+  __syncthreads();
+  // inclusive suffix sum over the 256 groups (Hillis-Steele)
+  for (int o = 1; o < 256; o <<= 1) {
+    const uint32_t add = (t + o < 256) ? suf[t + o] : 0u;
+    __syncthreads();
+    suf[t] += add;
+    __syncthreads();
+  }
+  const uint32_t mine = suf[t];
+  const uint32_t next = t < 255 ? suf[t + 1] : 0u;
+  if ((int64_t)mine >= kk && (int64_t)next < kk) {
+    uint32_t above = next;
+    int bin = t * (kBins / 256);
+    for (int j = kBins / 256 - 1; j >= 0; j--) {
+      const uint32_t c = h[t * (kBins / 256) + j];
+      if ((int64_t)(above + c) >= kk) { bin = t * (kBins / 256) + j; break; }
+      above += c;
+    }
+    *out_bin = bin;
+    *out_above = above;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void wave_append(bool p, uint64_t key, uint32_t* counter,
+                                            uint64_t* list, uint64_t cap) {
+  const uint64_t mask = ballot64(p);
+  if (!mask) return;
+  const int lane = threadIdx.x & 63;
+  const int leader = __builtin_ctzll(mask);
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(counter, (uint32_t)__builtin_popcountll(mask));
+  base = (uint32_t)__shfl((int)base, leader, 64);
+  if (p) {
+    const uint64_t at = (uint64_t)base + lanes_below(mask);
+    if (at < cap) list[at] = key;
+  }
+}
+
+__global__ __launch_bounds__(256) void index_collect_kernel(const int64_t* __restrict__ pos, int m,
+                                                             int Q, int64_t N, int k, int chunk,
+                                                             IdxWs ws) {
+  const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
+  const int64_t nv = visible_entries(pos, b, i, m, N);
+  const int64_t kk = nv < k ? nv : k;
+  const int64_t g0 = (int64_t)blockIdx.x * chunk;
+  if (kk == 0 || g0 >= nv) return;
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t suf[256];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_above;
+  find_threshold_bin(ws.hist(slot), kk, h, suf, &s_bin, &s_above);
+  const uint32_t bstar = (uint32_t)s_bin;
+  const int64_t g1 = g0 + chunk < nv ? g0 + chunk : nv;
+  const float* sc = ws.scores(slot);
+  uint32_t* ctr = ws.ctr(slot);
+  for (int64_t gb = g0; gb < g1; gb += 256) {
+    const int64_t g = gb + threadIdx.x;
+    bool sure = false, tie = false;
+    uint64_t key = 0;
+    if (g < g1) {
+      const uint32_t ok = order_key(sc[g]);
+      const uint32_t bin = ok >> kBinShift;
+      sure = bin > bstar;
+      tie = bin == bstar;
+      key = ((uint64_t)ok << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)g);
+    }
+    wave_append(sure, key, &ctr[0], ws.sure(slot), (uint64_t)k);
+    wave_append(tie, key, &ctr[1], ws.tie(slot), (uint64_t)N);
+  }
+}
+
+// ---- finalize ----------------------------------------------------------------------------------
+__device__ void bitonic_sort_desc(uint64_t* s, int n) {
+  // n: power of two; 1024 threads
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = threadIdx.x; t < n / 2; t += blockDim.x) {
+        const int a = 2 * t - (t & (stride - 1));
+        const int c = a + stride;
+        const uint64_t x = s[a], y = s[c];
+        const bool desc = (a & size) == 0;
+        if (desc ? (x < y) : (x > y)) { s[a] = y; s[c] = x; }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void index_finalize_kernel(const int64_t* __restrict__ pos,
+                                                               int m, int Q, int64_t N, int k,
+                                                               int32_t* __restrict__ idx_out,
+                                                               float* __restrict__ score_out,
+                                                               IdxWs ws) {
+  const int slot = blockIdx.x, b = slot / Q, i = slot - b * Q;
+  const int t = threadIdx.x;
+  const int64_t nv = visible_entries(pos, b, i, m, N);
+  const int kk = (int)(nv < k ? nv : k);
+  __shared__ uint64_t keys[kSortCap];
+  __shared__ uint32_t dh[256];
+  __shared__ uint64_t s_prefix, s_pmask;
+  __shared__ uint32_t s_r, s_cnt;
+  int32_t* io = idx_out + (int64_t)slot * k;
+  float* so = score_out ? score_out + (int64_t)slot * k : nullptr;
+  if (kk == 0) {
+    for (int j = t; j < k; j += blockDim.x) {
+      io[j] = -1;
+      if (so) so[j] = -INFINITY;
+    }
+    return;
+  }
+  const uint32_t* ctr = ws.ctr(slot);
+  uint32_t ns = ctr[0], nt = ctr[1];
+  ns = ns > (uint32_t)kk ? (uint32_t)kk : ns;
+  nt = (int64_t)nt > N ? (uint32_t)N : nt;
+  const uint64_t* sure = ws.sure(slot);
+  const uint64_t* tie = ws.tie(slot);
+  int n;
+  if (ns + nt <= (uint32_t)kSortCap) {
+    n = (int)(ns + nt);
+    for (int j = t; j < n; j += blockDim.x) keys[j] = j < (int)ns ? sure[j] : tie[j - ns];
+  } else {
+    // radix select the r-th largest tie key (keys are unique), 8 bits at a time below the bin
+    if (t == 0) {
+      s_r = (uint32_t)kk - ns;
+      s_prefix = 0;
+      s_pmask = 0;
+    }
+    __syncthreads();
+    for (int shift = 45;; shift = shift > 8 ? shift - 8 : 0) {
+      const int width = shift >= 5 ? 8 : 5;
+      const uint64_t dmask = ((uint64_t)1 << width) - 1;
+      for (int j = t; j < 256; j += blockDim.x) dh[j] = 0;
+      __syncthreads();
+      const uint64_t pm = s_pmask, pv = s_prefix;
+      for (uint32_t j = t; j < nt; j += blockDim.x) {
+        const uint64_t x = tie[j];
+        if ((x & pm) == pv) atomicAdd(&dh[(x >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      if (t == 0) {
+        uint32_t r = s_r, cum = 0;
+        int d = (int)dmask;
+        for (; d > 0; d--) {
+          if (cum + dh[d] >= r) break;
+          cum += dh[d];
+        }
+        s_r = r - cum;
+        s_prefix = pv | ((uint64_t)d << shift);
+        s_pmask = pm | (dmask << shift);
+      }
+      __syncthreads();
+      if (shift == 0) break;
+    }
+    // bits above 53 are the (shared) bin: compare the low 53 bits only
+    const uint64_t low = ((uint64_t)1 << 53) - 1;
+    const uint64_t thr = s_prefix;
+    if (t == 0) s_cnt = 0;
+    __syncthreads();
+    for (int j = t; j < (int)ns; j += blockDim.x) keys[j] = sure[j];
+    for (uint32_t j = t; j < nt; j += blockDim.x) {
+      const uint64_t x = tie[j];
+      if ((x & low) >= thr) {
+        const uint32_t at = atomicAdd(&s_cnt, 1u);
+        if (ns + at < (uint32_t)kSortCap) keys[ns + at] = x;
+      }
+    }
+    __syncthreads();
+    n = (int)(ns + (s_cnt < (uint32_t)kSortCap - ns ? s_cnt : (uint32_t)kSortCap - ns));
+  }
+  int p2 = 2;
+  while (p2 < n) p2 <<= 1;
+  for (int j = n + t; j < p2; j += blockDim.x) keys[j] = 0;
+  __syncthreads();
+  bitonic_sort_desc(keys, p2);
+  for (int j = t; j < k; j += blockDim.x) {
+    if (j < kk && j < n) {
+      const uint64_t x = keys[j];
+      io[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)x);
+      if (so) so[j] = key_to_float((uint32_t)(x >> 32));
+    } else {
+      io[j] = -1;
+      if (so) so[j] = -INFINITY;
+    }
+  }
+}
+
+template <int NB>
+static void launch_scan(const IndexArgs& a, const IdxWs& w, int chunk, dim3 grid, hipStream_t s) {
+  index_scan_kernel<NB, 4><<<grid, 256, 0, s>>>(a.k_codes, a.k_scales, a.k_seq_stride, a.N, a.pos,
+                                                a.m, a.Q, chunk, w);
+}
+
+hipError_t launch_index_topk(const IndexArgs& a) {
+  hipStream_t s = (hipStream_t)a.stream;
+  const int slots = a.B * a.Q;
+  IdxWs w = make_ws(a.ws, a.N, a.k);
+  index_prep_kernel<<<slots, 256, 0, s>>>(a.q_codes, a.q_scales, a.HI, a.dI, w);
+  // scan: about 2048 workgroups in total, each streaming a contiguous range of entries
+  const int64_t total = (int64_t)slots * (a.N > 0 ? a.N : 1);
+  int64_t chunk = (total + 2047) / 2048;
+  chunk = ((chunk + 1023) / 1024) * 1024;
+  if (chunk < 1024) chunk = 1024;
+  if (chunk > (1 << 20)) chunk = 1 << 20;
+  const int64_t nchunks = a.N > 0 ? (a.N + chunk - 1) / chunk : 1;
+  dim3 gs((unsigned)nchunks, (unsigned)slots);
+  switch (a.dI) {
+    case 32: launch_scan<1>(a, w, (int)chunk, gs, s); break;
+    case 64: launch_scan<2>(a, w, (int)chunk, gs, s); break;
+    default: launch_scan<4>(a, w, (int)chunk, gs, s); break;
+  }
+  const int64_t cchunk = 16384;
+  const int64_t ncc = a.N > 0 ? (a.N + cchunk - 1) / cchunk : 1;
+  index_collect_kernel<<<dim3((unsigned)ncc, (unsigned)slots), 256, 0, s>>>(a.pos, a.m, a.Q, a.N,
+                                                                             a.k, (int)cchunk, w);
+  index_finalize_kernel<<<slots, 1024, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, a.idx_out, a.score_out,
+                                               w);
+  return hipGetLastError();
+}
+
+}  // namespace csah

@@ -134,15 +134,27 @@ def row_bytes(fmt: int, D: int) -> int:
     return int(lib().oc_row_bytes(fmt, D))
 
 
-def encode_rows(x, fmt: int):
-    """x: [..., D] real values -> (rows uint8 [..., row_bytes], scales uint8 [..., D/32] | None)."""
-    x = _c(x, np.float64)
+def encode_rows(x, fmt: int, chunk_rows: int = 1 << 16):
+    """x: [..., D] real values -> (rows uint8 [..., row_bytes], scales uint8 [..., D/32] | None).
+
+    Large inputs are converted to fp64 in chunks of ``chunk_rows`` rows.
+    """
+    x = np.asarray(x)
     D = x.shape[-1]
     lead = x.shape[:-1]
     n = int(np.prod(lead)) if lead else 1
-    rows = np.zeros(lead + (row_bytes(fmt, D),), np.uint8)
-    scales = np.zeros(lead + (D // 32,), np.uint8) if fmt == FMT_FP4_E8M0 else None
-    _check(lib().oc_encode_rows(_p(x), n, D, fmt, _p(rows), _p(scales)), "encode_rows")
+    flat = x.reshape(n, D)
+    rows = np.zeros((n, row_bytes(fmt, D)), np.uint8)
+    scales = np.zeros((n, D // 32), np.uint8) if fmt == FMT_FP4_E8M0 else None
+    for r0 in range(0, n, chunk_rows):
+        r1 = min(n, r0 + chunk_rows)
+        xc = _c(flat[r0:r1], np.float64)
+        rc = rows[r0:r1]
+        sc = None if scales is None else scales[r0:r1]
+        _check(lib().oc_encode_rows(_p(xc), r1 - r0, D, fmt, _p(rc), _p(sc)), "encode_rows")
+    rows = rows.reshape(lead + (rows.shape[-1],))
+    if scales is not None:
+        scales = scales.reshape(lead + (D // 32,))
     return rows, scales
 
 

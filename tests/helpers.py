@@ -1,0 +1,171 @@
+"""Shared builders for the GPU parity tests.
+
+Inputs are drawn on the CPU (long_context_attention_03_amd.synth), encoded with the oracle's codecs
+and copied to the GPU, so both sides see identical bytes. Nothing here reads GPU results back into
+an oracle input.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+from long_context_attention_03_amd import synth
+
+ATOL = 1e-3
+RTOL = 1e-3
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def dev(a):
+    """numpy -> cuda tensor (uint16 bf16 bits come back as bfloat16)."""
+    if isinstance(a, np.ndarray) and a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    if isinstance(a, np.ndarray):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return a.cuda()
+
+
+def assert_close(gpu, ref, what: str, atol=ATOL, rtol=RTOL):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    both_inf = np.isinf(gpu) & np.isinf(ref) & (np.sign(gpu) == np.sign(ref))
+    err = np.abs(gpu - ref)
+    lim = atol + rtol * np.abs(ref)
+    bad = ~both_inf & ~(err <= lim)
+    worst = float(np.max(np.where(both_inf, 0, err / lim))) if gpu.size else 0.0
+    say(f"  {what}: max err/tol = {worst:.3g} over {gpu.size} values")
+    assert not bad.any(), f"{what}: {int(bad.sum())} values outside atol=rtol=1e-3 (worst {worst})"
+
+
+class DecodeCase:
+    """One decode step (one query per sequence unless Q > 1) of a workload, encoded on demand."""
+
+    def __init__(self, name: str, B=None, N=None, Q=1, pos=None, seed=None, H=None):
+        wl = synth.WORKLOADS[name]
+        if Q != wl.Q or H is not None:
+            import dataclasses
+            wl = dataclasses.replace(wl, Q=Q, H=H if H is not None else wl.H)
+        self.wl = wl
+        self._v = synth.decode_inputs(wl, "cpu", B=B, n_entries=N, seed=seed)
+        v = self._v
+        self.B, self.N = v["cache"].shape[0], v["cache"].shape[1]
+        self.m = wl.m_csa or wl.m_hca
+        self.fmt = O.FMT_ROW_E4M3_BF16 if wl.row_fmt == 1 else O.FMT_ROW_F32
+        self.q = bf16_bits(v["q"]) if wl.q_dtype == 1 else v["q"].numpy()
+        self.sink = v["sink"].numpy()
+        if pos is None:
+            pos = self.N * self.m - Q  # the last query sees every entry
+        self.pos = np.full(self.B, pos, np.int64) if np.isscalar(pos) else np.asarray(pos, np.int64)
+        self.scale = wl.scale
+        self._enc = {}
+
+    def _get(self, key):
+        if key not in self._enc:
+            v = self._v
+            if key == "cache":
+                self._enc[key] = O.encode_rows(v["cache"].numpy(), self.fmt)[0]
+            elif key == "window":
+                self._enc[key] = O.encode_rows(v["window"].numpy(), self.fmt)[0]
+            elif key in ("kc", "ks"):
+                self._enc["kc"], self._enc["ks"] = O.encode_rows(v["ikeys"].numpy(), O.FMT_FP4_E8M0)
+            elif key in ("qc", "qs"):
+                self._enc["qc"], self._enc["qs"] = O.encode_rows(v["iq"].numpy(), O.FMT_FP4_E8M0)
+        return self._enc[key]
+
+    cache = property(lambda self: self._get("cache"))
+    window = property(lambda self: self._get("window"))
+    kc = property(lambda self: self._get("kc"))
+    ks = property(lambda self: self._get("ks"))
+    qc = property(lambda self: self._get("qc"))
+    qs = property(lambda self: self._get("qs"))
+
+    def gpu(self, *names):
+        return [dev(getattr(self, n)) for n in names]
+
+
+def pooling_tolerance(x, m: int, pre):
+    """Bound on |fp32 pooled value - fp64 pooled value| for kv_compress, per element.
+
+    The GPU pools in one fp32 pass (online softmax over the m tokens), so its error is a few
+    units of binary32 round-off per step times the group's magnitudes, plus a relative 1e-5 for
+    the softmax weights: (m + 16) * 2^-23 * max_t |x_t,d| + 1e-5 |c_d|.
+    """
+    x = np.abs(np.asarray(x, np.float64))
+    B, T, D = x.shape
+    gmax = x.reshape(B, T // m, m, D).max(axis=2)
+    return (m + 16) * 2.0 ** -23 * gmax + 1e-5 * np.abs(pre)
+
+
+def midpoint_ok(v: float, a: float, b: float, tol: float) -> bool:
+    """a and b are neighbours and v is within tol of their midpoint (fp32 vs fp64 rounding)."""
+    mid = 0.5 * (a + b)
+    return abs(v - mid) <= tol
+
+
+def check_rows_e4m3_bf16(gpu_rows, ref_rows, pre, tol):
+    """Encoded rows must match byte for byte except where the fp64 value lies within the fp32
+    pooling error of a rounding midpoint."""
+    gpu_rows = np.asarray(gpu_rows).reshape(-1, 576)
+    ref_rows = np.asarray(ref_rows).reshape(-1, 576)
+    pre = np.asarray(pre).reshape(-1, 512)
+    tol = np.asarray(tol).reshape(-1, 512)
+    diff = np.nonzero(gpu_rows[:, :448] != ref_rows[:, :448])
+    for r, d in zip(*diff):
+        a, b = O.e4m3_value(int(gpu_rows[r, d])), O.e4m3_value(int(ref_rows[r, d]))
+        assert midpoint_ok(pre[r, d], a, b, tol[r, d]), (r, d, pre[r, d], a, b, tol[r, d])
+    g16 = gpu_rows[:, 448:].copy().view(np.uint16)
+    r16 = ref_rows[:, 448:].copy().view(np.uint16)
+    diff2 = np.nonzero(g16 != r16)
+    for r, d in zip(*diff2):
+        a, b = O.bf16_value(int(g16[r, d])), O.bf16_value(int(r16[r, d]))
+        assert midpoint_ok(pre[r, 448 + d], a, b, tol[r, 448 + d]), \
+            (r, d, pre[r, 448 + d], a, b, tol[r, 448 + d])
+    return len(diff[0]) + len(diff2[0])
+
+
+def check_rows_fp4(gpu_rows, gpu_scales, ref_rows, ref_scales, pre, tol):
+    D = pre.shape[-1]
+    gpu_rows = np.asarray(gpu_rows).reshape(-1, D // 2)
+    ref_rows = np.asarray(ref_rows).reshape(-1, D // 2)
+    gs = np.asarray(gpu_scales).reshape(-1, D // 32)
+    rs = np.asarray(ref_scales).reshape(-1, D // 32)
+    pre = np.asarray(pre).reshape(-1, D)
+    tol = np.asarray(tol).reshape(-1, D)
+    nd = 0
+    for r in range(gpu_rows.shape[0]):
+        if np.array_equal(gpu_rows[r], ref_rows[r]) and np.array_equal(gs[r], rs[r]):
+            continue
+        for blk in range(D // 32):
+            v = pre[r, 32 * blk: 32 * blk + 32]
+            t = tol[r, 32 * blk: 32 * blk + 32]
+            if gs[r, blk] != rs[r, blk]:
+                # the block scale flips only if amax sits within round-off of a power of two
+                j = int(np.argmax(np.abs(v)))
+                amax = abs(v[j])
+                p2 = 2.0 ** np.round(np.log2(amax))
+                assert abs(amax - p2) <= t.max(), (r, blk, amax)
+                nd += 1
+                continue
+            X = 2.0 ** (int(rs[r, blk]) - 127)
+            for i in range(32):
+                col = 32 * blk + i
+                cg = (gpu_rows[r, col // 2] >> (4 * (col & 1))) & 15
+                cr = (ref_rows[r, col // 2] >> (4 * (col & 1))) & 15
+                a, b = O.e2m1_value(int(cg)), O.e2m1_value(int(cr))
+                if a == b:
+                    continue
+                nd += 1
+                assert midpoint_ok(v[i] / X, a, b, t[i] / X), (r, col, v[i] / X, a, b)
+    return nd
