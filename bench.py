@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Benchmark of the compress-then-sparsify decode hot path on one MI355X.
+
+One step = one decode token for 16 sequences at 1,048,576 tokens of context through one CSA layer
+and one HCA layer, i.e. every row of the decode hot path:
+  1. kv_compress of the newest complete groups of every sequence: CSA K=V (m=4, E4M3+bf16 rows),
+     indexer keys (m=4, FP4+E8M0) and HCA K=V (m=128), written at the caches' append position.
+     This runs every step, an upper bound (in steady state it is due every 4th / 128th token).
+  2. CSA layer, as 4 batches of 4 sequences (the CSA 1M configuration): index_topk over 262,144
+     FP4 indexer entries per sequence -> top-1024, then csa_attend (64 heads x 512, top-1024
+     entries + 128-token window + sink).
+  3. HCA layer, one batch of 16 sequences (the HCA 1M configuration): hca_attend over 8,192
+     entries + 128-token window + sink.
+Inputs are seeded synthetic values (~N(0,1) before quantisation) generated and encoded on the
+GPU with the library's own kv_compress (m = 1 is its quantiser). The step's working set is
+~2.8 GB, so consecutive steps stream from HBM rather than from the 256 MB last-level cache.
+
+The timed region replays a HIP graph of the step (the eager launch path is CPU-bound); value is
+queries (sequences) per second. The roofline object reports the dominant kernel (the indexer
+scan) timed with HIP events around it on the library's stream (csah_profile_next_call). The
+cpu_baseline object times the CPU oracle on one sequence of each layer.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+import long_context_attention_03_amd as L  # noqa: E402
+from long_context_attention_03_amd import synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "CSA+HCA decode queries/sec at 1M ctx; achieved HBM GB/s vs peak"
+CTX = 1 << 20
+N_CSA = CTX // 4       # 262,144 entries
+N_HCA = CTX // 128     # 8,192 entries
+B_CSA, N_CSA_BATCHES, B_HCA = 4, 4, 16
+H, D, HI, DI, K, W = 64, 512, 4, 128, 1024, 128
+ROW = 576
+SCAN_BYTES_PER_SEQ = N_CSA * (DI // 2 + DI // 32)   # 17,825,792 B of FP4 keys + E8M0 scales
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def encode(values, m, fmt, rows=None, scales=None):
+    """Quantise [B, T, D] fp32 values with the library (m=1 compression is the identity)."""
+    w = torch.zeros(values.shape[-1], dtype=torch.float32, device=values.device)
+    b = torch.zeros(m, dtype=torch.float32, device=values.device)
+    return L.kv_compress(values, m, w, b, fmt, out_rows=rows, out_scales=scales)
+
+
+class DecodeStep:
+    def __init__(self, seed: int = 4):
+        dev = torch.device("cuda")
+        self.scale = D ** -0.5
+        self.pos_csa = torch.full((B_CSA,), CTX - 1, dtype=torch.int64, device=dev)
+        self.pos_hca = torch.full((B_HCA,), CTX - 1, dtype=torch.int64, device=dev)
+        self.csa = []
+        for j in range(N_CSA_BATCHES):
+            d = synth.Draws(seed + 100 * j, dev)
+            cache = torch.empty((B_CSA, N_CSA, ROW), dtype=torch.uint8, device=dev)
+            kc = torch.empty((B_CSA, N_CSA, DI // 2), dtype=torch.uint8, device=dev)
+            ks = torch.empty((B_CSA, N_CSA, DI // 32), dtype=torch.uint8, device=dev)
+            step = 1 << 16
+            for b in range(B_CSA):
+                for r0 in range(0, N_CSA, step):
+                    encode(d.normal((1, step, D)), 1, L.FMT_ROW_E4M3_BF16,
+                           rows=cache[b:b + 1, r0:r0 + step])
+                    encode(d.normal((1, step, DI)), 1, L.FMT_FP4_E8M0,
+                           rows=kc[b:b + 1, r0:r0 + step], scales=ks[b:b + 1, r0:r0 + step])
+            win, _ = encode(d.normal((B_CSA, W, D)), 1, L.FMT_ROW_E4M3_BF16)
+            iqc, iqs = encode(d.normal((B_CSA, HI, DI)), 1, L.FMT_FP4_E8M0)
+            self.csa.append(dict(
+                cache=cache, kc=kc, ks=ks, win=win,
+                iqc=iqc.view(B_CSA, 1, HI, DI // 2), iqs=iqs.view(B_CSA, 1, HI, DI // 32),
+                q=d.normal((B_CSA, 1, H, D), dtype=torch.bfloat16),
+                xt=d.normal((B_CSA, 4, D), dtype=torch.bfloat16),
+                xit=d.normal((B_CSA, 4, DI)),
+                idx=torch.empty((B_CSA, 1, K), dtype=torch.int32, device=dev),
+                out=torch.empty((B_CSA, 1, H, D), dtype=torch.float32, device=dev),
+                lse=torch.empty((B_CSA, 1, H), dtype=torch.float32, device=dev)))
+        d = synth.Draws(seed + 1000, dev)
+        self.sink = d.normal((H,))
+        self.w_csa, self.b_csa = synth.compressor_params(D, 4, d)
+        self.w_idx, self.b_idx = synth.compressor_params(DI, 4, d)
+        self.w_hca, self.b_hca = synth.compressor_params(D, 128, d)
+        hcache = torch.empty((B_HCA, N_HCA, ROW), dtype=torch.uint8, device=dev)
+        encode(d.normal((B_HCA, N_HCA, D)), 1, L.FMT_ROW_E4M3_BF16, rows=hcache)
+        hwin, _ = encode(d.normal((B_HCA, W, D)), 1, L.FMT_ROW_E4M3_BF16)
+        self.hca = dict(cache=hcache, win=hwin, q=d.normal((B_HCA, 1, H, D), dtype=torch.bfloat16),
+                        xt=d.normal((B_HCA, 128, D), dtype=torch.bfloat16),
+                        out=torch.empty((B_HCA, 1, H, D), dtype=torch.float32, device=dev),
+                        lse=torch.empty((B_HCA, 1, H), dtype=torch.float32, device=dev))
+        self.ws_idx = torch.empty(L.index_topk_workspace(B_CSA, 1, N_CSA, K, DI), dtype=torch.uint8,
+                                  device=dev)
+        self.ws_csa = torch.empty(max(256, L.attend_workspace(B_CSA, 1, H, D, K + W)),
+                                  dtype=torch.uint8, device=dev)
+        self.ws_hca = torch.empty(max(256, L.attend_workspace(B_HCA, 1, H, D, N_HCA + W)),
+                                  dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    # ---- the three stages of one step
+    def compress(self):
+        for c in self.csa:
+            L.kv_compress(c["xt"], 4, self.w_csa, self.b_csa, L.FMT_ROW_E4M3_BF16,
+                          out_rows=c["cache"][:, N_CSA - 1:N_CSA])
+            L.kv_compress(c["xit"], 4, self.w_idx, self.b_idx, L.FMT_FP4_E8M0,
+                          out_rows=c["kc"][:, N_CSA - 1:N_CSA], out_scales=c["ks"][:, N_CSA - 1:N_CSA])
+        h = self.hca
+        L.kv_compress(h["xt"], 128, self.w_hca, self.b_hca, L.FMT_ROW_E4M3_BF16,
+                      out_rows=h["cache"][:, N_HCA - 1:N_HCA])
+
+    def index(self, c, ev=None):
+        if ev is not None:
+            L.profile_next_call(*ev)
+        L.index_topk(c["iqc"], c["iqs"], c["kc"], c["ks"], self.pos_csa, 4, K, want_scores=False,
+                     ws=self.ws_idx, idx_out=c["idx"])
+
+    def csa_attend(self, c, ev=None):
+        if ev is not None:
+            L.profile_next_call(*ev)
+        L.csa_attend(c["q"], c["cache"], c["idx"], c["win"], W, self.pos_csa, self.sink,
+                     self.scale, ws=self.ws_csa, out=c["out"], lse=c["lse"])
+
+    def hca_attend(self, ev=None):
+        h = self.hca
+        if ev is not None:
+            L.profile_next_call(*ev)
+        L.hca_attend(h["q"], h["cache"], 128, h["win"], W, self.pos_hca, self.sink, self.scale,
+                     ws=self.ws_hca, out=h["out"], lse=h["lse"])
+
+    def step(self):
+        self.compress()
+        for c in self.csa:
+            self.index(c)
+            self.csa_attend(c)
+        self.hca_attend()
+
+
+def event_pair():
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    b.record()  # materialise the underlying hipEvent_t
+    return a, b
+
+
+def kernel_times(ws: DecodeStep, reps: int):
+    """Average duration (ms) of each stage's dominant kernel, from events around it."""
+    evs = {"index_scan": [], "csa_attend": [], "hca_attend": []}
+    for _ in range(reps):
+        for c in ws.csa:
+            e = event_pair()
+            ws.index(c, e)
+            evs["index_scan"].append(e)
+            e = event_pair()
+            ws.csa_attend(c, e)
+            evs["csa_attend"].append(e)
+        e = event_pair()
+        ws.hca_attend(e)
+        evs["hca_attend"].append(e)
+    torch.cuda.synchronize()
+    return {k: statistics.mean(a.elapsed_time(b) for a, b in v) for k, v in evs.items()}
+
+
+def traffic_from_profile():
+    """HBM bytes per scan launch from the committed counter summary, if it matches the source."""
+    path = os.path.join(ROOT, "profiles", "index_scan_csa1m_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        import hashlib
+        src = os.path.join(ROOT, "long_context_attention_03_amd", "csrc", "index_topk.hip")
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        return rec["hbm_bytes_per_launch"] if rec.get("source_sha256_16") == h else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(min_seconds: float):
+    """The oracle on one sequence of each layer at 1M context (index + attention + compression)."""
+    import numpy as np
+
+    import oracle as O
+    d = synth.Draws(99)
+    kc, ks = O.encode_rows(d.normal((1, N_CSA, DI)).numpy(), O.FMT_FP4_E8M0)
+    qc, qs = O.encode_rows(d.normal((1, 1, HI, DI)).numpy(), O.FMT_FP4_E8M0)
+    # the CSA cache only needs real rows where the selection lands; rows are drawn in full
+    cache, _ = O.encode_rows(d.normal((1, N_CSA, D)).numpy(), O.FMT_ROW_E4M3_BF16)
+    win, _ = O.encode_rows(d.normal((1, W, D)).numpy(), O.FMT_ROW_E4M3_BF16)
+    hcache, _ = O.encode_rows(d.normal((1, N_HCA, D)).numpy(), O.FMT_ROW_E4M3_BF16)
+    q = d.normal((1, 1, H, D), dtype=torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    sink = d.normal((H,)).numpy()
+    xt = d.normal((1, 128, D)).numpy()
+    xit = d.normal((1, 4, DI)).numpy()
+    w512, b4, b128 = d.normal((D,), 0.02).numpy(), d.normal((4,), 0.1).numpy(), \
+        d.normal((128,), 0.1).numpy()
+    w128 = d.normal((DI,), 0.02).numpy()
+    pos = np.array([CTX - 1], np.int64)
+    times = []
+    t_end = time.perf_counter() + min_seconds
+    while len(times) < 3 or time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        O.kv_compress(xt[:, -4:], O.DT_F32, 4, w512, b4, O.FMT_ROW_E4M3_BF16)
+        O.kv_compress(xit, O.DT_F32, 4, w128, b4, O.FMT_FP4_E8M0)
+        O.kv_compress(xt, O.DT_F32, 128, w512, b128, O.FMT_ROW_E4M3_BF16)
+        idx, _, _ = O.index_topk(qc, qs, kc, ks, pos, 4, K)
+        O.csa_attend(q, cache, O.FMT_ROW_E4M3_BF16, idx, win, W, pos, sink, D ** -0.5)
+        O.hca_attend(q, hcache, O.FMT_ROW_E4M3_BF16, 128, win, W, pos, sink, D ** -0.5)
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 50:
+            break
+    t = statistics.median(times)
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": 1.0 / t, "unit": "queries/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"one sequence through one CSA and one HCA layer at 1M context (compress the "
+                      f"newest groups, exact FP4 index over 262,144 entries + top-1024, CSA and HCA "
+                      f"attention, 64 heads, fp64), median of {len(times)} runs, "
+                      f"{t * 1e3:.0f} ms each, CPU: {cpu}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    log("building inputs (about 2.8 GB of encoded caches on the GPU)...")
+    ws = DecodeStep()
+    log("warmup...")
+    for _ in range(args.warmup):
+        ws.step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            ws.step()
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            ws.step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+    log(f"timing {args.steps} steps ({'graph replay' if graph else 'eager'})...")
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            ws.step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    log(f"  {ms * 1e3:.1f} us per step")
+    kt = kernel_times(ws, args.kernel_reps)
+    log("  dominant kernels (us): " + ", ".join(f"{k} {v * 1e3:.2f}" for k, v in kt.items()))
+    scan_bytes = B_CSA * SCAN_BYTES_PER_SEQ
+    achieved = scan_bytes / (kt["index_scan"] * 1e-3) / 1e9
+    queries = N_CSA_BATCHES * B_CSA
+    line = {
+        "metric": METRIC,
+        "value": queries / (ms * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode step, 16 sequences x 1,048,576-token context, one CSA layer "
+                        "(4 batches x 4 sequences: FP4 index over 262,144 entries, top-1024, "
+                        "sparse attention + 128-token window + sink) and one HCA layer (batch 16: "
+                        "dense attention over 8,192 entries + window + sink), newest-group "
+                        "kv_compress every step; 64 heads x 512 (448 e4m3 + 64 bf16)",
+            "global_batch": queries, "seq_len": CTX, "heads": H, "head_dim": D,
+            "indexer": "4 heads x 128, FP4 e2m1 + E8M0/32", "top_k": K, "window": W,
+            "timing": "hip graph replay" if graph is not None else "eager",
+            "compute": "indexer scan fp32 (exact), attention bf16 MFMA with fp32 accumulation",
+        },
+        "roofline": {
+            "kernel": "index_scan_kernel (csah_index_topk, 4 x 262,144 entries)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": traffic_from_profile(),
+            "algorithmic_bytes_per_launch": scan_bytes,
+            "avg_launch_us": kt["index_scan"] * 1e3,
+        },
+        "kernels_us": {k: v * 1e3 for k, v in kt.items()},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one sequence per layer...")
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

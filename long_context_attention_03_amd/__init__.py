@@ -26,7 +26,7 @@ FMT_ROW_F32, FMT_ROW_E4M3_BF16, FMT_FP4_E8M0 = 0, 1, 2
 
 EXPORTS = ("csah_abi_version", "csah_status_string", "csah_row_bytes", "csah_kv_compress",
            "csah_index_topk_workspace", "csah_index_topk", "csah_attend_workspace",
-           "csah_csa_attend", "csah_hca_attend")
+           "csah_csa_attend", "csah_hca_attend", "csah_profile_next_call")
 
 _lib = None
 
@@ -59,6 +59,7 @@ def lib():
                                     P, P, P, SZ, P]),
             "csah_hca_attend": (I, [P, I, I, I, P, I, I64, I64, I, P, I64, I, P, P, F, I, I, P,
                                     P, P, SZ, P]),
+            "csah_profile_next_call": (I, [P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -70,6 +71,16 @@ def lib():
 
 def status_string(status: int) -> str:
     return lib().csah_status_string(int(status)).decode()
+
+
+def profile_next_call(begin, end):
+    """Record torch.cuda.Events ``begin``/``end`` around the next call's dominant kernel.
+
+    Both events must already exist on the device (record them once beforehand).
+    """
+    st = lib().csah_profile_next_call(ctypes.c_void_p(begin.cuda_event),
+                                      ctypes.c_void_p(end.cuda_event))
+    _check("csah_profile_next_call", st)
 
 
 def row_bytes(fmt: int, D: int) -> int:

@@ -30,6 +30,15 @@ int check_device() {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? CSAH_OK : CSAH_ERR_LAUNCH; }
 
+thread_local ProfileHook g_next_prof;
+
+// Take (and clear) this thread's pending profiling request.
+ProfileHook take_profile() {
+  ProfileHook h = g_next_prof;
+  g_next_prof = ProfileHook{};
+  return h;
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int row_bytes(int fmt, int D) {
@@ -58,9 +67,17 @@ const char* csah_status_string(int status) {
 
 int64_t csah_row_bytes(int fmt, int D) { return D > 0 ? row_bytes(fmt, D) : -1; }
 
+int csah_profile_next_call(void* begin_event, void* end_event) {
+  if ((begin_event == nullptr) != (end_event == nullptr)) return CSAH_ERR_INVALID_ARGUMENT;
+  g_next_prof.begin = (hipEvent_t)begin_event;
+  g_next_prof.end = (hipEvent_t)end_event;
+  return CSAH_OK;
+}
+
 int csah_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B, int64_t T,
                      int D, int m, const float* w, const float* beta, void* out_rows, int out_fmt,
                      int64_t out_seq_stride, uint8_t* out_scales, void* stream) {
+  const ProfileHook prof = take_profile();
   if (!raw || !w || !beta || !out_rows || B < 0 || T < 0 || D <= 0 || m <= 0)
     return CSAH_ERR_INVALID_ARGUMENT;
   if (raw_dtype != CSAH_DT_F32 && raw_dtype != CSAH_DT_BF16) return CSAH_ERR_INVALID_ARGUMENT;
@@ -75,8 +92,9 @@ int csah_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int
   if (m > 65536) return CSAH_ERR_UNSUPPORTED;
   int st = check_device();
   if (st) return st;
-  KvCompressArgs a{raw, raw_dtype, raw_seq_stride, B, T / m, D, m, w, beta, out_rows, out_fmt,
-                   out_seq_stride, out_scales, stream};
+  KvCompressArgs a{raw,     raw_dtype, raw_seq_stride, B,      T / m,          D,          m,
+                   w,       beta,      out_rows,       out_fmt, out_seq_stride, out_scales, stream,
+                   prof};
   return launch_status(launch_kv_compress(a));
 }
 
@@ -89,6 +107,7 @@ int csah_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int
                     const uint8_t* k_codes, const uint8_t* k_scales, int64_t k_seq_stride,
                     int64_t N, const int64_t* pos, int m, int B, int Q, int k, int32_t* idx_out,
                     float* score_out, void* ws, size_t ws_bytes, void* stream) {
+  const ProfileHook prof = take_profile();
   if (!q_codes || !q_scales || !k_codes || !k_scales || !pos || !idx_out || !ws)
     return CSAH_ERR_INVALID_ARGUMENT;
   if (HI <= 0 || dI <= 0 || m <= 0 || B <= 0 || Q <= 0 || k <= 0 || N < 0 || k_seq_stride < N)
@@ -101,7 +120,7 @@ int csah_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int
   if (st) return st;
   if (ws_bytes < index_workspace_bytes(B, Q, N, k, dI)) return CSAH_ERR_WORKSPACE_TOO_SMALL;
   IndexArgs a{q_codes, q_scales, HI, dI, k_codes, k_scales, k_seq_stride, N, pos, m, B, Q, k,
-              idx_out, score_out, ws, ws_bytes, stream};
+              idx_out, score_out, ws, ws_bytes, stream, prof};
   return launch_status(launch_index_topk(a));
 }
 
@@ -114,7 +133,7 @@ static int attend_common(const void* q, int q_dtype, int H, int D, const void* c
                          int64_t cache_seq_stride, int64_t N, const int32_t* idx, int k, int m,
                          const void* win, int64_t win_seq_stride, int w, const int64_t* pos,
                          const float* sink, float scale, int B, int Q, float* out, float* lse,
-                         void* ws, size_t ws_bytes, void* stream) {
+                         void* ws, size_t ws_bytes, void* stream, ProfileHook prof) {
   if (!q || !cache || !pos || !out || H <= 0 || D <= 0 || B <= 0 || Q <= 0 || N < 0 || w < 0)
     return CSAH_ERR_INVALID_ARGUMENT;
   if (q_dtype != CSAH_DT_F32 && q_dtype != CSAH_DT_BF16) return CSAH_ERR_INVALID_ARGUMENT;
@@ -135,7 +154,7 @@ static int attend_common(const void* q, int q_dtype, int H, int D, const void* c
   if (ws_bytes < need) return CSAH_ERR_WORKSPACE_TOO_SMALL;
   AttendArgs a{q,   q_dtype, H,     D,     cache, fmt, cache_seq_stride, N,        idx,   k,
                m,   win,     win_seq_stride, w, pos, sink, scale,   B,  Q, out, lse, ws, ws_bytes,
-               stream, max_rows};
+               stream, max_rows, prof};
   return launch_status(launch_attend(a));
 }
 
@@ -144,9 +163,11 @@ int csah_csa_attend(const void* q, int q_dtype, int H, int D, const void* cache,
                     const void* win, int64_t win_seq_stride, int w, const int64_t* pos,
                     const float* sink, float scale, int B, int Q, float* out, float* lse,
                     void* ws, size_t ws_bytes, void* stream) {
+  const ProfileHook prof = take_profile();
   if (!idx || k < 0) return CSAH_ERR_INVALID_ARGUMENT;
   return attend_common(q, q_dtype, H, D, cache, fmt, cache_seq_stride, N, idx, k, 1, win,
-                       win_seq_stride, w, pos, sink, scale, B, Q, out, lse, ws, ws_bytes, stream);
+                       win_seq_stride, w, pos, sink, scale, B, Q, out, lse, ws, ws_bytes, stream,
+                       prof);
 }
 
 int csah_hca_attend(const void* q, int q_dtype, int H, int D, const void* cache, int fmt,
@@ -154,9 +175,11 @@ int csah_hca_attend(const void* q, int q_dtype, int H, int D, const void* cache,
                     int64_t win_seq_stride, int w, const int64_t* pos, const float* sink,
                     float scale, int B, int Q, float* out, float* lse, void* ws, size_t ws_bytes,
                     void* stream) {
+  const ProfileHook prof = take_profile();
   if (m <= 0) return CSAH_ERR_INVALID_ARGUMENT;
   return attend_common(q, q_dtype, H, D, cache, fmt, cache_seq_stride, N, nullptr, 0, m, win,
-                       win_seq_stride, w, pos, sink, scale, B, Q, out, lse, ws, ws_bytes, stream);
+                       win_seq_stride, w, pos, sink, scale, B, Q, out, lse, ws, ws_bytes, stream,
+                       prof);
 }
 
 }  // extern "C"

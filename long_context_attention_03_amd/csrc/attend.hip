@@ -17,14 +17,19 @@
 //   - Y (E4M3 + bf16 rows) converts exactly to bf16, so Q.Y products are exact; fp32 rows are split
 //     into hi + lo bf16 terms. P in (0, 1] is split into hi + lo bf16 terms (about 16 significant
 //     bits), so the PV contraction keeps fp32-level accuracy.
-//   - The QK A-operand is loaded straight from HBM (lane l: row l%16, 8 dims at 8*(l/16)), converted
-//     in registers, and the same registers are written transposed into a per-wavefront LDS tile
-//     Yt[d][slot] that feeds the PV A-operand with 16-byte reads. Slot order matches the C layout of
-//     S^T, so P never moves between lanes. The 16-byte segments of a Yt row are XOR-swizzled by
-//     (d / 8) % 4 to spread the transposing writes over the LDS banks.
-//   - Online softmax in base 2 (running max per head, lazy rescale of the accumulators only when
-//     the max moves).
-// Grid: (row splits x head groups of 16, sequences x queries). The 4 wavefronts of a workgroup take
+//   - The QK A-operand is loaded straight from HBM (lane l: row l%16, 8 dims at 8*(l/16)) and
+//     converted in registers; the same bf16 fragments are stored row-major into a per-wavefront
+//     LDS tile (one 16-byte write each, rows padded by 32 bytes). The PV A-operand Y^T is read
+//     back with gfx950's transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group,
+//     output lane n, element e comes from input lane 4e + n/4, element n%4, so lane (e, q) of
+//     group g points at row 4g+e (then 16+4g+e), dims 16t+4q, and receives dim 16t+n of those
+//     four rows. The K-slot order this produces matches the C layout of S^T, so P never moves
+//     between lanes.
+//   - The next tile's row loads are issued as soon as the QK phase has consumed the registers, so
+//     they overlap the softmax and PV phase.
+//   - Online softmax in base 2 with a lazily updated reference max per head: the accumulators are
+//     rescaled only when a head's max grows by more than 2^8 (P <= 256 otherwise).
+// Grid: one workgroup per (sequence x query, row split, head group of 16), mapped XCD-aware. The 4 wavefronts of a workgroup take
 // 32-row tiles of the split in turn and are merged in LDS at the end; with one split the workgroup
 // applies the sink and writes the output, otherwise it writes (max, sum, acc) partials that
 // attend_merge_kernel combines with the sink.
@@ -32,6 +37,9 @@
 #include "device_common.h"
 
 namespace csah {
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef short short8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kTile = 32;   // rows per wavefront tile
 constexpr int kWaves = 4;
@@ -60,7 +68,7 @@ struct AttendK {
   const int64_t* pos;
   const float* sink;
   float scale_log2;
-  int Q, splits, rows_per_split, hg;
+  int Q, splits, rows_per_split, hg, slots;
   float* out;
   float* lse;
   float* part;
@@ -73,47 +81,72 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
   return r;
 }
 
-// 8 consecutive dims [32c + 8g, +8) of one row as bf16 (hi, and lo for fp32 rows).
+// Raw register image of one lane's share of a 32-row tile: rows n and 16+n, dims [32c+8g, +8)
+// of every 32-wide chunk c. Loaded unconditionally (masked rows read a valid dummy row) so that a
+// whole tile's loads are in flight together and never wait inside a branch.
 template <int FMT>
-__device__ __forceinline__ void load_row_frag(const uint8_t* row, bool valid, int c, int g,
-                                              bf16x8& hi, bf16x8& lo) {
-  if constexpr (FMT == CSAH_FMT_ROW_E4M3_BF16) {
-    if (!valid) {
-      hi = bf16x8{};
-      return;
-    }
-    if (c < 14) {
-      const u32x2 v = *(const u32x2*)(row + 32 * c + 8 * g);
-      bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, false);
-      bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.0f, true);
-      bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, false);
-      bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.0f, true);
-      hi = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-    } else {
-      const u32x4 v = *(const u32x4*)(row + 448 + 64 * (c - 14) + 16 * g);
-      hi = __builtin_bit_cast(bf16x8, v);
-    }
-  } else {
-    if (!valid) {
-      hi = bf16x8{};
-      lo = bf16x8{};
-      return;
-    }
-    const f32x4 a = *(const f32x4*)(row + 4 * (32 * c + 8 * g));
-    const f32x4 b = *(const f32x4*)(row + 4 * (32 * c + 8 * g) + 16);
-    float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    float r[8];
-    hi = pack_bf16x8(x);
+struct TileRaw;
+template <>
+struct TileRaw<CSAH_FMT_ROW_E4M3_BF16> {
+  u32x2 e[2][14];  // E4M3 bytes of dims 32c+8g.. (c < 14)
+  u32x4 r[2][2];   // bf16 rotary dims 448+32(c-14)+8g..
+};
+template <>
+struct TileRaw<CSAH_FMT_ROW_F32> {
+  f32x4 v[2][4][2];
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_tile(const uint8_t* p0, const uint8_t* p1, int g,
+                                          TileRaw<FMT>& t) {
+  const uint8_t* ps[2] = {p0, p1};
 #pragma unroll
-    for (int e = 0; e < 8; e++) r[e] = x[e] - (float)hi[e];
-    lo = pack_bf16x8(r);
+  for (int r = 0; r < 2; r++) {
+    if constexpr (FMT == CSAH_FMT_ROW_E4M3_BF16) {
+#pragma unroll
+      for (int c = 0; c < 14; c++) t.e[r][c] = *(const u32x2*)(ps[r] + 32 * c + 8 * g);
+#pragma unroll
+      for (int c = 0; c < 2; c++) t.r[r][c] = *(const u32x4*)(ps[r] + 448 + 64 * c + 16 * g);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        t.v[r][c][0] = *(const f32x4*)(ps[r] + 4 * (32 * c + 8 * g));
+        t.v[r][c][1] = *(const f32x4*)(ps[r] + 4 * (32 * c + 8 * g) + 16);
+      }
+    }
   }
 }
 
-// LDS element index of Yt[d][slot] inside one wavefront's tile (32 slots per row, swizzled).
-__device__ __forceinline__ int yt_index(int d, int slot) {
-  const int seg = (slot >> 3) ^ ((d >> 3) & 3);
-  return d * kTile + seg * 8 + (slot & 7);
+// bf16 fragment (hi, and lo for fp32 rows) of row r, chunk c; zero when the row is masked.
+template <int FMT>
+__device__ __forceinline__ void tile_frag(const TileRaw<FMT>& t, int r, int c, bool valid,
+                                          bf16x8& hi, bf16x8& lo) {
+  if constexpr (FMT == CSAH_FMT_ROW_E4M3_BF16) {
+    if (c < 14) {
+      const u32x2 v = t.e[r][c];
+      const uint32_t w0 = valid ? v[0] : 0u, w1 = valid ? v[1] : 0u;
+      bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+      bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+      bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+      bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+      hi = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    } else {
+      u32x4 v = t.r[r][c - 14];
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[e] = valid ? v[e] : 0u;
+      hi = __builtin_bit_cast(bf16x8, v);
+    }
+  } else {
+    const f32x4 a = t.v[r][c][0], b = t.v[r][c][1];
+    float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    float rr[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) x[e] = valid ? x[e] : 0.0f;
+    hi = pack_bf16x8(x);
+#pragma unroll
+    for (int e = 0; e < 8; e++) rr[e] = x[e] - (float)hi[e];
+    lo = pack_bf16x8(rr);
+  }
 }
 
 template <int FMT, int QDT, bool DENSE>
@@ -121,7 +154,8 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttendK p) {
   using C = RowCfg<FMT>;
   constexpr int D = C::D, NCH = C::NCH, YS = C::YS, NT = D / 16;
   constexpr int QS = QDT == CSAH_DT_F32 ? 2 : 1;
-  constexpr int YT_ELEMS = D * kTile;  // bf16 elements per wavefront per split term
+  constexpr int RS = D + 16;                    // LDS row stride (bf16 elements)
+  constexpr int YT_ELEMS = kTile * RS;          // bf16 elements per wavefront per split term
   constexpr int LDS_YT = kWaves * YS * YT_ELEMS * 2;
   constexpr int LDS_COMB = kWaves * 16 * D * 4;
   constexpr int LDS_BYTES = LDS_YT > LDS_COMB ? LDS_YT : LDS_COMB;
@@ -130,32 +164,45 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttendK p) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, n = lane & 15;
-  const int slot = blockIdx.y;
+  // Workgroups are dispatched round-robin over the 8 XCDs (id % 8). Consecutive workgroups of one
+  // XCD take the head groups of one (query, split) unit, so the rows they all read are fetched
+  // into that XCD's L2 once.
+  const int64_t wg = blockIdx.x;
+  const int64_t unit = (wg / (8 * p.hg)) * 8 + (wg & 7);
+  const int hgi = (int)((wg >> 3) % p.hg);
+  if (unit >= (int64_t)p.splits * p.slots) return;
+  const int slot = (int)(unit / p.splits), split = (int)(unit - (int64_t)slot * p.splits);
   const int b = slot / p.Q, qi = slot - b * p.Q;
-  const int split = blockIdx.x / p.hg, hgi = blockIdx.x - split * p.hg;
-  const int head = hgi * 16 + n;
-  const bool head_ok = head < p.H;
 
   // ---- query fragments: B operand of S^T = Y Q^T (k = dims 32c + 8g + e, n = head) ----
   bf16x8 qf[QS][NCH];
+  {
+    const int head = hgi * 16 + n;
 #pragma unroll
-  for (int c = 0; c < NCH; c++) {
-    if (!head_ok) {
+    for (int c = 0; c < NCH; c++) {
+      float x[8];
+      if (head < p.H) {
+        const int64_t qo = ((int64_t)slot * p.H + head) * D + 32 * c + 8 * g;
+        if constexpr (QDT == CSAH_DT_BF16) {
+          qf[0][c] = __builtin_bit_cast(bf16x8, *(const u32x4*)((const uint16_t*)p.q + qo));
+          continue;
+        } else {
+          const float* qp = (const float*)p.q + qo;
+          const f32x4 a = *(const f32x4*)qp, bb = *(const f32x4*)(qp + 4);
+          x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+          x[4] = bb[0]; x[5] = bb[1]; x[6] = bb[2]; x[7] = bb[3];
+        }
+      } else {
 #pragma unroll
-      for (int s = 0; s < QS; s++) qf[s][c] = bf16x8{};
-      continue;
-    }
-    const int64_t qo = ((int64_t)slot * p.H + head) * D + 32 * c + 8 * g;
-    if constexpr (QDT == CSAH_DT_BF16) {
-      qf[0][c] = __builtin_bit_cast(bf16x8, *(const u32x4*)((const uint16_t*)p.q + qo));
-    } else {
-      const float* qp = (const float*)p.q + qo;
-      const f32x4 a = *(const f32x4*)qp, bb = *(const f32x4*)(qp + 4);
-      float x[8] = {a[0], a[1], a[2], a[3], bb[0], bb[1], bb[2], bb[3]}, r[8];
+        for (int e = 0; e < 8; e++) x[e] = 0.0f;
+      }
       qf[0][c] = pack_bf16x8(x);
+      if constexpr (QS == 2) {
+        float r8[8];
 #pragma unroll
-      for (int e = 0; e < 8; e++) r[e] = x[e] - (float)qf[0][c][e];
-      qf[QS - 1][c] = pack_bf16x8(r);
+        for (int e = 0; e < 8; e++) r8[e] = x[e] - (float)qf[0][c][e];
+        qf[QS - 1][c] = pack_bf16x8(r8);
+      }
     }
   }
 
@@ -171,210 +218,317 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttendK p) {
   const int64_t R = Rc + p.w;
   const int64_t r0 = (int64_t)split * p.rows_per_split;
   const int64_t r1 = r0 + p.rows_per_split < R ? r0 + p.rows_per_split : R;
+  const int64_t rc_end = Rc < r1 ? Rc : r1;  // compressed rows of this split end here
+  // a readable row for masked slots (a tile with any valid row implies N > 0 or w > 0)
+  const uint8_t* dummy = p.N > 0 ? p.cache + (int64_t)b * p.cstride * C::RB
+                                 : p.win + (int64_t)b * p.wstride * C::RB;
 
-  auto row_ptr = [&](int64_t j, bool& valid) -> const uint8_t* {
-    valid = false;
-    if (j >= r1) return nullptr;
-    if (j < Rc) {
-      int64_t e;
-      if constexpr (DENSE) {
-        e = j;
-      } else {
-        e = p.idx[(int64_t)slot * p.k + j];
-        if (e < 0 || e >= p.N) return nullptr;
-      }
-      valid = true;
-      return p.cache + ((int64_t)b * p.cstride + e) * C::RB;
+  // entry id of tile row (lane & 31), fetched one tile ahead of its use (CSA only)
+  auto fetch_idx = [&](int64_t t) -> int32_t {
+    if constexpr (DENSE) {
+      return 0;
+    } else {
+      if (p.k == 0) return -1;
+      int64_t j = t + (lane & 31);
+      j = j < Rc ? j : Rc - 1;
+      j = j < 0 ? 0 : j;
+      return p.idx[(int64_t)slot * p.k + j];
     }
-    const int64_t r = qi + (j - Rc);                 // window buffer row
-    const int64_t rpos = pos_b - (p.w - 1) + r;      // its token position
-    if (rpos < 0) return nullptr;
-    valid = true;
-    return p.win + ((int64_t)b * p.wstride + r) * C::RB;
+  };
+  // row j -> (pointer, valid); e = entry id for CSA rows
+  auto resolve = [&](int64_t j, int32_t e, bool& valid) -> const uint8_t* {
+    const uint8_t* ptr = dummy;
+    valid = false;
+    if (j < rc_end) {
+      const int64_t ent = DENSE ? j : (int64_t)e;
+      if (ent >= 0 && ent < p.N) {
+        valid = true;
+        ptr = p.cache + ((int64_t)b * p.cstride + ent) * C::RB;
+      }
+    } else if (j < r1) {
+      const int64_t r = qi + (j - Rc);              // window buffer row
+      if (pos_b - (p.w - 1) + r >= 0) {             // its token position is >= 0
+        valid = true;
+        ptr = p.win + ((int64_t)b * p.wstride + r) * C::RB;
+      }
+    }
+    return ptr;
+  };
+  // pointers of rows n and 16+n, the tile's validity mask, and the loads of its rows
+  auto prep_tile = [&](int64_t t, int32_t e_lane, TileRaw<FMT>& raw, uint32_t& mask) {
+    bool vm;
+    (void)resolve(t + (lane & 31), e_lane, vm);
+    mask = (uint32_t)ballot64(vm);
+    const int32_t e0 = __shfl(e_lane, n, 64), e1 = __shfl(e_lane, 16 + n, 64);
+    bool v0, v1;
+    const uint8_t* p0 = resolve(t + n, e0, v0);
+    const uint8_t* p1 = resolve(t + 16 + n, e1, v1);
+    load_tile<FMT>(p0, p1, g, raw);
   };
 
+  // per-wavefront row-major bf16 tile: Y[row][RS]
   __bf16* yt = (__bf16*)smem + wave * YS * YT_ELEMS;
+  // transposing-read base: lane (e, q) of group g reads row 4g+e, dims 4q.. (+16t per d-tile)
+  const int tr_row = 4 * g + ((lane & 15) >> 2), tr_col = 4 * (lane & 3);
+  typedef __attribute__((address_space(3))) short4_t* lds_s4_ptr;
   f32x4 O[NT];
 #pragma unroll
   for (int t = 0; t < NT; t++) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
-  const int slot0 = 8 * (n >> 2) + (n & 3);  // Yt slot of tile row n; row 16+n uses slot0 + 4
+  constexpr int64_t kStep = (int64_t)kTile * kWaves;
 
-  for (int64_t tb = r0 + (int64_t)kTile * wave; tb < r1; tb += (int64_t)kTile * kWaves) {
-    bool vm;
-    (void)row_ptr(tb + (lane & 31), vm);
-    const uint32_t mask = (uint32_t)ballot64(vm);
-    if (mask == 0u) continue;
-    bool v0, v1;
-    const uint8_t* p0 = row_ptr(tb + n, v0);
-    const uint8_t* p1 = row_ptr(tb + 16 + n, v1);
-
-    // S^T for rows tb..tb+15 (S0) and tb+16..tb+31 (S1); stage Y^T in LDS on the way
+  int64_t tb = r0 + (int64_t)kTile * wave;
+  TileRaw<FMT> raw;
+  uint32_t mask_cur = 0;
+  int32_t e_next = 0;
+  if (tb < r1) {
+    const int32_t e0 = fetch_idx(tb);
+    e_next = fetch_idx(tb + kStep);
+    prep_tile(tb, e0, raw, mask_cur);
+  }
+  for (; tb < r1; tb += kStep) {
+    const uint32_t mask = mask_cur;
     f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 S0b = {0.f, 0.f, 0.f, 0.f}, S1b = {0.f, 0.f, 0.f, 0.f};  // odd chunks: shorter chains
+    if (mask != 0u) {
+      const bool v0 = (mask >> n) & 1u, v1 = (mask >> (16 + n)) & 1u;
+      // S^T for rows tb..tb+15 (S0) and tb+16..tb+31 (S1); stage Y row-major in LDS
 #pragma unroll
-    for (int c = 0; c < NCH; c++) {
-      bf16x8 a0h, a0l, a1h, a1l;
-      load_row_frag<FMT>(p0, v0, c, g, a0h, a0l);
-      load_row_frag<FMT>(p1, v1, c, g, a1h, a1l);
-      S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0h, qf[0][c], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1h, qf[0][c], S1, 0, 0, 0);
-      if constexpr (QS == 2) {
-        S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0h, qf[1][c], S0, 0, 0, 0);
-        S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1h, qf[1][c], S1, 0, 0, 0);
-      }
-      if constexpr (YS == 2) {
-        S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0l, qf[0][c], S0, 0, 0, 0);
-        S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1l, qf[0][c], S1, 0, 0, 0);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const int d = 32 * c + 8 * g + e;
-        yt[yt_index(d, slot0)] = a0h[e];
-        yt[yt_index(d, slot0 + 4)] = a1h[e];
+      for (int c = 0; c < NCH; c++) {
+        bf16x8 a0h, a0l, a1h, a1l;
+        tile_frag<FMT>(raw, 0, c, v0, a0h, a0l);
+        tile_frag<FMT>(raw, 1, c, v1, a1h, a1l);
+        f32x4& A0 = (c & 1) ? S0b : S0;
+        f32x4& A1 = (c & 1) ? S1b : S1;
+        A0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0h, qf[0][c], A0, 0, 0, 0);
+        A1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1h, qf[0][c], A1, 0, 0, 0);
+        if constexpr (QS == 2) {
+          A0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0h, qf[1][c], A0, 0, 0, 0);
+          A1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1h, qf[1][c], A1, 0, 0, 0);
+        }
         if constexpr (YS == 2) {
-          yt[YT_ELEMS + yt_index(d, slot0)] = a0l[e];
-          yt[YT_ELEMS + yt_index(d, slot0 + 4)] = a1l[e];
+          A0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0l, qf[0][c], A0, 0, 0, 0);
+          A1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1l, qf[0][c], A1, 0, 0, 0);
+        }
+        *(bf16x8*)(yt + n * RS + 32 * c + 8 * g) = a0h;
+        *(bf16x8*)(yt + (16 + n) * RS + 32 * c + 8 * g) = a1h;
+        if constexpr (YS == 2) {
+          *(bf16x8*)(yt + YT_ELEMS + n * RS + 32 * c + 8 * g) = a0l;
+          *(bf16x8*)(yt + YT_ELEMS + (16 + n) * RS + 32 * c + 8 * g) = a1l;
         }
       }
     }
-
-    // online softmax (base 2); lane holds rows 4g+i (S0) and 16+4g+i (S1) of head n
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      v[i] = ((mask >> (4 * g + i)) & 1u) ? S0[i] * p.scale_log2 : -INFINITY;
-      v[4 + i] = ((mask >> (16 + 4 * g + i)) & 1u) ? S1[i] * p.scale_log2 : -INFINITY;
+    S0 += S0b;
+    S1 += S1b;
+    // the row registers are free: start the next tile's loads (and the ids of the one after)
+    uint32_t mask_nxt = 0;
+    if (tb + kStep < r1) {
+      const int32_t e_after = fetch_idx(tb + 2 * kStep);
+      prep_tile(tb + kStep, e_next, raw, mask_nxt);
+      e_next = e_after;
     }
-    float tmax = v[0];
+    if (mask != 0u) {
+      // online softmax (base 2); lane holds rows 4g+i (S0) and 16+4g+i (S1) of head n
+      float v[8];
 #pragma unroll
-    for (int i = 1; i < 8; i++) tmax = fmaxf(tmax, v[i]);
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
-    float P[8], psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      P[i] = exp2f(v[i] - m_new);
-      psum += P[i];
-    }
-    l_run = fmaf(l_run, alpha, psum);
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int t = 0; t < NT; t++) O[t] *= alpha;
-    }
-    m_run = m_new;
-    bf16x8 ph, pl;
-#pragma unroll
-    for (int e = 0; e < 8; e++) {
-      ph[e] = (__bf16)P[e];
-      pl[e] = (__bf16)(P[e] - (float)ph[e]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // O^T += Y^T P^T
-#pragma unroll
-    for (int t = 0; t < NT; t++) {
-      const int d = 16 * t + n;
-      const bf16x8 ya = *(const bf16x8*)(yt + yt_index(d, 8 * g));
-      O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya, ph, O[t], 0, 0, 0);
-      O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya, pl, O[t], 0, 0, 0);
-      if constexpr (YS == 2) {
-        const bf16x8 yl = *(const bf16x8*)(yt + YT_ELEMS + yt_index(d, 8 * g));
-        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yl, ph, O[t], 0, 0, 0);
+      for (int i = 0; i < 4; i++) {
+        v[i] = ((mask >> (4 * g + i)) & 1u) ? S0[i] * p.scale_log2 : -INFINITY;
+        v[4 + i] = ((mask >> (16 + 4 * g + i)) & 1u) ? S1[i] * p.scale_log2 : -INFINITY;
       }
+      float tmax = v[0];
+#pragma unroll
+      for (int i = 1; i < 8; i++) tmax = fmaxf(tmax, v[i]);
+      tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
+      tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+      // lazy rescale: the reference max moves only when a head's max grows by more than 2^8, so
+      // P stays below 256 and the accumulators are rescaled rarely
+      const float m_new = fmaxf(m_run, tmax);
+      if (__ballot(m_new > m_run + 8.0f)) {
+        const float alpha = exp2f(m_run - m_new);  // 0 while nothing was accumulated
+        if (__ballot(m_run != -INFINITY && alpha != 1.0f)) {
+#pragma unroll
+          for (int t = 0; t < NT; t++) O[t] *= alpha;
+        }
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      float P[8], psum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        P[i] = exp2f(v[i] - m_run);
+        psum += P[i];
+      }
+      l_run += psum;
+      bf16x8 ph, pl;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        ph[e] = (__bf16)P[e];
+        pl[e] = (__bf16)(P[e] - (float)ph[e]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // O^T += Y^T P^T, Y^T fragments by transposing reads of the row-major tile
+      auto ytr = [&](int t, int term) -> bf16x8 {
+        const __bf16* base0 = yt + term * YT_ELEMS + tr_row * RS + 16 * t + tr_col;
+        const short4_t y0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)base0);
+        const short4_t y1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(base0 + 16 * RS));
+        return __builtin_bit_cast(
+            bf16x8, short8_t{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]});
+      };
+      // two d-tiles at a time so that dependent accumulations are never back to back
+#pragma unroll
+      for (int t = 0; t < NT; t += 2) {
+        const bf16x8 ya = ytr(t, 0), yb = ytr(t + 1, 0);
+        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya, ph, O[t], 0, 0, 0);
+        O[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yb, ph, O[t + 1], 0, 0, 0);
+        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya, pl, O[t], 0, 0, 0);
+        O[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yb, pl, O[t + 1], 0, 0, 0);
+        if constexpr (YS == 2) {
+          const bf16x8 za = ytr(t, 1), zb = ytr(t + 1, 1);
+          O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za, ph, O[t], 0, 0, 0);
+          O[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zb, ph, O[t + 1], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    mask_cur = mask_nxt;
   }
 
   // ---- merge the 4 wavefronts ----
   l_run += shfl_xor_f(l_run, 16);
   l_run += shfl_xor_f(l_run, 32);
+  constexpr int CS = D + 4;  // padded row: the 16 heads of one wave land in different banks
+  static_assert(kWaves * 16 * CS * 4 <= LDS_BYTES, "merge buffer fits the tile buffers");
   __syncthreads();
-  float* comb = (float*)smem;  // [wave][16 heads][D]
+  float* comb = (float*)smem;  // [wave][16 heads][CS]
 #pragma unroll
   for (int t = 0; t < NT; t++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) comb[(wave * 16 + n) * D + 16 * t + 4 * g + i] = O[t][i];
+    *(f32x4*)(comb + (wave * 16 + n) * CS + 16 * t + 4 * g) = O[t];
   if (g == 0) {
     s_ml[wave][n][0] = m_run;
     s_ml[wave][n][1] = l_run;
+  }
+  __syncthreads();
+  // per head: M = max over waves, weights 2^(m_w - M), L = sum of weighted sums (64 threads)
+  __shared__ float s_wgt[kWaves][16];
+  __shared__ float s_hm[16][2];
+  if (threadIdx.x < 16) {
+    const int hl = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; wv++) M = fmaxf(M, s_ml[wv][hl][0]);
+    float L = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; wv++) {
+      const float mw = s_ml[wv][hl][0];
+      const float om = mw == -INFINITY ? 0.0f : exp2f(mw - M);
+      s_wgt[wv][hl] = om;
+      L = fmaf(s_ml[wv][hl][1], om, L);
+    }
+    const int hh = hgi * 16 + hl;
+    if (p.splits == 1) {
+      float Mf = M, den = L, a = 1.0f;
+      if (p.sink && hh < p.H) {
+        const float sg = p.sink[hh] * kLog2e;
+        Mf = fmaxf(M, sg);
+        a = M == -INFINITY ? 0.0f : exp2f(M - Mf);
+        den = L * a + exp2f(sg - Mf);
+      }
+      s_hm[hl][0] = den > 0.0f ? a / den : 0.0f;  // output scale
+      if (p.lse && hh < p.H)
+        p.lse[(int64_t)slot * p.H + hh] = den > 0.0f ? (Mf + log2f(den)) * kLn2 : -INFINITY;
+    } else {
+      s_hm[hl][0] = M;
+      s_hm[hl][1] = L;
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < 16 * D; e += 256) {
     const int hl = e / D, d = e - hl * D;
     const int hh = hgi * 16 + hl;
     if (hh >= p.H) continue;
-    float M = -INFINITY;
+    float acc = 0.0f;
 #pragma unroll
-    for (int wv = 0; wv < kWaves; wv++) M = fmaxf(M, s_ml[wv][hl][0]);
-    float L = 0.0f, acc = 0.0f;
-#pragma unroll
-    for (int wv = 0; wv < kWaves; wv++) {
-      const float mw = s_ml[wv][hl][0];
-      const float om = mw == -INFINITY ? 0.0f : exp2f(mw - M);
-      L = fmaf(s_ml[wv][hl][1], om, L);
-      acc = fmaf(comb[(wv * 16 + hl) * D + d], om, acc);
-    }
+    for (int wv = 0; wv < kWaves; wv++) acc = fmaf(comb[(wv * 16 + hl) * CS + d], s_wgt[wv][hl], acc);
     if (p.splits == 1) {
-      float Mf = M, den = L;
-      if (p.sink) {
-        const float sg = p.sink[hh] * kLog2e;
-        Mf = fmaxf(M, sg);
-        const float a = M == -INFINITY ? 0.0f : exp2f(M - Mf);
-        den = L * a + exp2f(sg - Mf);
-        acc *= a;
-      }
-      const int64_t oo = ((int64_t)slot * p.H + hh);
-      p.out[oo * D + d] = den > 0.0f ? acc / den : 0.0f;
-      if (d == 0 && p.lse) p.lse[oo] = den > 0.0f ? (Mf + log2f(den)) * kLn2 : -INFINITY;
+      p.out[((int64_t)slot * p.H + hh) * D + d] = acc * s_hm[hl][0];
     } else {
-      float* pp = p.part + (((int64_t)slot * p.splits + split) * p.H + hh) * (D + 2);
-      pp[2 + d] = acc;
+      // partial row: acc[D], max, sum, 2 pad floats (16-byte aligned rows)
+      float* pp = p.part + (((int64_t)slot * p.splits + split) * p.H + hh) * (D + 4);
+      pp[d] = acc;
       if (d == 0) {
-        pp[0] = M;
-        pp[1] = L;
+        pp[D] = s_hm[hl][0];
+        pp[D + 1] = s_hm[hl][1];
       }
     }
   }
 }
 
-// Combine the split partials of one (query, head) with the sink.
+// Combine the split partials of one (query, head) with the sink. The per-split weights are computed
+// once into LDS; each thread then owns D/128 consecutive dims and reads every split's values with
+// independent vector loads.
+constexpr int kMaxSplits = 64;
+
 template <int D>
 __global__ __launch_bounds__(128) void attend_merge_kernel(const float* __restrict__ part,
                                                            int splits, int H,
                                                            const float* __restrict__ sink,
                                                            float* __restrict__ out,
                                                            float* __restrict__ lse) {
-  const int hh = blockIdx.x, slot = blockIdx.y;
-  const float* base = part + ((int64_t)slot * splits * H + hh) * (D + 2);
-  const int64_t sstride = (int64_t)H * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < splits; s++) M = fmaxf(M, base[s * sstride]);
-  float Mf = M;
-  float sg = 0.0f;
-  if (sink) {
-    sg = sink[hh] * kLog2e;
-    Mf = fmaxf(M, sg);
+  constexpr int DPT = D / 128;
+  const int hh = blockIdx.x, slot = blockIdx.y, t = threadIdx.x;
+  const float* base = part + ((int64_t)slot * splits * H + hh) * (D + 4);
+  const int64_t sstride = (int64_t)H * (D + 4);
+  __shared__ float s_m[kMaxSplits], s_w[kMaxSplits];
+  __shared__ float s_den, s_mf;
+  float ml = -INFINITY, ll = 0.0f;
+  if (t < splits) {
+    ml = base[t * sstride + D];
+    ll = base[t * sstride + D + 1];
+    s_m[t] = ml;
   }
-  float den = sink ? exp2f(sg - Mf) : 0.0f;
-  for (int s = 0; s < splits; s++) {
-    const float ms = base[s * sstride];
-    if (ms != -INFINITY) den = fmaf(base[s * sstride + 1], exp2f(ms - Mf), den);
+  // max over splits (and the sink) within the first wave
+  float M = ml;
+  if (t < 64) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    float Mf = M;
+    const float sg = sink ? sink[hh] * kLog2e : 0.0f;
+    if (sink) Mf = fmaxf(M, sg);
+    const float wgt = (t < splits && ml != -INFINITY) ? exp2f(ml - Mf) : 0.0f;
+    if (t < splits) s_w[t] = wgt;
+    float den = ll * wgt;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
+    if (t == 0) {
+      s_den = den + (sink ? exp2f(sg - Mf) : 0.0f);
+      s_mf = Mf;
+    }
+  }
+  __syncthreads();
+  const float den = s_den;
+  float acc[DPT];
+#pragma unroll
+  for (int e = 0; e < DPT; e++) acc[e] = 0.0f;
+  for (int s0 = 0; s0 < splits; s0++) {
+    const float wgt = s_w[s0];
+    const float* src = base + s0 * sstride + t * DPT;
+    if constexpr (DPT == 4) {
+      const f32x4 v = *(const f32x4*)src;
+#pragma unroll
+      for (int e = 0; e < 4; e++) acc[e] = fmaf(v[e], wgt, acc[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < DPT; e++) acc[e] = fmaf(src[e], wgt, acc[e]);
+    }
   }
   const int64_t oo = (int64_t)slot * H + hh;
-  for (int d = threadIdx.x; d < D; d += 128) {
-    float acc = 0.0f;
-    for (int s = 0; s < splits; s++) {
-      const float ms = base[s * sstride];
-      if (ms != -INFINITY) acc = fmaf(base[s * sstride + 2 + d], exp2f(ms - Mf), acc);
-    }
-    out[oo * D + d] = den > 0.0f ? acc / den : 0.0f;
-  }
-  if (threadIdx.x == 0 && lse) lse[oo] = den > 0.0f ? (Mf + log2f(den)) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int e = 0; e < DPT; e++) out[oo * D + t * DPT + e] = den > 0.0f ? acc[e] / den : 0.0f;
+  if (t == 0 && lse) lse[oo] = den > 0.0f ? (s_mf + log2f(den)) * kLn2 : -INFINITY;
 }
 
 AttendPlan attend_plan(int B, int Q, int H, int D, int64_t max_rows) {
@@ -387,6 +541,7 @@ AttendPlan attend_plan(int B, int Q, int H, int D, int64_t max_rows) {
   int64_t cap = (tiles + kWaves - 1) / kWaves;
   if (cap < 1) cap = 1;
   int64_t S = want < cap ? want : cap;
+  if (S > kMaxSplits) S = kMaxSplits;
   if (S < 1) S = 1;
   int64_t tps = tiles > 0 ? (tiles + S - 1) / S : 1;
   S = tiles > 0 ? (tiles + tps - 1) / tps : 1;
@@ -398,7 +553,7 @@ AttendPlan attend_plan(int B, int Q, int H, int D, int64_t max_rows) {
 size_t attend_workspace_bytes(int B, int Q, int H, int D, int64_t max_rows) {
   AttendPlan pl = attend_plan(B, Q, H, D, max_rows);
   if (pl.splits <= 1) return 0;
-  return (size_t)B * Q * pl.splits * H * (D + 2) * sizeof(float);
+  return (size_t)B * Q * pl.splits * H * (D + 4) * sizeof(float);
 }
 
 template <int FMT, int QDT>
@@ -430,17 +585,23 @@ hipError_t launch_attend(const AttendArgs& a) {
   k.splits = pl.splits;
   k.rows_per_split = pl.rows_per_split;
   k.hg = pl.head_groups;
+  k.slots = a.B * a.Q;
   k.out = a.out;
   k.lse = a.lse;
   k.part = (float*)a.ws;
-  dim3 grid((unsigned)(pl.splits * pl.head_groups), (unsigned)(a.B * a.Q));
+  // 1-D grid padded to whole XCD rounds (8 x head groups); padding workgroups exit at once
+  const int64_t units = (int64_t)pl.splits * a.B * a.Q;
+  const int64_t per_round = 8LL * pl.head_groups;
+  dim3 grid((unsigned)(((units + 7) / 8) * per_round));
   hipError_t e;
+  a.prof.before(s);
   if (a.fmt == CSAH_FMT_ROW_E4M3_BF16)
     e = a.q_dtype == CSAH_DT_BF16 ? launch_fmt<CSAH_FMT_ROW_E4M3_BF16, CSAH_DT_BF16>(a, k, grid, s)
                                   : launch_fmt<CSAH_FMT_ROW_E4M3_BF16, CSAH_DT_F32>(a, k, grid, s);
   else
     e = a.q_dtype == CSAH_DT_BF16 ? launch_fmt<CSAH_FMT_ROW_F32, CSAH_DT_BF16>(a, k, grid, s)
                                   : launch_fmt<CSAH_FMT_ROW_F32, CSAH_DT_F32>(a, k, grid, s);
+  a.prof.after(s);
   if (e != hipSuccess || pl.splits == 1) return e;
   dim3 mg((unsigned)a.H, (unsigned)(a.B * a.Q));
   if (a.D == 512)

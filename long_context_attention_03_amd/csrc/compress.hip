@@ -8,12 +8,14 @@
 //
 //   z_t = w . x_t + beta[t - g m],  pi = softmax(z),  c_g = sum_t pi_t x_t.
 //
-// One wavefront owns one group. Lane l owns DPL = D/64 consecutive dimensions, so every token
-// row is read with one coalesced vector load per lane. The softmax is evaluated online in one pass
-// over the group (running max, running denominator, running weighted sum), which keeps a group of
-// any size in registers. The gate dot product is a wavefront reduction per token. The pooled row
-// is then encoded in the output format by the same wavefront and written with vector stores.
-// HBM traffic is one read of the raw rows and one write of the compressed rows.
+// Lane l of a wavefront owns DPL = D/64 consecutive dimensions, so every token row is read with
+// one coalesced vector load per lane. Tokens go in batches of 8 whose loads and gate reductions
+// (wavefront butterflies) are in flight together. The softmax is evaluated online (running max,
+// running denominator, running weighted sum), which keeps a group of any size in registers. Short
+// groups take one wavefront each; long groups (m > 16) take a workgroup whose 4 wavefronts pool
+// a quarter of the tokens each and merge their states in LDS. The pooled row is encoded in the
+// output format and written with vector stores. HBM traffic is one read of the raw rows and one
+// write of the compressed rows.
 #include "csah_internal.h"
 #include "device_common.h"
 
@@ -54,40 +56,101 @@ __device__ __forceinline__ void load_token(const void* raw, int64_t row, int lan
   }
 }
 
-template <int DPL, bool RAW_BF16, int OUT_FMT>
+constexpr int kTokBatch = 8;  // tokens whose loads and gate reductions are in flight together
+
+// WAVES = 1: one wavefront per group, 4 groups per workgroup (small m).
+// WAVES = 4: one workgroup per group; wavefront w pools tokens [w*ceil(m/4), ...) and the four
+//            online-softmax states (max, sum, weighted sum) are merged in LDS.
+template <int DPL, bool RAW_BF16, int OUT_FMT, int WAVES>
 __global__ __launch_bounds__(256) void kv_compress_kernel(
     const void* __restrict__ raw, int64_t raw_seq_stride, int B, int64_t G, int m,
     const float* __restrict__ w, const float* __restrict__ beta, uint8_t* __restrict__ out_rows,
     int64_t out_seq_stride, uint8_t* __restrict__ out_scales) {
   constexpr int D = DPL * 64;
-  const int lane = threadIdx.x & 63;
-  const int64_t gid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (gid >= (int64_t)B * G) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t gid = WAVES == 1 ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
+  if (gid >= (int64_t)B * G) return;  // uniform per wavefront (WAVES = 1) or workgroup (4)
   const int64_t b = gid / G, g = gid - b * G;
 
   float wv[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; e++) wv[e] = w[lane * DPL + e];
 
+  int t_begin = 0, t_end = m;
+  if constexpr (WAVES > 1) {
+    const int per = (m + WAVES - 1) / WAVES;
+    t_begin = wave * per;
+    t_end = t_begin + per < m ? t_begin + per : m;
+  }
   float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; e++) acc[e] = 0.0f;
   float M = -INFINITY, L = 0.0f;
   const int64_t row0 = b * raw_seq_stride + g * m;
-  for (int t = 0; t < m; t++) {
-    float x[DPL];
-    load_token<DPL, RAW_BF16>(raw, row0 + t, lane, x);
-    float z = 0.0f;
+  for (int t0 = t_begin; t0 < t_end; t0 += kTokBatch) {
+    float x[kTokBatch][DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; e++) z = fmaf(wv[e], x[e], z);
-    z = wave_sum(z) + beta[t];
-    const float Mn = fmaxf(M, z);
-    const float sc = expf(M - Mn);  // 0 on the first token (M = -inf)
-    const float p = expf(z - Mn);
+    for (int u = 0; u < kTokBatch; u++) {
+      const int t = t0 + u < t_end ? t0 + u : t_end - 1;  // clamped: loads stay unconditional
+      load_token<DPL, RAW_BF16>(raw, row0 + t, lane, x[u]);
+    }
+    float z[kTokBatch];
 #pragma unroll
-    for (int e = 0; e < DPL; e++) acc[e] = fmaf(acc[e], sc, p * x[e]);
-    L = fmaf(L, sc, p);
+    for (int u = 0; u < kTokBatch; u++) {
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < DPL; e++) s = fmaf(wv[e], x[u][e], s);
+      z[u] = s;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+      for (int u = 0; u < kTokBatch; u++) z[u] += __shfl_xor(z[u], o, 64);
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kTokBatch; u++) {
+      z[u] = t0 + u < t_end ? z[u] + beta[t0 + u] : -INFINITY;
+      bmax = fmaxf(bmax, z[u]);
+    }
+    const float Mn = fmaxf(M, bmax);
+    const float sc = expf(M - Mn);  // 0 on the first batch (M = -inf)
+#pragma unroll
+    for (int e = 0; e < DPL; e++) acc[e] *= sc;
+    L *= sc;
+#pragma unroll
+    for (int u = 0; u < kTokBatch; u++) {
+      const float p = expf(z[u] - Mn);  // 0 for padding tokens
+#pragma unroll
+      for (int e = 0; e < DPL; e++) acc[e] = fmaf(p, x[u][e], acc[e]);
+      L += p;
+    }
     M = Mn;
+  }
+  if constexpr (WAVES > 1) {
+    __shared__ float s_acc[WAVES][D];
+    __shared__ float s_ml[WAVES][2];
+#pragma unroll
+    for (int e = 0; e < DPL; e++) s_acc[wave][lane * DPL + e] = acc[e];
+    if (lane == 0) {
+      s_ml[wave][0] = M;
+      s_ml[wave][1] = L;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < WAVES; v++) Mt = fmaxf(Mt, s_ml[v][0]);
+    L = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL; e++) acc[e] = 0.0f;
+#pragma unroll
+    for (int v = 0; v < WAVES; v++) {
+      const float mv = s_ml[v][0];
+      const float f = mv == -INFINITY ? 0.0f : expf(mv - Mt);
+      L = fmaf(s_ml[v][1], f, L);
+#pragma unroll
+      for (int e = 0; e < DPL; e++) acc[e] = fmaf(s_acc[v][lane * DPL + e], f, acc[e]);
+    }
   }
   float c[DPL];
 #pragma unroll
@@ -134,49 +197,55 @@ __global__ __launch_bounds__(256) void kv_compress_kernel(
       sexp = sexp < -127 ? -127 : (sexp > 127 ? 127 : sexp);
     }
     uint8_t* o = out_rows + orow * (int64_t)(D / 2) + lane * (DPL / 2);
-    uint32_t packed[DPL / 2 > 0 ? DPL / 2 : 1];
     uint32_t nib[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; e++) nib[e] = f32_to_e2m1(ldexpf(c[e], -sexp));
     if constexpr (DPL == 1) {
       // two lanes share a byte: the even lane writes (own | neighbour << 4)
       uint32_t other = (uint32_t)__shfl_xor((int)nib[0], 1, 64);
-      if ((lane & 1) == 0) out_rows[orow * (int64_t)(D / 2) + lane / 2] = (uint8_t)(nib[0] | (other << 4));
+      if ((lane & 1) == 0)
+        out_rows[orow * (int64_t)(D / 2) + lane / 2] = (uint8_t)(nib[0] | (other << 4));
     } else {
 #pragma unroll
-      for (int e = 0; e < DPL / 2; e++) packed[e] = nib[2 * e] | (nib[2 * e + 1] << 4);
-#pragma unroll
-      for (int e = 0; e < DPL / 2; e++) o[e] = (uint8_t)packed[e];
+      for (int e = 0; e < DPL / 2; e++) o[e] = (uint8_t)(nib[2 * e] | (nib[2 * e + 1] << 4));
     }
     if (lane % LPB == 0) out_scales[orow * (int64_t)(D / 32) + lane / LPB] = (uint8_t)(sexp + 127);
   }
 }
 
-template <int DPL, bool RAW_BF16>
-static hipError_t launch_dpl(const KvCompressArgs& a) {
+template <int DPL, bool RAW_BF16, int WAVES>
+static hipError_t launch_waves(const KvCompressArgs& a) {
   const int64_t groups = (int64_t)a.B * a.G;
-  dim3 grid((unsigned)((groups + 3) / 4)), block(256);
+  dim3 grid((unsigned)(WAVES == 1 ? (groups + 3) / 4 : groups)), block(256);
   hipStream_t s = (hipStream_t)a.stream;
+  a.prof.before(s);
   switch (a.out_fmt) {
     case CSAH_FMT_ROW_F32:
-      kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_F32><<<grid, block, 0, s>>>(
+      kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_F32, WAVES><<<grid, block, 0, s>>>(
           a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.w, a.beta, (uint8_t*)a.out_rows,
           a.out_seq_stride, a.out_scales);
       break;
     case CSAH_FMT_ROW_E4M3_BF16:
       if constexpr (DPL == 8)
-        kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_E4M3_BF16><<<grid, block, 0, s>>>(
+        kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_E4M3_BF16, WAVES><<<grid, block, 0, s>>>(
             a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.w, a.beta, (uint8_t*)a.out_rows,
             a.out_seq_stride, a.out_scales);
       else
         return hipErrorInvalidValue;
       break;
     default:
-      kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_FP4_E8M0><<<grid, block, 0, s>>>(
+      kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_FP4_E8M0, WAVES><<<grid, block, 0, s>>>(
           a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.w, a.beta, (uint8_t*)a.out_rows,
           a.out_seq_stride, a.out_scales);
   }
+  a.prof.after(s);
   return hipGetLastError();
+}
+
+template <int DPL, bool RAW_BF16>
+static hipError_t launch_dpl(const KvCompressArgs& a) {
+  // a whole workgroup per group once the group is long enough to keep 4 wavefronts busy
+  return a.m > 2 * kTokBatch ? launch_waves<DPL, RAW_BF16, 4>(a) : launch_waves<DPL, RAW_BF16, 1>(a);
 }
 
 template <bool RAW_BF16>

@@ -9,6 +9,17 @@
 
 namespace csah {
 
+// Events recorded around a call's dominant kernel (both null: no recording).
+struct ProfileHook {
+  hipEvent_t begin = nullptr, end = nullptr;
+  void before(hipStream_t s) const {
+    if (begin) (void)hipEventRecord(begin, s);
+  }
+  void after(hipStream_t s) const {
+    if (end) (void)hipEventRecord(end, s);
+  }
+};
+
 struct KvCompressArgs {
   const void* raw;
   int raw_dtype;
@@ -23,6 +34,7 @@ struct KvCompressArgs {
   int64_t out_seq_stride;
   uint8_t* out_scales;
   void* stream;
+  ProfileHook prof;
 };
 hipError_t launch_kv_compress(const KvCompressArgs& a);
 
@@ -41,6 +53,7 @@ struct IndexArgs {
   void* ws;
   size_t ws_bytes;
   void* stream;
+  ProfileHook prof;
 };
 size_t index_workspace_bytes(int B, int Q, int64_t N, int k, int dI);
 hipError_t launch_index_topk(const IndexArgs& a);
@@ -75,6 +88,7 @@ struct AttendArgs {
   size_t ws_bytes;
   void* stream;
   int64_t max_rows;
+  ProfileHook prof;
 };
 hipError_t launch_attend(const AttendArgs& a);
 

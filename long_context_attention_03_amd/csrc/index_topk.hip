@@ -16,24 +16,28 @@
 // fewer than 24 bits of the finest granularity each fp32 operation is exact: the result is the
 // exact score in any order, and the selection below is bit-exact.
 //
-// Pipeline per (sequence, query) "slot":
+// Pipeline per (sequence, query) "slot", four kernels (kernel boundaries carry the cross-workgroup
+// dependencies; on multi-XCD gfx950 a device-scope release fence per workgroup costs more than a
+// launch):
 //   prep      qt (fp32, dI values) + clear the histogram / counters        (1 WG per slot)
 //   scan      stream the FP4 keys (coalesced 16-byte loads, one 32-element block per lane,
-//             dI/32 lanes per entry), write fp32 scores, build a 2048-bin histogram of the top
-//             11 bits of each score's order key in LDS, flush it with global atomics
-//   collect   find the bin holding the k-th largest score; entries above it ("sure") and in it
-//             ("tie") are appended with one atomic per wavefront, as 64-bit keys
-//             (order_key(score) << 32 | ~g), unique per entry
-//   finalize  one WG per slot: bitonic sort of the candidates in LDS (descending key = score
-//             descending, index ascending); a radix select over the tie list first when the
-//             candidates exceed LDS (massive ties)
+//             dI/32 lanes per entry, loads double-buffered), write fp32 scores, build a 4096-bin
+//             histogram of the top 12 bits of each score's order key in LDS, flush it with
+//             global atomics
+//   select    every workgroup finds the bin holding the k-th largest score from the histogram;
+//             entries above it ("sure") and in it ("tie") are appended as 64-bit keys
+//             (order_key(score) << 32 | ~g, unique per entry) at offsets from a block prefix sum
+//             and one atomic per workgroup and list
+//   finalize  one workgroup per slot sorts the candidates in LDS (bitonic, descending key =
+//             score descending, index ascending); when they exceed LDS (massive ties) it first
+//             radix-selects the tie list
 #include "csah_internal.h"
 #include "device_common.h"
 
 namespace csah {
 
-constexpr int kBins = 2048;
-constexpr int kBinShift = 21;  // top 11 bits of the order key
+constexpr int kBins = 4096;
+constexpr int kBinShift = 20;  // top 12 bits of the order key
 constexpr int kSortCap = 4096;
 
 struct IdxWs {
@@ -95,7 +99,6 @@ __global__ __launch_bounds__(256) void index_prep_kernel(const uint8_t* __restri
 }
 
 // ---- scan --------------------------------------------------------------------------------------
-template <int NB>
 __device__ __forceinline__ float block_dot(const u32x4 c, const float* qv) {
   float t = 0.0f;
 #pragma unroll
@@ -116,12 +119,59 @@ __device__ __forceinline__ float block_dot(const u32x4 c, const float* qv) {
   return t;
 }
 
+// Threshold bin of the kk-th largest score from the histogram written by the previous
+// kernel (h, suf in LDS).
+__device__ void find_threshold_bin(const uint32_t* __restrict__ gh, int64_t kk, uint32_t* h,
+                                   uint32_t* suf, uint32_t* out_bin, uint32_t* out_above) {
+  // threads >= 256 only take part in the barriers
+  const int t = threadIdx.x;
+  if (t < 256) {
+    uint32_t local = 0;
+#pragma unroll
+    for (int j = 0; j < kBins / 256; j++) {
+      const uint32_t c = gh[t * (kBins / 256) + j];
+      h[t * (kBins / 256) + j] = c;
+      local += c;
+    }
+    suf[t] = local;
+  }
+  __syncthreads();
+  // inclusive suffix sum over the 256 groups (Hillis-Steele)
+  for (int o = 1; o < 256; o <<= 1) {
+    uint32_t add = 0;
+    if (t < 256) add = (t + o < 256) ? suf[t + o] : 0u;
+    __syncthreads();
+    if (t < 256) suf[t] += add;
+    __syncthreads();
+  }
+  if (t < 256) {
+    const uint32_t mine = suf[t];
+    const uint32_t next = t < 255 ? suf[t + 1] : 0u;
+    if ((int64_t)mine >= kk && (int64_t)next < kk) {
+      uint32_t above = next;
+      uint32_t bin = t * (kBins / 256);
+      for (int j = kBins / 256 - 1; j >= 0; j--) {
+        const uint32_t c = h[t * (kBins / 256) + j];
+        if ((int64_t)(above + c) >= kk) {
+          bin = t * (kBins / 256) + j;
+          break;
+        }
+        above += c;
+      }
+      *out_bin = bin;
+      *out_above = above;
+    }
+  }
+  __syncthreads();
+}
+
 template <int NB, int U>
 __global__ __launch_bounds__(256) void index_scan_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
     int64_t k_seq_stride, int64_t N, const int64_t* __restrict__ pos, int m, int Q, int chunk,
     IdxWs ws) {
-  constexpr int EPR = 256 / NB;  // entries per WG row of lanes
+  constexpr int EPR = 256 / NB;          // entries per WG row of lanes
+  constexpr int STEP = EPR * U;          // entries per buffered group
   const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
   const int tid = threadIdx.x, sub = tid % NB, ent = tid / NB;
   __shared__ uint32_t hist[kBins];
@@ -139,24 +189,21 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
     const uint8_t* kc = k_codes + (int64_t)b * k_seq_stride * (16 * NB) + 16 * sub;
     const uint8_t* ks = k_scales + (int64_t)b * k_seq_stride * NB + sub;
     float* sc = ws.scores(slot);
-    for (int64_t gb = g0 + ent; gb < g1; gb += (int64_t)EPR * U) {
-      u32x4 c[U];
-      uint32_t e[U];
+    // loads are unconditional (clamped to the last entry) so a group's loads fly together
+    auto load = [&](int64_t gb, u32x4* c, uint32_t* e) {
 #pragma unroll
       for (int u = 0; u < U; u++) {
-        const int64_t g = gb + (int64_t)u * EPR;
-        if (g < g1) {
-          c[u] = __builtin_nontemporal_load((const u32x4*)(kc + g * (16 * NB)));
-          e[u] = ks[g * NB];
-        } else {
-          c[u] = u32x4{0, 0, 0, 0};
-          e[u] = 127;
-        }
+        int64_t g = gb + (int64_t)u * EPR;
+        g = g < g1 ? g : g1 - 1;
+        c[u] = __builtin_nontemporal_load((const u32x4*)(kc + g * (16 * NB)));
+        e[u] = ks[g * NB];
       }
+    };
+    auto score = [&](int64_t gb, const u32x4* c, const uint32_t* e) {
 #pragma unroll
       for (int u = 0; u < U; u++) {
         const int64_t g = gb + (int64_t)u * EPR;
-        float s = block_dot<NB>(c[u], qv) * e8m0_to_f32(e[u]);
+        float s = block_dot(c[u], qv) * e8m0_to_f32(e[u]);
         if constexpr (NB >= 2) s = quad_xor1_add(s);
         if constexpr (NB >= 4) s = quad_xor2_add(s);
         s = s + 0.0f;  // fold -0 into +0: equal scores must get equal keys
@@ -165,6 +212,18 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
           atomicAdd(&hist[order_key(s) >> kBinShift], 1u);
         }
       }
+    };
+    // control flow depends only on workgroup-uniform values
+    u32x4 ca[U], cb[U];
+    uint32_t ea[U], eb[U];
+    load(g0 + ent, ca, ea);
+    for (int64_t gw = g0; gw < g1; gw += 2 * STEP) {
+      const bool has_b = gw + STEP < g1;
+      if (has_b) load(gw + STEP + ent, cb, eb);
+      score(gw + ent, ca, ea);
+      if (!has_b) break;
+      if (gw + 2 * STEP < g1) load(gw + 2 * STEP + ent, ca, ea);
+      score(gw + STEP + ent, cb, eb);
     }
   }
   __syncthreads();
@@ -175,94 +234,9 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
   }
 }
 
-// ---- threshold + candidate collection ----------------------------------------------------------
-__device__ void find_threshold_bin(const uint32_t* __restrict__ gh, int64_t kk, uint32_t* h,
-                                   uint32_t* suf, int* out_bin, uint32_t* out_above) {
-  // h: kBins counts, suf: 256 partial sums (8 bins per thread), both in LDS.
-  const int t = threadIdx.x;
-  uint32_t local = 0;
-#pragma unroll
-  for (int j = 0; j < kBins / 256; j++) {
-    const uint32_t c = gh[t * (kBins / 256) + j];
-    h[t * (kBins / 256) + j] = c;
-    local += c;
-  }
-  suf[t] = local;
-  __syncthreads();
-  // inclusive suffix sum over the 256 groups (Hillis-Steele)
-  for (int o = 1; o < 256; o <<= 1) {
-    const uint32_t add = (t + o < 256) ? suf[t + o] : 0u;
-    __syncthreads();
-    suf[t] += add;
-    __syncthreads();
-  }
-  const uint32_t mine = suf[t];
-  const uint32_t next = t < 255 ? suf[t + 1] : 0u;
-  if ((int64_t)mine >= kk && (int64_t)next < kk) {
-    uint32_t above = next;
-    int bin = t * (kBins / 256);
-    for (int j = kBins / 256 - 1; j >= 0; j--) {
-      const uint32_t c = h[t * (kBins / 256) + j];
-      if ((int64_t)(above + c) >= kk) { bin = t * (kBins / 256) + j; break; }
-      above += c;
-    }
-    *out_bin = bin;
-    *out_above = above;
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ void wave_append(bool p, uint64_t key, uint32_t* counter,
-                                            uint64_t* list, uint64_t cap) {
-  const uint64_t mask = ballot64(p);
-  if (!mask) return;
-  const int lane = threadIdx.x & 63;
-  const int leader = __builtin_ctzll(mask);
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(counter, (uint32_t)__builtin_popcountll(mask));
-  base = (uint32_t)__shfl((int)base, leader, 64);
-  if (p) {
-    const uint64_t at = (uint64_t)base + lanes_below(mask);
-    if (at < cap) list[at] = key;
-  }
-}
-
-__global__ __launch_bounds__(256) void index_collect_kernel(const int64_t* __restrict__ pos, int m,
-                                                             int Q, int64_t N, int k, int chunk,
-                                                             IdxWs ws) {
-  const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
-  const int64_t nv = visible_entries(pos, b, i, m, N);
-  const int64_t kk = nv < k ? nv : k;
-  const int64_t g0 = (int64_t)blockIdx.x * chunk;
-  if (kk == 0 || g0 >= nv) return;
-  __shared__ uint32_t h[kBins];
-  __shared__ uint32_t suf[256];
-  __shared__ int s_bin;
-  __shared__ uint32_t s_above;
-  find_threshold_bin(ws.hist(slot), kk, h, suf, &s_bin, &s_above);
-  const uint32_t bstar = (uint32_t)s_bin;
-  const int64_t g1 = g0 + chunk < nv ? g0 + chunk : nv;
-  const float* sc = ws.scores(slot);
-  uint32_t* ctr = ws.ctr(slot);
-  for (int64_t gb = g0; gb < g1; gb += 256) {
-    const int64_t g = gb + threadIdx.x;
-    bool sure = false, tie = false;
-    uint64_t key = 0;
-    if (g < g1) {
-      const uint32_t ok = order_key(sc[g]);
-      const uint32_t bin = ok >> kBinShift;
-      sure = bin > bstar;
-      tie = bin == bstar;
-      key = ((uint64_t)ok << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)g);
-    }
-    wave_append(sure, key, &ctr[0], ws.sure(slot), (uint64_t)k);
-    wave_append(tie, key, &ctr[1], ws.tie(slot), (uint64_t)N);
-  }
-}
-
-// ---- finalize ----------------------------------------------------------------------------------
+// ---- select: candidates above / in the threshold bin, then the exact ordered top-k ----------
 __device__ void bitonic_sort_desc(uint64_t* s, int n) {
-  // n: power of two; 1024 threads
+  // n: power of two; all threads of the block
   for (int size = 2; size <= n; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int t = threadIdx.x; t < n / 2; t += blockDim.x) {
@@ -270,26 +244,26 @@ __device__ void bitonic_sort_desc(uint64_t* s, int n) {
         const int c = a + stride;
         const uint64_t x = s[a], y = s[c];
         const bool desc = (a & size) == 0;
-        if (desc ? (x < y) : (x > y)) { s[a] = y; s[c] = x; }
+        if (desc ? (x < y) : (x > y)) {
+          s[a] = y;
+          s[c] = x;
+        }
       }
       __syncthreads();
     }
   }
 }
 
-__global__ __launch_bounds__(1024) void index_finalize_kernel(const int64_t* __restrict__ pos,
-                                                               int m, int Q, int64_t N, int k,
-                                                               int32_t* __restrict__ idx_out,
-                                                               float* __restrict__ score_out,
-                                                               IdxWs ws) {
-  const int slot = blockIdx.x, b = slot / Q, i = slot - b * Q;
-  const int t = threadIdx.x;
-  const int64_t nv = visible_entries(pos, b, i, m, N);
-  const int kk = (int)(nv < k ? nv : k);
-  __shared__ uint64_t keys[kSortCap];
-  __shared__ uint32_t dh[256];
+constexpr int kSelThreads = 1024;
+constexpr int kSelPerThread = 8;
+constexpr int kSelChunk = kSelThreads * kSelPerThread;
+
+__device__ void finalize_slot(int slot, int64_t N, int k, int kk, int32_t* __restrict__ idx_out,
+                              float* __restrict__ score_out, IdxWs ws, uint64_t* keys,
+                              uint32_t* dh) {
   __shared__ uint64_t s_prefix, s_pmask;
   __shared__ uint32_t s_r, s_cnt;
+  const int t = threadIdx.x;
   int32_t* io = idx_out + (int64_t)slot * k;
   float* so = score_out ? score_out + (int64_t)slot * k : nullptr;
   if (kk == 0) {
@@ -299,7 +273,7 @@ __global__ __launch_bounds__(1024) void index_finalize_kernel(const int64_t* __r
     }
     return;
   }
-  const uint32_t* ctr = ws.ctr(slot);
+  uint32_t* ctr = ws.ctr(slot);
   uint32_t ns = ctr[0], nt = ctr[1];
   ns = ns > (uint32_t)kk ? (uint32_t)kk : ns;
   nt = (int64_t)nt > N ? (uint32_t)N : nt;
@@ -311,14 +285,16 @@ __global__ __launch_bounds__(1024) void index_finalize_kernel(const int64_t* __r
     for (int j = t; j < n; j += blockDim.x) keys[j] = j < (int)ns ? sure[j] : tie[j - ns];
   } else {
     // radix select the r-th largest tie key (keys are unique), 8 bits at a time below the bin
+    constexpr int kLowBits = 64 - (32 - kBinShift);  // key bits below the shared bin
     if (t == 0) {
       s_r = (uint32_t)kk - ns;
       s_prefix = 0;
       s_pmask = 0;
     }
     __syncthreads();
-    for (int shift = 45;; shift = shift > 8 ? shift - 8 : 0) {
-      const int width = shift >= 5 ? 8 : 5;
+    for (int hi = kLowBits; hi > 0;) {
+      const int width = hi >= 8 ? 8 : hi;
+      const int shift = hi - width;
       const uint64_t dmask = ((uint64_t)1 << width) - 1;
       for (int j = t; j < 256; j += blockDim.x) dh[j] = 0;
       __syncthreads();
@@ -340,10 +316,10 @@ __global__ __launch_bounds__(1024) void index_finalize_kernel(const int64_t* __r
         s_pmask = pm | (dmask << shift);
       }
       __syncthreads();
-      if (shift == 0) break;
+      hi = shift;
     }
-    // bits above 53 are the (shared) bin: compare the low 53 bits only
-    const uint64_t low = ((uint64_t)1 << 53) - 1;
+    // bits above kLowBits are the (shared) bin: compare the low bits only
+    const uint64_t low = ((uint64_t)1 << kLowBits) - 1;
     const uint64_t thr = s_prefix;
     if (t == 0) s_cnt = 0;
     __syncthreads();
@@ -375,9 +351,92 @@ __global__ __launch_bounds__(1024) void index_finalize_kernel(const int64_t* __r
   }
 }
 
+__global__ __launch_bounds__(kSelThreads) void index_select_kernel(
+    const int64_t* __restrict__ pos, int m, int Q, int64_t N, int k, IdxWs ws) {
+  const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t nv = visible_entries(pos, b, i, m, N);
+  const int kk = (int)(nv < k ? nv : k);
+  if (kk == 0 || (int64_t)blockIdx.x * kSelChunk >= nv) return;
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t suf[256];
+  __shared__ uint32_t s_bin, s_above;
+  __shared__ uint32_t wsum[kSelThreads / 64];
+  __shared__ uint32_t s_base[2];
+  uint32_t* ctr = ws.ctr(slot);
+  const int64_t g0 = (int64_t)blockIdx.x * kSelChunk + (int64_t)t * kSelPerThread;
+  const float* sc = ws.scores(slot);
+  float v[kSelPerThread];
+  if (g0 + kSelPerThread <= nv) {
+    const f32x4 a = *(const f32x4*)(sc + g0), c = *(const f32x4*)(sc + g0 + 4);
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    v[4] = c[0]; v[5] = c[1]; v[6] = c[2]; v[7] = c[3];
+  } else {
+#pragma unroll
+    for (int e = 0; e < kSelPerThread; e++) v[e] = g0 + e < nv ? sc[g0 + e] : -INFINITY;
+  }
+  find_threshold_bin(ws.hist(slot), kk, h, suf, &s_bin, &s_above);
+  const uint32_t bstar = s_bin;
+  uint32_t cls[kSelPerThread];  // 0 drop, 1 sure, 2 tie
+  uint32_t cnt = 0;             // sure count | tie count << 16
+#pragma unroll
+  for (int e = 0; e < kSelPerThread; e++) {
+    const uint32_t bin = order_key(v[e]) >> kBinShift;
+    cls[e] = (g0 + e < nv) ? (bin > bstar ? 1u : (bin == bstar ? 2u : 0u)) : 0u;
+    cnt += cls[e] == 1u ? 1u : (cls[e] == 2u ? 0x10000u : 0u);
+  }
+  // block-wide exclusive prefix of (sure, tie) counts; one atomic per list per workgroup
+  uint32_t incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  if (t == 0) {
+    uint32_t tot = 0;
+    for (int w = 0; w < kSelThreads / 64; w++) {
+      const uint32_t x = wsum[w];
+      wsum[w] = tot;
+      tot += x;
+    }
+    s_base[0] = (tot & 0xFFFFu) ? atomicAdd(&ctr[0], tot & 0xFFFFu) : 0u;
+    s_base[1] = (tot >> 16) ? atomicAdd(&ctr[1], tot >> 16) : 0u;
+  }
+  __syncthreads();
+  const uint32_t excl = wsum[wave] + incl - cnt;
+  uint32_t ps = s_base[0] + (excl & 0xFFFFu), pt = s_base[1] + (excl >> 16);
+  uint64_t* sure = ws.sure(slot);
+  uint64_t* tie = ws.tie(slot);
+#pragma unroll
+  for (int e = 0; e < kSelPerThread; e++) {
+    const uint64_t key = ((uint64_t)order_key(v[e]) << 32) |
+                         (uint64_t)(0xFFFFFFFFu - (uint32_t)(g0 + e));
+    if (cls[e] == 1u) {
+      if (ps < (uint32_t)k) sure[ps] = key;
+      ps++;
+    } else if (cls[e] == 2u) {
+      if ((int64_t)pt < N) tie[pt] = key;
+      pt++;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void index_finalize_kernel(
+    const int64_t* __restrict__ pos, int m, int Q, int64_t N, int k,
+    int32_t* __restrict__ idx_out, float* __restrict__ score_out, IdxWs ws) {
+  const int slot = blockIdx.x, b = slot / Q, i = slot - b * Q;
+  const int64_t nv = visible_entries(pos, b, i, m, N);
+  const int kk = (int)(nv < k ? nv : k);
+  __shared__ uint64_t keys[kSortCap];
+  __shared__ uint32_t dh[256];
+  finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh);
+}
+
 template <int NB>
 static void launch_scan(const IndexArgs& a, const IdxWs& w, int chunk, dim3 grid, hipStream_t s) {
-  index_scan_kernel<NB, 4><<<grid, 256, 0, s>>>(a.k_codes, a.k_scales, a.k_seq_stride, a.N, a.pos,
+  index_scan_kernel<NB, 2><<<grid, 256, 0, s>>>(a.k_codes, a.k_scales, a.k_seq_stride, a.N, a.pos,
                                                 a.m, a.Q, chunk, w);
 }
 
@@ -386,25 +445,26 @@ hipError_t launch_index_topk(const IndexArgs& a) {
   const int slots = a.B * a.Q;
   IdxWs w = make_ws(a.ws, a.N, a.k);
   index_prep_kernel<<<slots, 256, 0, s>>>(a.q_codes, a.q_scales, a.HI, a.dI, w);
-  // scan: about 2048 workgroups in total, each streaming a contiguous range of entries
+  // scan: about 1024 workgroups in total (four per CU), each streaming a contiguous range
   const int64_t total = (int64_t)slots * (a.N > 0 ? a.N : 1);
-  int64_t chunk = (total + 2047) / 2048;
+  int64_t chunk = (total + 1023) / 1024;
   chunk = ((chunk + 1023) / 1024) * 1024;
   if (chunk < 1024) chunk = 1024;
-  if (chunk > (1 << 20)) chunk = 1 << 20;
+  if (chunk > (1 << 22)) chunk = 1 << 22;
   const int64_t nchunks = a.N > 0 ? (a.N + chunk - 1) / chunk : 1;
   dim3 gs((unsigned)nchunks, (unsigned)slots);
+  a.prof.before(s);
   switch (a.dI) {
     case 32: launch_scan<1>(a, w, (int)chunk, gs, s); break;
     case 64: launch_scan<2>(a, w, (int)chunk, gs, s); break;
     default: launch_scan<4>(a, w, (int)chunk, gs, s); break;
   }
-  const int64_t cchunk = 16384;
-  const int64_t ncc = a.N > 0 ? (a.N + cchunk - 1) / cchunk : 1;
-  index_collect_kernel<<<dim3((unsigned)ncc, (unsigned)slots), 256, 0, s>>>(a.pos, a.m, a.Q, a.N,
-                                                                             a.k, (int)cchunk, w);
-  index_finalize_kernel<<<slots, 1024, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, a.idx_out, a.score_out,
-                                               w);
+  a.prof.after(s);
+  const int64_t nsel = a.N > 0 ? (a.N + kSelChunk - 1) / kSelChunk : 1;
+  index_select_kernel<<<dim3((unsigned)nsel, (unsigned)slots), kSelThreads, 0, s>>>(
+      a.pos, a.m, a.Q, a.N, a.k, w);
+  index_finalize_kernel<<<slots, kSelThreads, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, a.idx_out,
+                                                       a.score_out, w);
   return hipGetLastError();
 }
 

@@ -55,6 +55,7 @@ def lib():
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         sig = {
             "oc_version": (I, []),
+            "oc_num_threads": (I, []),
             "oc_e2m1_value": (D, [I]),
             "oc_e2m1_encode": (I, [D]),
             "oc_e8m0_value": (D, [I]),
@@ -91,6 +92,11 @@ def _check(rc, what):
 
 def _c(a, dtype):
     return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().oc_num_threads())
 
 
 # ------------------------------------------------------------------------------------ codecs

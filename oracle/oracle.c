@@ -50,6 +50,13 @@
 
 int oc_version(void) { return 1; }
 
+#ifdef _OPENMP
+#include <omp.h>
+int oc_num_threads(void) { return omp_get_max_threads(); }
+#else
+int oc_num_threads(void) { return 1; }
+#endif
+
 /* ------------------------------------------------------------------------------------------ */
 /* Rounding a real number onto a binary floating-point grid.                                   */
 /* p = significand bits (including the implicit one), emin = smallest normal exponent.         */
