@@ -21,16 +21,17 @@
 // launch):
 //   prep      qt (fp32, dI values) + clear the histogram / counters        (1 WG per slot)
 //   scan      stream the FP4 keys (coalesced 16-byte loads, one 32-element block per lane,
-//             dI/32 lanes per entry, loads double-buffered), write fp32 scores, build a 4096-bin
+//             dI/32 lanes per entry, 8 groups of loads in flight), write fp32 scores, build a 4096-bin
 //             histogram of the top 12 bits of each score's order key in LDS, flush it with
 //             global atomics
 //   select    every workgroup finds the bin holding the k-th largest score from the histogram;
 //             entries above it ("sure") and in it ("tie") are appended as 64-bit keys
 //             (order_key(score) << 32 | ~g, unique per entry) at offsets from a block prefix sum
 //             and one atomic per workgroup and list
-//   finalize  one workgroup per slot sorts the candidates in LDS (bitonic, descending key =
-//             score descending, index ascending); when they exceed LDS (massive ties) it first
-//             radix-selects the tie list
+//   rank      the output position of each candidate is the number of candidates with a greater
+//             key (keys are unique; descending key = score descending, index ascending), counted
+//             by 16 lanes per candidate over many workgroups; when the candidates exceed LDS
+//             (massive ties) one workgroup radix-selects the tie list and sorts in LDS
 #include "csah_internal.h"
 #include "device_common.h"
 
@@ -99,14 +100,17 @@ __global__ __launch_bounds__(256) void index_prep_kernel(const uint8_t* __restri
 }
 
 // ---- scan --------------------------------------------------------------------------------------
-__device__ __forceinline__ float block_dot(const u32x4 c, const float* qv) {
+// dI/32 consecutive lanes score one entry, one 32-element block each: a wavefront's 16-byte loads
+// cover one contiguous kilobyte of codes. Each lane holds its block's 32 head-summed query values.
+template <int NB>
+__device__ __forceinline__ float block_score(const u32x4 c, uint32_t e, const float* qv) {
   float t = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    f32x2 v0 = fp4x2_to_f32<0>(c[j]);
-    f32x2 v1 = fp4x2_to_f32<1>(c[j]);
-    f32x2 v2 = fp4x2_to_f32<2>(c[j]);
-    f32x2 v3 = fp4x2_to_f32<3>(c[j]);
+    const f32x2 v0 = fp4x2_to_f32<0>(c[j]);
+    const f32x2 v1 = fp4x2_to_f32<1>(c[j]);
+    const f32x2 v2 = fp4x2_to_f32<2>(c[j]);
+    const f32x2 v3 = fp4x2_to_f32<3>(c[j]);
     t = fmaf(v0[0], qv[8 * j + 0], t);
     t = fmaf(v0[1], qv[8 * j + 1], t);
     t = fmaf(v1[0], qv[8 * j + 2], t);
@@ -116,7 +120,79 @@ __device__ __forceinline__ float block_dot(const u32x4 c, const float* qv) {
     t = fmaf(v3[0], qv[8 * j + 6], t);
     t = fmaf(v3[1], qv[8 * j + 7], t);
   }
-  return t;
+  // times 2^(E-127): exact (the block sum is a multiple of a power of two well inside range)
+  float s = ldexpf(t, (int)e - 127);
+  if constexpr (NB >= 2) s = quad_xor1_add(s);
+  if constexpr (NB >= 4) s = quad_xor2_add(s);
+  return s + 0.0f;  // fold -0 into +0: equal scores must get equal keys
+}
+
+template <int NB>
+__global__ __launch_bounds__(256) void index_scan_kernel(
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
+    int64_t k_seq_stride, int64_t N, const int64_t* __restrict__ pos, int m, int Q, int chunk,
+    IdxWs ws) {
+  constexpr int EPR = 256 / NB;  // entries per workgroup-wide group of lanes
+  constexpr int U = 4;           // groups whose loads are in flight together
+  constexpr int STEP = EPR * U;
+  const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
+  const int tid = threadIdx.x, sub = tid % NB, ent = tid / NB;
+  __shared__ uint32_t hist[kBins];
+  for (int j = tid; j < kBins; j += 256) hist[j] = 0u;
+  __syncthreads();
+
+  const int64_t nv = visible_entries(pos, b, i, m, N);
+  const int64_t g0 = (int64_t)blockIdx.x * chunk;
+  const int64_t g1 = g0 + chunk < nv ? g0 + chunk : nv;
+  if (g0 < nv) {
+    float qv[32];
+    const float* qt = ws.qt(slot) + 32 * sub;
+#pragma unroll
+    for (int j = 0; j < 32; j++) qv[j] = qt[j];
+    // per-lane bases; offsets within a chunk fit in 32 bits
+    const uint8_t* kc = k_codes + ((int64_t)b * k_seq_stride + g0) * (16 * NB) + 16 * sub;
+    const uint8_t* ks = k_scales + ((int64_t)b * k_seq_stride + g0) * NB + sub;
+    float* sc = ws.scores(slot) + g0;
+    const int n = (int)(g1 - g0);
+    auto load = [&](int r0, u32x4* c, uint32_t* e, bool clamp) {
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        int r = r0 + u * EPR + ent;
+        if (clamp) r = r < n ? r : n - 1;
+        c[u] = __builtin_nontemporal_load((const u32x4*)(kc + (uint32_t)r * (16u * NB)));
+        e[u] = ks[(uint32_t)r * NB];
+      }
+    };
+    auto score = [&](int r0, const u32x4* c, const uint32_t* e) {
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const int r = r0 + u * EPR + ent;
+        const float s = block_score<NB>(c[u], e[u], qv);
+        if (sub == 0 && r < n) {
+          sc[r] = s;
+          atomicAdd(&hist[order_key(s) >> kBinShift], 1u);
+        }
+      }
+    };
+    // double-buffered groups; full groups need no clamping (control flow is workgroup-uniform)
+    u32x4 ca[U], cb[U];
+    uint32_t ea[U], eb[U];
+    load(0, ca, ea, STEP > n);
+    for (int r0 = 0; r0 < n; r0 += 2 * STEP) {
+      const bool has_b = r0 + STEP < n;
+      if (has_b) load(r0 + STEP, cb, eb, r0 + 2 * STEP > n);
+      score(r0, ca, ea);
+      if (!has_b) break;
+      if (r0 + 2 * STEP < n) load(r0 + 2 * STEP, ca, ea, r0 + 3 * STEP > n);
+      score(r0 + STEP, cb, eb);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = ws.hist(slot);
+  for (int j = tid; j < kBins; j += 256) {
+    const uint32_t c = hist[j];
+    if (c) atomicAdd(&gh[j], c);
+  }
 }
 
 // Threshold bin of the kk-th largest score from the histogram written by the previous
@@ -163,75 +239,6 @@ __device__ void find_threshold_bin(const uint32_t* __restrict__ gh, int64_t kk, 
     }
   }
   __syncthreads();
-}
-
-template <int NB, int U>
-__global__ __launch_bounds__(256) void index_scan_kernel(
-    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
-    int64_t k_seq_stride, int64_t N, const int64_t* __restrict__ pos, int m, int Q, int chunk,
-    IdxWs ws) {
-  constexpr int EPR = 256 / NB;          // entries per WG row of lanes
-  constexpr int STEP = EPR * U;          // entries per buffered group
-  const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
-  const int tid = threadIdx.x, sub = tid % NB, ent = tid / NB;
-  __shared__ uint32_t hist[kBins];
-  for (int j = tid; j < kBins; j += 256) hist[j] = 0u;
-  __syncthreads();
-
-  const int64_t nv = visible_entries(pos, b, i, m, N);
-  const int64_t g0 = (int64_t)blockIdx.x * chunk;
-  const int64_t g1 = g0 + chunk < nv ? g0 + chunk : nv;
-  if (g0 < nv) {
-    float qv[32];
-    const float* qt = ws.qt(slot) + 32 * sub;
-#pragma unroll
-    for (int j = 0; j < 32; j++) qv[j] = qt[j];
-    const uint8_t* kc = k_codes + (int64_t)b * k_seq_stride * (16 * NB) + 16 * sub;
-    const uint8_t* ks = k_scales + (int64_t)b * k_seq_stride * NB + sub;
-    float* sc = ws.scores(slot);
-    // loads are unconditional (clamped to the last entry) so a group's loads fly together
-    auto load = [&](int64_t gb, u32x4* c, uint32_t* e) {
-#pragma unroll
-      for (int u = 0; u < U; u++) {
-        int64_t g = gb + (int64_t)u * EPR;
-        g = g < g1 ? g : g1 - 1;
-        c[u] = __builtin_nontemporal_load((const u32x4*)(kc + g * (16 * NB)));
-        e[u] = ks[g * NB];
-      }
-    };
-    auto score = [&](int64_t gb, const u32x4* c, const uint32_t* e) {
-#pragma unroll
-      for (int u = 0; u < U; u++) {
-        const int64_t g = gb + (int64_t)u * EPR;
-        float s = block_dot(c[u], qv) * e8m0_to_f32(e[u]);
-        if constexpr (NB >= 2) s = quad_xor1_add(s);
-        if constexpr (NB >= 4) s = quad_xor2_add(s);
-        s = s + 0.0f;  // fold -0 into +0: equal scores must get equal keys
-        if (sub == 0 && g < g1) {
-          sc[g] = s;
-          atomicAdd(&hist[order_key(s) >> kBinShift], 1u);
-        }
-      }
-    };
-    // control flow depends only on workgroup-uniform values
-    u32x4 ca[U], cb[U];
-    uint32_t ea[U], eb[U];
-    load(g0 + ent, ca, ea);
-    for (int64_t gw = g0; gw < g1; gw += 2 * STEP) {
-      const bool has_b = gw + STEP < g1;
-      if (has_b) load(gw + STEP + ent, cb, eb);
-      score(gw + ent, ca, ea);
-      if (!has_b) break;
-      if (gw + 2 * STEP < g1) load(gw + 2 * STEP + ent, ca, ea);
-      score(gw + STEP + ent, cb, eb);
-    }
-  }
-  __syncthreads();
-  uint32_t* gh = ws.hist(slot);
-  for (int j = tid; j < kBins; j += 256) {
-    const uint32_t c = hist[j];
-    if (c) atomicAdd(&gh[j], c);
-  }
 }
 
 // ---- select: candidates above / in the threshold bin, then the exact ordered top-k ----------
@@ -423,21 +430,66 @@ __global__ __launch_bounds__(kSelThreads) void index_select_kernel(
   }
 }
 
-__global__ __launch_bounds__(kSelThreads) void index_finalize_kernel(
+// Ordered top-k by rank counting: keys are unique, so the output position of candidate x is the
+// number of candidates greater than x. A workgroup of 256 lanes ranks 16 candidates; each
+// 16-lane group splits the candidate list 16 ways and sums the partial counts with lane shuffles.
+// Massive ties (more candidates than kSortCap) fall back to finalize_slot in workgroup 0.
+constexpr int kRankThreads = 256;
+constexpr int kRankPerWG = kRankThreads / 16;
+
+__global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
     const int64_t* __restrict__ pos, int m, int Q, int64_t N, int k,
     int32_t* __restrict__ idx_out, float* __restrict__ score_out, IdxWs ws) {
-  const int slot = blockIdx.x, b = slot / Q, i = slot - b * Q;
+  const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
+  const int t = threadIdx.x;
   const int64_t nv = visible_entries(pos, b, i, m, N);
   const int kk = (int)(nv < k ? nv : k);
   __shared__ uint64_t keys[kSortCap];
   __shared__ uint32_t dh[256];
-  finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh);
+  const uint32_t* ctr = ws.ctr(slot);
+  uint32_t ns = 0, nt = 0;
+  if (kk > 0) {
+    ns = ctr[0];
+    nt = ctr[1];
+    ns = ns > (uint32_t)kk ? (uint32_t)kk : ns;
+    nt = (int64_t)nt > N ? (uint32_t)N : nt;
+  }
+  const uint32_t n = ns + nt;
+  if (kk == 0 || n > (uint32_t)kSortCap) {
+    if (blockIdx.x == 0) finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh);
+    return;
+  }
+  int32_t* io = idx_out + (int64_t)slot * k;
+  float* so = score_out ? score_out + (int64_t)slot * k : nullptr;
+  if (blockIdx.x == 0)
+    for (int j = kk + t; j < k; j += kRankThreads) {
+      io[j] = -1;
+      if (so) so[j] = -INFINITY;
+    }
+  const uint32_t e = (uint32_t)blockIdx.x * kRankPerWG + (t >> 4);  // candidate ranked here
+  if ((uint32_t)blockIdx.x * kRankPerWG >= n) return;
+  const uint64_t* sure = ws.sure(slot);
+  const uint64_t* tie = ws.tie(slot);
+  for (uint32_t j = t; j < n; j += kRankThreads) keys[j] = j < ns ? sure[j] : tie[j - ns];
+  __syncthreads();
+  const int part = t & 15;
+  const uint64_t x = e < n ? keys[e] : ~(uint64_t)0;
+  const uint32_t per = (n + 15) / 16;
+  const uint32_t j0 = part * per, j1 = j0 + per < n ? j0 + per : n;
+  uint32_t above = 0;
+  for (uint32_t j = j0; j < j1; j++) above += keys[j] > x ? 1u : 0u;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) above += (uint32_t)__shfl_xor((int)above, o, 64);
+  if (part == 0 && e < n && above < (uint32_t)kk) {
+    io[above] = (int32_t)(0xFFFFFFFFu - (uint32_t)x);
+    if (so) so[above] = key_to_float((uint32_t)(x >> 32));
+  }
 }
 
 template <int NB>
 static void launch_scan(const IndexArgs& a, const IdxWs& w, int chunk, dim3 grid, hipStream_t s) {
-  index_scan_kernel<NB, 2><<<grid, 256, 0, s>>>(a.k_codes, a.k_scales, a.k_seq_stride, a.N, a.pos,
-                                                a.m, a.Q, chunk, w);
+  index_scan_kernel<NB><<<grid, 256, 0, s>>>(a.k_codes, a.k_scales, a.k_seq_stride, a.N, a.pos,
+                                             a.m, a.Q, chunk, w);
 }
 
 hipError_t launch_index_topk(const IndexArgs& a) {
@@ -463,8 +515,10 @@ hipError_t launch_index_topk(const IndexArgs& a) {
   const int64_t nsel = a.N > 0 ? (a.N + kSelChunk - 1) / kSelChunk : 1;
   index_select_kernel<<<dim3((unsigned)nsel, (unsigned)slots), kSelThreads, 0, s>>>(
       a.pos, a.m, a.Q, a.N, a.k, w);
-  index_finalize_kernel<<<slots, kSelThreads, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, a.idx_out,
-                                                       a.score_out, w);
+  const int64_t cand = (a.N < kSortCap ? a.N : kSortCap);
+  const unsigned nrank = (unsigned)((cand + kRankPerWG - 1) / kRankPerWG);
+  index_rank_kernel<<<dim3(nrank > 0 ? nrank : 1, (unsigned)slots), kRankThreads, 0, s>>>(
+      a.pos, a.m, a.Q, a.N, a.k, a.idx_out, a.score_out, w);
   return hipGetLastError();
 }
 
