@@ -16,8 +16,9 @@ GPU with the library's own kv_compress (m = 1 is its quantiser). The step's work
 ~2.8 GB, so consecutive steps stream from HBM rather than from the 256 MB last-level cache.
 
 The timed region replays a HIP graph of the step (the eager launch path is CPU-bound); value is
-queries (sequences) per second. The roofline object reports the dominant kernel (the indexer
-scan) timed with HIP events around it on the library's stream (csah_profile_next_call). The
+queries (sequences) per second. The roofline object reports the kernel with the largest share of
+the step, timed with HIP events attached to its dispatch on the library's stream
+(csah_profile_next_call); the "kernels" object gives the same figures for every stage. The
 cpu_baseline object times the CPU oracle on one sequence of each layer.
 """
 from __future__ import annotations
@@ -155,9 +156,33 @@ def event_pair():
     return a, b
 
 
+# Algorithmic HBM bytes and flops per launch of each stage's dominant kernel: what the method must
+# move (selected rows, not the whole cache) and compute (QK and PV, 2 flops per MAC).
+#   index_scan: 4 sequences x 262,144 FP4 keys x (64 B codes + 4 B scales); 512 MAC per key.
+#   csa_attend: 4 x [(1024 + 128) rows x 576 B + 1024 ids x 4 B + q 64x512 bf16 + out 64x512 fp32
+#               + lse 64 fp32]; 64 heads x 1152 rows x 512 x 4 flops.
+#   hca_attend: 16 x [(8192 + 128) rows x 576 B + q + out + lse]; 64 x 8320 x 512 x 4 flops.
+KERNELS = {
+    "index_scan": dict(per_step=N_CSA_BATCHES, bytes=B_CSA * SCAN_BYTES_PER_SEQ,
+                       flops=B_CSA * N_CSA * 512 * 2, peak_flops=157.3e12,
+                       name="index_scan_kernel (csah_index_topk)", source="index_topk.hip",
+                       profile="index_scan_csa1m"),
+    "csa_attend": dict(per_step=N_CSA_BATCHES,
+                       bytes=B_CSA * ((K + W) * ROW + K * 4 + H * D * 2 + H * D * 4 + H * 4) + H * 4,
+                       flops=B_CSA * H * (K + W) * D * 4, peak_flops=2.5e15,
+                       name="attend_kernel (csah_csa_attend)", source="attend.hip",
+                       profile="csa_attend_csa1m"),
+    "hca_attend": dict(per_step=1,
+                       bytes=B_HCA * ((N_HCA + W) * ROW + H * D * 2 + H * D * 4 + H * 4) + H * 4,
+                       flops=B_HCA * H * (N_HCA + W) * D * 4, peak_flops=2.5e15,
+                       name="attend_kernel (csah_hca_attend)", source="attend.hip",
+                       profile="hca_attend_hca1m"),
+}
+
+
 def kernel_times(ws: DecodeStep, reps: int):
-    """Average duration (ms) of each stage's dominant kernel, from events around it."""
-    evs = {"index_scan": [], "csa_attend": [], "hca_attend": []}
+    """Average duration (ms) of each stage's dominant kernel, from events attached to its dispatch."""
+    evs = {k: [] for k in KERNELS}
     for _ in range(reps):
         for c in ws.csa:
             e = event_pair()
@@ -173,18 +198,41 @@ def kernel_times(ws: DecodeStep, reps: int):
     return {k: statistics.mean(a.elapsed_time(b) for a, b in v) for k, v in evs.items()}
 
 
-def traffic_from_profile():
-    """HBM bytes per scan launch from the committed counter summary, if it matches the source."""
-    path = os.path.join(ROOT, "profiles", "index_scan_csa1m_counters.json")
+def traffic_from_profile(kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the kernel's source.
+
+    profiles/<kernel>_<workload>_counters.txt holds `key = value` lines written from two rocprofv3 --pmc
+    runs (FETCH_SIZE, WRITE_SIZE) scaled by a copy-kernel calibration; its source_sha256_16 is the
+    hash of the .hip file the kernel was built from when the counters were taken.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{KERNELS[kernel]['profile']}_counters.txt")
     try:
+        rec = {}
         with open(path) as f:
-            rec = json.load(f)
-        import hashlib
-        src = os.path.join(ROOT, "long_context_attention_03_amd", "csrc", "index_topk.hip")
+            for ln in f:
+                if "=" in ln and not ln.lstrip().startswith("#"):
+                    k, v = ln.split("=", 1)
+                    rec[k.strip()] = v.strip()
+        src = os.path.join(ROOT, "long_context_attention_03_amd", "csrc", KERNELS[kernel]["source"])
         h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        return rec["hbm_bytes_per_launch"] if rec.get("source_sha256_16") == h else None
+        if rec.get("source_sha256_16") != h:
+            return None
+        return float(rec["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def copy_calibration(reps: int = 3):
+    """A plain device copy of known size (1 GiB read + 1 GiB written per launch), for scaling the
+    FETCH_SIZE / WRITE_SIZE counters of a --pmc run to bytes."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} launches of neg() over {n * 4} bytes in, {n * 4} bytes out")
 
 
 def cpu_baseline(min_seconds: float):
@@ -246,6 +294,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB copy kernel (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -286,8 +336,28 @@ def main():
     log(f"  {ms * 1e3:.1f} us per step")
     kt = kernel_times(ws, args.kernel_reps)
     log("  dominant kernels (us): " + ", ".join(f"{k} {v * 1e3:.2f}" for k, v in kt.items()))
-    scan_bytes = B_CSA * SCAN_BYTES_PER_SEQ
-    achieved = scan_bytes / (kt["index_scan"] * 1e-3) / 1e9
+    # the roofline object reports the kernel with the largest share of the step
+    dom = max(KERNELS, key=lambda k: KERNELS[k]["per_step"] * kt[k])
+    kinfo = {}
+    for k, spec in KERNELS.items():
+        t = kt[k] * 1e-3
+        t_hbm, t_mfma = spec["bytes"] / (PEAK_HBM_GBS * 1e9), spec["flops"] / spec["peak_flops"]
+        kinfo[k] = {"avg_launch_us": t * 1e6, "launches_per_step": spec["per_step"],
+                    "algorithmic_bytes_per_launch": spec["bytes"],
+                    "algorithmic_flops_per_launch": spec["flops"],
+                    "achieved_GBps": spec["bytes"] / t / 1e9,
+                    "achieved_TFLOPs": spec["flops"] / t / 1e12,
+                    "roofline_bound": "hbm" if t_hbm >= t_mfma else "compute",
+                    "frac_of_roofline": max(t_hbm, t_mfma) / t}
+    spec = KERNELS[dom]
+    t_dom = kt[dom] * 1e-3
+    if spec["bytes"] / (PEAK_HBM_GBS * 1e9) >= spec["flops"] / spec["peak_flops"]:
+        roof = {"bound": "hbm", "achieved": spec["bytes"] / t_dom / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma" if dom != "index_scan" else "alu",
+                "achieved": spec["flops"] / t_dom / 1e12, "peak": spec["peak_flops"] / 1e12,
+                "unit": "TFLOP/s"}
     queries = N_CSA_BATCHES * B_CSA
     line = {
         "metric": METRIC,
@@ -314,18 +384,17 @@ def main():
             "compute": "indexer scan fp32 (exact), attention bf16 MFMA with fp32 accumulation",
         },
         "roofline": {
-            "kernel": "index_scan_kernel (csah_index_topk, 4 x 262,144 entries)",
-            "bound": "hbm",
-            "achieved": achieved,
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBS,
-            "traffic": traffic_from_profile(),
-            "algorithmic_bytes_per_launch": scan_bytes,
-            "avg_launch_us": kt["index_scan"] * 1e3,
+            "kernel": spec["name"],
+            **roof,
+            "frac": roof["achieved"] / roof["peak"],
+            "traffic": traffic_from_profile(dom),
+            "algorithmic_bytes_per_launch": spec["bytes"],
+            "avg_launch_us": kt[dom] * 1e3,
         },
-        "kernels_us": {k: v * 1e3 for k, v in kt.items()},
+        "kernels": kinfo,
     }
+    if args.calibrate_copy:
+        copy_calibration()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one sequence per layer...")
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

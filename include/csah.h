@@ -168,10 +168,11 @@ int csah_hca_attend(const void* q, int q_dtype, int H, int D, const void* cache,
 
 /*
  * csah_profile_next_call -- profiling aid (not part of the method). The next csah_kv_compress,
- * csah_index_topk, csah_csa_attend or csah_hca_attend call made by the SAME host thread records
- * `begin` on its stream immediately before its dominant kernel and `end` immediately after it
- * (the compressor; the indexer scan; the attention kernel). Both are hipEvent_t passed as void*,
- * created by the caller; NULL for both cancels a pending request. The request is consumed by that
+ * csah_index_topk, csah_csa_attend or csah_hca_attend call made by the SAME host thread launches
+ * its dominant kernel (the compressor; the indexer scan; the attention kernel) with `begin` and
+ * `end` attached to that dispatch, so that hipEventElapsedTime(begin, end) is the kernel's own
+ * duration. Both are hipEvent_t passed as void*, created by the caller with timing enabled; NULL
+ * for both cancels a pending request. The request is consumed by that
  * next call whether or not it succeeds. Returns CSAH_OK, or CSAH_ERR_INVALID_ARGUMENT if exactly
  * one event is NULL.
  */

@@ -558,8 +558,8 @@ size_t attend_workspace_bytes(int B, int Q, int H, int D, int64_t max_rows) {
 
 template <int FMT, int QDT>
 static hipError_t launch_fmt(const AttendArgs& a, const AttendK& k, dim3 grid, hipStream_t s) {
-  if (a.idx) attend_kernel<FMT, QDT, false><<<grid, 256, 0, s>>>(k);
-  else attend_kernel<FMT, QDT, true><<<grid, 256, 0, s>>>(k);
+  if (a.idx) a.prof.launch(attend_kernel<FMT, QDT, false>, grid, dim3(256), s, k);
+  else a.prof.launch(attend_kernel<FMT, QDT, true>, grid, dim3(256), s, k);
   return hipGetLastError();
 }
 
@@ -594,14 +594,12 @@ hipError_t launch_attend(const AttendArgs& a) {
   const int64_t per_round = 8LL * pl.head_groups;
   dim3 grid((unsigned)(((units + 7) / 8) * per_round));
   hipError_t e;
-  a.prof.before(s);
   if (a.fmt == CSAH_FMT_ROW_E4M3_BF16)
     e = a.q_dtype == CSAH_DT_BF16 ? launch_fmt<CSAH_FMT_ROW_E4M3_BF16, CSAH_DT_BF16>(a, k, grid, s)
                                   : launch_fmt<CSAH_FMT_ROW_E4M3_BF16, CSAH_DT_F32>(a, k, grid, s);
   else
     e = a.q_dtype == CSAH_DT_BF16 ? launch_fmt<CSAH_FMT_ROW_F32, CSAH_DT_BF16>(a, k, grid, s)
                                   : launch_fmt<CSAH_FMT_ROW_F32, CSAH_DT_F32>(a, k, grid, s);
-  a.prof.after(s);
   if (e != hipSuccess || pl.splits == 1) return e;
   dim3 mg((unsigned)a.H, (unsigned)(a.B * a.Q));
   if (a.D == 512)

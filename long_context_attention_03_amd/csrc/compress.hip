@@ -218,27 +218,25 @@ static hipError_t launch_waves(const KvCompressArgs& a) {
   const int64_t groups = (int64_t)a.B * a.G;
   dim3 grid((unsigned)(WAVES == 1 ? (groups + 3) / 4 : groups)), block(256);
   hipStream_t s = (hipStream_t)a.stream;
-  a.prof.before(s);
   switch (a.out_fmt) {
     case CSAH_FMT_ROW_F32:
-      kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_F32, WAVES><<<grid, block, 0, s>>>(
+      a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_F32, WAVES>, grid, block, s,
           a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.w, a.beta, (uint8_t*)a.out_rows,
           a.out_seq_stride, a.out_scales);
       break;
     case CSAH_FMT_ROW_E4M3_BF16:
       if constexpr (DPL == 8)
-        kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_E4M3_BF16, WAVES><<<grid, block, 0, s>>>(
+        a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_E4M3_BF16, WAVES>, grid, block, s,
             a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.w, a.beta, (uint8_t*)a.out_rows,
             a.out_seq_stride, a.out_scales);
       else
         return hipErrorInvalidValue;
       break;
     default:
-      kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_FP4_E8M0, WAVES><<<grid, block, 0, s>>>(
+      a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_FP4_E8M0, WAVES>, grid, block, s,
           a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.w, a.beta, (uint8_t*)a.out_rows,
           a.out_seq_stride, a.out_scales);
   }
-  a.prof.after(s);
   return hipGetLastError();
 }
 

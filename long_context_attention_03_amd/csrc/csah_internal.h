@@ -1,6 +1,7 @@
 // csah_internal.h -- launch descriptors shared between the C-ABI layer and the kernel files.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -9,14 +10,17 @@
 
 namespace csah {
 
-// Events recorded around a call's dominant kernel (both null: no recording).
+// Events attached to the dispatch of a call's dominant kernel (both null: plain launch). The
+// runtime stamps them with that dispatch's own start and end, so they time the kernel alone.
 struct ProfileHook {
   hipEvent_t begin = nullptr, end = nullptr;
-  void before(hipStream_t s) const {
-    if (begin) (void)hipEventRecord(begin, s);
-  }
-  void after(hipStream_t s) const {
-    if (end) (void)hipEventRecord(end, s);
+  template <typename... KArgs, typename... Args>
+  void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+              Args... args) const {
+    if (begin || end)
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, s, begin, end, 0, (KArgs)args...);
+    else
+      kernel<<<grid, block, 0, s>>>((KArgs)args...);
   }
 };
 

@@ -488,8 +488,8 @@ __global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
 
 template <int NB>
 static void launch_scan(const IndexArgs& a, const IdxWs& w, int chunk, dim3 grid, hipStream_t s) {
-  index_scan_kernel<NB><<<grid, 256, 0, s>>>(a.k_codes, a.k_scales, a.k_seq_stride, a.N, a.pos,
-                                             a.m, a.Q, chunk, w);
+  a.prof.launch(index_scan_kernel<NB>, grid, dim3(256), s, a.k_codes, a.k_scales,
+                a.k_seq_stride, a.N, a.pos, a.m, a.Q, chunk, w);
 }
 
 hipError_t launch_index_topk(const IndexArgs& a) {
@@ -505,13 +505,11 @@ hipError_t launch_index_topk(const IndexArgs& a) {
   if (chunk > (1 << 22)) chunk = 1 << 22;
   const int64_t nchunks = a.N > 0 ? (a.N + chunk - 1) / chunk : 1;
   dim3 gs((unsigned)nchunks, (unsigned)slots);
-  a.prof.before(s);
   switch (a.dI) {
     case 32: launch_scan<1>(a, w, (int)chunk, gs, s); break;
     case 64: launch_scan<2>(a, w, (int)chunk, gs, s); break;
     default: launch_scan<4>(a, w, (int)chunk, gs, s); break;
   }
-  a.prof.after(s);
   const int64_t nsel = a.N > 0 ? (a.N + kSelChunk - 1) / kSelChunk : 1;
   index_select_kernel<<<dim3((unsigned)nsel, (unsigned)slots), kSelThreads, 0, s>>>(
       a.pos, a.m, a.Q, a.N, a.k, w);
