@@ -467,6 +467,292 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttendK p) {
   }
 }
 
+// ================================================================================================
+// E4M3 + bf16 rows (D = 512) with bf16 queries: workgroups that share converted row tiles.
+//
+// A workgroup of 8 wavefronts owns one (query, row split, block of 64 heads). Wavefront w works on
+// row stream w/4 and head group w%4 (16 heads). The two streams take alternate 32-row tiles of the
+// split. The 256 threads of a stream load each tile once: thread t takes row t/8, bytes 64i+8(t%8)
+// (i < 7) of the E4M3 part and 448+16(t%8) of the bf16 part, so every load instruction reads
+// 64 contiguous bytes per row. The tile is converted exactly to bf16 and stored row-major (1056-byte
+// LDS rows, the stride measured conflict-free for both read patterns) in a double-buffered tile
+// that the stream's four head groups share: 16-byte reads give the A-fragments of S^T = Y Q^T, the
+// transposing read gives the Y^T fragments of O^T += Y^T P^T, as in attend_kernel. One workgroup
+// barrier per tile orders the buffer reuse (a buffer is rewritten two tiles later, after every
+// wavefront has passed the barrier of the tile in between). The next tile's loads are issued after
+// the S^T phase and land during the softmax and P.Y phases. At the end the two streams' (max, sum,
+// accumulator) states are merged in LDS.
+constexpr int kXTile = 32, kXRS = 528, kXTileElems = kXTile * kXRS;
+
+struct TileRawX {
+  u32x2 e[7];  // E4M3 bytes 64i + 8(t%8) .. +8
+  u32x4 r;     // bf16 dims 448 + 8(t%8) .. +8
+};
+
+template <bool DENSE, int NS>
+__global__ __launch_bounds__(256 * NS, 3 - NS) void attend_x_kernel(AttendK p) {
+  constexpr int D = 512, NCH = 16, NT = 32, RB = 576;
+  __shared__ __attribute__((aligned(16))) __bf16 ytile[NS][2][kXTileElems];  // [stream][buffer]
+  __shared__ uint32_t s_mask[NS][2][4];  // [stream][buffer][head group]: 8 row bits each
+  __shared__ float s_ml[4][16][2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int st = NS == 1 ? 0 : wave >> 2, hgl = wave & 3;
+  const int g = lane >> 4, n = lane & 15;
+  const int lrow = (tid & 255) >> 3, lk = tid & 7;  // the tile row this thread loads, its slot
+  // Workgroups are dispatched round-robin over the 8 XCDs; consecutive workgroups of one XCD take
+  // the head blocks of one (query, split) unit so that its rows are fetched into one L2.
+  const int64_t wg = blockIdx.x;
+  const int64_t unit = (wg / (8 * p.hg)) * 8 + (wg & 7);
+  const int hb = (int)((wg >> 3) % p.hg);
+  if (unit >= (int64_t)p.splits * p.slots) return;
+  const int slot = (int)(unit / p.splits), split = (int)(unit - (int64_t)slot * p.splits);
+  const int b = slot / p.Q, qi = slot - b * p.Q;
+  const int head = hb * 64 + hgl * 16 + n;
+
+  // query fragments: B operand of S^T = Y Q^T (k = dims 32c + 8g + e, n = head)
+  bf16x8 qf[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; c++) {
+    if (head < p.H)
+      qf[c] = __builtin_bit_cast(
+          bf16x8, *(const u32x4*)((const uint16_t*)p.q + ((int64_t)slot * p.H + head) * D +
+                                  32 * c + 8 * g));
+    else
+      qf[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  }
+
+  // the logical rows of this split: compressed rows [0, Rc), then the w window rows
+  const int64_t pos_b = p.pos[b];
+  int64_t Rc;
+  if constexpr (DENSE) {
+    int64_t nv = (pos_b + qi + 1) / p.m;
+    Rc = nv < 0 ? 0 : (nv > p.N ? p.N : nv);
+  } else {
+    Rc = p.k;
+  }
+  const int64_t R = Rc + p.w;
+  const int64_t r0 = (int64_t)split * p.rows_per_split;
+  const int64_t r1 = r0 + p.rows_per_split < R ? r0 + p.rows_per_split : R;
+  const int64_t rc_end = Rc < r1 ? Rc : r1;
+  const uint8_t* dummy = p.N > 0 ? p.cache + (int64_t)b * p.cstride * RB
+                                 : p.win + (int64_t)b * p.wstride * RB;
+  const int ntiles = r1 > r0 ? (int)((r1 - r0 + kXTile - 1) / kXTile) : 0;
+  const int iters = (ntiles + NS - 1) / NS;
+
+  // entry id of this thread's row in the tile starting at tbase (CSA only)
+  auto fetch_id = [&](int64_t tbase) -> int32_t {
+    if constexpr (DENSE) {
+      return 0;
+    } else {
+      const int64_t j = tbase + lrow;
+      return j < rc_end ? p.idx[(int64_t)slot * p.k + j] : -1;
+    }
+  };
+  auto resolve = [&](int64_t j, int32_t e, bool& valid) -> const uint8_t* {
+    valid = false;
+    const uint8_t* ptr = dummy;
+    if (j < rc_end) {
+      const int64_t ent = DENSE ? j : (int64_t)e;
+      if (ent >= 0 && ent < p.N) {
+        valid = true;
+        ptr = p.cache + ((int64_t)b * p.cstride + ent) * RB;
+      }
+    } else if (j < r1) {
+      const int64_t r = qi + (j - Rc);   // window buffer row
+      if (pos_b - (p.w - 1) + r >= 0) {  // its token position is >= 0
+        valid = true;
+        ptr = p.win + ((int64_t)b * p.wstride + r) * RB;
+      }
+    }
+    return ptr;
+  };
+  auto load_rows = [&](const uint8_t* ptr, TileRawX& t) {
+#pragma unroll
+    for (int i = 0; i < 7; i++) t.e[i] = *(const u32x2*)(ptr + 64 * i + 8 * lk);
+    t.r = *(const u32x4*)(ptr + 448 + 16 * lk);
+  };
+
+  const int tr_row = 4 * g + ((lane & 15) >> 2), tr_col = 4 * (lane & 3);
+  typedef __attribute__((address_space(3))) short4_t* lds_s4_ptr;
+  f32x4 O[NT];
+#pragma unroll
+  for (int t = 0; t < NT; t++) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  TileRawX raw;
+  bool v_raw = false;
+  int32_t e_next = -1;
+  if (iters > 0) {
+    const int64_t t0 = r0 + (int64_t)st * kXTile;
+    const int32_t e0 = fetch_id(t0);
+    e_next = fetch_id(t0 + NS * kXTile);
+    load_rows(resolve(t0 + lrow, e0, v_raw), raw);
+  }
+  for (int it = 0; it < iters; it++) {
+    const int buf = it & 1;
+    __bf16* yt = &ytile[st][buf][0];
+    {
+      // convert and store this thread's share of the tile (masked rows become zeros)
+      __bf16* dst = yt + lrow * kXRS;
+#pragma unroll
+      for (int i = 0; i < 7; i++) {
+        const uint32_t w0 = v_raw ? raw.e[i][0] : 0u, w1 = v_raw ? raw.e[i][1] : 0u;
+        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+        *(bf16x8*)(dst + 64 * i + 8 * lk) =
+            bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      }
+      u32x4 v = raw.r;
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[e] = v_raw ? v[e] : 0u;
+      *(u32x4*)(dst + 448 + 8 * lk) = v;
+      const uint64_t ball = ballot64(v_raw);
+      if (lane == 0) {
+        uint32_t m8 = 0;
+#pragma unroll
+        for (int r = 0; r < 8; r++) m8 |= (uint32_t)((ball >> (8 * r)) & 1u) << r;
+        s_mask[st][buf][hgl] = m8;
+      }
+    }
+    __syncthreads();
+    const uint32_t mask = s_mask[st][buf][0] | (s_mask[st][buf][1] << 8) |
+                          (s_mask[st][buf][2] << 16) | (s_mask[st][buf][3] << 24);
+    f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
+    if (mask != 0u) {
+      // S^T for rows tb..tb+15 (S0) and tb+16..tb+31 (S1)
+#pragma unroll
+      for (int c = 0; c < NCH; c++) {
+        const bf16x8 a0 = *(const bf16x8*)(yt + n * kXRS + 32 * c + 8 * g);
+        const bf16x8 a1 = *(const bf16x8*)(yt + (16 + n) * kXRS + 32 * c + 8 * g);
+        S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[c], S0, 0, 0, 0);
+        S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[c], S1, 0, 0, 0);
+      }
+    }
+    // the next tile of this stream: issue its loads now (and fetch the ids of the one after)
+    v_raw = false;
+    if (it + 1 < iters) {
+      const int64_t tn = r0 + (int64_t)(NS * (it + 1) + st) * kXTile;
+      const int32_t e_after = fetch_id(tn + NS * kXTile);
+      load_rows(resolve(tn + lrow, e_next, v_raw), raw);
+      e_next = e_after;
+    }
+    if (mask != 0u) {
+      // online softmax (base 2); lane holds rows 4g+i (S0) and 16+4g+i (S1) of head n
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        v[i] = ((mask >> (4 * g + i)) & 1u) ? S0[i] * p.scale_log2 : -INFINITY;
+        v[4 + i] = ((mask >> (16 + 4 * g + i)) & 1u) ? S1[i] * p.scale_log2 : -INFINITY;
+      }
+      float tmax = v[0];
+#pragma unroll
+      for (int i = 1; i < 8; i++) tmax = fmaxf(tmax, v[i]);
+      tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
+      tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+      // lazy rescale: the reference max moves only when a head's max grows by more than 2^8
+      const float m_new = fmaxf(m_run, tmax);
+      if (__ballot(m_new > m_run + 8.0f)) {
+        const float alpha = exp2f(m_run - m_new);  // 0 while nothing was accumulated
+        if (__ballot(m_run != -INFINITY && alpha != 1.0f)) {
+#pragma unroll
+          for (int t = 0; t < NT; t++) O[t] *= alpha;
+        }
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      float P[8], psum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        P[i] = exp2f(v[i] - m_run);
+        psum += P[i];
+      }
+      l_run += psum;
+      bf16x8 ph, pl;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        ph[e] = (__bf16)P[e];
+        pl[e] = (__bf16)(P[e] - (float)ph[e]);
+      }
+      auto ytr = [&](int t) -> bf16x8 {
+        const __bf16* base0 = yt + tr_row * kXRS + 16 * t + tr_col;
+        const short4_t y0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)base0);
+        const short4_t y1 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(base0 + 16 * kXRS));
+        return __builtin_bit_cast(
+            bf16x8, short8_t{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]});
+      };
+#pragma unroll
+      for (int t = 0; t < NT; t += 2) {
+        const bf16x8 ya = ytr(t), yb = ytr(t + 1);
+        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya, ph, O[t], 0, 0, 0);
+        O[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yb, ph, O[t + 1], 0, 0, 0);
+        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya, pl, O[t], 0, 0, 0);
+        O[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yb, pl, O[t + 1], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- merge the streams, then write the output or this split's partial ----
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+  constexpr int CS = D + 4;
+  static_assert(NS == 1 || 4 * 16 * CS * 4 <= (int)sizeof(ytile), "merge buffer fits the tiles");
+  float* comb = (float*)&ytile[0][0][0];  // [head group][16 heads][CS]
+  float m1 = -INFINITY, l1 = 0.0f;
+  if constexpr (NS == 2) {
+    __syncthreads();
+    if (st == 1) {
+#pragma unroll
+      for (int t = 0; t < NT; t++) *(f32x4*)(comb + (hgl * 16 + n) * CS + 16 * t + 4 * g) = O[t];
+      if (g == 0) {
+        s_ml[hgl][n][0] = m_run;
+        s_ml[hgl][n][1] = l_run;
+      }
+    }
+    __syncthreads();
+    m1 = s_ml[hgl][n][0];
+    l1 = s_ml[hgl][n][1];
+  }
+  if (st == 0 && head < p.H) {
+    const float M = fmaxf(m_run, m1);
+    const float w0 = m_run == -INFINITY ? 0.0f : exp2f(m_run - M);
+    const float w1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - M);
+    const float L = l_run * w0 + l1 * w1;
+    const float* cb = comb + (hgl * 16 + n) * CS + 4 * g;
+    auto combined = [&](int t) -> f32x4 {
+      if constexpr (NS == 2) return O[t] * w0 + *(const f32x4*)(cb + 16 * t) * w1;
+      else return O[t] * w0;
+    };
+    if (p.splits == 1) {
+      float Mf = M, den = L, a = 1.0f;
+      if (p.sink) {
+        const float sg = p.sink[head] * kLog2e;
+        Mf = fmaxf(M, sg);
+        a = M == -INFINITY ? 0.0f : exp2f(M - Mf);
+        den = L * a + exp2f(sg - Mf);
+      }
+      const float so = den > 0.0f ? a / den : 0.0f;
+      float* op = p.out + ((int64_t)slot * p.H + head) * D + 4 * g;
+#pragma unroll
+      for (int t = 0; t < NT; t++) *(f32x4*)(op + 16 * t) = combined(t) * so;
+      if (p.lse && g == 0)
+        p.lse[(int64_t)slot * p.H + head] = den > 0.0f ? (Mf + log2f(den)) * kLn2 : -INFINITY;
+    } else {
+      // partial row: acc[D], max, sum, 2 pad floats (16-byte aligned rows)
+      float* pp = p.part + (((int64_t)slot * p.splits + split) * p.H + head) * (D + 4);
+#pragma unroll
+      for (int t = 0; t < NT; t++) *(f32x4*)(pp + 16 * t + 4 * g) = combined(t);
+      if (g == 0) {
+        pp[D] = M;
+        pp[D + 1] = L;
+      }
+    }
+  }
+}
+
 // Combine the split partials of one (query, head) with the sink. The per-split weights are computed
 // once into LDS; each thread then owns D/128 consecutive dims and reads every split's values with
 // independent vector loads.
@@ -531,29 +817,54 @@ __global__ __launch_bounds__(128) void attend_merge_kernel(const float* __restri
   if (t == 0 && lse) lse[oo] = den > 0.0f ? (s_mf + log2f(den)) * kLn2 : -INFINITY;
 }
 
-AttendPlan attend_plan(int B, int Q, int H, int D, int64_t max_rows) {
-  (void)D;
+// Row splits: enough (query, split, head group) workgroups to fill the chip, at least `min_tiles`
+// tiles per split, at most kMaxSplits splits.
+static AttendPlan make_plan(int64_t base, int64_t tiles, int64_t want_wgs, int64_t min_tiles) {
   AttendPlan pl;
-  pl.head_groups = (H + 15) / 16;
-  const int64_t tiles = (max_rows + kTile - 1) / kTile;
-  const int64_t base = (int64_t)B * Q * pl.head_groups;
-  int64_t want = (512 + base - 1) / base;
-  int64_t cap = (tiles + kWaves - 1) / kWaves;
+  int64_t want = (want_wgs + base - 1) / base;
+  int64_t cap = (tiles + min_tiles - 1) / min_tiles;
   if (cap < 1) cap = 1;
   int64_t S = want < cap ? want : cap;
   if (S > kMaxSplits) S = kMaxSplits;
   if (S < 1) S = 1;
-  int64_t tps = tiles > 0 ? (tiles + S - 1) / S : 1;
-  S = tiles > 0 ? (tiles + tps - 1) / tps : 1;
-  pl.splits = (int)S;
+  const int64_t tps = tiles > 0 ? (tiles + S - 1) / S : 1;
+  pl.splits = tiles > 0 ? (int)((tiles + tps - 1) / tps) : 1;
   pl.rows_per_split = (int)(tps * kTile);
   return pl;
 }
 
+// attend_kernel: workgroups of 4 wavefronts over one head group of 16, each wavefront its own tiles.
+AttendPlan attend_plan(int B, int Q, int H, int D, int64_t max_rows) {
+  (void)D;
+  const int hg = (H + 15) / 16;
+  AttendPlan pl = make_plan((int64_t)B * Q * hg, (max_rows + kTile - 1) / kTile, 512, kWaves);
+  pl.head_groups = hg;
+  return pl;
+}
+
+// attend_x_kernel: workgroups of 8 wavefronts over one block of 64 heads, two tiles per step;
+// one workgroup per CU, so about 256 of them.
+constexpr int kXStreams = 1;
+static AttendPlan attend_x_plan(int B, int Q, int H, int64_t max_rows) {
+  const int hb = (H + 63) / 64;
+  AttendPlan pl = make_plan((int64_t)B * Q * hb, (max_rows + kXTile - 1) / kXTile,
+                            kXStreams == 1 ? 512 : 256, 2 * kXStreams);
+  pl.head_groups = hb;
+  return pl;
+}
+
+static size_t partial_bytes(int B, int Q, int H, int D, const AttendPlan& pl) {
+  return pl.splits <= 1 ? 0 : (size_t)B * Q * pl.splits * H * (D + 4) * sizeof(float);
+}
+
 size_t attend_workspace_bytes(int B, int Q, int H, int D, int64_t max_rows) {
-  AttendPlan pl = attend_plan(B, Q, H, D, max_rows);
-  if (pl.splits <= 1) return 0;
-  return (size_t)B * Q * pl.splits * H * (D + 4) * sizeof(float);
+  // D = 512 rows are E4M3 + bf16: bf16 queries take attend_x_kernel, fp32 queries attend_kernel
+  size_t need = partial_bytes(B, Q, H, D, attend_plan(B, Q, H, D, max_rows));
+  if (D == 512) {
+    const size_t x = partial_bytes(B, Q, H, D, attend_x_plan(B, Q, H, max_rows));
+    need = x > need ? x : need;
+  }
+  return need;
 }
 
 template <int FMT, int QDT>
@@ -565,7 +876,9 @@ static hipError_t launch_fmt(const AttendArgs& a, const AttendK& k, dim3 grid, h
 
 hipError_t launch_attend(const AttendArgs& a) {
   hipStream_t s = (hipStream_t)a.stream;
-  AttendPlan pl = attend_plan(a.B, a.Q, a.H, a.D, a.max_rows);
+  const bool shared_tiles = a.fmt == CSAH_FMT_ROW_E4M3_BF16 && a.q_dtype == CSAH_DT_BF16;
+  const AttendPlan pl = shared_tiles ? attend_x_plan(a.B, a.Q, a.H, a.max_rows)
+                                     : attend_plan(a.B, a.Q, a.H, a.D, a.max_rows);
   AttendK k;
   k.q = a.q;
   k.H = a.H;
@@ -594,9 +907,12 @@ hipError_t launch_attend(const AttendArgs& a) {
   const int64_t per_round = 8LL * pl.head_groups;
   dim3 grid((unsigned)(((units + 7) / 8) * per_round));
   hipError_t e;
-  if (a.fmt == CSAH_FMT_ROW_E4M3_BF16)
-    e = a.q_dtype == CSAH_DT_BF16 ? launch_fmt<CSAH_FMT_ROW_E4M3_BF16, CSAH_DT_BF16>(a, k, grid, s)
-                                  : launch_fmt<CSAH_FMT_ROW_E4M3_BF16, CSAH_DT_F32>(a, k, grid, s);
+  if (shared_tiles) {
+    if (a.idx) a.prof.launch(attend_x_kernel<false, kXStreams>, grid, dim3(256 * kXStreams), s, k);
+    else a.prof.launch(attend_x_kernel<true, kXStreams>, grid, dim3(256 * kXStreams), s, k);
+    e = hipGetLastError();
+  } else if (a.fmt == CSAH_FMT_ROW_E4M3_BF16)
+    e = launch_fmt<CSAH_FMT_ROW_E4M3_BF16, CSAH_DT_F32>(a, k, grid, s);
   else
     e = a.q_dtype == CSAH_DT_BF16 ? launch_fmt<CSAH_FMT_ROW_F32, CSAH_DT_BF16>(a, k, grid, s)
                                   : launch_fmt<CSAH_FMT_ROW_F32, CSAH_DT_F32>(a, k, grid, s);
