@@ -103,7 +103,7 @@ class DecodeStep:
                         xt=d.normal((B_HCA, 128, D), dtype=torch.bfloat16),
                         out=torch.empty((B_HCA, 1, H, D), dtype=torch.float32, device=dev),
                         lse=torch.empty((B_HCA, 1, H), dtype=torch.float32, device=dev))
-        self.ws_idx = torch.empty(L.index_topk_workspace(B_CSA, 1, N_CSA, K, DI), dtype=torch.uint8,
+        self.ws_idx = torch.empty(L.index_topk_workspace(B_CSA, 1, N_CSA, K, HI, DI), dtype=torch.uint8,
                                   device=dev)
         self.ws_csa = torch.empty(max(256, L.attend_workspace(B_CSA, 1, H, D, K + W)),
                                   dtype=torch.uint8, device=dev)

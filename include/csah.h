@@ -106,15 +106,19 @@ int csah_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int
  *   Query i of sequence b sees entries g < min(floor((pos[b]+i+1)/m), N): a group is visible once
  *   it is complete. The output lists the first min(k, visible) entries ordered by (score
  *   descending, index ascending); remaining slots are -1 (score -inf).
- * q_codes   [B][Q][HI][dI/2] E2M1 codes, q_scales [B][Q][HI][dI/32] E8M0.
+ * q_codes   [B][Q][HI][dI/2] E2M1 codes (16-byte aligned), q_scales [B][Q][HI][dI/32] E8M0.
  * k_codes   [B][k_seq_stride][dI/2], k_scales [B][k_seq_stride][dI/32]; N <= k_seq_stride.
  * pos       [B] int64 device array, position of query 0 of each sequence.
  * idx_out   [B][Q][k] int32; score_out [B][Q][k] fp32 or NULL.
- * ws        device workspace of at least csah_index_topk_workspace(B, Q, N, k, dI) bytes,
+ * ws        device workspace of at least csah_index_topk_workspace(B, Q, N, k, HI, dI) bytes,
  *           256-byte aligned; its contents need no initialisation and are clobbered.
- * Supported: 1 <= HI <= 16, dI in {32, 64, 128}, 1 <= k <= 4096, N < 2^31, m >= 1.
+ * Supported: 1 <= HI <= 16, dI in {32, 64, 128}, 1 <= k <= 4096, N < 2^31, m >= 1, B*Q < 65536.
+ * Two schedules compute the same result. With dI = 128 and Q >= 16 (a prefill chunk: many
+ * queries of one sequence share its keys) the scores come from the scaled FP4 MFMA and are
+ * recomputed rather than stored; the workspace then holds, per query, a histogram, counters and
+ * candidate lists of up to N 8-byte keys. Otherwise every score is stored (4 more bytes per entry).
  */
-size_t csah_index_topk_workspace(int B, int Q, int64_t N, int k, int dI);
+size_t csah_index_topk_workspace(int B, int Q, int64_t N, int k, int HI, int dI);
 int csah_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int dI,
                     const uint8_t* k_codes, const uint8_t* k_scales, int64_t k_seq_stride,
                     int64_t N, const int64_t* pos, int m, int B, int Q, int k, int32_t* idx_out,

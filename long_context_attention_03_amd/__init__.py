@@ -52,7 +52,7 @@ def lib():
             "csah_status_string": (ctypes.c_char_p, [I]),
             "csah_row_bytes": (I64, [I, I]),
             "csah_kv_compress": (I, [P, I, I64, I, I64, I, I, P, P, P, I, I64, P, P]),
-            "csah_index_topk_workspace": (SZ, [I, I, I64, I, I]),
+            "csah_index_topk_workspace": (SZ, [I, I, I64, I, I, I]),
             "csah_index_topk": (I, [P, P, I, I, P, P, I64, I64, P, I, I, I, I, P, P, P, SZ, P]),
             "csah_attend_workspace": (SZ, [I, I, I, I, I64]),
             "csah_csa_attend": (I, [P, I, I, I, P, I, I64, I64, P, I, P, I64, I, P, P, F, I, I,
@@ -141,8 +141,8 @@ def kv_compress(raw, m: int, w, beta, out_fmt: int, out_rows=None, out_scales=No
 
 
 # ----------------------------------------------------------------------------- index_topk
-def index_topk_workspace(B: int, Q: int, N: int, k: int, dI: int) -> int:
-    return int(lib().csah_index_topk_workspace(B, Q, N, k, dI))
+def index_topk_workspace(B: int, Q: int, N: int, k: int, HI: int, dI: int) -> int:
+    return int(lib().csah_index_topk_workspace(B, Q, N, k, HI, dI))
 
 
 def index_topk(q_codes, q_scales, k_codes, k_scales, pos, m: int, k: int, N: int | None = None,
@@ -157,7 +157,7 @@ def index_topk(q_codes, q_scales, k_codes, k_scales, pos, m: int, k: int, N: int
         idx_out = torch.empty((B, Q, k), dtype=torch.int32, device=dev)
     if want_scores and score_out is None:
         score_out = torch.empty((B, Q, k), dtype=torch.float32, device=dev)
-    need = index_topk_workspace(B, Q, N, k, dI)
+    need = index_topk_workspace(B, Q, N, k, HI, dI)
     ws = _workspace(need, dev, ws)
     st = lib().csah_index_topk(_ptr(q_codes), _ptr(q_scales), HI, dI, _ptr(k_codes),
                                _ptr(k_scales), kstride, N, _ptr(pos), m, B, Q, k, _ptr(idx_out),

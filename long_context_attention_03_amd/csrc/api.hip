@@ -98,9 +98,9 @@ int csah_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int
   return launch_status(launch_kv_compress(a));
 }
 
-size_t csah_index_topk_workspace(int B, int Q, int64_t N, int k, int dI) {
-  if (B <= 0 || Q <= 0 || N < 0 || k <= 0) return 0;
-  return index_workspace_bytes(B, Q, N, k, dI);
+size_t csah_index_topk_workspace(int B, int Q, int64_t N, int k, int HI, int dI) {
+  if (B <= 0 || Q <= 0 || N < 0 || k <= 0 || HI <= 0) return 0;
+  return index_workspace_bytes(B, Q, N, k, HI, dI);
 }
 
 int csah_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int dI,
@@ -112,13 +112,14 @@ int csah_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int
     return CSAH_ERR_INVALID_ARGUMENT;
   if (HI <= 0 || dI <= 0 || m <= 0 || B <= 0 || Q <= 0 || k <= 0 || N < 0 || k_seq_stride < N)
     return CSAH_ERR_INVALID_ARGUMENT;
-  if (!aligned(k_codes, 16) || !aligned(ws, 256)) return CSAH_ERR_INVALID_ARGUMENT;
+  if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(ws, 256))
+    return CSAH_ERR_INVALID_ARGUMENT;
   if (HI > 16 || (dI != 32 && dI != 64 && dI != 128) || k > 4096 || N >= ((int64_t)1 << 31) ||
       (int64_t)B * Q >= 65536)
     return CSAH_ERR_UNSUPPORTED;
   int st = check_device();
   if (st) return st;
-  if (ws_bytes < index_workspace_bytes(B, Q, N, k, dI)) return CSAH_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < index_workspace_bytes(B, Q, N, k, HI, dI)) return CSAH_ERR_WORKSPACE_TOO_SMALL;
   IndexArgs a{q_codes, q_scales, HI, dI, k_codes, k_scales, k_seq_stride, N, pos, m, B, Q, k,
               idx_out, score_out, ws, ws_bytes, stream, prof};
   return launch_status(launch_index_topk(a));

@@ -59,7 +59,7 @@ struct IndexArgs {
   void* stream;
   ProfileHook prof;
 };
-size_t index_workspace_bytes(int B, int Q, int64_t N, int k, int dI);
+size_t index_workspace_bytes(int B, int Q, int64_t N, int k, int HI, int dI);
 hipError_t launch_index_topk(const IndexArgs& a);
 
 // ---- attention ---------------------------------------------------------------------------------

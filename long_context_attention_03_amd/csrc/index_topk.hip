@@ -55,21 +55,25 @@ struct IdxWs {
 
 static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static IdxWs make_ws(void* base, int64_t N, int k) {
+// Per-slot layout. The scan path stores every score; the MFMA path recomputes them instead.
+static IdxWs make_ws(void* base, int64_t N, int k, bool with_scores) {
   IdxWs w;
   w.base = (char*)base;
   w.off_hist = al256(128 * sizeof(float));
   w.off_ctr = w.off_hist + al256(kBins * sizeof(uint32_t));
   w.off_scores = w.off_ctr + 256;
-  w.off_sure = w.off_scores + al256((size_t)N * sizeof(float));
+  w.off_sure = w.off_scores + (with_scores ? al256((size_t)N * sizeof(float)) : 0);
   w.off_tie = w.off_sure + al256((size_t)k * sizeof(uint64_t));
   w.slot_bytes = w.off_tie + al256((size_t)N * sizeof(uint64_t));
   return w;
 }
 
-size_t index_workspace_bytes(int B, int Q, int64_t N, int k, int dI) {
-  (void)dI;
-  IdxWs w = make_ws(nullptr, N, k);
+// Queries of one sequence share its keys; from 16 of them on (one MFMA tile) with 128-dim keys and
+// at most 16 indexer heads the scores come from the scaled FP4 MFMA (see index_mfma_hist_kernel).
+static bool use_mfma_path(int Q, int HI, int dI) { return dI == 128 && Q >= 16 && HI <= 16; }
+
+size_t index_workspace_bytes(int B, int Q, int64_t N, int k, int HI, int dI) {
+  IdxWs w = make_ws(nullptr, N, k, !use_mfma_path(Q, HI, dI));
   return (size_t)B * (size_t)Q * w.slot_bytes;
 }
 
@@ -195,18 +199,20 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
   }
 }
 
-// Threshold bin of the kk-th largest score from the histogram written by the previous
-// kernel (h, suf in LDS).
+// Threshold bin of the kk-th largest score from a BINS-bin histogram written by the previous
+// kernel (h, suf in LDS): the highest bin whose suffix count reaches kk, and the count above it.
+template <int BINS>
 __device__ void find_threshold_bin(const uint32_t* __restrict__ gh, int64_t kk, uint32_t* h,
                                    uint32_t* suf, uint32_t* out_bin, uint32_t* out_above) {
+  constexpr int PER = BINS / 256;
   // threads >= 256 only take part in the barriers
   const int t = threadIdx.x;
   if (t < 256) {
     uint32_t local = 0;
 #pragma unroll
-    for (int j = 0; j < kBins / 256; j++) {
-      const uint32_t c = gh[t * (kBins / 256) + j];
-      h[t * (kBins / 256) + j] = c;
+    for (int j = 0; j < PER; j++) {
+      const uint32_t c = gh[t * PER + j];
+      h[t * PER + j] = c;
       local += c;
     }
     suf[t] = local;
@@ -225,11 +231,11 @@ __device__ void find_threshold_bin(const uint32_t* __restrict__ gh, int64_t kk, 
     const uint32_t next = t < 255 ? suf[t + 1] : 0u;
     if ((int64_t)mine >= kk && (int64_t)next < kk) {
       uint32_t above = next;
-      uint32_t bin = t * (kBins / 256);
-      for (int j = kBins / 256 - 1; j >= 0; j--) {
-        const uint32_t c = h[t * (kBins / 256) + j];
+      uint32_t bin = t * PER;
+      for (int j = PER - 1; j >= 0; j--) {
+        const uint32_t c = h[t * PER + j];
         if ((int64_t)(above + c) >= kk) {
-          bin = t * (kBins / 256) + j;
+          bin = t * PER + j;
           break;
         }
         above += c;
@@ -265,9 +271,10 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelPerThread = 8;
 constexpr int kSelChunk = kSelThreads * kSelPerThread;
 
+// bin_bits: width of the histogram bin (top bits of the order key) shared by every tie candidate
 __device__ void finalize_slot(int slot, int64_t N, int k, int kk, int32_t* __restrict__ idx_out,
                               float* __restrict__ score_out, IdxWs ws, uint64_t* keys,
-                              uint32_t* dh) {
+                              uint32_t* dh, int bin_bits) {
   __shared__ uint64_t s_prefix, s_pmask;
   __shared__ uint32_t s_r, s_cnt;
   const int t = threadIdx.x;
@@ -292,7 +299,7 @@ __device__ void finalize_slot(int slot, int64_t N, int k, int kk, int32_t* __res
     for (int j = t; j < n; j += blockDim.x) keys[j] = j < (int)ns ? sure[j] : tie[j - ns];
   } else {
     // radix select the r-th largest tie key (keys are unique), 8 bits at a time below the bin
-    constexpr int kLowBits = 64 - (32 - kBinShift);  // key bits below the shared bin
+    const int kLowBits = 64 - bin_bits;  // key bits below the shared bin
     if (t == 0) {
       s_r = (uint32_t)kk - ns;
       s_prefix = 0;
@@ -382,7 +389,7 @@ __global__ __launch_bounds__(kSelThreads) void index_select_kernel(
 #pragma unroll
     for (int e = 0; e < kSelPerThread; e++) v[e] = g0 + e < nv ? sc[g0 + e] : -INFINITY;
   }
-  find_threshold_bin(ws.hist(slot), kk, h, suf, &s_bin, &s_above);
+  find_threshold_bin<kBins>(ws.hist(slot), kk, h, suf, &s_bin, &s_above);
   const uint32_t bstar = s_bin;
   uint32_t cls[kSelPerThread];  // 0 drop, 1 sure, 2 tie
   uint32_t cnt = 0;             // sure count | tie count << 16
@@ -456,7 +463,8 @@ __global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
   }
   const uint32_t n = ns + nt;
   if (kk == 0 || n > (uint32_t)kSortCap) {
-    if (blockIdx.x == 0) finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh);
+    if (blockIdx.x == 0)
+      finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh, 32 - kBinShift);
     return;
   }
   int32_t* io = idx_out + (int64_t)slot * k;
@@ -486,6 +494,308 @@ __global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
   }
 }
 
+// ================================================================================================
+// Many queries per sequence (prefill chunks): scores on the scaled FP4 MFMA.
+//
+// v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1 operands (format code 4) multiplies a 16 x 128 block
+// of FP4 codes by a 128 x 16 block; lane l supplies one 32-element block (16 bytes, the low four
+// dwords of the operand) of row l%16, block l/16, with that block's E8M0 scale, and the exactly
+// scaled products are accumulated in fp32. With A = 16 keys and B = 16 queries of one indexer head,
+// one instruction per head into the same accumulator leaves score(key 4*(l/16)+i, query l%16) in
+// register i of lane l. Every product is exact, so under the same precondition as the scan (the
+// absolute sum spans fewer than 24 bits of the finest granularity) the scores are the exact ones in
+// any accumulation order, and the two passes below recompute bit-identical values.
+//   clear    zero the per-query histograms and counters
+//   hist     scores -> per-query histogram of the top 11 bits of the order key (16-bit LDS counters
+//            for the workgroup's 16 queries x 16,384 keys, flushed with global atomics)
+//   thresh   per query: the bin holding its kk-th largest score and the count above it
+//   select   scores again -> keys above the bin ("sure") and in it ("tie") appended to the query's
+//            lists, as index_select_kernel does from stored scores
+//   sort     per query: bitonic sort of the candidates in LDS (after a radix select when the tie
+//            list is longer than kSortCap), then the ordered top-k
+constexpr int kPBins = 2048, kPBinShift = 21;
+constexpr int kPKeys = 16384;                // keys per workgroup: a 16-bit counter cannot overflow
+constexpr uint32_t kNoThreshold = 0xFFFFFFFFu;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int HP>  // HP >= HI: heads padded with zero codes contribute exactly 0
+struct QueryOps {
+  i32x8 c[HP];
+  int e[HP];
+};
+
+template <int HP>
+__device__ __forceinline__ void load_query_ops(const uint8_t* __restrict__ q_codes,
+                                               const uint8_t* __restrict__ q_scales, int HI,
+                                               int64_t qrow, bool valid, int blk, QueryOps<HP>& o) {
+#pragma unroll
+  for (int h = 0; h < HP; h++) {
+    o.c[h] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    o.e[h] = 127;
+    if (valid && h < HI) {
+      const u32x4 v = *(const u32x4*)(q_codes + (qrow * HI + h) * 64 + 16 * blk);
+      o.c[h][0] = (int)v[0];
+      o.c[h][1] = (int)v[1];
+      o.c[h][2] = (int)v[2];
+      o.c[h][3] = (int)v[3];
+      o.e[h] = q_scales[(qrow * HI + h) * 4 + blk];
+    }
+  }
+}
+
+template <int HP>
+__device__ __forceinline__ f32x4 tile_scores(const u32x4 kc, uint32_t ke, const QueryOps<HP>& o) {
+  const i32x8 a = i32x8{(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int h = 0; h < HP; h++)
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, o.c[h], acc, 4, 4, 0, (int)ke, 0,
+                                                           o.e[h]);
+  return acc;
+}
+
+// Shared walk over the workgroup's keys: each wavefront takes every 4th tile of 16 keys. Loads go
+// in rounds of U tiles, double-buffered, so one round's loads are in flight while the previous
+// round is scored; `visit(key, score)` sees every visible (key, query) pair of the lane.
+// Work split: the keys are cut into nkr ranges (a multiple of 8, at most kPKeys keys each) and the
+// queries into blocks of 16. Workgroups are dispatched round-robin over the 8 XCDs (id % 8), so
+// XCD x takes the key ranges x, x+8, ... for every query block: its few ranges stay resident in
+// its own L2 while all query blocks stream over them.
+struct MfmaSplit {
+  int nkr, nqb, B;  // grid = nkr * nqb * B workgroups (a multiple of 8)
+  int64_t keys_per_range;
+};
+
+__device__ __forceinline__ void mfma_unit(const MfmaSplit& sp, int& b, int& qb, int& kr) {
+  const int w = blockIdx.x, xcd = w & 7, i = w >> 3;
+  const int per = sp.nkr >> 3;  // key ranges per XCD
+  const int kl = i % per, rest = i / per;
+  kr = xcd + 8 * kl;
+  qb = rest % sp.nqb;
+  b = rest / sp.nqb;
+}
+
+template <int HP, typename F>
+__device__ __forceinline__ void mfma_walk(const uint8_t* __restrict__ q_codes,
+                                          const uint8_t* __restrict__ q_scales, int HI,
+                                          const uint8_t* __restrict__ k_codes,
+                                          const uint8_t* __restrict__ k_scales,
+                                          int64_t k_seq_stride, int64_t N,
+                                          const int64_t* __restrict__ pos, int m, int Q,
+                                          const MfmaSplit& sp, int b, int qb, int kr, F visit) {
+  constexpr int U = 4;
+  const int q0 = qb * 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, blk = lane >> 4;
+  const int qi = q0 + n;
+  const bool qv = qi < Q;
+  const int64_t nv = qv ? visible_entries(pos, b, qi, m, N) : 0;
+  // visibility is nondecreasing in the query index: the block's last query sees the most
+  const int64_t nvmax = visible_entries(pos, b, (q0 + 15 < Q ? q0 + 15 : Q - 1), m, N);
+  const int64_t g0 = (int64_t)kr * sp.keys_per_range;
+  const int64_t g1 = g0 + sp.keys_per_range < nvmax ? g0 + sp.keys_per_range : nvmax;
+  if (g0 >= g1) return;
+  QueryOps<HP> qo;
+  load_query_ops<HP>(q_codes, q_scales, HI, (int64_t)b * Q + qi, qv, blk, qo);
+  const uint8_t* kc = k_codes + ((int64_t)b * k_seq_stride + g0) * 64 + 16 * blk;
+  const uint8_t* ks = k_scales + ((int64_t)b * k_seq_stride + g0) * 4 + blk;
+  const int nk = (int)(g1 - g0);
+  const int ntile = (nk + 15) / 16;
+  const int my_tiles = ntile > wave ? (ntile - wave + 3) / 4 : 0;  // tiles wave, wave+4, ...
+  auto load = [&](int j0, u32x4* c, uint32_t* e) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      int r = 16 * (wave + 4 * (j0 + u)) + n;  // key row of this lane in the A operand
+      r = r < nk ? r : nk - 1;                 // rows past the range read a valid row (masked)
+      c[u] = __builtin_nontemporal_load((const u32x4*)(kc + (uint32_t)r * 64u));
+      e[u] = ks[(uint32_t)r * 4u];
+    }
+  };
+  // keys of this lane's query that are visible, relative to g0 (so compares are 32-bit)
+  const int lim = (int)((nv < g1 ? nv : g1) - g0 > 0 ? (nv < g1 ? nv : g1) - g0 : 0);
+  auto score = [&](int j0, const u32x4* c, const uint32_t* e) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      if (j0 + u >= my_tiles) break;
+      const f32x4 sc = tile_scores<HP>(c[u], e[u], qo);
+      const int kr0 = 16 * (wave + 4 * (j0 + u)) + 4 * blk;
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        if (kr0 + i < lim) visit(g0 + kr0 + i, sc[i] + 0.0f);  // fold -0 into +0
+    }
+  };
+  u32x4 ca[U], cb[U];
+  uint32_t ea[U], eb[U];
+  if (my_tiles > 0) load(0, ca, ea);
+  for (int j = 0; j < my_tiles; j += 2 * U) {
+    if (j + U < my_tiles) load(j + U, cb, eb);
+    score(j, ca, ea);
+    if (j + U >= my_tiles) break;
+    if (j + 2 * U < my_tiles) load(j + 2 * U, ca, ea);
+    score(j + U, cb, eb);
+  }
+}
+
+__global__ __launch_bounds__(256) void index_clear_kernel(IdxWs ws) {
+  uint32_t* h = ws.hist(blockIdx.x);
+  for (int j = threadIdx.x; j < kPBins; j += 256) h[j] = 0u;
+  if (threadIdx.x < 64) ws.ctr(blockIdx.x)[threadIdx.x] = 0u;
+}
+
+template <int HP>
+__global__ __launch_bounds__(256, 2) void index_mfma_hist_kernel(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
+    int64_t k_seq_stride, int64_t N, const int64_t* __restrict__ pos, int m, int Q, MfmaSplit sp,
+    IdxWs ws) {
+  __shared__ uint32_t hist[16 * kPBins / 2];  // two 16-bit counters per word
+  int b, qb, kr;
+  mfma_unit(sp, b, qb, kr);
+  for (int j = threadIdx.x; j < 16 * kPBins / 2; j += 256) hist[j] = 0u;
+  __syncthreads();
+  const int n = threadIdx.x & 15;
+  uint32_t* hq = hist + n * (kPBins / 2);
+  mfma_walk<HP>(q_codes, q_scales, HI, k_codes, k_scales, k_seq_stride, N, pos, m, Q, sp, b, qb,
+                kr, [&](int64_t, float s) {
+                  const uint32_t bin = order_key(s) >> kPBinShift;
+                  atomicAdd(&hq[bin >> 1], 1u << (16 * (bin & 1)));
+                });
+  __syncthreads();
+  const int q0 = qb * 16;
+  for (int j = threadIdx.x; j < 16 * kPBins / 2; j += 256) {
+    const int qn = j / (kPBins / 2), wd = j - qn * (kPBins / 2);
+    const uint32_t v = hist[j];
+    if (v == 0u || q0 + qn >= Q) continue;
+    uint32_t* gh = ws.hist((int64_t)b * Q + q0 + qn);
+    if (v & 0xFFFFu) atomicAdd(&gh[2 * wd], v & 0xFFFFu);
+    if (v >> 16) atomicAdd(&gh[2 * wd + 1], v >> 16);
+  }
+}
+
+__global__ __launch_bounds__(256) void index_thresh_kernel(const int64_t* __restrict__ pos, int m,
+                                                           int Q, int64_t N, int k, IdxWs ws) {
+  const int slot = blockIdx.x, b = slot / Q, i = slot - b * Q;
+  const int64_t nv = visible_entries(pos, b, i, m, N);
+  const int64_t kk = nv < k ? nv : k;
+  __shared__ uint32_t h[kPBins];
+  __shared__ uint32_t suf[256];
+  __shared__ uint32_t s_bin, s_above;
+  uint32_t* ctr = ws.ctr(slot);
+  if (kk == 0) {
+    if (threadIdx.x == 0) ctr[2] = kNoThreshold;
+    return;
+  }
+  find_threshold_bin<kPBins>(ws.hist(slot), kk, h, suf, &s_bin, &s_above);
+  if (threadIdx.x == 0) ctr[2] = s_bin;
+}
+
+// Candidates are staged per query in LDS and appended to the global lists with one atomic per
+// list per query per workgroup; a staging list that fills up spills straight to the global list.
+constexpr int kPStage = 128;
+
+template <int HP>
+__global__ __launch_bounds__(256) void index_mfma_select_kernel(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
+    int64_t k_seq_stride, int64_t N, const int64_t* __restrict__ pos, int m, int Q, int k,
+    MfmaSplit sp, IdxWs ws) {
+  __shared__ uint64_t stage[2][16][kPStage];  // [sure / tie][query][slot]
+  __shared__ uint32_t scount[2][16], sbase[2][16];
+  int b, qb, kr;
+  mfma_unit(sp, b, qb, kr);
+  const int q0 = qb * 16, n = threadIdx.x & 15;
+  if (threadIdx.x < 32) scount[threadIdx.x >> 4][threadIdx.x & 15] = 0u;
+  __syncthreads();
+  const int qi = q0 + n;
+  const int64_t slot = (int64_t)b * Q + (qi < Q ? qi : Q - 1);
+  uint32_t* ctr = ws.ctr((int)slot);
+  const uint32_t thr = qi < Q ? ctr[2] : kNoThreshold;
+  // the smallest score of the threshold bin: scores below it are dropped with one compare
+  const float smin = thr == kNoThreshold ? INFINITY : key_to_float(thr << kPBinShift);
+  uint64_t* sure = ws.sure((int)slot);
+  uint64_t* tie = ws.tie((int)slot);
+  mfma_walk<HP>(q_codes, q_scales, HI, k_codes, k_scales, k_seq_stride, N, pos, m, Q, sp, b, qb,
+                kr, [&](int64_t key, float s) {
+                  if (!(s >= smin)) return;
+                  const uint32_t ok = order_key(s), bin = ok >> kPBinShift;
+                  const uint64_t x = ((uint64_t)ok << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)key);
+                  const int list = bin > thr ? 0 : 1;
+                  const uint32_t at = atomicAdd(&scount[list][n], 1u);
+                  if (at < (uint32_t)kPStage) {
+                    stage[list][n][at] = x;
+                  } else if (list == 0) {
+                    const uint32_t g = atomicAdd(&ctr[0], 1u);
+                    if (g < (uint32_t)k) sure[g] = x;
+                  } else {
+                    const uint32_t g = atomicAdd(&ctr[1], 1u);
+                    if ((int64_t)g < N) tie[g] = x;
+                  }
+                });
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    const int list = threadIdx.x >> 4, qn = threadIdx.x & 15;
+    const uint32_t c = scount[list][qn];
+    const uint32_t staged = c < (uint32_t)kPStage ? c : (uint32_t)kPStage;
+    sbase[list][qn] = (staged && q0 + qn < Q)
+                          ? atomicAdd(&ws.ctr((int)((int64_t)b * Q + q0 + qn))[list], staged)
+                          : 0u;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < 2 * 16 * kPStage; j += 256) {
+    const int list = j / (16 * kPStage), qn = (j / kPStage) % 16, e = j % kPStage;
+    const uint32_t c = scount[list][qn];
+    if ((uint32_t)e >= (c < (uint32_t)kPStage ? c : (uint32_t)kPStage) || q0 + qn >= Q) continue;
+    const int64_t sl = (int64_t)b * Q + q0 + qn;
+    const uint32_t g = sbase[list][qn] + e;
+    if (list == 0) {
+      if (g < (uint32_t)k) ws.sure((int)sl)[g] = stage[0][qn][e];
+    } else {
+      if ((int64_t)g < N) ws.tie((int)sl)[g] = stage[1][qn][e];
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void index_sort_kernel(const int64_t* __restrict__ pos, int m,
+                                                          int Q, int64_t N, int k,
+                                                          int32_t* __restrict__ idx_out,
+                                                          float* __restrict__ score_out,
+                                                          IdxWs ws) {
+  const int slot = blockIdx.x, b = slot / Q, i = slot - b * Q;
+  const int64_t nv = visible_entries(pos, b, i, m, N);
+  const int kk = (int)(nv < k ? nv : k);
+  __shared__ uint64_t keys[kSortCap];
+  __shared__ uint32_t dh[256];
+  finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh, 32 - kPBinShift);
+}
+
+template <int HP>
+static hipError_t launch_mfma_hp(const IndexArgs& a, const IdxWs& w, hipStream_t s) {
+  const int slots = a.B * a.Q;
+  MfmaSplit sp;
+  sp.nkr = 8 * (int)((a.N + 8 * kPKeys - 1) / (8 * kPKeys));
+  if (sp.nkr < 8) sp.nkr = 8;
+  sp.keys_per_range = ((a.N + sp.nkr - 1) / sp.nkr + 15) / 16 * 16;
+  sp.nqb = (a.Q + 15) / 16;
+  sp.B = a.B;
+  const dim3 grid((unsigned)((int64_t)sp.nkr * sp.nqb * a.B));
+  index_clear_kernel<<<slots, 256, 0, s>>>(w);
+  a.prof.launch(index_mfma_hist_kernel<HP>, grid, dim3(256), s, a.q_codes, a.q_scales, a.HI,
+                a.k_codes, a.k_scales, a.k_seq_stride, a.N, a.pos, a.m, a.Q, sp, w);
+  index_thresh_kernel<<<slots, 256, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, w);
+  index_mfma_select_kernel<HP><<<grid, 256, 0, s>>>(a.q_codes, a.q_scales, a.HI, a.k_codes,
+                                                    a.k_scales, a.k_seq_stride, a.N, a.pos, a.m,
+                                                    a.Q, a.k, sp, w);
+  index_sort_kernel<<<slots, 1024, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, a.idx_out, a.score_out, w);
+  return hipGetLastError();
+}
+
+static hipError_t launch_index_mfma(const IndexArgs& a) {
+  hipStream_t s = (hipStream_t)a.stream;
+  const IdxWs w = make_ws(a.ws, a.N, a.k, false);
+  if (a.HI <= 4) return launch_mfma_hp<4>(a, w, s);
+  if (a.HI <= 8) return launch_mfma_hp<8>(a, w, s);
+  return launch_mfma_hp<16>(a, w, s);
+}
+
 template <int NB>
 static void launch_scan(const IndexArgs& a, const IdxWs& w, int chunk, dim3 grid, hipStream_t s) {
   a.prof.launch(index_scan_kernel<NB>, grid, dim3(256), s, a.k_codes, a.k_scales,
@@ -495,7 +805,8 @@ static void launch_scan(const IndexArgs& a, const IdxWs& w, int chunk, dim3 grid
 hipError_t launch_index_topk(const IndexArgs& a) {
   hipStream_t s = (hipStream_t)a.stream;
   const int slots = a.B * a.Q;
-  IdxWs w = make_ws(a.ws, a.N, a.k);
+  if (use_mfma_path(a.Q, a.HI, a.dI)) return launch_index_mfma(a);
+  IdxWs w = make_ws(a.ws, a.N, a.k, true);
   index_prep_kernel<<<slots, 256, 0, s>>>(a.q_codes, a.q_scales, a.HI, a.dI, w);
   // scan: about 1024 workgroups in total (four per CU), each streaming a contiguous range
   const int64_t total = (int64_t)slots * (a.N > 0 ? a.N : 1);

@@ -43,11 +43,15 @@ def test_status_strings_and_row_bytes():
 
 
 def test_workspace_sizes_are_host_only_and_monotone():
-    a = L.index_topk_workspace(4, 1, 262144, 1024, 128)
-    b = L.index_topk_workspace(4, 1, 2 * 262144, 1024, 128)
+    a = L.index_topk_workspace(4, 1, 262144, 1024, 4, 128)
+    b = L.index_topk_workspace(4, 1, 2 * 262144, 1024, 4, 128)
     assert 0 < a < b
     assert L.attend_workspace(4, 1, 64, 512, 1152) > 0
-    assert L.index_topk_workspace(0, 1, 10, 1, 64) == 0
+    assert L.index_topk_workspace(0, 1, 10, 1, 4, 64) == 0
+    # many queries per sequence: scores are recomputed on MFMA rather than stored (4 B per entry)
+    per_q_scan = L.index_topk_workspace(1, 8, 262144, 1024, 4, 128) / 8
+    per_q_mfma = L.index_topk_workspace(1, 16, 262144, 1024, 4, 128) / 16
+    assert per_q_scan - per_q_mfma >= 4 * 262144
 
 
 FAKE = ctypes.c_void_p(4096)  # never dereferenced: validation fails first

@@ -5,7 +5,7 @@ import torch
 
 import long_context_attention_03_amd as L
 import oracle as O
-from helpers import DecodeCase, assert_close, dev, say
+from helpers import DecodeCase, assert_close, bf16_bits, dev, say
 
 pytestmark = pytest.mark.gpu
 
@@ -143,3 +143,67 @@ def test_fp32_query_on_e4m3_rows():
     o, l, ro, rl = _csa(c, idx)
     assert_close(o, ro, "fp32 q out")
     assert_close(l, rl, "fp32 q lse")
+
+
+# ---- the prefill chunk at full size: 4096 queries at positions 1,048,576 + i ---------------------
+PF_Q, PF_POS0, PF_H, PF_D, PF_W = 4096, 1 << 20, 64, 512, 128
+PF_SAMPLE = (0, 1, 2, 3, 4, 126, 127, 128, 129, 2047, 4094, 4095)
+
+
+def _prefill_common(seed, n_rows):
+    """Seeded chunk inputs: cache rows, window buffer (127 cached + 4096 chunk tokens), bf16
+    queries and sink logits, drawn on the CPU and encoded with the oracle's codecs."""
+    from long_context_attention_03_amd import synth
+    d = synth.Draws(seed)
+    cache, _ = O.encode_rows(d.normal((1, n_rows, PF_D)).numpy(), O.FMT_ROW_E4M3_BF16)
+    win, _ = O.encode_rows(d.normal((1, PF_W - 1 + PF_Q, PF_D)).numpy(), O.FMT_ROW_E4M3_BF16)
+    q = d.normal((1, PF_Q, PF_H, PF_D), dtype=torch.bfloat16)
+    sink = d.normal((PF_H,)).numpy()
+    return cache, win, q, sink
+
+
+def _check_sampled(out, lse, oracle_fn, what):
+    rng = np.random.default_rng(77)
+    sample = sorted({*PF_SAMPLE, *rng.choice(PF_Q, size=4, replace=False).tolist()})
+    for i in sample:
+        ro, rl = oracle_fn(i)
+        assert_close(out[:, i:i + 1], ro, f"{what} out, query {i}")
+        assert_close(lse[:, i:i + 1], rl, f"{what} lse, query {i}")
+
+
+def test_csa_prefill_chunk_full_size_sampled_queries():
+    """CSA over the prefill chunk: 263,168 entries (262,144 cached + 1,024 from the chunk), each
+    query's own 1,024 ids among its visible entries (5% empty slots), its own causal window."""
+    N = 262144 + 1024
+    cache, win, q, sink = _prefill_common(51, N)
+    rng = np.random.default_rng(52)
+    nv = (PF_POS0 + np.arange(PF_Q) + 1) // 4
+    idx = rng.integers(0, nv[:, None], size=(PF_Q, 1024)).astype(np.int32)[None]
+    idx[rng.random(idx.shape) < 0.05] = -1
+    pos = np.array([PF_POS0], np.int64)
+    say(f"[csa_attend] prefill full: Q={PF_Q} N={N} k=1024")
+    out, lse = L.csa_attend(dev(q), dev(cache), dev(idx), dev(win), PF_W, dev(pos), dev(sink),
+                            PF_D ** -0.5)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qb = bf16_bits(q)
+    _check_sampled(out, lse, lambda i: O.csa_attend(
+        qb[:, i:i + 1], cache, O.FMT_ROW_E4M3_BF16, idx[:, i:i + 1], win[:, i:i + PF_W], PF_W,
+        np.array([PF_POS0 + i], np.int64), sink, PF_D ** -0.5), "csa prefill")
+
+
+def test_hca_prefill_chunk_full_size_sampled_queries():
+    """HCA over the prefill chunk: 8,224 entries (8,192 cached + 32 from the chunk); query i sees
+    8,192 + floor((i+1)/128) of them plus its causal window."""
+    N = 8192 + 32
+    cache, win, q, sink = _prefill_common(53, N)
+    pos = np.array([PF_POS0], np.int64)
+    say(f"[hca_attend] prefill full: Q={PF_Q} N={N}")
+    out, lse = L.hca_attend(dev(q), dev(cache), 128, dev(win), PF_W, dev(pos), dev(sink),
+                            PF_D ** -0.5)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qb = bf16_bits(q)
+    _check_sampled(out, lse, lambda i: O.hca_attend(
+        qb[:, i:i + 1], cache, O.FMT_ROW_E4M3_BF16, 128, win[:, i:i + PF_W], PF_W,
+        np.array([PF_POS0 + i], np.int64), sink, PF_D ** -0.5), "hca prefill")

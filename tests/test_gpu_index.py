@@ -83,3 +83,69 @@ def test_n_limits_visibility_below_stride():
     qc, qs = O.encode_rows(rng.normal(size=(B, 1, 4, dI)), O.FMT_FP4_E8M0)
     pos = np.array([4 * S - 1, 4 * S - 1], np.int64)
     _compare("N<stride", kc, ks, qc, qs, pos, 4, 128, N=N)
+
+
+# ---- many queries per sequence (prefill chunks): the scaled-FP4-MFMA schedule ----------------
+def _fp4_inputs(rng, B, Q, N, HI, dI=128, coarse=False):
+    kv = rng.normal(size=(B, N, dI))
+    kc, ks = O.encode_rows(np.round(kv) if coarse else kv, O.FMT_FP4_E8M0)
+    qc, qs = O.encode_rows(rng.normal(size=(B, Q, HI, dI)), O.FMT_FP4_E8M0)
+    return kc, ks, qc, qs
+
+
+@pytest.mark.parametrize("HI", [3, 4, 8])
+def test_prefill_schedule_blocks_ranges_and_causality(HI):
+    """40 queries (3 blocks of 16, the last partial) over 40,000 keys (3 key ranges, the last
+    ragged); sequence 1's queries see 20,000..20,010 entries, so visibility changes inside a
+    block. HI = 3 pads the MFMA operands with a zero head."""
+    rng = np.random.default_rng(20 + HI)
+    B, Q, N, m, k = 2, 40, 40000, 4, 256
+    kc, ks, qc, qs = _fp4_inputs(rng, B, Q, N, HI)
+    pos = np.array([N * m - Q - 37, 4 * 20000 - 1], np.int64)
+    _compare(f"prefill HI={HI}", kc, ks, qc, qs, pos, m, k)
+
+
+def test_prefill_schedule_ties_and_fewer_visible_than_k():
+    """Coarse keys (many equal scores); the first queries see fewer entries than k."""
+    rng = np.random.default_rng(31)
+    B, Q, N, m, k = 1, 48, 2000, 4, 256
+    kc, ks, qc, qs = _fp4_inputs(rng, B, Q, N, 4, coarse=True)
+    pos = np.array([4 * 100 - 5], np.int64)  # query i sees floor((396 + i) / 4) = 99..110 entries
+    _compare("prefill ties/short", kc, ks, qc, qs, pos, m, k)
+    gi, _ = _run(kc, ks, qc, qs, pos, m, k)
+    assert (gi[0, 0, 99:] == -1).all() and (gi[0, 0, :99] >= 0).all()
+
+
+def test_prefill_schedule_all_equal_scores():
+    """Zero keys: 20,000 tied candidates per query exceed the sort buffer (radix-select path)."""
+    rng = np.random.default_rng(32)
+    B, Q, N, m, k = 1, 16, 20000, 4, 1000
+    kc = np.zeros((B, N, 64), np.uint8)
+    ks = np.full((B, N, 4), 127, np.uint8)
+    qc, qs = O.encode_rows(rng.normal(size=(B, Q, 4, 128)), O.FMT_FP4_E8M0)
+    pos = np.array([N * m - Q], np.int64)
+    _compare("prefill all-equal", kc, ks, qc, qs, pos, m, k)
+    gi, _ = _run(kc, ks, qc, qs, pos, m, k)
+    assert (gi[0, :, :] == np.arange(k)).all()
+
+
+def test_prefill_chunk_full_size_sampled_queries():
+    """The prefill chunk at full size: 4096 queries at positions 1,048,576 + i over 263,168 FP4
+    keys (262,144 cached + 1,024 from the chunk), top-1024 each. All queries run on the GPU;
+    sampled rows (chunk edges, group boundaries, random) are checked against the oracle, which
+    scores one query at a time."""
+    rng = np.random.default_rng(5)
+    B, Q, N, m, k, HI = 1, 4096, 262144 + 1024, 4, 1024, 4
+    kc, ks, qc, qs = _fp4_inputs(rng, B, Q, N, HI)
+    pos0 = 1 << 20
+    say(f"[index_topk] prefill full: Q={Q} N={N} k={k}")
+    gi, gs = _run(kc, ks, qc, qs, np.array([pos0], np.int64), m, k)
+    sample = sorted({0, 1, 2, 3, 4, 127, 128, 2047, 4094, 4095,
+                     *rng.choice(Q, size=6, replace=False).tolist()})
+    for i in sample:
+        ri, rs, ex = O.index_topk(qc[:, i:i + 1], qs[:, i:i + 1], kc, ks,
+                                  np.array([pos0 + i], np.int64), m, k)
+        assert ex.all()
+        assert np.array_equal(gi[:, i:i + 1], ri), f"query {i}: index mismatch"
+        assert np.array_equal(gs[:, i:i + 1], rs.astype(np.float32)), f"query {i}: score mismatch"
+    say(f"  {len(sample)} sampled queries bit-exact")
