@@ -6,11 +6,12 @@ and one HCA layer, i.e. every row of the decode hot path:
   1. kv_compress of the newest complete groups of every sequence: CSA K=V (m=4, E4M3+bf16 rows),
      indexer keys (m=4, FP4+E8M0) and HCA K=V (m=128), written at the caches' append position.
      This runs every step, an upper bound (in steady state it is due every 4th / 128th token).
-  2. CSA layer, as 4 batches of 4 sequences (the CSA 1M configuration): index_topk over 262,144
-     FP4 indexer entries per sequence -> top-1024, then csa_attend (64 heads x 512, top-1024
-     entries + 128-token window + sink).
-  3. HCA layer, one batch of 16 sequences (the HCA 1M configuration): hca_attend over 8,192
-     entries + 128-token window + sink.
+  2. CSA layer, all 16 sequences in one call: index_topk over 262,144 FP4 indexer entries per
+     sequence -> top-1024, then csa_attend (64 heads x 512, top-1024 entries + 128-token window
+     + sink).
+  3. HCA layer, the same 16 sequences: hca_attend over 8,192 entries + window + sink.
+The CSA decode step of the 4-sequence 1M configuration (index_topk + csa_attend on 4 of the
+sequences) is timed separately and reported with its fraction of peak HBM bandwidth.
 Inputs are seeded synthetic values (~N(0,1) before quantisation) generated and encoded on the
 GPU with the library's own kv_compress (m = 1 is its quantiser). The step's working set is
 ~2.8 GB, so consecutive steps stream from HBM rather than from the 256 MB last-level cache.
@@ -44,7 +45,8 @@ METRIC = "CSA+HCA decode queries/sec at 1M ctx; achieved HBM GB/s vs peak"
 CTX = 1 << 20
 N_CSA = CTX // 4       # 262,144 entries
 N_HCA = CTX // 128     # 8,192 entries
-B_CSA, N_CSA_BATCHES, B_HCA = 4, 4, 16
+B_STEP = 16      # sequences per decode step (both layers)
+B_CSA4 = 4       # the 1M-context CSA decode configuration
 H, D, HI, DI, K, W = 64, 512, 4, 128, 1024, 128
 ROW = 576
 SCAN_BYTES_PER_SEQ = N_CSA * (DI // 2 + DI // 32)   # 17,825,792 B of FP4 keys + E8M0 scales
@@ -62,91 +64,100 @@ def encode(values, m, fmt, rows=None, scales=None):
 
 
 class DecodeStep:
+    """The decode step's inputs, workspaces and calls (one CSA and one HCA layer, 16 sequences)."""
+
     def __init__(self, seed: int = 4):
         dev = torch.device("cuda")
         self.scale = D ** -0.5
-        self.pos_csa = torch.full((B_CSA,), CTX - 1, dtype=torch.int64, device=dev)
-        self.pos_hca = torch.full((B_HCA,), CTX - 1, dtype=torch.int64, device=dev)
-        self.csa = []
-        for j in range(N_CSA_BATCHES):
-            d = synth.Draws(seed + 100 * j, dev)
-            cache = torch.empty((B_CSA, N_CSA, ROW), dtype=torch.uint8, device=dev)
-            kc = torch.empty((B_CSA, N_CSA, DI // 2), dtype=torch.uint8, device=dev)
-            ks = torch.empty((B_CSA, N_CSA, DI // 32), dtype=torch.uint8, device=dev)
-            step = 1 << 16
-            for b in range(B_CSA):
-                for r0 in range(0, N_CSA, step):
-                    encode(d.normal((1, step, D)), 1, L.FMT_ROW_E4M3_BF16,
-                           rows=cache[b:b + 1, r0:r0 + step])
-                    encode(d.normal((1, step, DI)), 1, L.FMT_FP4_E8M0,
-                           rows=kc[b:b + 1, r0:r0 + step], scales=ks[b:b + 1, r0:r0 + step])
-            win, _ = encode(d.normal((B_CSA, W, D)), 1, L.FMT_ROW_E4M3_BF16)
-            iqc, iqs = encode(d.normal((B_CSA, HI, DI)), 1, L.FMT_FP4_E8M0)
-            self.csa.append(dict(
-                cache=cache, kc=kc, ks=ks, win=win,
-                iqc=iqc.view(B_CSA, 1, HI, DI // 2), iqs=iqs.view(B_CSA, 1, HI, DI // 32),
-                q=d.normal((B_CSA, 1, H, D), dtype=torch.bfloat16),
-                xt=d.normal((B_CSA, 4, D), dtype=torch.bfloat16),
-                xit=d.normal((B_CSA, 4, DI)),
-                idx=torch.empty((B_CSA, 1, K), dtype=torch.int32, device=dev),
-                out=torch.empty((B_CSA, 1, H, D), dtype=torch.float32, device=dev),
-                lse=torch.empty((B_CSA, 1, H), dtype=torch.float32, device=dev)))
-        d = synth.Draws(seed + 1000, dev)
+        self.pos = torch.full((B_STEP,), CTX - 1, dtype=torch.int64, device=dev)
+        d = synth.Draws(seed, dev)
+        cache = torch.empty((B_STEP, N_CSA, ROW), dtype=torch.uint8, device=dev)
+        kc = torch.empty((B_STEP, N_CSA, DI // 2), dtype=torch.uint8, device=dev)
+        ks = torch.empty((B_STEP, N_CSA, DI // 32), dtype=torch.uint8, device=dev)
+        step = 1 << 16
+        for b in range(B_STEP):
+            for r0 in range(0, N_CSA, step):
+                encode(d.normal((1, step, D)), 1, L.FMT_ROW_E4M3_BF16,
+                       rows=cache[b:b + 1, r0:r0 + step])
+                encode(d.normal((1, step, DI)), 1, L.FMT_FP4_E8M0,
+                       rows=kc[b:b + 1, r0:r0 + step], scales=ks[b:b + 1, r0:r0 + step])
+        win, _ = encode(d.normal((B_STEP, W, D)), 1, L.FMT_ROW_E4M3_BF16)
+        iqc, iqs = encode(d.normal((B_STEP, HI, DI)), 1, L.FMT_FP4_E8M0)
+        self.csa = dict(
+            cache=cache, kc=kc, ks=ks, win=win,
+            iqc=iqc.view(B_STEP, 1, HI, DI // 2), iqs=iqs.view(B_STEP, 1, HI, DI // 32),
+            q=d.normal((B_STEP, 1, H, D), dtype=torch.bfloat16),
+            xt=d.normal((B_STEP, 4, D), dtype=torch.bfloat16),
+            xit=d.normal((B_STEP, 4, DI)),
+            idx=torch.empty((B_STEP, 1, K), dtype=torch.int32, device=dev),
+            out=torch.empty((B_STEP, 1, H, D), dtype=torch.float32, device=dev),
+            lse=torch.empty((B_STEP, 1, H), dtype=torch.float32, device=dev))
         self.sink = d.normal((H,))
         self.w_csa, self.b_csa = synth.compressor_params(D, 4, d)
         self.w_idx, self.b_idx = synth.compressor_params(DI, 4, d)
         self.w_hca, self.b_hca = synth.compressor_params(D, 128, d)
-        hcache = torch.empty((B_HCA, N_HCA, ROW), dtype=torch.uint8, device=dev)
-        encode(d.normal((B_HCA, N_HCA, D)), 1, L.FMT_ROW_E4M3_BF16, rows=hcache)
-        hwin, _ = encode(d.normal((B_HCA, W, D)), 1, L.FMT_ROW_E4M3_BF16)
-        self.hca = dict(cache=hcache, win=hwin, q=d.normal((B_HCA, 1, H, D), dtype=torch.bfloat16),
-                        xt=d.normal((B_HCA, 128, D), dtype=torch.bfloat16),
-                        out=torch.empty((B_HCA, 1, H, D), dtype=torch.float32, device=dev),
-                        lse=torch.empty((B_HCA, 1, H), dtype=torch.float32, device=dev))
-        self.ws_idx = torch.empty(L.index_topk_workspace(B_CSA, 1, N_CSA, K, HI, DI), dtype=torch.uint8,
-                                  device=dev)
-        self.ws_csa = torch.empty(max(256, L.attend_workspace(B_CSA, 1, H, D, K + W)),
+        hcache = torch.empty((B_STEP, N_HCA, ROW), dtype=torch.uint8, device=dev)
+        encode(d.normal((B_STEP, N_HCA, D)), 1, L.FMT_ROW_E4M3_BF16, rows=hcache)
+        hwin, _ = encode(d.normal((B_STEP, W, D)), 1, L.FMT_ROW_E4M3_BF16)
+        self.hca = dict(cache=hcache, win=hwin, q=d.normal((B_STEP, 1, H, D), dtype=torch.bfloat16),
+                        xt=d.normal((B_STEP, 128, D), dtype=torch.bfloat16),
+                        out=torch.empty((B_STEP, 1, H, D), dtype=torch.float32, device=dev),
+                        lse=torch.empty((B_STEP, 1, H), dtype=torch.float32, device=dev))
+        self.ws_idx = torch.empty(L.index_topk_workspace(B_STEP, 1, N_CSA, K, HI, DI),
                                   dtype=torch.uint8, device=dev)
-        self.ws_hca = torch.empty(max(256, L.attend_workspace(B_HCA, 1, H, D, N_HCA + W)),
+        self.ws_csa = torch.empty(max(256, L.attend_workspace(B_STEP, 1, H, D, K + W),
+                                      L.attend_workspace(B_CSA4, 1, H, D, K + W)),
+                                  dtype=torch.uint8, device=dev)
+        self.ws_hca = torch.empty(max(256, L.attend_workspace(B_STEP, 1, H, D, N_HCA + W)),
                                   dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
-    # ---- the three stages of one step
+    def csa_slice(self, nb):
+        """The first nb sequences of the CSA layer (views; nothing is copied)."""
+        return {k: v[:nb] for k, v in self.csa.items()}
+
+    # ---- the stages of one step
     def compress(self):
-        for c in self.csa:
-            L.kv_compress(c["xt"], 4, self.w_csa, self.b_csa, L.FMT_ROW_E4M3_BF16,
-                          out_rows=c["cache"][:, N_CSA - 1:N_CSA])
-            L.kv_compress(c["xit"], 4, self.w_idx, self.b_idx, L.FMT_FP4_E8M0,
-                          out_rows=c["kc"][:, N_CSA - 1:N_CSA], out_scales=c["ks"][:, N_CSA - 1:N_CSA])
-        h = self.hca
+        c, h = self.csa, self.hca
+        L.kv_compress(c["xt"], 4, self.w_csa, self.b_csa, L.FMT_ROW_E4M3_BF16,
+                      out_rows=c["cache"][:, N_CSA - 1:N_CSA])
+        L.kv_compress(c["xit"], 4, self.w_idx, self.b_idx, L.FMT_FP4_E8M0,
+                      out_rows=c["kc"][:, N_CSA - 1:N_CSA], out_scales=c["ks"][:, N_CSA - 1:N_CSA])
         L.kv_compress(h["xt"], 128, self.w_hca, self.b_hca, L.FMT_ROW_E4M3_BF16,
                       out_rows=h["cache"][:, N_HCA - 1:N_HCA])
 
-    def index(self, c, ev=None):
+    def index(self, c=None, ev=None):
+        c = self.csa if c is None else c
         if ev is not None:
             L.profile_next_call(*ev)
-        L.index_topk(c["iqc"], c["iqs"], c["kc"], c["ks"], self.pos_csa, 4, K, want_scores=False,
-                     ws=self.ws_idx, idx_out=c["idx"])
+        L.index_topk(c["iqc"], c["iqs"], c["kc"], c["ks"], self.pos[:c["kc"].shape[0]], 4, K,
+                     want_scores=False, ws=self.ws_idx, idx_out=c["idx"])
 
-    def csa_attend(self, c, ev=None):
+    def csa_attend(self, c=None, ev=None):
+        c = self.csa if c is None else c
         if ev is not None:
             L.profile_next_call(*ev)
-        L.csa_attend(c["q"], c["cache"], c["idx"], c["win"], W, self.pos_csa, self.sink,
-                     self.scale, ws=self.ws_csa, out=c["out"], lse=c["lse"])
+        L.csa_attend(c["q"], c["cache"], c["idx"], c["win"], W, self.pos[:c["q"].shape[0]],
+                     self.sink, self.scale, ws=self.ws_csa, out=c["out"], lse=c["lse"])
 
     def hca_attend(self, ev=None):
         h = self.hca
         if ev is not None:
             L.profile_next_call(*ev)
-        L.hca_attend(h["q"], h["cache"], 128, h["win"], W, self.pos_hca, self.sink, self.scale,
+        L.hca_attend(h["q"], h["cache"], 128, h["win"], W, self.pos, self.sink, self.scale,
                      ws=self.ws_hca, out=h["out"], lse=h["lse"])
 
     def step(self):
         self.compress()
-        for c in self.csa:
-            self.index(c)
-            self.csa_attend(c)
+        self.index()
+        self.csa_attend()
         self.hca_attend()
+
+    def csa4_step(self):
+        """The 1M-context CSA decode step of 4 sequences: index_topk + csa_attend."""
+        c = self.csa_slice(B_CSA4)
+        self.index(c)
+        self.csa_attend(c)
 
 
 def event_pair():
@@ -158,44 +169,76 @@ def event_pair():
 
 # Algorithmic HBM bytes and flops per launch of each stage's dominant kernel: what the method must
 # move (selected rows, not the whole cache) and compute (QK and PV, 2 flops per MAC).
-#   index_scan: 4 sequences x 262,144 FP4 keys x (64 B codes + 4 B scales); 512 MAC per key.
-#   csa_attend: 4 x [(1024 + 128) rows x 576 B + 1024 ids x 4 B + q 64x512 bf16 + out 64x512 fp32
-#               + lse 64 fp32]; 64 heads x 1152 rows x 512 x 4 flops.
-#   hca_attend: 16 x [(8192 + 128) rows x 576 B + q + out + lse]; 64 x 8320 x 512 x 4 flops.
+#   index_scan: 16 sequences x 262,144 FP4 keys x (64 B codes + 4 B scales); 512 MAC per key.
+#   csa_attend: 16 x [(1024 + 128) rows x 576 B + 1024 ids x 4 B + q 64x512 bf16 + out 64x512 fp32
+#               + lse 64 fp32] + sink; 64 heads x 1152 rows x 512 x 4 flops.
+#   hca_attend: 16 x [(8192 + 128) rows x 576 B + q + out + lse] + sink; 64 x 8320 x 512 x 4 flops.
+CSA_SEQ_BYTES = (K + W) * ROW + K * 4 + H * D * 2 + H * D * 4 + H * 4
 KERNELS = {
-    "index_scan": dict(per_step=N_CSA_BATCHES, bytes=B_CSA * SCAN_BYTES_PER_SEQ,
-                       flops=B_CSA * N_CSA * 512 * 2, peak_flops=157.3e12,
+    "index_scan": dict(per_step=1, bytes=B_STEP * SCAN_BYTES_PER_SEQ,
+                       flops=B_STEP * N_CSA * 512 * 2, peak_flops=157.3e12,
                        name="index_scan_kernel (csah_index_topk)", source="index_topk.hip",
-                       profile="index_scan_csa1m"),
-    "csa_attend": dict(per_step=N_CSA_BATCHES,
-                       bytes=B_CSA * ((K + W) * ROW + K * 4 + H * D * 2 + H * D * 4 + H * 4) + H * 4,
-                       flops=B_CSA * H * (K + W) * D * 4, peak_flops=2.5e15,
-                       name="attend_kernel (csah_csa_attend)", source="attend.hip",
-                       profile="csa_attend_csa1m"),
+                       profile="index_scan_csa1m_b16"),
+    "csa_attend": dict(per_step=1, bytes=B_STEP * CSA_SEQ_BYTES + H * 4,
+                       flops=B_STEP * H * (K + W) * D * 4, peak_flops=2.5e15,
+                       name="attend_x_kernel (csah_csa_attend)", source="attend.hip",
+                       profile="csa_attend_csa1m_b16"),
     "hca_attend": dict(per_step=1,
-                       bytes=B_HCA * ((N_HCA + W) * ROW + H * D * 2 + H * D * 4 + H * 4) + H * 4,
-                       flops=B_HCA * H * (N_HCA + W) * D * 4, peak_flops=2.5e15,
-                       name="attend_kernel (csah_hca_attend)", source="attend.hip",
-                       profile="hca_attend_hca1m"),
+                       bytes=B_STEP * ((N_HCA + W) * ROW + H * D * 2 + H * D * 4 + H * 4) + H * 4,
+                       flops=B_STEP * H * (N_HCA + W) * D * 4, peak_flops=2.5e15,
+                       name="attend_x_kernel (csah_hca_attend)", source="attend.hip",
+                       profile="hca_attend_hca1m_b16"),
 }
+# The 1M-context CSA decode step of 4 sequences (index_topk + csa_attend): what the method must
+# move per sequence is its FP4 keys, the selected rows, the window, q and the output.
+CSA4_BYTES = B_CSA4 * (SCAN_BYTES_PER_SEQ + CSA_SEQ_BYTES) + H * 4
 
 
 def kernel_times(ws: DecodeStep, reps: int):
     """Average duration (ms) of each stage's dominant kernel, from events attached to its dispatch."""
     evs = {k: [] for k in KERNELS}
     for _ in range(reps):
-        for c in ws.csa:
-            e = event_pair()
-            ws.index(c, e)
-            evs["index_scan"].append(e)
-            e = event_pair()
-            ws.csa_attend(c, e)
-            evs["csa_attend"].append(e)
+        e = event_pair()
+        ws.index(ev=e)
+        evs["index_scan"].append(e)
+        e = event_pair()
+        ws.csa_attend(ev=e)
+        evs["csa_attend"].append(e)
         e = event_pair()
         ws.hca_attend(e)
         evs["hca_attend"].append(e)
     torch.cuda.synchronize()
     return {k: statistics.mean(a.elapsed_time(b) for a, b in v) for k, v in evs.items()}
+
+
+def capture(fn):
+    """A HIP graph of fn() (warmed up on a side stream first), replayed a few times."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(g, fn, steps):
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        if g is not None:
+            g.replay()
+        else:
+            fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
 
 
 def traffic_from_profile(kernel: str):
@@ -285,6 +328,148 @@ def cpu_baseline(min_seconds: float):
                       f"{t * 1e3:.0f} ms each, CPU: {cpu}"}
 
 
+# ---- prefill chunk: 4096 new tokens appended to a 1,048,576-token cache ---------------------------
+PF_Q = 4096
+PF_POS0 = CTX                       # query i sits at position 1,048,576 + i
+PF_N_CSA = N_CSA + PF_Q // 4        # 263,168 entries once the chunk is compressed
+PF_N_HCA = N_HCA + PF_Q // 128      # 8,224
+PF_PEAK_BF16, PF_PEAK_FP4 = 2.5e15, 10.1e15
+
+
+class PrefillStep:
+    """One prefill chunk through one CSA and one HCA layer.
+
+    Per step: kv_compress the chunk's raw K=V rows (m=4 into the CSA cache, m=128 into the HCA
+    cache, m=1 into the window buffer) and raw indexer keys (m=4, FP4), then index_topk for the
+    4096 queries (causal top-1024 each), csa_attend and hca_attend (64 heads x 512, window 128,
+    sink). Caches and queries are seeded ~N(0,1) values encoded on the GPU by the library.
+    """
+
+    def __init__(self, seed: int = 5):
+        dev = torch.device("cuda")
+        d = synth.Draws(seed, dev)
+        self.scale = D ** -0.5
+        self.cache = torch.empty((1, PF_N_CSA, ROW), dtype=torch.uint8, device=dev)
+        self.kc = torch.empty((1, PF_N_CSA, DI // 2), dtype=torch.uint8, device=dev)
+        self.ks = torch.empty((1, PF_N_CSA, DI // 32), dtype=torch.uint8, device=dev)
+        step = 1 << 16
+        for r0 in range(0, N_CSA, step):
+            encode(d.normal((1, step, D)), 1, L.FMT_ROW_E4M3_BF16, rows=self.cache[:, r0:r0 + step])
+            encode(d.normal((1, step, DI)), 1, L.FMT_FP4_E8M0, rows=self.kc[:, r0:r0 + step],
+                   scales=self.ks[:, r0:r0 + step])
+        self.hcache = torch.empty((1, PF_N_HCA, ROW), dtype=torch.uint8, device=dev)
+        encode(d.normal((1, N_HCA, D)), 1, L.FMT_ROW_E4M3_BF16, rows=self.hcache[:, :N_HCA])
+        # window buffer: the 127 cached tokens before the chunk, then the chunk's own tokens
+        self.win = torch.empty((1, W - 1 + PF_Q, ROW), dtype=torch.uint8, device=dev)
+        encode(d.normal((1, W - 1, D)), 1, L.FMT_ROW_E4M3_BF16, rows=self.win[:, :W - 1])
+        self.x = d.normal((1, PF_Q, D), dtype=torch.bfloat16)       # chunk K=V tokens
+        self.xi = d.normal((1, PF_Q, DI))                           # chunk indexer-key tokens
+        self.q = d.normal((1, PF_Q, H, D), dtype=torch.bfloat16)
+        iqc, iqs = encode(d.normal((PF_Q, HI, DI)), 1, L.FMT_FP4_E8M0)
+        self.iqc, self.iqs = iqc.view(1, PF_Q, HI, DI // 2), iqs.view(1, PF_Q, HI, DI // 32)
+        self.sink = d.normal((H,))
+        self.w_csa, self.b_csa = synth.compressor_params(D, 4, d)
+        self.w_idx, self.b_idx = synth.compressor_params(DI, 4, d)
+        self.w_hca, self.b_hca = synth.compressor_params(D, 128, d)
+        self.w_one, self.b_one = torch.zeros(D, device=dev), torch.zeros(1, device=dev)
+        self.pos = torch.full((1,), PF_POS0, dtype=torch.int64, device=dev)
+        self.idx = torch.empty((1, PF_Q, K), dtype=torch.int32, device=dev)
+        self.out = torch.empty((1, PF_Q, H, D), dtype=torch.float32, device=dev)
+        self.lse = torch.empty((1, PF_Q, H), dtype=torch.float32, device=dev)
+        self.ws_idx = torch.empty(L.index_topk_workspace(1, PF_Q, PF_N_CSA, K, HI, DI),
+                                  dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def compress(self):
+        L.kv_compress(self.x, 4, self.w_csa, self.b_csa, L.FMT_ROW_E4M3_BF16,
+                      out_rows=self.cache[:, N_CSA:])
+        L.kv_compress(self.xi, 4, self.w_idx, self.b_idx, L.FMT_FP4_E8M0,
+                      out_rows=self.kc[:, N_CSA:], out_scales=self.ks[:, N_CSA:])
+        L.kv_compress(self.x, 128, self.w_hca, self.b_hca, L.FMT_ROW_E4M3_BF16,
+                      out_rows=self.hcache[:, N_HCA:])
+        L.kv_compress(self.x, 1, self.w_one, self.b_one, L.FMT_ROW_E4M3_BF16,
+                      out_rows=self.win[:, W - 1:])
+
+    def index(self, ev=None):
+        if ev is not None:
+            L.profile_next_call(*ev)
+        L.index_topk(self.iqc, self.iqs, self.kc, self.ks, self.pos, 4, K, want_scores=False,
+                     ws=self.ws_idx, idx_out=self.idx)
+
+    def csa(self, ev=None):
+        if ev is not None:
+            L.profile_next_call(*ev)
+        L.csa_attend(self.q, self.cache, self.idx, self.win, W, self.pos, self.sink, self.scale,
+                     out=self.out, lse=self.lse)
+
+    def hca(self, ev=None):
+        if ev is not None:
+            L.profile_next_call(*ev)
+        L.hca_attend(self.q, self.hcache, 128, self.win, W, self.pos, self.sink, self.scale,
+                     out=self.out, lse=self.lse)
+
+    def step(self):
+        self.compress()
+        self.index()
+        self.csa()
+        self.hca()
+
+
+def prefill_measure(steps: int, warmup: int):
+    """Whole-chunk time and the dominant kernel of each stage against its MFMA roofline."""
+    ps = PrefillStep()
+    for _ in range(warmup):
+        ps.step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        ps.step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    ev = {"index_hist": [], "csa_attend": [], "hca_attend": []}
+    for _ in range(max(1, steps // 2)):
+        ps.compress()
+        e = event_pair()
+        ps.index(e)
+        ev["index_hist"].append(e)
+        e = event_pair()
+        ps.csa(e)
+        ev["csa_attend"].append(e)
+        e = event_pair()
+        ps.hca(e)
+        ev["hca_attend"].append(e)
+    torch.cuda.synchronize()
+    kt = {k: statistics.mean(a.elapsed_time(b) for a, b in v) for k, v in ev.items()}
+    # algorithmic operations: FP4 MACs of the indexer (512 per visible entry per query, one pass),
+    # QK + PV flops of the attention over each query's rows (1152 CSA, 8192 + (i+1)//128 + 128 HCA)
+    n_vis = sum(min(PF_N_CSA, (PF_POS0 + i + 1) // 4) for i in range(PF_Q))
+    hca_rows = sum(min(PF_N_HCA, (PF_POS0 + i + 1) // 128) + W for i in range(PF_Q))
+    ops = {"index_hist": (2.0 * 512 * n_vis, PF_PEAK_FP4, "fp4"),
+           "csa_attend": (4.0 * H * D * PF_Q * (K + W), PF_PEAK_BF16, "bf16"),
+           "hca_attend": (4.0 * H * D * hca_rows, PF_PEAK_BF16, "bf16")}
+    kernels = {}
+    for k, (fl, peak, dt) in ops.items():
+        t = kt[k] * 1e-3
+        kernels[k] = {"avg_launch_us": t * 1e6, "algorithmic_ops": fl, "achieved_TFLOPs": fl / t / 1e12,
+                      "peak_TFLOPs": peak / 1e12, "frac": fl / t / peak, "dtype": dt}
+    dom = max(kernels, key=lambda k: kernels[k]["avg_launch_us"])
+    log(f"  prefill chunk: {ms:.3f} ms; " + ", ".join(f"{k} {v['avg_launch_us']:.0f} us"
+                                                      for k, v in kernels.items()))
+    return {
+        "metric": "prefill chunk tokens/s (4096 new tokens on a 1M cache, one CSA + one HCA layer)",
+        "value": PF_Q / (ms * 1e-3), "unit": "tokens/s", "ms_per_chunk": ms, "steps": steps,
+        "workload": "1 sequence, 1,048,576 cached tokens + 4,096 new: kv_compress of the chunk "
+                    "(m=4, FP4 indexer keys, m=128, window rows), per-query causal top-1024 over "
+                    "263,168 FP4 entries (scaled FP4 MFMA), CSA and HCA attention, 64 heads x 512",
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved_TFLOPs"],
+                     "peak": kernels[dom]["peak_TFLOPs"], "unit": "TFLOP/s",
+                     "frac": kernels[dom]["frac"]},
+        "kernels": kernels,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -294,6 +479,7 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB copy kernel (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -308,32 +494,13 @@ def main():
     for _ in range(args.warmup):
         ws.step()
     torch.cuda.synchronize()
-    graph = None
-    if not args.no_graph:
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            ws.step()
-        torch.cuda.current_stream().wait_stream(s)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            ws.step()
-        for _ in range(3):
-            graph.replay()
-        torch.cuda.synchronize()
+    graph = None if args.no_graph else capture(ws.step)
     log(f"timing {args.steps} steps ({'graph replay' if graph else 'eager'})...")
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            ws.step()
-    t1.record()
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = time_replays(graph, ws.step, args.steps)
     log(f"  {ms * 1e3:.1f} us per step")
+    g4 = None if args.no_graph else capture(ws.csa4_step)
+    ms4 = time_replays(g4, ws.csa4_step, args.steps)
+    log(f"  CSA decode step, 4 sequences at 1M: {ms4 * 1e3:.1f} us")
     kt = kernel_times(ws, args.kernel_reps)
     log("  dominant kernels (us): " + ", ".join(f"{k} {v * 1e3:.2f}" for k, v in kt.items()))
     # the roofline object reports the kernel with the largest share of the step
@@ -358,7 +525,7 @@ def main():
         roof = {"bound": "mfma" if dom != "index_scan" else "alu",
                 "achieved": spec["flops"] / t_dom / 1e12, "peak": spec["peak_flops"] / 1e12,
                 "unit": "TFLOP/s"}
-    queries = N_CSA_BATCHES * B_CSA
+    queries = B_STEP
     line = {
         "metric": METRIC,
         "value": queries / (ms * 1e-3),
@@ -373,11 +540,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "decode step, 16 sequences x 1,048,576-token context, one CSA layer "
-                        "(4 batches x 4 sequences: FP4 index over 262,144 entries, top-1024, "
-                        "sparse attention + 128-token window + sink) and one HCA layer (batch 16: "
-                        "dense attention over 8,192 entries + window + sink), newest-group "
-                        "kv_compress every step; 64 heads x 512 (448 e4m3 + 64 bf16)",
+            "workload": "decode step, 16 sequences x 1,048,576-token context through one CSA "
+                        "layer (FP4 index over 262,144 entries per sequence, top-1024, sparse "
+                        "attention + 128-token window + sink) and one HCA layer (dense attention "
+                        "over 8,192 entries + window + sink), newest-group kv_compress every "
+                        "step; 64 heads x 512 (448 e4m3 + 64 bf16)",
             "global_batch": queries, "seq_len": CTX, "heads": H, "head_dim": D,
             "indexer": "4 heads x 128, FP4 e2m1 + E8M0/32", "top_k": K, "window": W,
             "timing": "hip graph replay" if graph is not None else "eager",
@@ -392,7 +559,20 @@ def main():
             "avg_launch_us": kt[dom] * 1e3,
         },
         "kernels": kinfo,
+        "csa_decode_1m_b4": {
+            "what": "index_topk + csa_attend for 4 sequences at 1,048,576 tokens (262,144 FP4 "
+                    "keys each, top-1024, window 128, sink)",
+            "us_per_step": ms4 * 1e3, "algorithmic_bytes": CSA4_BYTES,
+            "achieved_GBps": CSA4_BYTES / (ms4 * 1e-3) / 1e9,
+            "frac_of_hbm_peak": CSA4_BYTES / (ms4 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "queries_per_s": B_CSA4 / (ms4 * 1e-3),
+        },
     }
+    if not args.no_prefill:
+        log("prefill chunk (4096 tokens on a 1M cache)...")
+        del ws, graph, g4
+        torch.cuda.empty_cache()
+        line["prefill"] = prefill_measure(max(2, min(args.steps, 10)), max(1, min(args.warmup, 2)))
     if args.calibrate_copy:
         copy_calibration()
     if not args.no_cpu_baseline:
