@@ -9,7 +9,8 @@ and one HCA layer, i.e. every row of the decode hot path:
   2. CSA layer, all 16 sequences in one call: index_topk over 262,144 FP4 indexer entries per
      sequence -> top-1024, then csa_attend (64 heads x 512, top-1024 entries + 128-token window
      + sink).
-  3. HCA layer, the same 16 sequences: hca_attend over 8,192 entries + window + sink.
+  3. HCA layer, the same 16 sequences: hca_attend over 8,192 entries + window + sink; it runs
+     on a second stream, concurrently with the CSA layer (the two are independent).
 The CSA decode step of the 4-sequence 1M configuration (index_topk + csa_attend on 4 of the
 sequences) is timed separately and reported with its fraction of peak HBM bandwidth.
 Inputs are seeded synthetic values (~N(0,1) before quantisation) generated and encoded on the
@@ -110,6 +111,7 @@ class DecodeStep:
                                   dtype=torch.uint8, device=dev)
         self.ws_hca = torch.empty(max(256, L.attend_workspace(B_STEP, 1, H, D, N_HCA + W)),
                                   dtype=torch.uint8, device=dev)
+        self.side = torch.cuda.Stream(device=dev)  # default priority
         torch.cuda.synchronize()
 
     def csa_slice(self, nb):
@@ -117,12 +119,15 @@ class DecodeStep:
         return {k: v[:nb] for k, v in self.csa.items()}
 
     # ---- the stages of one step
-    def compress(self):
-        c, h = self.csa, self.hca
+    def compress_csa(self):
+        c = self.csa
         L.kv_compress(c["xt"], 4, self.w_csa, self.b_csa, L.FMT_ROW_E4M3_BF16,
                       out_rows=c["cache"][:, N_CSA - 1:N_CSA])
         L.kv_compress(c["xit"], 4, self.w_idx, self.b_idx, L.FMT_FP4_E8M0,
                       out_rows=c["kc"][:, N_CSA - 1:N_CSA], out_scales=c["ks"][:, N_CSA - 1:N_CSA])
+
+    def compress_hca(self):
+        h = self.hca
         L.kv_compress(h["xt"], 128, self.w_hca, self.b_hca, L.FMT_ROW_E4M3_BF16,
                       out_rows=h["cache"][:, N_HCA - 1:N_HCA])
 
@@ -147,17 +152,51 @@ class DecodeStep:
         L.hca_attend(h["q"], h["cache"], 128, h["win"], W, self.pos, self.sink, self.scale,
                      ws=self.ws_hca, out=h["out"], lse=h["lse"])
 
-    def step(self):
-        self.compress()
+    def csa_branch(self):
+        self.compress_csa()
         self.index()
         self.csa_attend()
+
+    def hca_branch(self):
+        self.compress_hca()
         self.hca_attend()
+
+    def step(self):
+        """Eager step: the HCA branch on a second stream beside the CSA branch."""
+        main = torch.cuda.current_stream()
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            self.hca_branch()
+        self.csa_branch()
+        main.wait_stream(self.side)
 
     def csa4_step(self):
         """The 1M-context CSA decode step of 4 sequences: index_topk + csa_attend."""
         c = self.csa_slice(B_CSA4)
         self.index(c)
         self.csa_attend(c)
+
+
+class StepGraphs:
+    """The step as two HIP graphs, one per layer, replayed on two streams so that the HCA branch
+    (compress + dense attention, bound by the matrix cores) runs concurrently with the CSA branch
+    (compress + index scan, bound by HBM, then sparse attention). The layers are independent."""
+
+    def __init__(self, ws: "DecodeStep"):
+        self.ws = ws
+        self.g_csa = capture(ws.csa_branch)
+        with torch.cuda.stream(ws.side):
+            self.g_hca = capture(ws.hca_branch)
+        torch.cuda.synchronize()
+
+    def replay(self):
+        main, side = torch.cuda.current_stream(), self.ws.side
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            self.g_hca.replay()
+        self.g_csa.replay()
+        main.wait_stream(side)
+
 
 
 def event_pair():
@@ -212,14 +251,16 @@ def kernel_times(ws: DecodeStep, reps: int):
 
 
 def capture(fn):
-    """A HIP graph of fn() (warmed up on a side stream first), replayed a few times."""
+    """A HIP graph of fn() (warmed up on a scratch stream first), replayed a few times on the
+    current stream."""
+    cur = torch.cuda.current_stream()
     s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
+    s.wait_stream(cur)
     with torch.cuda.stream(s):
         fn()
-    torch.cuda.current_stream().wait_stream(s)
+    cur.wait_stream(s)
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
         fn()
     for _ in range(3):
         g.replay()
@@ -494,7 +535,7 @@ def main():
     for _ in range(args.warmup):
         ws.step()
     torch.cuda.synchronize()
-    graph = None if args.no_graph else capture(ws.step)
+    graph = None if args.no_graph else StepGraphs(ws)
     log(f"timing {args.steps} steps ({'graph replay' if graph else 'eager'})...")
     ms = time_replays(graph, ws.step, args.steps)
     log(f"  {ms * 1e3:.1f} us per step")

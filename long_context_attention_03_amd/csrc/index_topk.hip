@@ -438,11 +438,13 @@ __global__ __launch_bounds__(kSelThreads) void index_select_kernel(
 }
 
 // Ordered top-k by rank counting: keys are unique, so the output position of candidate x is the
-// number of candidates greater than x. A workgroup of 256 lanes ranks 16 candidates; each
-// 16-lane group splits the candidate list 16 ways and sums the partial counts with lane shuffles.
-// Massive ties (more candidates than kSortCap) fall back to finalize_slot in workgroup 0.
+// number of candidates greater than x. A workgroup of 256 lanes ranks 16 candidates; each group
+// of kRankLanes lanes splits the candidate list kRankLanes ways and sums the partial counts with
+// lane shuffles. Massive ties (more candidates than kSortCap) fall back to finalize_slot in
+// workgroup 0.
 constexpr int kRankThreads = 256;
-constexpr int kRankPerWG = kRankThreads / 16;
+constexpr int kRankLanes = 16;
+constexpr int kRankPerWG = kRankThreads / kRankLanes;
 
 __global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
     const int64_t* __restrict__ pos, int m, int Q, int64_t N, int k,
@@ -474,20 +476,19 @@ __global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
       io[j] = -1;
       if (so) so[j] = -INFINITY;
     }
-  const uint32_t e = (uint32_t)blockIdx.x * kRankPerWG + (t >> 4);  // candidate ranked here
+  const uint32_t e = (uint32_t)blockIdx.x * kRankPerWG + (t / kRankLanes);  // ranked here
   if ((uint32_t)blockIdx.x * kRankPerWG >= n) return;
   const uint64_t* sure = ws.sure(slot);
   const uint64_t* tie = ws.tie(slot);
   for (uint32_t j = t; j < n; j += kRankThreads) keys[j] = j < ns ? sure[j] : tie[j - ns];
   __syncthreads();
-  const int part = t & 15;
+  const int part = t % kRankLanes;
   const uint64_t x = e < n ? keys[e] : ~(uint64_t)0;
-  const uint32_t per = (n + 15) / 16;
-  const uint32_t j0 = part * per, j1 = j0 + per < n ? j0 + per : n;
+  // lanes of a group read interleaved keys (j = part, part + kRankLanes, ...): no bank conflicts
   uint32_t above = 0;
-  for (uint32_t j = j0; j < j1; j++) above += keys[j] > x ? 1u : 0u;
+  for (uint32_t j = part; j < n; j += kRankLanes) above += keys[j] > x ? 1u : 0u;
 #pragma unroll
-  for (int o = 1; o < 16; o <<= 1) above += (uint32_t)__shfl_xor((int)above, o, 64);
+  for (int o = 1; o < kRankLanes; o <<= 1) above += (uint32_t)__shfl_xor((int)above, o, 64);
   if (part == 0 && e < n && above < (uint32_t)kk) {
     io[above] = (int32_t)(0xFFFFFFFFu - (uint32_t)x);
     if (so) so[above] = key_to_float((uint32_t)(x >> 32));
@@ -758,13 +759,13 @@ __global__ __launch_bounds__(1024) void index_sort_kernel(const int64_t* __restr
                                                           int Q, int64_t N, int k,
                                                           int32_t* __restrict__ idx_out,
                                                           float* __restrict__ score_out,
-                                                          IdxWs ws) {
+                                                          IdxWs ws, int bin_bits) {
   const int slot = blockIdx.x, b = slot / Q, i = slot - b * Q;
   const int64_t nv = visible_entries(pos, b, i, m, N);
   const int kk = (int)(nv < k ? nv : k);
   __shared__ uint64_t keys[kSortCap];
   __shared__ uint32_t dh[256];
-  finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh, 32 - kPBinShift);
+  finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh, bin_bits);
 }
 
 template <int HP>
@@ -784,7 +785,8 @@ static hipError_t launch_mfma_hp(const IndexArgs& a, const IdxWs& w, hipStream_t
   index_mfma_select_kernel<HP><<<grid, 256, 0, s>>>(a.q_codes, a.q_scales, a.HI, a.k_codes,
                                                     a.k_scales, a.k_seq_stride, a.N, a.pos, a.m,
                                                     a.Q, a.k, sp, w);
-  index_sort_kernel<<<slots, 1024, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, a.idx_out, a.score_out, w);
+  index_sort_kernel<<<slots, 1024, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, a.idx_out, a.score_out, w,
+                                           32 - kPBinShift);
   return hipGetLastError();
 }
 
