@@ -37,6 +37,14 @@
 
 namespace csah {
 
+// Scan launch shape: workgroups per launch (the key range is split evenly among them) and load
+// groups in flight per lane (each double-buffered).
+#ifndef CSAH_SCAN_WGS
+#define CSAH_SCAN_WGS 1024
+#endif
+#ifndef CSAH_SCAN_U
+#define CSAH_SCAN_U 4
+#endif
 constexpr int kBins = 4096;
 constexpr int kBinShift = 20;  // top 12 bits of the order key
 constexpr int kSortCap = 4096;
@@ -137,7 +145,7 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
     int64_t k_seq_stride, int64_t N, const int64_t* __restrict__ pos, int m, int Q, int chunk,
     IdxWs ws) {
   constexpr int EPR = 256 / NB;  // entries per workgroup-wide group of lanes
-  constexpr int U = 4;           // groups whose loads are in flight together
+  constexpr int U = CSAH_SCAN_U;  // groups whose loads are in flight together
   constexpr int STEP = EPR * U;
   const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
   const int tid = threadIdx.x, sub = tid % NB, ent = tid / NB;
@@ -810,9 +818,9 @@ hipError_t launch_index_topk(const IndexArgs& a) {
   if (use_mfma_path(a.Q, a.HI, a.dI)) return launch_index_mfma(a);
   IdxWs w = make_ws(a.ws, a.N, a.k, true);
   index_prep_kernel<<<slots, 256, 0, s>>>(a.q_codes, a.q_scales, a.HI, a.dI, w);
-  // scan: about 1024 workgroups in total (four per CU), each streaming a contiguous range
+  // scan: about CSAH_SCAN_WGS workgroups in total, each streaming a contiguous range
   const int64_t total = (int64_t)slots * (a.N > 0 ? a.N : 1);
-  int64_t chunk = (total + 1023) / 1024;
+  int64_t chunk = (total + CSAH_SCAN_WGS - 1) / CSAH_SCAN_WGS;
   chunk = ((chunk + 1023) / 1024) * 1024;
   if (chunk < 1024) chunk = 1024;
   if (chunk > (1 << 22)) chunk = 1 << 22;

@@ -85,6 +85,18 @@ def test_n_limits_visibility_below_stride():
     _compare("N<stride", kc, ks, qc, qs, pos, 4, 128, N=N)
 
 
+@pytest.mark.parametrize("HI,dI", [(1, 128), (8, 64), (16, 32), (5, 128)])
+def test_decode_head_counts_and_key_widths(HI, dI):
+    """One query per sequence with other indexer shapes: heads beyond the first MFMA row group
+    (summed across lane rows), and 64- / 32-dim keys (zero-padded operand blocks)."""
+    rng = np.random.default_rng(40 + HI + dI)
+    B, N, m, k = 3, 9001, 4, 512
+    kc, ks = O.encode_rows(rng.normal(size=(B, N, dI)), O.FMT_FP4_E8M0)
+    qc, qs = O.encode_rows(rng.normal(size=(B, 1, HI, dI)), O.FMT_FP4_E8M0)
+    pos = np.array([N * m - 1, 4 * 3000 + 2, 4 * 700 - 1], np.int64)
+    _compare(f"decode HI={HI} dI={dI}", kc, ks, qc, qs, pos, m, k)
+
+
 # ---- many queries per sequence (prefill chunks): the scaled-FP4-MFMA schedule ----------------
 def _fp4_inputs(rng, B, Q, N, HI, dI=128, coarse=False):
     kv = rng.normal(size=(B, N, dI))
