@@ -446,11 +446,11 @@ __global__ __launch_bounds__(kSelThreads) void index_select_kernel(
 }
 
 // Ordered top-k by rank counting: keys are unique, so the output position of candidate x is the
-// number of candidates greater than x. A workgroup of 256 lanes ranks 16 candidates; each group
+// number of candidates greater than x. A workgroup of 1024 lanes ranks 64 candidates; each group
 // of kRankLanes lanes splits the candidate list kRankLanes ways and sums the partial counts with
 // lane shuffles. Massive ties (more candidates than kSortCap) fall back to finalize_slot in
 // workgroup 0.
-constexpr int kRankThreads = 256;
+constexpr int kRankThreads = 1024;
 constexpr int kRankLanes = 16;
 constexpr int kRankPerWG = kRankThreads / kRankLanes;
 
