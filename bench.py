@@ -48,6 +48,7 @@ N_CSA = CTX // 4       # 262,144 entries
 N_HCA = CTX // 128     # 8,192 entries
 B_STEP = 16      # sequences per decode step (both layers)
 B_CSA4 = 4       # the 1M-context CSA decode configuration
+MTP_Q = 5        # draft tokens verified per sequence in the multi-query decode measurement
 H, D, HI, DI, K, W = 64, 512, 4, 128, 1024, 128
 ROW = 576
 SCAN_BYTES_PER_SEQ = N_CSA * (DI // 2 + DI // 32)   # 17,825,792 B of FP4 keys + E8M0 scales
@@ -112,7 +113,38 @@ class DecodeStep:
         self.ws_hca = torch.empty(max(256, L.attend_workspace(B_STEP, 1, H, D, N_HCA + W)),
                                   dtype=torch.uint8, device=dev)
         self.side = torch.cuda.Stream(device=dev)  # default priority
+        # speculative verification: 5 query tokens per sequence for the first 4 sequences
+        QM, BM = MTP_Q, B_CSA4
+        self.pos_m = torch.full((BM,), CTX - QM, dtype=torch.int64, device=dev)
+        iqc5, iqs5 = encode(d.normal((BM * QM, HI, DI)), 1, L.FMT_FP4_E8M0)
+        win5, _ = encode(d.normal((BM, W - 1 + QM, D)), 1, L.FMT_ROW_E4M3_BF16)
+        hwin5, _ = encode(d.normal((BM, W - 1 + QM, D)), 1, L.FMT_ROW_E4M3_BF16)
+        self.mtp = dict(
+            iqc=iqc5.view(BM, QM, HI, DI // 2), iqs=iqs5.view(BM, QM, HI, DI // 32),
+            q=d.normal((BM, QM, H, D), dtype=torch.bfloat16), win=win5, hwin=hwin5,
+            idx=torch.empty((BM, QM, K), dtype=torch.int32, device=dev),
+            out=torch.empty((BM, QM, H, D), dtype=torch.float32, device=dev),
+            lse=torch.empty((BM, QM, H), dtype=torch.float32, device=dev),
+            hout=torch.empty((BM, QM, H, D), dtype=torch.float32, device=dev),
+            hlse=torch.empty((BM, QM, H), dtype=torch.float32, device=dev),
+            ws_idx=torch.empty(L.index_topk_workspace(BM, QM, N_CSA, K, HI, DI),
+                               dtype=torch.uint8, device=dev),
+            ws_att=torch.empty(max(256, L.attend_workspace(BM, QM, H, D, N_HCA + W),
+                                   L.attend_workspace(BM, QM, H, D, K + W)),
+                               dtype=torch.uint8, device=dev))
         torch.cuda.synchronize()
+
+    def mtp_step(self):
+        """Verification of 5 draft tokens for 4 sequences: each query gets its own causal top-k,
+        sparse attention and dense HCA attention (the CSA and HCA caches of sequences 0-3)."""
+        c, t = self.csa_slice(B_CSA4), self.mtp
+        hc = self.hca["cache"][:B_CSA4]
+        L.index_topk(t["iqc"], t["iqs"], c["kc"], c["ks"], self.pos_m, 4, K, want_scores=False,
+                     ws=t["ws_idx"], idx_out=t["idx"])
+        L.csa_attend(t["q"], c["cache"], t["idx"], t["win"], W, self.pos_m, self.sink, self.scale,
+                     ws=t["ws_att"], out=t["out"], lse=t["lse"])
+        L.hca_attend(t["q"], hc, 128, t["hwin"], W, self.pos_m, self.sink, self.scale,
+                     ws=t["ws_att"], out=t["hout"], lse=t["hlse"])
 
     def csa_slice(self, nb):
         """The first nb sequences of the CSA layer (views; nothing is copied)."""
@@ -605,6 +637,21 @@ def main():
         },
         "kernels": kinfo,
     }
+    if not args.no_csa4:
+        gm = None if args.no_graph else capture(ws.mtp_step)
+        msm = time_replays(gm, ws.mtp_step, args.steps)
+        log(f"  multi-query decode (4 sequences x {MTP_Q} queries): {msm * 1e3:.1f} us")
+        # unique bytes: each sequence's keys and HCA rows once, each query's selected rows, the
+        # windows, q and both outputs
+        mbytes = (B_CSA4 * (SCAN_BYTES_PER_SEQ + N_HCA * ROW + 2 * (W - 1 + MTP_Q) * ROW)
+                  + B_CSA4 * MTP_Q * (K * ROW + K * 4 + 2 * H * D * 2 + 2 * H * D * 4 + 2 * H * 4))
+        line["decode_multi_query"] = {
+            "what": f"{B_CSA4} sequences x {MTP_Q} query tokens (draft verification) at 1,048,576 "
+                    "tokens: per-query causal top-1024 over 262,144 FP4 keys, CSA attention, HCA "
+                    "attention over 8,192 entries, window 128, sink",
+            "us_per_step": msm * 1e3, "queries_per_s": B_CSA4 * MTP_Q / (msm * 1e-3),
+            "unique_bytes": mbytes, "achieved_GBps": mbytes / (msm * 1e-3) / 1e9,
+        }
     if ms4 is not None:
         line["csa_decode_1m_b4"] = {
             "what": "index_topk + csa_attend for 4 sequences at 1,048,576 tokens (262,144 FP4 "

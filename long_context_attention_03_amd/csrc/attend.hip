@@ -847,8 +847,12 @@ AttendPlan attend_plan(int B, int Q, int H, int D, int64_t max_rows) {
 constexpr int kXStreams = 1;
 static AttendPlan attend_x_plan(int B, int Q, int H, int64_t max_rows) {
   const int hb = (H + 63) / 64;
-  AttendPlan pl = make_plan((int64_t)B * Q * hb, (max_rows + kXTile - 1) / kXTile,
-                            kXStreams == 1 ? 512 : 256, 2 * kXStreams);
+  const int64_t base = (int64_t)B * Q * hb;
+  // each split writes a 64-head partial as large as 7 rows of input: with 16 or more queries
+  // in flight, longer splits (fewer partials) win; with fewer, short splits keep the GPU busy
+  const int min_tiles = (base >= 16 ? 4 : 2) * kXStreams;
+  AttendPlan pl = make_plan(base, (max_rows + kXTile - 1) / kXTile, kXStreams == 1 ? 512 : 256,
+                            min_tiles);
   pl.head_groups = hb;
   return pl;
 }

@@ -207,3 +207,34 @@ def test_hca_prefill_chunk_full_size_sampled_queries():
     _check_sampled(out, lse, lambda i: O.hca_attend(
         qb[:, i:i + 1], cache, O.FMT_ROW_E4M3_BF16, 128, win[:, i:i + PF_W], PF_W,
         np.array([PF_POS0 + i], np.int64), sink, PF_D ** -0.5), "hca prefill")
+
+
+def test_multi_query_decode_1m_five_drafts():
+    """5 query tokens per sequence at the end of a 1M context: CSA over 262,144 entries with each
+    query's own 1,024 ids, and HCA over 8,192 entries; each query has its own causal window."""
+    from long_context_attention_03_amd import synth
+    B, Q, W = 2, 5, PF_W
+    d = synth.Draws(61)
+    rng = np.random.default_rng(62)
+    win, _ = O.encode_rows(d.normal((B, W - 1 + Q, PF_D)).numpy(), O.FMT_ROW_E4M3_BF16)
+    q = bf16_bits(d.normal((B, Q, PF_H, PF_D), dtype=torch.bfloat16))
+    sink = d.normal((PF_H,)).numpy()
+    for name, N, m in (("csa", 262144, 4), ("hca", 8192, 128)):
+        cache, _ = O.encode_rows(d.normal((B, N, PF_D)).numpy(), O.FMT_ROW_E4M3_BF16)
+        pos = np.full(B, N * m - Q, np.int64)
+        say(f"[{name}_attend] decode Q=5 at 1M: B={B} N={N}")
+        if name == "csa":
+            nv = (pos[:, None] + np.arange(Q)[None] + 1) // m
+            idx = rng.integers(0, nv[..., None], size=(B, Q, 1024)).astype(np.int32)
+            out, lse = L.csa_attend(dev(q), dev(cache), dev(idx), dev(win), W, dev(pos), dev(sink),
+                                    PF_D ** -0.5)
+            ro, rl = O.csa_attend(q, cache, O.FMT_ROW_E4M3_BF16, idx, win, W, pos, sink,
+                                  PF_D ** -0.5)
+        else:
+            out, lse = L.hca_attend(dev(q), dev(cache), m, dev(win), W, dev(pos), dev(sink),
+                                    PF_D ** -0.5)
+            ro, rl = O.hca_attend(q, cache, O.FMT_ROW_E4M3_BF16, m, win, W, pos, sink,
+                                  PF_D ** -0.5)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), ro, f"{name} Q=5 out")
+        assert_close(lse.cpu().numpy(), rl, f"{name} Q=5 lse")

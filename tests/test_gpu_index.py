@@ -161,3 +161,13 @@ def test_prefill_chunk_full_size_sampled_queries():
         assert np.array_equal(gi[:, i:i + 1], ri), f"query {i}: index mismatch"
         assert np.array_equal(gs[:, i:i + 1], rs.astype(np.float32)), f"query {i}: score mismatch"
     say(f"  {len(sample)} sampled queries bit-exact")
+
+
+def test_multi_query_decode_1m_five_drafts():
+    """Speculative verification: 5 query tokens per sequence at the end of a 1M context
+    (positions L-5 .. L-1), 262,144 FP4 keys, top-1024 each; every query on the oracle."""
+    rng = np.random.default_rng(60)
+    B, Q, N, m, k = 2, 5, 262144, 4, 1024
+    kc, ks, qc, qs = _fp4_inputs(rng, B, Q, N, 4)
+    pos = np.full(B, N * m - Q, np.int64)
+    _compare("decode Q=5 at 1M", kc, ks, qc, qs, pos, m, k)
