@@ -68,6 +68,8 @@ def lib():
             "oc_encode_rows": (I, [P, I64, I, I, P, P]),
             "oc_decode_rows": (I, [P, P, I64, I, I, P]),
             "oc_kv_compress": (I, [P, I, I64, I, I64, I, I, P, P, P, I, I64, P, P, P]),
+            "oc_kv_compress_span": (I, [P, I, I64, I, I64, I, I, I, I64, P, P, P, I, I64, P, P,
+                                        P]),
             "oc_index_topk": (I, [P, P, I, I, P, P, I64, I64, P, I, I, I, I, P, P, P]),
             "oc_index_scores": (I, [P, P, I, I, P, P, I64, P, P]),
             "oc_csa_attend": (I, [P, I, I, I, P, I, I64, I64, P, I, P, I64, I, P, P, D, I, I, P, P]),
@@ -175,19 +177,25 @@ def decode_rows(rows, D: int, fmt: int, scales=None):
 
 
 # ------------------------------------------------------------------------------------ method
-def kv_compress(raw, raw_dtype: int, m: int, w, beta, out_fmt: int):
-    """raw [B, T, D] (float32, or uint16 bf16 bits) -> dict(rows, scales, pre, pi)."""
+def kv_compress(raw, raw_dtype: int, m: int, w, beta, out_fmt: int, span: int | None = None,
+                skip: int = 0):
+    """raw [B, T, D] (float32, or uint16 bf16 bits) -> dict(rows, scales, pre, pi).
+
+    span (default m) tokens per entry at stride m; the first `skip` groups are context only.
+    pi is [B, T/m - skip, span] (0 for tokens before the buffer)."""
     raw = _c(raw, np.float32 if raw_dtype == DT_F32 else np.uint16)
     B, T, D = raw.shape
-    G = T // m
+    span = m if span is None else span
+    G = T // m - skip
     w = _c(w, np.float32)
     beta = _c(beta, np.float32)
     rows = np.zeros((B, G, row_bytes(out_fmt, D)), np.uint8)
     scales = np.zeros((B, G, D // 32), np.uint8) if out_fmt == FMT_FP4_E8M0 else None
     pre = np.zeros((B, G, D), np.float64)
-    pi = np.zeros((B, G, m), np.float64)
-    _check(lib().oc_kv_compress(_p(raw), raw_dtype, T, B, T, D, m, _p(w), _p(beta), _p(rows),
-                                out_fmt, G, _p(scales), _p(pre), _p(pi)), "kv_compress")
+    pi = np.zeros((B, G, span), np.float64)
+    _check(lib().oc_kv_compress_span(_p(raw), raw_dtype, T, B, T, D, m, span, skip, _p(w),
+                                     _p(beta), _p(rows), out_fmt, G, _p(scales), _p(pre),
+                                     _p(pi)), "kv_compress")
     return dict(rows=rows, scales=scales, pre=pre, pi=pi)
 
 

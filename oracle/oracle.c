@@ -24,6 +24,8 @@
  *
  * Readings where the pages are silent (each one is listed with its reason in the design notes):
  *   R1 groups are the non-overlapping runs of m consecutive tokens [EXPL].
+ *   R1b with a span of s > m tokens per entry at stride m [BSWEN], entry g pools the s tokens
+ *       ending with the last token of group g (see oc_kv_compress_span).
  *   R2 the gate is one scalar logit per token: z_t = w.x_t + beta[t - g*m].
  *   R7 indexer heads are combined by a plain sum of per-head dot products.
  *   R8 top-k order is (score descending, index ascending); missing slots are -1.
@@ -273,49 +275,69 @@ static double load_elem(const void* base, int dtype, int64_t i) {
 /* pre_out (nullable): fp64 c_g before encoding, [B][T/m][D].                                  */
 /* pi_out  (nullable): fp64 group weights, [B][T/m][m].                                        */
 /* ------------------------------------------------------------------------------------------ */
-int oc_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B, int64_t T, int D,
-                   int m, const float* w, const float* beta, unsigned char* out_rows, int out_fmt,
-                   int64_t out_seq_stride, unsigned char* out_scales, double* pre_out,
-                   double* pi_out) {
-    if (!raw || !w || !beta || !out_rows || B <= 0 || T < 0 || D <= 0 || m <= 0 || T % m)
+/* Entries of `span` tokens at stride m: [BSWEN] "Component 2: Multi-Level KV Compression" lists
+ * a level that compresses 8 tokens into one entry with a stride of 4. Reading R1b: entry g pools
+ * the span tokens that end with the last token of group g, [m(g+1) - span, m(g+1)); tokens before
+ * the start of the buffer do not exist and are left out of the softmax; the positional bias is
+ * indexed by the token's place in the span, 0 .. span-1. span = m is the non-overlapping case.
+ * The first `skip` groups only provide context: their entries are neither computed nor written,
+ * and entry g (g >= skip) goes to output row g - skip. */
+int oc_kv_compress_span(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B, int64_t T,
+                        int D, int m, int span, int64_t skip, const float* w, const float* beta,
+                        unsigned char* out_rows, int out_fmt, int64_t out_seq_stride,
+                        unsigned char* out_scales, double* pre_out, double* pi_out) {
+    if (!raw || !w || !beta || !out_rows || B <= 0 || T < 0 || D <= 0 || m <= 0 || T % m ||
+        span < m || skip < 0 || skip > T / m)
         return OC_EINVAL;
     if (out_fmt == OC_FMT_FP4_E8M0 && (D % 32 || !out_scales)) return OC_EINVAL;
     if (out_fmt == OC_FMT_ROW_E4M3_BF16 && D < 64) return OC_EINVAL;
-    int64_t G = T / m, rb = oc_row_bytes(out_fmt, D);
+    int64_t G = T / m - skip, rb = oc_row_bytes(out_fmt, D);
 #pragma omp parallel for collapse(2) schedule(static)
     for (int b = 0; b < B; b++) {
-        for (int64_t g = 0; g < G; g++) {
-            double* x = (double*)malloc(sizeof(double) * (size_t)m * D);
-            double* z = (double*)malloc(sizeof(double) * (size_t)m);
+        for (int64_t go = 0; go < G; go++) {
+            int64_t g = go + skip, first = m * (g + 1) - span; /* token of span position 0 */
+            double* x = (double*)malloc(sizeof(double) * (size_t)span * D);
+            double* z = (double*)malloc(sizeof(double) * (size_t)span);
             double* c = (double*)malloc(sizeof(double) * (size_t)D);
-            for (int t = 0; t < m; t++)
-                for (int d = 0; d < D; d++)
-                    x[(int64_t)t * D + d] =
-                        load_elem(raw, raw_dtype, ((int64_t)b * raw_seq_stride + g * m + t) * D + d);
             double zmax = -INFINITY;
-            for (int t = 0; t < m; t++) {
+            for (int j = 0; j < span; j++) {
+                z[j] = -INFINITY; /* a token before the buffer: weight 0 */
+                if (first + j < 0) continue;
                 double s = 0.0;
-                for (int d = 0; d < D; d++) s += (double)w[d] * x[(int64_t)t * D + d];
-                z[t] = s + (double)beta[t];
-                if (z[t] > zmax) zmax = z[t];
+                for (int d = 0; d < D; d++) {
+                    x[(int64_t)j * D + d] =
+                        load_elem(raw, raw_dtype, ((int64_t)b * raw_seq_stride + first + j) * D + d);
+                    s += (double)w[d] * x[(int64_t)j * D + d];
+                }
+                z[j] = s + (double)beta[j];
+                if (z[j] > zmax) zmax = z[j];
             }
             double den = 0.0;
-            for (int t = 0; t < m; t++) { z[t] = exp(z[t] - zmax); den += z[t]; }
-            for (int t = 0; t < m; t++) z[t] /= den; /* z now holds pi */
+            for (int j = 0; j < span; j++) { z[j] = exp(z[j] - zmax); den += z[j]; }
+            for (int j = 0; j < span; j++) z[j] /= den; /* z now holds pi */
             for (int d = 0; d < D; d++) {
                 double s = 0.0;
-                for (int t = 0; t < m; t++) s += z[t] * x[(int64_t)t * D + d];
+                for (int j = 0; j < span; j++)
+                    if (first + j >= 0) s += z[j] * x[(int64_t)j * D + d];
                 c[d] = s;
             }
-            int64_t orow = (int64_t)b * out_seq_stride + g;
+            int64_t orow = (int64_t)b * out_seq_stride + go;
             encode_row(c, out_fmt, D, out_rows + orow * rb,
                        out_fmt == OC_FMT_FP4_E8M0 ? out_scales + orow * (D / 32) : NULL);
-            if (pre_out) memcpy(pre_out + ((int64_t)b * G + g) * D, c, sizeof(double) * D);
-            if (pi_out) memcpy(pi_out + ((int64_t)b * G + g) * m, z, sizeof(double) * m);
+            if (pre_out) memcpy(pre_out + ((int64_t)b * G + go) * D, c, sizeof(double) * D);
+            if (pi_out) memcpy(pi_out + ((int64_t)b * G + go) * span, z, sizeof(double) * span);
             free(x); free(z); free(c);
         }
     }
     return OC_OK;
+}
+
+int oc_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B, int64_t T, int D,
+                   int m, const float* w, const float* beta, unsigned char* out_rows, int out_fmt,
+                   int64_t out_seq_stride, unsigned char* out_scales, double* pre_out,
+                   double* pi_out) {
+    return oc_kv_compress_span(raw, raw_dtype, raw_seq_stride, B, T, D, m, m, 0, w, beta, out_rows,
+                               out_fmt, out_seq_stride, out_scales, pre_out, pi_out);
 }
 
 /* ------------------------------------------------------------------------------------------ */

@@ -114,6 +114,52 @@ def _fp4(x):
     return O.encode_rows(np.asarray(x, np.float64), O.FMT_FP4_E8M0)
 
 
+# ---- entries of `span` tokens at stride m (8 tokens per entry, stride 4) -----------------------
+def _windows(T, m, span, skip=0):
+    """Token indices of each entry: the span tokens ending with the group's last token."""
+    return [np.arange(max(0, m * (g + 1) - span), m * (g + 1)) for g in range(skip, T // m)]
+
+
+@pytest.mark.parametrize("span,skip", [(8, 0), (8, 1), (12, 2)])
+def test_span_zero_gate_is_mean_of_the_window(span, skip):
+    """w = 0, beta = 0: every entry is the plain mean of the tokens in its window (the first
+    windows clipped at the start of the buffer)."""
+    m, T, D = 4, 40, 16
+    x = _rand((2, T, D), 51)
+    r = O.kv_compress(x, F32, m, np.zeros(D, np.float32), np.zeros(span, np.float32),
+                      O.FMT_ROW_F32, span=span, skip=skip)
+    want = np.stack([np.stack([x[b, ix].astype(np.float64).mean(0) for ix in _windows(T, m, span, skip)])
+                     for b in range(2)])
+    np.testing.assert_allclose(r["pre"], want, rtol=1e-12, atol=1e-12)
+
+
+def test_span_bias_only_gate_is_softmax_of_biases_by_window_position():
+    """w = 0: the weights are softmax(beta) over the window's positions 0..span-1 (only the
+    positions holding a token take part); entry 0's window starts before the buffer, so its
+    tokens 0..3 sit at positions 4..7 and take beta[4..7]."""
+    m, span, T, D = 4, 8, 24, 8
+    x = _rand((1, T, D), 52)
+    beta = _rand((span,), 53)
+    r = O.kv_compress(x, F32, m, np.zeros(D, np.float32), beta, O.FMT_ROW_F32, span=span)
+    for g, ix in enumerate(_windows(T, m, span)):
+        posn = ix - (m * (g + 1) - span)  # position of each token in its window
+        pi = scipy.special.softmax(beta[posn].astype(np.float64))
+        np.testing.assert_allclose(r["pi"][0, g, posn], pi, rtol=1e-12, atol=1e-15)
+        assert np.all(r["pi"][0, g, np.setdiff1d(np.arange(span), posn)] == 0.0)
+        np.testing.assert_allclose(r["pre"][0, g], pi @ x[0, ix].astype(np.float64), rtol=1e-12,
+                                   atol=1e-12)
+
+
+def test_span_skip_is_context_only():
+    """Entries after `skip` context groups equal the same entries of a call without skip."""
+    m, span, T, D = 4, 8, 32, 16
+    x = _rand((2, T, D), 54)
+    w, beta = _rand((D,), 55, 0.3), _rand((span,), 56)
+    full = O.kv_compress(x, F32, m, w, beta, O.FMT_ROW_F32, span=span)
+    part = O.kv_compress(x[:, 8:], F32, m, w, beta, O.FMT_ROW_F32, span=span, skip=1)
+    np.testing.assert_array_equal(part["pre"], full["pre"][:, 3:])
+
+
 def test_index_scores_vs_decoded_float_matmul():
     """Exact integer scores == fp64 matmul of the decoded FP4 values (exact: dyadic, few bits)."""
     rng = np.random.default_rng(20)
