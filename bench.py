@@ -522,6 +522,26 @@ def prefill_measure(steps: int, warmup: int):
     ops = {"index_hist": (2.0 * 512 * n_vis, PF_PEAK_FP4, "fp4"),
            "csa_attend": (4.0 * H * D * PF_Q * (K + W), PF_PEAK_BF16, "bf16"),
            "hca_attend": (4.0 * H * D * hca_rows, PF_PEAK_BF16, "bf16")}
+    # overlapping entries (8 tokens each at stride 4) for the chunk: the 4 tokens before it are
+    # context; E4M3+bf16 rows and FP4 indexer keys, timed on events around the two calls
+    xs = torch.cat([ps.x[:, :4], ps.x], dim=1)
+    xis = torch.cat([ps.xi[:, :4], ps.xi], dim=1)
+    b8 = torch.zeros(8, device="cuda")
+    rows8 = torch.empty((1, PF_Q // 4, ROW), dtype=torch.uint8, device="cuda")
+    k8 = torch.empty((1, PF_Q // 4, DI // 2), dtype=torch.uint8, device="cuda")
+    s8 = torch.empty((1, PF_Q // 4, DI // 32), dtype=torch.uint8, device="cuda")
+    span_ms = []
+    for _ in range(max(2, steps)):
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        L.kv_compress(xs, 4, ps.w_csa, b8, L.FMT_ROW_E4M3_BF16, out_rows=rows8, span=8, skip=1)
+        L.kv_compress(xis, 4, ps.w_idx, b8, L.FMT_FP4_E8M0, out_rows=k8, out_scales=s8, span=8,
+                      skip=1)
+        e.record()
+        torch.cuda.synchronize()
+        span_ms.append(a.elapsed_time(e))
+    span_bytes = (PF_Q + 4) * (D * 2 + DI * 4) + (PF_Q // 4) * (ROW + DI // 2 + DI // 32)
+    t_span = statistics.median(span_ms[1:]) * 1e-3
     kernels = {}
     for k, (fl, peak, dt) in ops.items():
         t = kt[k] * 1e-3
@@ -540,6 +560,12 @@ def prefill_measure(steps: int, warmup: int):
                      "peak": kernels[dom]["peak_TFLOPs"], "unit": "TFLOP/s",
                      "frac": kernels[dom]["frac"]},
         "kernels": kernels,
+        "compress_span8": {
+            "what": "the chunk's overlapping entries: 8 tokens each at stride 4 (1024 E4M3+bf16 "
+                    "rows and 1024 FP4 indexer keys, the 4 preceding tokens as context)",
+            "us": t_span * 1e6, "algorithmic_bytes": span_bytes,
+            "achieved_GBps": span_bytes / t_span / 1e9,
+        },
     }
 
 

@@ -94,6 +94,27 @@ int csah_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int
                      int64_t out_seq_stride, uint8_t* out_scales, void* stream);
 
 /*
+ * csah_kv_compress_span -- the same pooling with entries of `span` tokens at stride m.
+ *   [BSWEN] "Component 2: Multi-Level KV Compression": one level compresses 8 tokens into one
+ *   entry with a stride of 4 (span = 8, m = 4). Entry g pools the span tokens that end with the
+ *   last token of group g, tokens [m(g+1) - span, m(g+1)) of raw:
+ *     z_t = w . x_t + beta[t - (m(g+1) - span)],  pi = softmax over the entry's tokens,
+ *     c_g = sum_t pi_t x_t,  encoded as in csah_kv_compress.
+ *   Tokens before the start of raw are left out of the softmax (the start of a sequence). The
+ *   first `skip` groups are context only: entry g >= skip is written to output row g - skip, so a
+ *   caller appending entries passes the span - m tokens before the new groups and skip =
+ *   (span - m) / m. span = m, skip = 0 is exactly csah_kv_compress.
+ * beta      fp32 positional biases [span], indexed by the token's place in its span.
+ * out_rows  [B][out_seq_stride] rows, out_seq_stride >= T/m - skip; T/m - skip entries written.
+ * Other arguments, layouts and statuses as csah_kv_compress; also CSAH_ERR_INVALID_ARGUMENT if
+ * span < m or skip > T/m, CSAH_ERR_UNSUPPORTED if span > 65536.
+ */
+int csah_kv_compress_span(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B,
+                          int64_t T, int D, int m, int span, int64_t skip, const float* w,
+                          const float* beta, void* out_rows, int out_fmt, int64_t out_seq_stride,
+                          uint8_t* out_scales, void* stream);
+
+/*
  * csah_index_topk -- the lightning indexer: score every visible compressed entry against the
  * query's FP4 indexer heads and keep the top k.
  *   [EXPL]: low-rank indexer queries are scored against compressed indexer keys and each query

@@ -25,6 +25,7 @@ DT_F32, DT_BF16 = 0, 1
 FMT_ROW_F32, FMT_ROW_E4M3_BF16, FMT_FP4_E8M0 = 0, 1, 2
 
 EXPORTS = ("csah_abi_version", "csah_status_string", "csah_row_bytes", "csah_kv_compress",
+           "csah_kv_compress_span",
            "csah_index_topk_workspace", "csah_index_topk", "csah_attend_workspace",
            "csah_csa_attend", "csah_hca_attend", "csah_profile_next_call")
 
@@ -52,6 +53,8 @@ def lib():
             "csah_status_string": (ctypes.c_char_p, [I]),
             "csah_row_bytes": (I64, [I, I]),
             "csah_kv_compress": (I, [P, I, I64, I, I64, I, I, P, P, P, I, I64, P, P]),
+            "csah_kv_compress_span": (I, [P, I, I64, I, I64, I, I, I, I64, P, P, P, I, I64, P,
+                                          P]),
             "csah_index_topk_workspace": (SZ, [I, I, I64, I, I, I]),
             "csah_index_topk": (I, [P, P, I, I, P, P, I64, I64, P, I, I, I, I, P, P, P, SZ, P]),
             "csah_attend_workspace": (SZ, [I, I, I, I, I64]),
@@ -120,23 +123,34 @@ def _workspace(nbytes: int, device, ws=None):
 
 
 # ----------------------------------------------------------------------------- kv_compress
-def kv_compress(raw, m: int, w, beta, out_fmt: int, out_rows=None, out_scales=None, stream=None):
+def kv_compress(raw, m: int, w, beta, out_fmt: int, out_rows=None, out_scales=None, stream=None,
+                span: int | None = None, skip: int = 0):
     """Pool every m tokens of raw [B, T, D] into one encoded entry.
 
-    Returns (rows [B, T/m, row_bytes], scales [B, T/m, D/32] or None). When ``out_rows`` is
-    given it may be a slice of a larger cache (its sequence stride is taken from dim 0).
+    With ``span`` (> m) each entry pools the span tokens ending with its group's last token
+    (beta has span values) and the first ``skip`` groups are context only.
+    Returns (rows [B, T/m - skip, row_bytes], scales [B, T/m - skip, D/32] or None). When
+    ``out_rows`` is given it may be a slice of a larger cache (its sequence stride is taken from
+    dim 0).
     """
     B, T, D = raw.shape
-    G = T // m
+    G = T // m - skip
     if out_rows is None:
         out_rows = torch.empty((B, G, row_bytes(out_fmt, D)), dtype=torch.uint8, device=raw.device)
         if out_fmt == FMT_FP4_E8M0:
             out_scales = torch.empty((B, G, D // 32), dtype=torch.uint8, device=raw.device)
     out_stride = out_rows.stride(0) // out_rows.stride(1)
-    st = lib().csah_kv_compress(_ptr(raw), _dt(raw), raw.stride(0) // raw.stride(1), B, T, D, m,
-                                _ptr(w), _ptr(beta), _ptr(out_rows), out_fmt, out_stride,
-                                _ptr(out_scales), _stream(stream))
-    _check("csah_kv_compress", st)
+    if span is None and skip == 0:
+        st = lib().csah_kv_compress(_ptr(raw), _dt(raw), raw.stride(0) // raw.stride(1), B, T, D,
+                                    m, _ptr(w), _ptr(beta), _ptr(out_rows), out_fmt, out_stride,
+                                    _ptr(out_scales), _stream(stream))
+        _check("csah_kv_compress", st)
+    else:
+        st = lib().csah_kv_compress_span(_ptr(raw), _dt(raw), raw.stride(0) // raw.stride(1), B,
+                                         T, D, m, m if span is None else span, skip, _ptr(w),
+                                         _ptr(beta), _ptr(out_rows), out_fmt, out_stride,
+                                         _ptr(out_scales), _stream(stream))
+        _check("csah_kv_compress_span", st)
     return out_rows, out_scales
 
 

@@ -74,28 +74,47 @@ int csah_profile_next_call(void* begin_event, void* end_event) {
   return CSAH_OK;
 }
 
-int csah_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B, int64_t T,
-                     int D, int m, const float* w, const float* beta, void* out_rows, int out_fmt,
-                     int64_t out_seq_stride, uint8_t* out_scales, void* stream) {
-  const ProfileHook prof = take_profile();
+static int kv_compress_impl(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B,
+                            int64_t T, int D, int m, int span, int64_t skip, const float* w,
+                            const float* beta, void* out_rows, int out_fmt, int64_t out_seq_stride,
+                            uint8_t* out_scales, void* stream, ProfileHook prof) {
   if (!raw || !w || !beta || !out_rows || B < 0 || T < 0 || D <= 0 || m <= 0)
     return CSAH_ERR_INVALID_ARGUMENT;
   if (raw_dtype != CSAH_DT_F32 && raw_dtype != CSAH_DT_BF16) return CSAH_ERR_INVALID_ARGUMENT;
   if (out_fmt != CSAH_FMT_ROW_F32 && out_fmt != CSAH_FMT_ROW_E4M3_BF16 &&
       out_fmt != CSAH_FMT_FP4_E8M0)
     return CSAH_ERR_INVALID_ARGUMENT;
-  if (T % m != 0 || raw_seq_stride < T || out_seq_stride < T / m) return CSAH_ERR_INVALID_ARGUMENT;
+  if (T % m != 0 || span < m || skip < 0 || skip > T / m || raw_seq_stride < T ||
+      out_seq_stride < T / m - skip)
+    return CSAH_ERR_INVALID_ARGUMENT;
   if ((out_fmt == CSAH_FMT_FP4_E8M0) != (out_scales != nullptr)) return CSAH_ERR_INVALID_ARGUMENT;
   if (!aligned(raw, 16) || !aligned(out_rows, 16)) return CSAH_ERR_INVALID_ARGUMENT;
   if (D != 64 && D != 128 && D != 256 && D != 512 && D != 1024) return CSAH_ERR_UNSUPPORTED;
   if (out_fmt == CSAH_FMT_ROW_E4M3_BF16 && D != 512) return CSAH_ERR_UNSUPPORTED;
-  if (m > 65536) return CSAH_ERR_UNSUPPORTED;
+  if (span > 65536) return CSAH_ERR_UNSUPPORTED;
   int st = check_device();
   if (st) return st;
-  KvCompressArgs a{raw,     raw_dtype, raw_seq_stride, B,      T / m,          D,          m,
-                   w,       beta,      out_rows,       out_fmt, out_seq_stride, out_scales, stream,
-                   prof};
+  KvCompressArgs a{raw,  raw_dtype, raw_seq_stride, B,        T / m - skip,   D,          m,
+                   span, skip,      w,              beta,     out_rows,       out_fmt,
+                   out_seq_stride,  out_scales,     stream,   prof};
   return launch_status(launch_kv_compress(a));
+}
+
+int csah_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B, int64_t T,
+                     int D, int m, const float* w, const float* beta, void* out_rows, int out_fmt,
+                     int64_t out_seq_stride, uint8_t* out_scales, void* stream) {
+  const ProfileHook prof = take_profile();
+  return kv_compress_impl(raw, raw_dtype, raw_seq_stride, B, T, D, m, m, 0, w, beta, out_rows,
+                          out_fmt, out_seq_stride, out_scales, stream, prof);
+}
+
+int csah_kv_compress_span(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B,
+                          int64_t T, int D, int m, int span, int64_t skip, const float* w,
+                          const float* beta, void* out_rows, int out_fmt, int64_t out_seq_stride,
+                          uint8_t* out_scales, void* stream) {
+  const ProfileHook prof = take_profile();
+  return kv_compress_impl(raw, raw_dtype, raw_seq_stride, B, T, D, m, span, skip, w, beta,
+                          out_rows, out_fmt, out_seq_stride, out_scales, stream, prof);
 }
 
 size_t csah_index_topk_workspace(int B, int Q, int64_t N, int k, int HI, int dI) {

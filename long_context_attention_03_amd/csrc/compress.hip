@@ -58,35 +58,41 @@ __device__ __forceinline__ void load_token(const void* raw, int64_t row, int lan
 
 constexpr int kTokBatch = 8;  // tokens whose loads and gate reductions are in flight together
 
-// WAVES = 1: one wavefront per group, 4 groups per workgroup (small m).
-// WAVES = 4: one workgroup per group; wavefront w pools tokens [w*ceil(m/4), ...) and the four
+// Entry g (after `skip` context-only groups) pools the `span` tokens that end with the last token
+// of group g, [m(g+1) - span, m(g+1)); tokens before the start of the buffer are left out and the
+// positional bias is indexed by the token's place in the span. span = m: one entry per group.
+// WAVES = 1: one wavefront per entry, 4 entries per workgroup (short spans).
+// WAVES = 4: one workgroup per entry; wavefront w pools a quarter of the span and the four
 //            online-softmax states (max, sum, weighted sum) are merged in LDS.
 template <int DPL, bool RAW_BF16, int OUT_FMT, int WAVES>
 __global__ __launch_bounds__(256) void kv_compress_kernel(
-    const void* __restrict__ raw, int64_t raw_seq_stride, int B, int64_t G, int m,
-    const float* __restrict__ w, const float* __restrict__ beta, uint8_t* __restrict__ out_rows,
-    int64_t out_seq_stride, uint8_t* __restrict__ out_scales) {
+    const void* __restrict__ raw, int64_t raw_seq_stride, int B, int64_t G, int m, int span,
+    int64_t skip, const float* __restrict__ w, const float* __restrict__ beta,
+    uint8_t* __restrict__ out_rows, int64_t out_seq_stride, uint8_t* __restrict__ out_scales) {
   constexpr int D = DPL * 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t gid = WAVES == 1 ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
   if (gid >= (int64_t)B * G) return;  // uniform per wavefront (WAVES = 1) or workgroup (4)
-  const int64_t b = gid / G, g = gid - b * G;
+  const int64_t b = gid / G, g = gid - b * G;  // g: output row; group g + skip
 
   float wv[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; e++) wv[e] = w[lane * DPL + e];
 
-  int t_begin = 0, t_end = m;
+  // span positions [jmin, span) hold tokens (the ones before the buffer start are left out)
+  const int64_t first = (int64_t)m * (g + skip + 1) - span;  // token at span position 0
+  const int jmin = first < 0 ? (int)(-first) : 0;
+  int t_begin = jmin, t_end = span;
   if constexpr (WAVES > 1) {
-    const int per = (m + WAVES - 1) / WAVES;
-    t_begin = wave * per;
-    t_end = t_begin + per < m ? t_begin + per : m;
+    const int per = (span - jmin + WAVES - 1) / WAVES;
+    t_begin = jmin + wave * per;
+    t_end = t_begin + per < span ? t_begin + per : span;
   }
   float acc[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; e++) acc[e] = 0.0f;
   float M = -INFINITY, L = 0.0f;
-  const int64_t row0 = b * raw_seq_stride + g * m;
+  const int64_t row0 = b * raw_seq_stride + first;  // + j >= 0 for every position read
   for (int t0 = t_begin; t0 < t_end; t0 += kTokBatch) {
     float x[kTokBatch][DPL];
 #pragma unroll
@@ -221,20 +227,20 @@ static hipError_t launch_waves(const KvCompressArgs& a) {
   switch (a.out_fmt) {
     case CSAH_FMT_ROW_F32:
       a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_F32, WAVES>, grid, block, s,
-          a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.w, a.beta, (uint8_t*)a.out_rows,
+          a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.span, a.skip, a.w, a.beta, (uint8_t*)a.out_rows,
           a.out_seq_stride, a.out_scales);
       break;
     case CSAH_FMT_ROW_E4M3_BF16:
       if constexpr (DPL == 8)
         a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_E4M3_BF16, WAVES>, grid, block, s,
-            a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.w, a.beta, (uint8_t*)a.out_rows,
+            a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.span, a.skip, a.w, a.beta, (uint8_t*)a.out_rows,
             a.out_seq_stride, a.out_scales);
       else
         return hipErrorInvalidValue;
       break;
     default:
       a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_FP4_E8M0, WAVES>, grid, block, s,
-          a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.w, a.beta, (uint8_t*)a.out_rows,
+          a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.span, a.skip, a.w, a.beta, (uint8_t*)a.out_rows,
           a.out_seq_stride, a.out_scales);
   }
   return hipGetLastError();
@@ -242,8 +248,9 @@ static hipError_t launch_waves(const KvCompressArgs& a) {
 
 template <int DPL, bool RAW_BF16>
 static hipError_t launch_dpl(const KvCompressArgs& a) {
-  // a whole workgroup per group once the group is long enough to keep 4 wavefronts busy
-  return a.m > 2 * kTokBatch ? launch_waves<DPL, RAW_BF16, 4>(a) : launch_waves<DPL, RAW_BF16, 1>(a);
+  // a whole workgroup per entry once the span is long enough to keep 4 wavefronts busy
+  return a.span > 2 * kTokBatch ? launch_waves<DPL, RAW_BF16, 4>(a)
+                                : launch_waves<DPL, RAW_BF16, 1>(a);
 }
 
 template <bool RAW_BF16>

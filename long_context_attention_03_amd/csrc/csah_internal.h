@@ -29,8 +29,10 @@ struct KvCompressArgs {
   int raw_dtype;
   int64_t raw_seq_stride;
   int B;
-  int64_t G;  // groups per sequence = T / m
+  int64_t G;     // entries written per sequence = T / m - skip
   int D, m;
+  int span;      // tokens per entry (m: one entry per group)
+  int64_t skip;  // leading groups that are context only
   const float* w;
   const float* beta;
   void* out_rows;

@@ -95,17 +95,24 @@ class DecodeCase:
         return [dev(getattr(self, n)) for n in names]
 
 
-def pooling_tolerance(x, m: int, pre):
+def pooling_tolerance(x, m: int, pre, span: int | None = None, skip: int = 0):
     """Bound on |fp32 pooled value - fp64 pooled value| for kv_compress, per element.
 
-    The GPU pools in one fp32 pass (online softmax over the m tokens), so its error is a few
-    units of binary32 round-off per step times the group's magnitudes, plus a relative 1e-5 for
-    the softmax weights: (m + 16) * 2^-23 * max_t |x_t,d| + 1e-5 |c_d|.
+    The GPU pools in one fp32 pass (online softmax over the entry's n tokens: n = m, or the span
+    when entries cover `span` tokens at stride m), so its error is a few units of binary32
+    round-off per step times the tokens' magnitudes, plus a relative 1e-5 for the softmax
+    weights: (n + 16) * 2^-23 * max_t |x_t,d| + 1e-5 |c_d|.
     """
     x = np.abs(np.asarray(x, np.float64))
     B, T, D = x.shape
-    gmax = x.reshape(B, T // m, m, D).max(axis=2)
-    return (m + 16) * 2.0 ** -23 * gmax + 1e-5 * np.abs(pre)
+    if span is None:
+        gmax = x.reshape(B, T // m, m, D).max(axis=2)[:, skip:]
+        n = m
+    else:
+        gmax = np.stack([x[:, max(0, m * (g + 1) - span):m * (g + 1)].max(axis=1)
+                         for g in range(skip, T // m)], axis=1)
+        n = span
+    return (n + 16) * 2.0 ** -23 * gmax + 1e-5 * np.abs(pre)
 
 
 def midpoint_ok(v: float, a: float, b: float, tol: float) -> bool:

@@ -78,6 +78,21 @@ def test_kv_compress_rejects_bad_arguments():
     assert f(FAKE, 0, 8, 1, 8, 96, 4, FAKE, FAKE, FAKE, 0, 2, None, None) == L.UNSUPPORTED
 
 
+def test_kv_compress_span_rejects_bad_arguments():
+    f = L.lib().csah_kv_compress_span
+    # span shorter than the stride
+    assert f(FAKE, 0, 8, 1, 8, 512, 4, 2, 0, FAKE, FAKE, FAKE, 1, 2, None, None) \
+        == L.INVALID_ARGUMENT
+    # more context groups than groups
+    assert f(FAKE, 0, 8, 1, 8, 512, 4, 8, 3, FAKE, FAKE, FAKE, 1, 2, None, None) \
+        == L.INVALID_ARGUMENT
+    # output stride below the entries written (T/m - skip = 2)
+    assert f(FAKE, 0, 12, 1, 12, 512, 4, 8, 1, FAKE, FAKE, FAKE, 1, 1, None, None) \
+        == L.INVALID_ARGUMENT
+    assert f(FAKE, 0, 8, 1, 8, 512, 4, 70000, 0, FAKE, FAKE, FAKE, 1, 2, None, None) \
+        == L.UNSUPPORTED
+
+
 def test_index_topk_rejects_bad_arguments():
     f = L.lib().csah_index_topk
     ok = dict(HI=4, dI=128, ks=100, N=100, m=4, B=1, Q=1, k=8)

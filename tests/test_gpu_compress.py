@@ -128,3 +128,60 @@ def test_append_into_cache_with_stride():
     ref = O.kv_compress(bf16_bits(x), O.DT_BF16, 4, w, beta, O.FMT_ROW_E4M3_BF16)
     check_rows_e4m3_bf16(c[:, 40:56], ref["rows"], ref["pre"],
                          pooling_tolerance(x.float().numpy(), 4, ref["pre"]))
+
+
+# ---- entries of `span` tokens at stride m (8 tokens per entry, stride 4) ------------------------
+def _gpu_span(raw_t, m, w, b, fmt, span, skip=0, out_rows=None, out_scales=None):
+    rows, sc = L.kv_compress(raw_t.cuda(), m, dev(w), dev(b), fmt, out_rows=out_rows,
+                             out_scales=out_scales, span=span, skip=skip)
+    torch.cuda.synchronize()
+    return rows.cpu().numpy(), None if sc is None else sc.cpu().numpy()
+
+
+@pytest.mark.parametrize("span,m,skip", [(8, 4, 0), (8, 4, 1), (256, 128, 1), (12, 4, 2)])
+def test_span_pooled_values_fp32_rows(span, m, skip):
+    """Pooled values of span-token entries (the first clipped at the buffer start when skip is
+    0); span 256 at m 128 takes the four-wavefront path."""
+    x, w, d = _raw((2, 4096 + skip * m, 512), 70 + span, True)
+    beta = d.normal((span,), 0.1).numpy()
+    say(f"[kv_compress_span] fp32 rows span={span} m={m} skip={skip}")
+    rows, _ = _gpu_span(x, m, w, beta, O.FMT_ROW_F32, span, skip)
+    ref = O.kv_compress(bf16_bits(x), O.DT_BF16, m, w, beta, O.FMT_ROW_F32, span=span, skip=skip)
+    got = rows.view(np.float32).reshape(ref["pre"].shape)
+    assert_close(got, ref["pre"], f"span={span} pooled", atol=1e-4, rtol=1e-4)
+
+
+def test_span_encoded_rows_and_indexer_keys_prefill_chunk():
+    """The prefill chunk with overlapping entries: the 4 tokens before the chunk are context
+    (skip = 1), 1024 entries of 8 tokens each as E4M3+bf16 rows and as FP4 indexer keys."""
+    wl = synth.WORKLOADS["prefill"]
+    raw = synth.raw_tokens(wl, 4096 + 4, seed=71)
+    x, xi = raw["x"], raw["xi"]
+    d = synth.Draws(72)
+    beta8, beta8i = d.normal((8,), 0.1).numpy(), d.normal((8,), 0.1).numpy()
+    say("[kv_compress_span] prefill chunk span=8 skip=1 -> E4M3+bf16 rows, FP4 keys")
+    rows, _ = _gpu_span(x, 4, raw["w_csa"].numpy(), beta8, O.FMT_ROW_E4M3_BF16, 8, 1)
+    ref = O.kv_compress(bf16_bits(x), O.DT_BF16, 4, raw["w_csa"].numpy(), beta8,
+                        O.FMT_ROW_E4M3_BF16, span=8, skip=1)
+    assert rows.shape[1] == 1024
+    tol = pooling_tolerance(x.float().numpy(), 4, ref["pre"], span=8, skip=1)
+    check_rows_e4m3_bf16(rows, ref["rows"], ref["pre"], tol)
+    krows, ksc = _gpu_span(xi, 4, raw["w_idx"].numpy(), beta8i, O.FMT_FP4_E8M0, 8, 1)
+    kref = O.kv_compress(xi.numpy(), O.DT_F32, 4, raw["w_idx"].numpy(), beta8i, O.FMT_FP4_E8M0,
+                         span=8, skip=1)
+    check_rows_fp4(krows, ksc, kref["rows"], kref["scales"], kref["pre"],
+                   pooling_tolerance(xi.numpy(), 4, kref["pre"], span=8, skip=1))
+
+
+def test_span_decode_append_into_cache():
+    """Decode: the newest entry from the last 8 tokens (skip 1), written at a cache's append row;
+    the other rows are untouched."""
+    x, w, d = _raw((3, 8, 512), 73, True)
+    beta = d.normal((8,), 0.1).numpy()
+    cache = torch.full((3, 10, 576), 0xAB, dtype=torch.uint8, device="cuda")
+    _gpu_span(x, 4, w, beta, O.FMT_ROW_E4M3_BF16, 8, 1, out_rows=cache[:, 7:8])
+    ref = O.kv_compress(bf16_bits(x), O.DT_BF16, 4, w, beta, O.FMT_ROW_E4M3_BF16, span=8, skip=1)
+    c = cache.cpu().numpy()
+    tol = pooling_tolerance(x.float().numpy(), 4, ref["pre"], span=8, skip=1)
+    check_rows_e4m3_bf16(c[:, 7:8], ref["rows"], ref["pre"], tol)
+    assert (c[:, :7] == 0xAB).all() and (c[:, 8:] == 0xAB).all()
