@@ -192,8 +192,75 @@ int csah_hca_attend(const void* q, int q_dtype, int H, int D, const void* cache,
                     void* stream);
 
 /*
- * csah_profile_next_call -- profiling aid (not part of the method). The next csah_kv_compress,
- * csah_index_topk, csah_csa_attend or csah_hca_attend call made by the SAME host thread launches
+ * Paged caches. A serving system keeps each compressed cache in a pool of fixed-size pages and
+ * gives every sequence a block table of page numbers, so that sequences grow without moving rows
+ * and memory is handed out page by page. The pages speak of the cache only in general terms
+ * (Baidu "Technical Analysis of DeepSeek V4 ...", "Engineering Optimizations": the KV cache is
+ * moved in pages; Baidu "Technical Breakdown of DeepSeek V4 Preview ...", "Hardware-Software
+ * Co-Optimization": the cache is cut into fixed-size chunks; [BSWEN] "What's Still Missing":
+ * inference frameworks must be adapted to the compressed caches). The layout below is this
+ * library's own:
+ *   pool         rows of the cache's format, page p holding rows [p*P, (p+1)*P) (P = page_size
+ *                entries, a power of two in [1, 2^20]). FP4 keys have a second pool of scale
+ *                bytes indexed by the same rows.
+ *   block_table  int32 [B][table_stride], 4-byte aligned: entry e of sequence b is row
+ *                block_table[b*table_stride + e/P] * P + e%P of the pool.
+ * Entries keep their LOGICAL numbers everywhere else: top-k indices, visibility, N. Each call
+ * computes exactly what its contiguous counterpart computes on the cache gathered back to logical
+ * order; only the addressing differs, so the results are bit-identical to that call's.
+ * Errors, beyond those of the contiguous call: CSAH_ERR_INVALID_ARGUMENT for a null or misaligned
+ * block_table, a page_size that is not a power of two, or a table_stride * P below the entries the
+ * call addresses; CSAH_ERR_UNSUPPORTED for page_size > 2^20. Table entries are device data: each
+ * one a call reads (the pages of entries [0, N), or of the entries written) must name a page that
+ * lies inside the pool; the library cannot check this.
+ */
+
+/*
+ * csah_kv_compress_paged -- csah_kv_compress_span writing its entries into a paged cache: output
+ * entry g of sequence b (g in [0, T/m - skip)) goes to logical entry first_entry + g of that
+ * sequence. out_pool / out_scale_pool as out_rows / out_scales. first_entry >= 0 and
+ * (first_entry + T/m - skip) <= table_stride * page_size.
+ */
+int csah_kv_compress_paged(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B,
+                           int64_t T, int D, int m, int span, int64_t skip, const float* w,
+                           const float* beta, void* out_pool, int out_fmt,
+                           uint8_t* out_scale_pool, const int32_t* block_table,
+                           int64_t table_stride, int page_size, int64_t first_entry,
+                           void* stream);
+
+/*
+ * csah_index_topk_paged -- csah_index_topk over FP4 keys held in a paged pool (codes and scales
+ * pools share the block table). table_stride * page_size >= N. Indices are logical entry numbers.
+ * Workspace as csah_index_topk_workspace(B, Q, N, k, HI, dI).
+ */
+int csah_index_topk_paged(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int dI,
+                          const uint8_t* k_pool_codes, const uint8_t* k_pool_scales,
+                          const int32_t* block_table, int64_t table_stride, int page_size,
+                          int64_t N, const int64_t* pos, int m, int B, int Q, int k,
+                          int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
+ * csah_csa_attend_paged / csah_hca_attend_paged -- csah_csa_attend / csah_hca_attend with the
+ * compressed cache in a paged pool; idx holds logical entry numbers. The window buffer stays a
+ * per-sequence array as in the contiguous calls. table_stride * page_size >= N.
+ */
+int csah_csa_attend_paged(const void* q, int q_dtype, int H, int D, const void* cache_pool,
+                          int fmt, const int32_t* block_table, int64_t table_stride,
+                          int page_size, int64_t N, const int32_t* idx, int k, const void* win,
+                          int64_t win_seq_stride, int w, const int64_t* pos, const float* sink,
+                          float scale, int B, int Q, float* out, float* lse, void* ws,
+                          size_t ws_bytes, void* stream);
+int csah_hca_attend_paged(const void* q, int q_dtype, int H, int D, const void* cache_pool,
+                          int fmt, const int32_t* block_table, int64_t table_stride,
+                          int page_size, int64_t N, int m, const void* win,
+                          int64_t win_seq_stride, int w, const int64_t* pos, const float* sink,
+                          float scale, int B, int Q, float* out, float* lse, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * csah_profile_next_call -- profiling aid (not part of the method). The next compression,
+ * indexer or attention call (any of the calls above) made by the SAME host thread launches
  * its dominant kernel (the compressor; the indexer scan; the attention kernel) with `begin` and
  * `end` attached to that dispatch, so that hipEventElapsedTime(begin, end) is the kernel's own
  * duration. Both are hipEvent_t passed as void*, created by the caller with timing enabled; NULL

@@ -9,6 +9,11 @@ Tensor conventions (device tensors, C-contiguous unless a stride argument says o
   q          [B, Q, H, D] bfloat16 or float32
   idx        [B, Q, k] int32;  pos [B] int64 (position of query 0)
   window     [B, w-1+Q, row_bytes] uint8
+Paged caches (the *_paged calls):
+  pool       [pages, page_size, row_bytes] uint8 (any shape whose rows are contiguous and whose
+             last dim is the row width); scale pool [pages, page_size, D/32] uint8 (FP4 only)
+  block_table [B, >= ceil(N / page_size)] int32: entry e of sequence b is row
+             block_table[b, e // page_size] * page_size + e % page_size of the pool
 """
 from __future__ import annotations
 
@@ -27,7 +32,9 @@ FMT_ROW_F32, FMT_ROW_E4M3_BF16, FMT_FP4_E8M0 = 0, 1, 2
 EXPORTS = ("csah_abi_version", "csah_status_string", "csah_row_bytes", "csah_kv_compress",
            "csah_kv_compress_span",
            "csah_index_topk_workspace", "csah_index_topk", "csah_attend_workspace",
-           "csah_csa_attend", "csah_hca_attend", "csah_profile_next_call")
+           "csah_csa_attend", "csah_hca_attend", "csah_kv_compress_paged",
+           "csah_index_topk_paged", "csah_csa_attend_paged", "csah_hca_attend_paged",
+           "csah_profile_next_call")
 
 _lib = None
 
@@ -62,6 +69,14 @@ def lib():
                                     P, P, P, SZ, P]),
             "csah_hca_attend": (I, [P, I, I, I, P, I, I64, I64, I, P, I64, I, P, P, F, I, I, P,
                                     P, P, SZ, P]),
+            "csah_kv_compress_paged": (I, [P, I, I64, I, I64, I, I, I, I64, P, P, P, I, P, P,
+                                           I64, I, I64, P]),
+            "csah_index_topk_paged": (I, [P, P, I, I, P, P, P, I64, I, I64, P, I, I, I, I, P, P,
+                                          P, SZ, P]),
+            "csah_csa_attend_paged": (I, [P, I, I, I, P, I, P, I64, I, I64, P, I, P, I64, I, P,
+                                          P, F, I, I, P, P, P, SZ, P]),
+            "csah_hca_attend_paged": (I, [P, I, I, I, P, I, P, I64, I, I64, I, P, I64, I, P, P,
+                                          F, I, I, P, P, P, SZ, P]),
             "csah_profile_next_call": (I, [P, P]),
         }
         for name, (res, args) in sig.items():
@@ -234,4 +249,90 @@ def hca_attend(q, cache, m: int, window, w: int, pos, sink, scale: float, N: int
                                float(scale), B, Q, _ptr(out), _ptr(lse), _ptr(ws), need,
                                _stream(stream))
     _check("csah_hca_attend", st)
+    return out, lse
+
+
+# ----------------------------------------------------------------------------- paged caches
+def _table(block_table):
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise TypeError("block_table must be an int32 [B, pages] tensor with contiguous rows")
+    return _ptr(block_table), block_table.stride(0)
+
+
+def kv_compress_paged(raw, m: int, w, beta, out_fmt: int, pool, block_table, page_size: int,
+                      first_entry: int = 0, scale_pool=None, span: int | None = None,
+                      skip: int = 0, stream=None):
+    """kv_compress writing entry g of sequence b to its logical entry first_entry + g of a paged
+    cache (pool / scale_pool rows through block_table). Returns (pool, scale_pool)."""
+    B, T, D = raw.shape
+    tp, ts = _table(block_table)
+    st = lib().csah_kv_compress_paged(_ptr(raw), _dt(raw), raw.stride(0) // raw.stride(1), B, T,
+                                      D, m, m if span is None else span, skip, _ptr(w),
+                                      _ptr(beta), _ptr(pool), out_fmt, _ptr(scale_pool), tp, ts,
+                                      page_size, first_entry, _stream(stream))
+    _check("csah_kv_compress_paged", st)
+    return pool, scale_pool
+
+
+def index_topk_paged(q_codes, q_scales, k_pool_codes, k_pool_scales, block_table,
+                     page_size: int, N: int, pos, m: int, k: int, want_scores: bool = True,
+                     ws=None, idx_out=None, score_out=None, stream=None):
+    """index_topk over FP4 keys in a paged pool -> (logical idx [B, Q, k], scores or None)."""
+    B, Q, HI, half = q_codes.shape
+    dI = 2 * half
+    dev = q_codes.device
+    tp, ts = _table(block_table)
+    if idx_out is None:
+        idx_out = torch.empty((B, Q, k), dtype=torch.int32, device=dev)
+    if want_scores and score_out is None:
+        score_out = torch.empty((B, Q, k), dtype=torch.float32, device=dev)
+    need = index_topk_workspace(B, Q, N, k, HI, dI)
+    ws = _workspace(need, dev, ws)
+    st = lib().csah_index_topk_paged(_ptr(q_codes), _ptr(q_scales), HI, dI, _ptr(k_pool_codes),
+                                     _ptr(k_pool_scales), tp, ts, page_size, N, _ptr(pos), m, B,
+                                     Q, k, _ptr(idx_out), _ptr(score_out), _ptr(ws), need,
+                                     _stream(stream))
+    _check("csah_index_topk_paged", st)
+    return idx_out, score_out
+
+
+def csa_attend_paged(q, cache_pool, block_table, page_size: int, N: int, idx, window, w: int,
+                     pos, sink, scale: float, ws=None, out=None, lse=None, stream=None):
+    """csa_attend with the compressed cache in a paged pool (idx: logical entries)."""
+    B, Q, H, D = q.shape
+    fmt = _fmt_of(cache_pool, D)
+    k = idx.shape[-1]
+    dev = q.device
+    tp, ts = _table(block_table)
+    out = torch.empty((B, Q, H, D), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev) if lse is None else lse
+    need = attend_workspace(B, Q, H, D, k + w)
+    ws = _workspace(need, dev, ws)
+    wstride = window.stride(0) // window.stride(1) if w > 0 else 0
+    st = lib().csah_csa_attend_paged(_ptr(q), _dt(q), H, D, _ptr(cache_pool), fmt, tp, ts,
+                                     page_size, N, _ptr(idx), k,
+                                     _ptr(window) if w > 0 else None, wstride, w, _ptr(pos),
+                                     _ptr(sink), float(scale), B, Q, _ptr(out), _ptr(lse),
+                                     _ptr(ws), need, _stream(stream))
+    _check("csah_csa_attend_paged", st)
+    return out, lse
+
+
+def hca_attend_paged(q, cache_pool, block_table, page_size: int, N: int, m: int, window, w: int,
+                     pos, sink, scale: float, ws=None, out=None, lse=None, stream=None):
+    """hca_attend with the compressed cache in a paged pool."""
+    B, Q, H, D = q.shape
+    fmt = _fmt_of(cache_pool, D)
+    dev = q.device
+    tp, ts = _table(block_table)
+    out = torch.empty((B, Q, H, D), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev) if lse is None else lse
+    need = attend_workspace(B, Q, H, D, N + w)
+    ws = _workspace(need, dev, ws)
+    wstride = window.stride(0) // window.stride(1) if w > 0 else 0
+    st = lib().csah_hca_attend_paged(_ptr(q), _dt(q), H, D, _ptr(cache_pool), fmt, tp, ts,
+                                     page_size, N, m, _ptr(window) if w > 0 else None, wstride,
+                                     w, _ptr(pos), _ptr(sink), float(scale), B, Q, _ptr(out),
+                                     _ptr(lse), _ptr(ws), need, _stream(stream))
+    _check("csah_hca_attend_paged", st)
     return out, lse

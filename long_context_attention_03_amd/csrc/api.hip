@@ -41,6 +41,24 @@ ProfileHook take_profile() {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// A block-table layout: page_size is a power of two in [1, 2^20]; `capacity` receives the
+// entries each sequence's table row can address (table_stride pages).
+int paged_map(const int32_t* table, int64_t table_stride, int page_size, EntryMap& map,
+              int64_t& capacity) {
+  if (!table || !aligned(table, 4) || page_size <= 0 || (page_size & (page_size - 1)) != 0 ||
+      table_stride < 0)
+    return CSAH_ERR_INVALID_ARGUMENT;
+  if (page_size > (1 << 20)) return CSAH_ERR_UNSUPPORTED;
+  int shift = 0;
+  while ((1 << shift) < page_size) shift++;
+  if (table_stride > (INT64_MAX >> 21)) return CSAH_ERR_INVALID_ARGUMENT;
+  map = EntryMap{table, table_stride, shift};
+  capacity = table_stride << shift;
+  return CSAH_OK;
+}
+
+EntryMap contiguous_map(int64_t seq_stride) { return EntryMap{nullptr, seq_stride, 0}; }
+
 int row_bytes(int fmt, int D) {
   if (fmt == CSAH_FMT_ROW_F32) return 4 * D;
   if (fmt == CSAH_FMT_ROW_E4M3_BF16) return D >= 64 ? D + 64 : -1;
@@ -74,10 +92,12 @@ int csah_profile_next_call(void* begin_event, void* end_event) {
   return CSAH_OK;
 }
 
+// out_capacity: output entries each sequence can take from first_entry on.
 static int kv_compress_impl(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B,
                             int64_t T, int D, int m, int span, int64_t skip, const float* w,
-                            const float* beta, void* out_rows, int out_fmt, int64_t out_seq_stride,
-                            uint8_t* out_scales, void* stream, ProfileHook prof) {
+                            const float* beta, void* out_rows, int out_fmt, EntryMap out_map,
+                            int64_t first_entry, int64_t out_capacity, uint8_t* out_scales,
+                            void* stream, ProfileHook prof) {
   if (!raw || !w || !beta || !out_rows || B < 0 || T < 0 || D <= 0 || m <= 0)
     return CSAH_ERR_INVALID_ARGUMENT;
   if (raw_dtype != CSAH_DT_F32 && raw_dtype != CSAH_DT_BF16) return CSAH_ERR_INVALID_ARGUMENT;
@@ -85,7 +105,7 @@ static int kv_compress_impl(const void* raw, int raw_dtype, int64_t raw_seq_stri
       out_fmt != CSAH_FMT_FP4_E8M0)
     return CSAH_ERR_INVALID_ARGUMENT;
   if (T % m != 0 || span < m || skip < 0 || skip > T / m || raw_seq_stride < T ||
-      out_seq_stride < T / m - skip)
+      out_capacity < T / m - skip)
     return CSAH_ERR_INVALID_ARGUMENT;
   if ((out_fmt == CSAH_FMT_FP4_E8M0) != (out_scales != nullptr)) return CSAH_ERR_INVALID_ARGUMENT;
   if (!aligned(raw, 16) || !aligned(out_rows, 16)) return CSAH_ERR_INVALID_ARGUMENT;
@@ -94,9 +114,9 @@ static int kv_compress_impl(const void* raw, int raw_dtype, int64_t raw_seq_stri
   if (span > 65536) return CSAH_ERR_UNSUPPORTED;
   int st = check_device();
   if (st) return st;
-  KvCompressArgs a{raw,  raw_dtype, raw_seq_stride, B,        T / m - skip,   D,          m,
-                   span, skip,      w,              beta,     out_rows,       out_fmt,
-                   out_seq_stride,  out_scales,     stream,   prof};
+  KvCompressArgs a{raw,  raw_dtype, raw_seq_stride, B,       T / m - skip, D,          m,
+                   span, skip,      w,              beta,    out_rows,     out_fmt,    out_map,
+                   first_entry,     out_scales,     stream,  prof};
   return launch_status(launch_kv_compress(a));
 }
 
@@ -105,7 +125,8 @@ int csah_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int
                      int64_t out_seq_stride, uint8_t* out_scales, void* stream) {
   const ProfileHook prof = take_profile();
   return kv_compress_impl(raw, raw_dtype, raw_seq_stride, B, T, D, m, m, 0, w, beta, out_rows,
-                          out_fmt, out_seq_stride, out_scales, stream, prof);
+                          out_fmt, contiguous_map(out_seq_stride), 0, out_seq_stride, out_scales,
+                          stream, prof);
 }
 
 int csah_kv_compress_span(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B,
@@ -114,7 +135,25 @@ int csah_kv_compress_span(const void* raw, int raw_dtype, int64_t raw_seq_stride
                           uint8_t* out_scales, void* stream) {
   const ProfileHook prof = take_profile();
   return kv_compress_impl(raw, raw_dtype, raw_seq_stride, B, T, D, m, span, skip, w, beta,
-                          out_rows, out_fmt, out_seq_stride, out_scales, stream, prof);
+                          out_rows, out_fmt, contiguous_map(out_seq_stride), 0, out_seq_stride,
+                          out_scales, stream, prof);
+}
+
+int csah_kv_compress_paged(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B,
+                           int64_t T, int D, int m, int span, int64_t skip, const float* w,
+                           const float* beta, void* out_pool, int out_fmt,
+                           uint8_t* out_scale_pool, const int32_t* block_table,
+                           int64_t table_stride, int page_size, int64_t first_entry,
+                           void* stream) {
+  const ProfileHook prof = take_profile();
+  EntryMap map;
+  int64_t cap;
+  const int st = paged_map(block_table, table_stride, page_size, map, cap);
+  if (st) return st;
+  if (first_entry < 0 || first_entry > cap) return CSAH_ERR_INVALID_ARGUMENT;
+  return kv_compress_impl(raw, raw_dtype, raw_seq_stride, B, T, D, m, span, skip, w, beta,
+                          out_pool, out_fmt, map, first_entry, cap - first_entry, out_scale_pool,
+                          stream, prof);
 }
 
 size_t csah_index_topk_workspace(int B, int Q, int64_t N, int k, int HI, int dI) {
@@ -122,14 +161,15 @@ size_t csah_index_topk_workspace(int B, int Q, int64_t N, int k, int HI, int dI)
   return index_workspace_bytes(B, Q, N, k, HI, dI);
 }
 
-int csah_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int dI,
-                    const uint8_t* k_codes, const uint8_t* k_scales, int64_t k_seq_stride,
-                    int64_t N, const int64_t* pos, int m, int B, int Q, int k, int32_t* idx_out,
-                    float* score_out, void* ws, size_t ws_bytes, void* stream) {
-  const ProfileHook prof = take_profile();
+// capacity: entries each sequence's keys can hold (the row stride, or what the table covers).
+static int index_impl(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int dI,
+                      const uint8_t* k_codes, const uint8_t* k_scales, EntryMap kmap,
+                      int64_t capacity, int64_t N, const int64_t* pos, int m, int B, int Q, int k,
+                      int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes, void* stream,
+                      ProfileHook prof) {
   if (!q_codes || !q_scales || !k_codes || !k_scales || !pos || !idx_out || !ws)
     return CSAH_ERR_INVALID_ARGUMENT;
-  if (HI <= 0 || dI <= 0 || m <= 0 || B <= 0 || Q <= 0 || k <= 0 || N < 0 || k_seq_stride < N)
+  if (HI <= 0 || dI <= 0 || m <= 0 || B <= 0 || Q <= 0 || k <= 0 || N < 0 || capacity < N)
     return CSAH_ERR_INVALID_ARGUMENT;
   if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(ws, 256))
     return CSAH_ERR_INVALID_ARGUMENT;
@@ -139,9 +179,34 @@ int csah_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int
   int st = check_device();
   if (st) return st;
   if (ws_bytes < index_workspace_bytes(B, Q, N, k, HI, dI)) return CSAH_ERR_WORKSPACE_TOO_SMALL;
-  IndexArgs a{q_codes, q_scales, HI, dI, k_codes, k_scales, k_seq_stride, N, pos, m, B, Q, k,
+  IndexArgs a{q_codes, q_scales, HI, dI, k_codes, k_scales, kmap, N, pos, m, B, Q, k,
               idx_out, score_out, ws, ws_bytes, stream, prof};
   return launch_status(launch_index_topk(a));
+}
+
+int csah_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int dI,
+                    const uint8_t* k_codes, const uint8_t* k_scales, int64_t k_seq_stride,
+                    int64_t N, const int64_t* pos, int m, int B, int Q, int k, int32_t* idx_out,
+                    float* score_out, void* ws, size_t ws_bytes, void* stream) {
+  const ProfileHook prof = take_profile();
+  return index_impl(q_codes, q_scales, HI, dI, k_codes, k_scales, contiguous_map(k_seq_stride),
+                    k_seq_stride, N, pos, m, B, Q, k, idx_out, score_out, ws, ws_bytes, stream,
+                    prof);
+}
+
+int csah_index_topk_paged(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int dI,
+                          const uint8_t* k_pool_codes, const uint8_t* k_pool_scales,
+                          const int32_t* block_table, int64_t table_stride, int page_size,
+                          int64_t N, const int64_t* pos, int m, int B, int Q, int k,
+                          int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes,
+                          void* stream) {
+  const ProfileHook prof = take_profile();
+  EntryMap map;
+  int64_t cap;
+  const int st = paged_map(block_table, table_stride, page_size, map, cap);
+  if (st) return st;
+  return index_impl(q_codes, q_scales, HI, dI, k_pool_codes, k_pool_scales, map, cap, N, pos, m,
+                    B, Q, k, idx_out, score_out, ws, ws_bytes, stream, prof);
 }
 
 size_t csah_attend_workspace(int B, int Q, int H, int D, int64_t max_rows) {
@@ -150,7 +215,7 @@ size_t csah_attend_workspace(int B, int Q, int H, int D, int64_t max_rows) {
 }
 
 static int attend_common(const void* q, int q_dtype, int H, int D, const void* cache, int fmt,
-                         int64_t cache_seq_stride, int64_t N, const int32_t* idx, int k, int m,
+                         EntryMap cmap, int64_t capacity, int64_t N, const int32_t* idx, int k, int m,
                          const void* win, int64_t win_seq_stride, int w, const int64_t* pos,
                          const float* sink, float scale, int B, int Q, float* out, float* lse,
                          void* ws, size_t ws_bytes, void* stream, ProfileHook prof) {
@@ -158,7 +223,7 @@ static int attend_common(const void* q, int q_dtype, int H, int D, const void* c
     return CSAH_ERR_INVALID_ARGUMENT;
   if (q_dtype != CSAH_DT_F32 && q_dtype != CSAH_DT_BF16) return CSAH_ERR_INVALID_ARGUMENT;
   if (fmt != CSAH_FMT_ROW_F32 && fmt != CSAH_FMT_ROW_E4M3_BF16) return CSAH_ERR_INVALID_ARGUMENT;
-  if (cache_seq_stride < N) return CSAH_ERR_INVALID_ARGUMENT;
+  if (capacity < N) return CSAH_ERR_INVALID_ARGUMENT;
   if (w > 0 && (!win || win_seq_stride < (int64_t)w - 1 + Q)) return CSAH_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(cache, 16) || (w > 0 && !aligned(win, 16)))
     return CSAH_ERR_INVALID_ARGUMENT;
@@ -172,7 +237,7 @@ static int attend_common(const void* q, int q_dtype, int H, int D, const void* c
   if (need > 0 && (!ws || !aligned(ws, 256))) return need > ws_bytes ? CSAH_ERR_WORKSPACE_TOO_SMALL
                                                                        : CSAH_ERR_INVALID_ARGUMENT;
   if (ws_bytes < need) return CSAH_ERR_WORKSPACE_TOO_SMALL;
-  AttendArgs a{q,   q_dtype, H,     D,     cache, fmt, cache_seq_stride, N,        idx,   k,
+  AttendArgs a{q,   q_dtype, H,     D,     cache, fmt, cmap,             N,        idx,   k,
                m,   win,     win_seq_stride, w, pos, sink, scale,   B,  Q, out, lse, ws, ws_bytes,
                stream, max_rows, prof};
   return launch_status(launch_attend(a));
@@ -185,7 +250,8 @@ int csah_csa_attend(const void* q, int q_dtype, int H, int D, const void* cache,
                     void* ws, size_t ws_bytes, void* stream) {
   const ProfileHook prof = take_profile();
   if (!idx || k < 0) return CSAH_ERR_INVALID_ARGUMENT;
-  return attend_common(q, q_dtype, H, D, cache, fmt, cache_seq_stride, N, idx, k, 1, win,
+  return attend_common(q, q_dtype, H, D, cache, fmt, contiguous_map(cache_seq_stride),
+                       cache_seq_stride, N, idx, k, 1, win,
                        win_seq_stride, w, pos, sink, scale, B, Q, out, lse, ws, ws_bytes, stream,
                        prof);
 }
@@ -197,7 +263,42 @@ int csah_hca_attend(const void* q, int q_dtype, int H, int D, const void* cache,
                     void* stream) {
   const ProfileHook prof = take_profile();
   if (m <= 0) return CSAH_ERR_INVALID_ARGUMENT;
-  return attend_common(q, q_dtype, H, D, cache, fmt, cache_seq_stride, N, nullptr, 0, m, win,
+  return attend_common(q, q_dtype, H, D, cache, fmt, contiguous_map(cache_seq_stride),
+                       cache_seq_stride, N, nullptr, 0, m, win,
+                       win_seq_stride, w, pos, sink, scale, B, Q, out, lse, ws, ws_bytes, stream,
+                       prof);
+}
+
+int csah_csa_attend_paged(const void* q, int q_dtype, int H, int D, const void* cache_pool,
+                          int fmt, const int32_t* block_table, int64_t table_stride,
+                          int page_size, int64_t N, const int32_t* idx, int k, const void* win,
+                          int64_t win_seq_stride, int w, const int64_t* pos, const float* sink,
+                          float scale, int B, int Q, float* out, float* lse, void* ws,
+                          size_t ws_bytes, void* stream) {
+  const ProfileHook prof = take_profile();
+  if (!idx || k < 0) return CSAH_ERR_INVALID_ARGUMENT;
+  EntryMap map;
+  int64_t cap;
+  const int st = paged_map(block_table, table_stride, page_size, map, cap);
+  if (st) return st;
+  return attend_common(q, q_dtype, H, D, cache_pool, fmt, map, cap, N, idx, k, 1, win,
+                       win_seq_stride, w, pos, sink, scale, B, Q, out, lse, ws, ws_bytes, stream,
+                       prof);
+}
+
+int csah_hca_attend_paged(const void* q, int q_dtype, int H, int D, const void* cache_pool,
+                          int fmt, const int32_t* block_table, int64_t table_stride,
+                          int page_size, int64_t N, int m, const void* win,
+                          int64_t win_seq_stride, int w, const int64_t* pos, const float* sink,
+                          float scale, int B, int Q, float* out, float* lse, void* ws,
+                          size_t ws_bytes, void* stream) {
+  const ProfileHook prof = take_profile();
+  if (m <= 0) return CSAH_ERR_INVALID_ARGUMENT;
+  EntryMap map;
+  int64_t cap;
+  const int st = paged_map(block_table, table_stride, page_size, map, cap);
+  if (st) return st;
+  return attend_common(q, q_dtype, H, D, cache_pool, fmt, map, cap, N, nullptr, 0, m, win,
                        win_seq_stride, w, pos, sink, scale, B, Q, out, lse, ws, ws_bytes, stream,
                        prof);
 }

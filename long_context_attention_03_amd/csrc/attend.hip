@@ -59,7 +59,8 @@ struct AttendK {
   const void* q;
   int H;
   const uint8_t* cache;
-  int64_t cstride, N;
+  EntryMap cmap;  // entry e of sequence b is row cmap.row(b, e) of `cache`
+  int64_t N;
   const int32_t* idx;
   int k, m;
   const uint8_t* win;
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttendK p) {
   const int64_t r1 = r0 + p.rows_per_split < R ? r0 + p.rows_per_split : R;
   const int64_t rc_end = Rc < r1 ? Rc : r1;  // compressed rows of this split end here
   // a readable row for masked slots (a tile with any valid row implies N > 0 or w > 0)
-  const uint8_t* dummy = p.N > 0 ? p.cache + (int64_t)b * p.cstride * C::RB
+  const uint8_t* dummy = p.N > 0 ? p.cache + p.cmap.row(b, 0) * C::RB
                                  : p.win + (int64_t)b * p.wstride * C::RB;
 
   // entry id of tile row (lane & 31), fetched one tile ahead of its use (CSA only)
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttendK p) {
       const int64_t ent = DENSE ? j : (int64_t)e;
       if (ent >= 0 && ent < p.N) {
         valid = true;
-        ptr = p.cache + ((int64_t)b * p.cstride + ent) * C::RB;
+        ptr = p.cache + p.cmap.row(b, ent) * C::RB;
       }
     } else if (j < r1) {
       const int64_t r = qi + (j - Rc);              // window buffer row
@@ -489,7 +490,7 @@ struct TileRawX {
   u32x4 r;     // bf16 dims 448 + 8(t%8) .. +8
 };
 
-template <bool DENSE, int NS>
+template <bool DENSE, int NS, bool PAGED>
 __global__ __launch_bounds__(256 * NS, 3 - NS) void attend_x_kernel(AttendK p) {
   constexpr int D = 512, NCH = 16, NT = 32, RB = 576;
   __shared__ __attribute__((aligned(16))) __bf16 ytile[NS][2][kXTileElems];  // [stream][buffer]
@@ -535,7 +536,7 @@ __global__ __launch_bounds__(256 * NS, 3 - NS) void attend_x_kernel(AttendK p) {
   const int64_t r0 = (int64_t)split * p.rows_per_split;
   const int64_t r1 = r0 + p.rows_per_split < R ? r0 + p.rows_per_split : R;
   const int64_t rc_end = Rc < r1 ? Rc : r1;
-  const uint8_t* dummy = p.N > 0 ? p.cache + (int64_t)b * p.cstride * RB
+  const uint8_t* dummy = p.N > 0 ? p.cache + (PAGED ? p.cmap.paged(b, 0) : p.cmap.flat(b, 0)) * RB
                                  : p.win + (int64_t)b * p.wstride * RB;
   const int ntiles = r1 > r0 ? (int)((r1 - r0 + kXTile - 1) / kXTile) : 0;
   const int iters = (ntiles + NS - 1) / NS;
@@ -556,11 +557,37 @@ __global__ __launch_bounds__(256 * NS, 3 - NS) void attend_x_kernel(AttendK p) {
       const int64_t ent = DENSE ? j : (int64_t)e;
       if (ent >= 0 && ent < p.N) {
         valid = true;
-        ptr = p.cache + ((int64_t)b * p.cstride + ent) * RB;
+        ptr = p.cache + p.cmap.flat(b, ent) * RB;
       }
     } else if (j < r1) {
       const int64_t r = qi + (j - Rc);   // window buffer row
       if (pos_b - (p.w - 1) + r >= 0) {  // its token position is >= 0
+        valid = true;
+        ptr = p.win + ((int64_t)b * p.wstride + r) * RB;
+      }
+    }
+    return ptr;
+  };
+  // Paged caches: a row's pool row comes from the block table, a load that depends on the
+  // entry id. Ids are fetched two tiles ahead and translated one tile ahead, so neither load
+  // is waited for while the current tile's rows are in flight.
+  auto pool_row = [&](int64_t j, int32_t e) -> int64_t {  // -1: not a valid compressed row
+    if (j >= rc_end) return -1;
+    const int64_t ent = DENSE ? j : (int64_t)e;
+    if (ent < 0 || ent >= p.N) return -1;
+    return p.cmap.paged(b, ent);
+  };
+  auto resolve_row = [&](int64_t j, int64_t prow, bool& valid) -> const uint8_t* {
+    valid = false;
+    const uint8_t* ptr = dummy;
+    if (j < rc_end) {
+      if (prow >= 0) {
+        valid = true;
+        ptr = p.cache + prow * RB;
+      }
+    } else if (j < r1) {
+      const int64_t r = qi + (j - Rc);
+      if (pos_b - (p.w - 1) + r >= 0) {
         valid = true;
         ptr = p.win + ((int64_t)b * p.wstride + r) * RB;
       }
@@ -582,12 +609,21 @@ __global__ __launch_bounds__(256 * NS, 3 - NS) void attend_x_kernel(AttendK p) {
 
   TileRawX raw;
   bool v_raw = false;
-  int32_t e_next = -1;
+  int32_t e_next = -1;   // contiguous: id of this thread's row in the next tile; paged: two ahead
+  int64_t prow_next = -1;  // paged: pool row of this thread's row in the next tile
   if (iters > 0) {
     const int64_t t0 = r0 + (int64_t)st * kXTile;
     const int32_t e0 = fetch_id(t0);
-    e_next = fetch_id(t0 + NS * kXTile);
-    load_rows(resolve(t0 + lrow, e0, v_raw), raw);
+    if constexpr (PAGED) {
+      const int32_t e1 = fetch_id(t0 + NS * kXTile);
+      e_next = fetch_id(t0 + 2 * NS * kXTile);
+      const int64_t prow0 = pool_row(t0 + lrow, e0);
+      prow_next = pool_row(t0 + NS * kXTile + lrow, e1);
+      load_rows(resolve_row(t0 + lrow, prow0, v_raw), raw);
+    } else {
+      e_next = fetch_id(t0 + NS * kXTile);
+      load_rows(resolve(t0 + lrow, e0, v_raw), raw);
+    }
   }
   for (int it = 0; it < iters; it++) {
     const int buf = it & 1;
@@ -635,9 +671,16 @@ __global__ __launch_bounds__(256 * NS, 3 - NS) void attend_x_kernel(AttendK p) {
     v_raw = false;
     if (it + 1 < iters) {
       const int64_t tn = r0 + (int64_t)(NS * (it + 1) + st) * kXTile;
-      const int32_t e_after = fetch_id(tn + NS * kXTile);
-      load_rows(resolve(tn + lrow, e_next, v_raw), raw);
-      e_next = e_after;
+      if constexpr (PAGED) {
+        const int32_t e_after = fetch_id(tn + 2 * NS * kXTile);
+        load_rows(resolve_row(tn + lrow, prow_next, v_raw), raw);
+        prow_next = pool_row(tn + NS * kXTile + lrow, e_next);
+        e_next = e_after;
+      } else {
+        const int32_t e_after = fetch_id(tn + NS * kXTile);
+        load_rows(resolve(tn + lrow, e_next, v_raw), raw);
+        e_next = e_after;
+      }
     }
     if (mask != 0u) {
       // online softmax (base 2); lane holds rows 4g+i (S0) and 16+4g+i (S1) of head n
@@ -887,7 +930,7 @@ hipError_t launch_attend(const AttendArgs& a) {
   k.q = a.q;
   k.H = a.H;
   k.cache = (const uint8_t*)a.cache;
-  k.cstride = a.cache_seq_stride;
+  k.cmap = a.cmap;
   k.N = a.N;
   k.idx = a.idx;
   k.k = a.k;
@@ -912,8 +955,14 @@ hipError_t launch_attend(const AttendArgs& a) {
   dim3 grid((unsigned)(((units + 7) / 8) * per_round));
   hipError_t e;
   if (shared_tiles) {
-    if (a.idx) a.prof.launch(attend_x_kernel<false, kXStreams>, grid, dim3(256 * kXStreams), s, k);
-    else a.prof.launch(attend_x_kernel<true, kXStreams>, grid, dim3(256 * kXStreams), s, k);
+    const dim3 blk(256 * kXStreams);
+    if (a.cmap.table) {
+      if (a.idx) a.prof.launch(attend_x_kernel<false, kXStreams, true>, grid, blk, s, k);
+      else a.prof.launch(attend_x_kernel<true, kXStreams, true>, grid, blk, s, k);
+    } else {
+      if (a.idx) a.prof.launch(attend_x_kernel<false, kXStreams, false>, grid, blk, s, k);
+      else a.prof.launch(attend_x_kernel<true, kXStreams, false>, grid, blk, s, k);
+    }
     e = hipGetLastError();
   } else if (a.fmt == CSAH_FMT_ROW_E4M3_BF16)
     e = launch_fmt<CSAH_FMT_ROW_E4M3_BF16, CSAH_DT_F32>(a, k, grid, s);

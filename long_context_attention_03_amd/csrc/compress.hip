@@ -68,7 +68,8 @@ template <int DPL, bool RAW_BF16, int OUT_FMT, int WAVES>
 __global__ __launch_bounds__(256) void kv_compress_kernel(
     const void* __restrict__ raw, int64_t raw_seq_stride, int B, int64_t G, int m, int span,
     int64_t skip, const float* __restrict__ w, const float* __restrict__ beta,
-    uint8_t* __restrict__ out_rows, int64_t out_seq_stride, uint8_t* __restrict__ out_scales) {
+    uint8_t* __restrict__ out_rows, EntryMap omap, int64_t first_entry,
+    uint8_t* __restrict__ out_scales) {
   constexpr int D = DPL * 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t gid = WAVES == 1 ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(256) void kv_compress_kernel(
 #pragma unroll
   for (int e = 0; e < DPL; e++) c[e] = acc[e] / L;
 
-  const int64_t orow = b * out_seq_stride + g;
+  const int64_t orow = omap.row((int)b, first_entry + g);
   if constexpr (OUT_FMT == CSAH_FMT_ROW_F32) {
     float* o = (float*)out_rows + orow * D + lane * DPL;
 #pragma unroll
@@ -228,20 +229,20 @@ static hipError_t launch_waves(const KvCompressArgs& a) {
     case CSAH_FMT_ROW_F32:
       a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_F32, WAVES>, grid, block, s,
           a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.span, a.skip, a.w, a.beta, (uint8_t*)a.out_rows,
-          a.out_seq_stride, a.out_scales);
+          a.out_map, a.first_entry, a.out_scales);
       break;
     case CSAH_FMT_ROW_E4M3_BF16:
       if constexpr (DPL == 8)
         a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_E4M3_BF16, WAVES>, grid, block, s,
             a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.span, a.skip, a.w, a.beta, (uint8_t*)a.out_rows,
-            a.out_seq_stride, a.out_scales);
+            a.out_map, a.first_entry, a.out_scales);
       else
         return hipErrorInvalidValue;
       break;
     default:
       a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_FP4_E8M0, WAVES>, grid, block, s,
           a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.span, a.skip, a.w, a.beta, (uint8_t*)a.out_rows,
-          a.out_seq_stride, a.out_scales);
+          a.out_map, a.first_entry, a.out_scales);
   }
   return hipGetLastError();
 }

@@ -10,6 +10,24 @@
 
 namespace csah {
 
+// Where entry e of sequence b of a cache lives, as a row number of the array the kernel gets.
+// Contiguous (table == NULL): row b * stride + e. Paged: row table[b * stride + (e >> shift)] *
+// 2^shift + (e mod 2^shift), i.e. sequence b's block-table row names the pool page that holds
+// its entries [2^shift * i, 2^shift * (i + 1)).
+struct EntryMap {
+  const int32_t* table;
+  int64_t stride;  // contiguous: rows per sequence; paged: table entries per sequence
+  int shift;       // paged: log2 of the page size in entries
+  __device__ __forceinline__ int64_t flat(int b, int64_t e) const { return (int64_t)b * stride + e; }
+  __device__ __forceinline__ int64_t paged(int b, int64_t e) const {
+    const int64_t page = table[(int64_t)b * stride + (e >> shift)];
+    return (page << shift) | (e & (((int64_t)1 << shift) - 1));
+  }
+  __device__ __forceinline__ int64_t row(int b, int64_t e) const {
+    return table ? paged(b, e) : flat(b, e);
+  }
+};
+
 // Events attached to the dispatch of a call's dominant kernel (both null: plain launch). The
 // runtime stamps them with that dispatch's own start and end, so they time the kernel alone.
 struct ProfileHook {
@@ -37,7 +55,8 @@ struct KvCompressArgs {
   const float* beta;
   void* out_rows;
   int out_fmt;
-  int64_t out_seq_stride;
+  EntryMap out_map;     // where output entry first_entry + g of sequence b goes
+  int64_t first_entry;  // logical index of the call's first output entry
   uint8_t* out_scales;
   void* stream;
   ProfileHook prof;
@@ -51,7 +70,8 @@ struct IndexArgs {
   int HI, dI;
   const uint8_t* k_codes;
   const uint8_t* k_scales;
-  int64_t k_seq_stride, N;
+  EntryMap kmap;
+  int64_t N;
   const int64_t* pos;
   int m, B, Q, k;
   int32_t* idx_out;
@@ -78,7 +98,8 @@ struct AttendArgs {
   int q_dtype, H, D;
   const void* cache;
   int fmt;
-  int64_t cache_seq_stride, N;
+  EntryMap cmap;
+  int64_t N;
   const int32_t* idx;  // NULL: dense (HCA) over g < floor((pos+i+1)/m)
   int k, m;
   const void* win;

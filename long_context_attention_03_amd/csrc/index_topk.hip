@@ -139,31 +139,55 @@ __device__ __forceinline__ float block_score(const u32x4 c, uint32_t e, const fl
   return s + 0.0f;  // fold -0 into +0: equal scores must get equal keys
 }
 
-template <int NB>
+// Paged keys: a workgroup first copies the block-table entries of the pages its keys span into
+// LDS, so each row's pool address costs an LDS read instead of a dependent global load.
+constexpr int kPageList = 1040;  // the host sizes key ranges to span at most 1026 pages
+
+// Page list of sequence b's entries [g0, g1) (g0 < g1) into LDS; every thread takes part.
+__device__ __forceinline__ void load_page_list(const EntryMap& km, int b, int64_t g0, int64_t g1,
+                                               int32_t* pages, int tid, int nthreads) {
+  const int64_t p0 = g0 >> km.shift;
+  const int np = (int)(((g1 - 1) >> km.shift) - p0 + 1);
+  const int32_t* t = km.table + (int64_t)b * km.stride + p0;
+  for (int j = tid; j < np; j += nthreads) pages[j] = t[j];
+}
+
+// Pool row of the entry at offset rr from the start of the first listed page.
+__device__ __forceinline__ uint64_t page_row(const int32_t* pages, uint32_t rr, int shift) {
+  return ((uint64_t)(uint32_t)pages[rr >> shift] << shift) | (rr & ((1u << shift) - 1u));
+}
+
+template <int NB, bool PAGED>
 __global__ __launch_bounds__(256) void index_scan_kernel(
-    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
-    int64_t k_seq_stride, int64_t N, const int64_t* __restrict__ pos, int m, int Q, int chunk,
-    IdxWs ws) {
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
+    int64_t N, const int64_t* __restrict__ pos, int m, int Q, int chunk, IdxWs ws) {
   constexpr int EPR = 256 / NB;  // entries per workgroup-wide group of lanes
   constexpr int U = CSAH_SCAN_U;  // groups whose loads are in flight together
   constexpr int STEP = EPR * U;
   const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
   const int tid = threadIdx.x, sub = tid % NB, ent = tid / NB;
   __shared__ uint32_t hist[kBins];
+  __shared__ int32_t pages[PAGED ? kPageList : 1];
   for (int j = tid; j < kBins; j += 256) hist[j] = 0u;
-  __syncthreads();
 
   const int64_t nv = visible_entries(pos, b, i, m, N);
   const int64_t g0 = (int64_t)blockIdx.x * chunk;
   const int64_t g1 = g0 + chunk < nv ? g0 + chunk : nv;
+  if constexpr (PAGED) {
+    if (g0 < nv) load_page_list(kmap, b, g0, g1, pages, tid, 256);
+  }
+  __syncthreads();
   if (g0 < nv) {
     float qv[32];
     const float* qt = ws.qt(slot) + 32 * sub;
 #pragma unroll
     for (int j = 0; j < 32; j++) qv[j] = qt[j];
-    // per-lane bases; offsets within a chunk fit in 32 bits
-    const uint8_t* kc = k_codes + ((int64_t)b * k_seq_stride + g0) * (16 * NB) + 16 * sub;
-    const uint8_t* ks = k_scales + ((int64_t)b * k_seq_stride + g0) * NB + sub;
+    // contiguous: per-lane bases, offsets within a chunk fit in 32 bits; paged: bases are the
+    // pool and each row goes through the page list (offsets counted from the first page start)
+    const int64_t base_row = PAGED ? 0 : kmap.row(b, g0);
+    const uint8_t* kc = k_codes + base_row * (16 * NB) + 16 * sub;
+    const uint8_t* ks = k_scales + base_row * NB + sub;
+    const uint32_t off0 = PAGED ? (uint32_t)(g0 & (((int64_t)1 << kmap.shift) - 1)) : 0u;
     float* sc = ws.scores(slot) + g0;
     const int n = (int)(g1 - g0);
     auto load = [&](int r0, u32x4* c, uint32_t* e, bool clamp) {
@@ -171,8 +195,14 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
       for (int u = 0; u < U; u++) {
         int r = r0 + u * EPR + ent;
         if (clamp) r = r < n ? r : n - 1;
-        c[u] = __builtin_nontemporal_load((const u32x4*)(kc + (uint32_t)r * (16u * NB)));
-        e[u] = ks[(uint32_t)r * NB];
+        if constexpr (PAGED) {
+          const uint64_t row = page_row(pages, off0 + (uint32_t)r, kmap.shift);
+          c[u] = __builtin_nontemporal_load((const u32x4*)(kc + row * (16u * NB)));
+          e[u] = ks[row * NB];
+        } else {
+          c[u] = __builtin_nontemporal_load((const u32x4*)(kc + (uint32_t)r * (16u * NB)));
+          e[u] = ks[(uint32_t)r * NB];
+        }
       }
     };
     auto score = [&](int r0, const u32x4* c, const uint32_t* e) {
@@ -584,14 +614,17 @@ __device__ __forceinline__ void mfma_unit(const MfmaSplit& sp, int& b, int& qb, 
   b = rest / sp.nqb;
 }
 
-template <int HP, typename F>
+// Paged keys: `pages` (LDS, kPageList entries) receives the range's block-table entries; the
+// walk's early return is uniform over the workgroup, so the barrier after filling it is safe.
+template <int HP, bool PAGED, typename F>
 __device__ __forceinline__ void mfma_walk(const uint8_t* __restrict__ q_codes,
                                           const uint8_t* __restrict__ q_scales, int HI,
                                           const uint8_t* __restrict__ k_codes,
                                           const uint8_t* __restrict__ k_scales,
-                                          int64_t k_seq_stride, int64_t N,
+                                          const EntryMap& kmap, int64_t N,
                                           const int64_t* __restrict__ pos, int m, int Q,
-                                          const MfmaSplit& sp, int b, int qb, int kr, F visit) {
+                                          const MfmaSplit& sp, int b, int qb, int kr,
+                                          int32_t* pages, F visit) {
   constexpr int U = 4;
   const int q0 = qb * 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, blk = lane >> 4;
@@ -603,10 +636,16 @@ __device__ __forceinline__ void mfma_walk(const uint8_t* __restrict__ q_codes,
   const int64_t g0 = (int64_t)kr * sp.keys_per_range;
   const int64_t g1 = g0 + sp.keys_per_range < nvmax ? g0 + sp.keys_per_range : nvmax;
   if (g0 >= g1) return;
+  if constexpr (PAGED) {
+    load_page_list(kmap, b, g0, g1, pages, threadIdx.x, 256);
+    __syncthreads();
+  }
   QueryOps<HP> qo;
   load_query_ops<HP>(q_codes, q_scales, HI, (int64_t)b * Q + qi, qv, blk, qo);
-  const uint8_t* kc = k_codes + ((int64_t)b * k_seq_stride + g0) * 64 + 16 * blk;
-  const uint8_t* ks = k_scales + ((int64_t)b * k_seq_stride + g0) * 4 + blk;
+  const int64_t base_row = PAGED ? 0 : kmap.row(b, g0);
+  const uint8_t* kc = k_codes + base_row * 64 + 16 * blk;
+  const uint8_t* ks = k_scales + base_row * 4 + blk;
+  const uint32_t off0 = PAGED ? (uint32_t)(g0 & (((int64_t)1 << kmap.shift) - 1)) : 0u;
   const int nk = (int)(g1 - g0);
   const int ntile = (nk + 15) / 16;
   const int my_tiles = ntile > wave ? (ntile - wave + 3) / 4 : 0;  // tiles wave, wave+4, ...
@@ -615,8 +654,14 @@ __device__ __forceinline__ void mfma_walk(const uint8_t* __restrict__ q_codes,
     for (int u = 0; u < U; u++) {
       int r = 16 * (wave + 4 * (j0 + u)) + n;  // key row of this lane in the A operand
       r = r < nk ? r : nk - 1;                 // rows past the range read a valid row (masked)
-      c[u] = __builtin_nontemporal_load((const u32x4*)(kc + (uint32_t)r * 64u));
-      e[u] = ks[(uint32_t)r * 4u];
+      if constexpr (PAGED) {
+        const uint64_t row = page_row(pages, off0 + (uint32_t)r, kmap.shift);
+        c[u] = __builtin_nontemporal_load((const u32x4*)(kc + row * 64u));
+        e[u] = ks[row * 4u];
+      } else {
+        c[u] = __builtin_nontemporal_load((const u32x4*)(kc + (uint32_t)r * 64u));
+        e[u] = ks[(uint32_t)r * 4u];
+      }
     }
   };
   // keys of this lane's query that are visible, relative to g0 (so compares are 32-bit)
@@ -650,21 +695,21 @@ __global__ __launch_bounds__(256) void index_clear_kernel(IdxWs ws) {
   if (threadIdx.x < 64) ws.ctr(blockIdx.x)[threadIdx.x] = 0u;
 }
 
-template <int HP>
+template <int HP, bool PAGED>
 __global__ __launch_bounds__(256, 2) void index_mfma_hist_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
-    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
-    int64_t k_seq_stride, int64_t N, const int64_t* __restrict__ pos, int m, int Q, MfmaSplit sp,
-    IdxWs ws) {
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
+    int64_t N, const int64_t* __restrict__ pos, int m, int Q, MfmaSplit sp, IdxWs ws) {
   __shared__ uint32_t hist[16 * kPBins / 2];  // two 16-bit counters per word
+  __shared__ int32_t pages[PAGED ? kPageList : 1];
   int b, qb, kr;
   mfma_unit(sp, b, qb, kr);
   for (int j = threadIdx.x; j < 16 * kPBins / 2; j += 256) hist[j] = 0u;
   __syncthreads();
   const int n = threadIdx.x & 15;
   uint32_t* hq = hist + n * (kPBins / 2);
-  mfma_walk<HP>(q_codes, q_scales, HI, k_codes, k_scales, k_seq_stride, N, pos, m, Q, sp, b, qb,
-                kr, [&](int64_t, float s) {
+  mfma_walk<HP, PAGED>(q_codes, q_scales, HI, k_codes, k_scales, kmap, N, pos, m, Q, sp, b, qb,
+                       kr, pages, [&](int64_t, float s) {
                   const uint32_t bin = order_key(s) >> kPBinShift;
                   atomicAdd(&hq[bin >> 1], 1u << (16 * (bin & 1)));
                 });
@@ -701,13 +746,13 @@ __global__ __launch_bounds__(256) void index_thresh_kernel(const int64_t* __rest
 // list per query per workgroup; a staging list that fills up spills straight to the global list.
 constexpr int kPStage = 128;
 
-template <int HP>
+template <int HP, bool PAGED>
 __global__ __launch_bounds__(256) void index_mfma_select_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
-    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
-    int64_t k_seq_stride, int64_t N, const int64_t* __restrict__ pos, int m, int Q, int k,
-    MfmaSplit sp, IdxWs ws) {
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
+    int64_t N, const int64_t* __restrict__ pos, int m, int Q, int k, MfmaSplit sp, IdxWs ws) {
   __shared__ uint64_t stage[2][16][kPStage];  // [sure / tie][query][slot]
+  __shared__ int32_t pages[PAGED ? kPageList : 1];
   __shared__ uint32_t scount[2][16], sbase[2][16];
   int b, qb, kr;
   mfma_unit(sp, b, qb, kr);
@@ -722,8 +767,8 @@ __global__ __launch_bounds__(256) void index_mfma_select_kernel(
   const float smin = thr == kNoThreshold ? INFINITY : key_to_float(thr << kPBinShift);
   uint64_t* sure = ws.sure((int)slot);
   uint64_t* tie = ws.tie((int)slot);
-  mfma_walk<HP>(q_codes, q_scales, HI, k_codes, k_scales, k_seq_stride, N, pos, m, Q, sp, b, qb,
-                kr, [&](int64_t key, float s) {
+  mfma_walk<HP, PAGED>(q_codes, q_scales, HI, k_codes, k_scales, kmap, N, pos, m, Q, sp, b, qb,
+                       kr, pages, [&](int64_t key, float s) {
                   if (!(s >= smin)) return;
                   const uint32_t ok = order_key(s), bin = ok >> kPBinShift;
                   const uint64_t x = ((uint64_t)ok << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)key);
@@ -776,23 +821,27 @@ __global__ __launch_bounds__(1024) void index_sort_kernel(const int64_t* __restr
   finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh, bin_bits);
 }
 
-template <int HP>
+template <int HP, bool PAGED>
 static hipError_t launch_mfma_hp(const IndexArgs& a, const IdxWs& w, hipStream_t s) {
   const int slots = a.B * a.Q;
+  // paged keys: a range spans at most 1024 pages (+2 partial ones), which fits the page list
+  const int64_t range_cap =
+      PAGED ? (kPKeys < ((int64_t)1024 << a.kmap.shift) ? kPKeys : ((int64_t)1024 << a.kmap.shift))
+            : kPKeys;
   MfmaSplit sp;
-  sp.nkr = 8 * (int)((a.N + 8 * kPKeys - 1) / (8 * kPKeys));
+  sp.nkr = 8 * (int)((a.N + 8 * range_cap - 1) / (8 * range_cap));
   if (sp.nkr < 8) sp.nkr = 8;
   sp.keys_per_range = ((a.N + sp.nkr - 1) / sp.nkr + 15) / 16 * 16;
   sp.nqb = (a.Q + 15) / 16;
   sp.B = a.B;
   const dim3 grid((unsigned)((int64_t)sp.nkr * sp.nqb * a.B));
   index_clear_kernel<<<slots, 256, 0, s>>>(w);
-  a.prof.launch(index_mfma_hist_kernel<HP>, grid, dim3(256), s, a.q_codes, a.q_scales, a.HI,
-                a.k_codes, a.k_scales, a.k_seq_stride, a.N, a.pos, a.m, a.Q, sp, w);
+  a.prof.launch(index_mfma_hist_kernel<HP, PAGED>, grid, dim3(256), s, a.q_codes, a.q_scales,
+                a.HI, a.k_codes, a.k_scales, a.kmap, a.N, a.pos, a.m, a.Q, sp, w);
   index_thresh_kernel<<<slots, 256, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, w);
-  index_mfma_select_kernel<HP><<<grid, 256, 0, s>>>(a.q_codes, a.q_scales, a.HI, a.k_codes,
-                                                    a.k_scales, a.k_seq_stride, a.N, a.pos, a.m,
-                                                    a.Q, a.k, sp, w);
+  index_mfma_select_kernel<HP, PAGED><<<grid, 256, 0, s>>>(a.q_codes, a.q_scales, a.HI,
+                                                           a.k_codes, a.k_scales, a.kmap, a.N,
+                                                           a.pos, a.m, a.Q, a.k, sp, w);
   index_sort_kernel<<<slots, 1024, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, a.idx_out, a.score_out, w,
                                            32 - kPBinShift);
   return hipGetLastError();
@@ -801,15 +850,24 @@ static hipError_t launch_mfma_hp(const IndexArgs& a, const IdxWs& w, hipStream_t
 static hipError_t launch_index_mfma(const IndexArgs& a) {
   hipStream_t s = (hipStream_t)a.stream;
   const IdxWs w = make_ws(a.ws, a.N, a.k, false);
-  if (a.HI <= 4) return launch_mfma_hp<4>(a, w, s);
-  if (a.HI <= 8) return launch_mfma_hp<8>(a, w, s);
-  return launch_mfma_hp<16>(a, w, s);
+  if (a.kmap.table) {
+    if (a.HI <= 4) return launch_mfma_hp<4, true>(a, w, s);
+    if (a.HI <= 8) return launch_mfma_hp<8, true>(a, w, s);
+    return launch_mfma_hp<16, true>(a, w, s);
+  }
+  if (a.HI <= 4) return launch_mfma_hp<4, false>(a, w, s);
+  if (a.HI <= 8) return launch_mfma_hp<8, false>(a, w, s);
+  return launch_mfma_hp<16, false>(a, w, s);
 }
 
 template <int NB>
 static void launch_scan(const IndexArgs& a, const IdxWs& w, int chunk, dim3 grid, hipStream_t s) {
-  a.prof.launch(index_scan_kernel<NB>, grid, dim3(256), s, a.k_codes, a.k_scales,
-                a.k_seq_stride, a.N, a.pos, a.m, a.Q, chunk, w);
+  if (a.kmap.table)
+    a.prof.launch(index_scan_kernel<NB, true>, grid, dim3(256), s, a.k_codes, a.k_scales, a.kmap,
+                  a.N, a.pos, a.m, a.Q, chunk, w);
+  else
+    a.prof.launch(index_scan_kernel<NB, false>, grid, dim3(256), s, a.k_codes, a.k_scales, a.kmap,
+                  a.N, a.pos, a.m, a.Q, chunk, w);
 }
 
 hipError_t launch_index_topk(const IndexArgs& a) {
@@ -824,6 +882,8 @@ hipError_t launch_index_topk(const IndexArgs& a) {
   chunk = ((chunk + 1023) / 1024) * 1024;
   if (chunk < 1024) chunk = 1024;
   if (chunk > (1 << 22)) chunk = 1 << 22;
+  // paged keys: a chunk spans at most 1024 pages (+1 partial one), which fits the page list
+  if (a.kmap.table && chunk > ((int64_t)1024 << a.kmap.shift)) chunk = (int64_t)1024 << a.kmap.shift;
   const int64_t nchunks = a.N > 0 ? (a.N + chunk - 1) / chunk : 1;
   dim3 gs((unsigned)nchunks, (unsigned)slots);
   switch (a.dI) {

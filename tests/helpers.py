@@ -176,3 +176,29 @@ def check_rows_fp4(gpu_rows, gpu_scales, ref_rows, ref_scales, pre, tol):
                 nd += 1
                 assert midpoint_ok(v[i] / X, a, b, t[i] / X), (r, col, v[i] / X, a, b)
     return nd
+
+
+def paginate(rows: np.ndarray, page_size: int, rng, spare: int = 3, fill: int = 0xFF):
+    """Scatter a logical cache rows [B, S, ...] into a pool of pages of page_size entries, pages
+    handed out in a shuffled order with `spare` pages never used. Unused pages and the tail of
+    each sequence's last page hold `fill` bytes (0xFF: NaN for E4M3 bytes and E8M0 scales), so a
+    read through a wrong table entry shows up in the results.
+    Returns (pool [pages, page_size, ...], block_table int32 [B, ceil(S / page_size)])."""
+    B, S = rows.shape[:2]
+    per = max(1, -(-S // page_size))
+    n = B * per + spare
+    table = rng.permutation(n)[:B * per].reshape(B, per).astype(np.int32)
+    pool = np.full((n, page_size) + rows.shape[2:], fill, rows.dtype)
+    for b in range(B):
+        for i in range(per):
+            part = rows[b, i * page_size:(i + 1) * page_size]
+            pool[table[b, i], :len(part)] = part
+    return pool, table
+
+
+def gather_pages(pool: np.ndarray, table: np.ndarray, S: int) -> np.ndarray:
+    """The logical cache [B, S, ...] held by a pool and block table (inverse of paginate)."""
+    B, per = table.shape
+    P = pool.shape[1]
+    out = pool[table.reshape(-1)].reshape((B, per * P) + pool.shape[2:])
+    return out[:, :S]

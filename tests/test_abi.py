@@ -136,6 +136,45 @@ def test_attend_rejects_bad_arguments():
              None, FAKE, 1 << 30, None) == L.INVALID_ARGUMENT        # m = 0
 
 
+def test_paged_calls_reject_bad_block_tables():
+    kc = L.lib().csah_kv_compress_paged
+
+    def comp(table=FAKE, ts=4, P=4, first=0, T=8, m=4):
+        # B=1, D=512, E4M3 rows: T/m entries written from logical entry `first`
+        return kc(FAKE, 0, T, 1, T, 512, m, m, 0, FAKE, FAKE, FAKE, 1, None, table, ts, P, first,
+                  None)
+
+    assert comp(table=None) == L.INVALID_ARGUMENT
+    assert comp(table=ctypes.c_void_p(4098)) == L.INVALID_ARGUMENT   # not 4-byte aligned
+    assert comp(P=3) == L.INVALID_ARGUMENT                          # not a power of two
+    assert comp(P=0) == L.INVALID_ARGUMENT
+    assert comp(P=1 << 21) == L.UNSUPPORTED
+    assert comp(first=-1) == L.INVALID_ARGUMENT
+    assert comp(ts=1, P=4, first=3) == L.INVALID_ARGUMENT           # entries 3, 4 > 4 slots
+    assert comp(ts=-1) == L.INVALID_ARGUMENT
+
+    ki = L.lib().csah_index_topk_paged
+
+    def index(ts, P, N):
+        return ki(FAKE, FAKE, 4, 128, FAKE, FAKE, FAKE, ts, P, N, FAKE, 4, 1, 1, 8, FAKE, None,
+                  FAKE, 1 << 30, None)
+
+    assert index(ts=2, P=64, N=129) == L.INVALID_ARGUMENT           # 2 pages hold 128 entries
+    assert index(ts=3, P=48, N=129) == L.INVALID_ARGUMENT
+
+    ka = L.lib().csah_csa_attend_paged
+    kh = L.lib().csah_hca_attend_paged
+
+    def csa(table=FAKE, ts=2, P=64, N=128):
+        return ka(FAKE, 1, 64, 512, FAKE, 1, table, ts, P, N, FAKE, 16, FAKE, 128, 128, FAKE,
+                  None, 0.1, 1, 1, FAKE, None, FAKE, 1 << 30, None)
+
+    assert csa(table=None) == L.INVALID_ARGUMENT
+    assert csa(N=129) == L.INVALID_ARGUMENT
+    assert kh(FAKE, 1, 64, 512, FAKE, 1, FAKE, 1, 64, 65, 128, FAKE, 128, 128, FAKE, None, 0.1, 1,
+              1, FAKE, None, FAKE, 1 << 30, None) == L.INVALID_ARGUMENT
+
+
 def test_valid_call_without_gpu_reports_unsupported():
     """With correct arguments but no gfx950 device the library refuses instead of launching."""
     import torch
@@ -143,3 +182,6 @@ def test_valid_call_without_gpu_reports_unsupported():
         pytest.skip("a GPU is present")
     f = L.lib().csah_kv_compress
     assert f(FAKE, 0, 8, 1, 8, 128, 4, FAKE, FAKE, FAKE, 0, 2, None, None) == L.UNSUPPORTED
+    g = L.lib().csah_kv_compress_paged
+    assert g(FAKE, 0, 8, 1, 8, 128, 4, 4, 0, FAKE, FAKE, FAKE, 0, None, FAKE, 1, 2, 0,
+             None) == L.UNSUPPORTED
