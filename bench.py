@@ -208,6 +208,47 @@ class DecodeStep:
         self.index(c)
         self.csa_attend(c)
 
+    def make_paged(self, page: int, seed: int = 41):
+        """The 4-sequence CSA caches (rows and FP4 keys) copied into page pools of `page` entries,
+        pages handed out in a shuffled order, plus the int32 block table (setup, not timed)."""
+        c = self.csa_slice(B_CSA4)
+        per = N_CSA // page
+        g = torch.Generator(device="cpu").manual_seed(seed)
+        perm = torch.randperm(B_CSA4 * per, generator=g).to(torch.int32)
+        table = perm.view(B_CSA4, per).cuda()
+        inv = torch.empty_like(perm)
+        inv[perm.long()] = torch.arange(B_CSA4 * per, dtype=torch.int32)
+        src = inv.long().cuda()  # pool page p holds logical page src[p]
+
+        def pool(t):
+            return t.reshape(B_CSA4 * per, page, t.shape[-1])[src].contiguous()
+
+        self.paged = dict(P=page, table=table, cache=pool(c["cache"]), kc=pool(c["kc"]),
+                          ks=pool(c["ks"]), idx=torch.empty_like(c["idx"]),
+                          out=torch.empty_like(c["out"]), lse=torch.empty_like(c["lse"]))
+        torch.cuda.synchronize()
+
+    def index_paged(self, ev=None):
+        c, p = self.csa_slice(B_CSA4), self.paged
+        if ev is not None:
+            L.profile_next_call(*ev)
+        L.index_topk_paged(c["iqc"], c["iqs"], p["kc"], p["ks"], p["table"], p["P"], N_CSA,
+                           self.pos[:B_CSA4], 4, K, want_scores=False, ws=self.ws_idx,
+                           idx_out=p["idx"])
+
+    def csa_attend_paged(self, ev=None):
+        c, p = self.csa_slice(B_CSA4), self.paged
+        if ev is not None:
+            L.profile_next_call(*ev)
+        L.csa_attend_paged(c["q"], p["cache"], p["table"], p["P"], N_CSA, p["idx"], c["win"], W,
+                           self.pos[:B_CSA4], self.sink, self.scale, ws=self.ws_csa,
+                           out=p["out"], lse=p["lse"])
+
+    def csa4_paged_step(self):
+        """The same 4-sequence CSA step with both caches paged."""
+        self.index_paged()
+        self.csa_attend_paged()
+
 
 class StepGraphs:
     """The step as two HIP graphs, one per layer, replayed on two streams so that the HCA branch
@@ -280,6 +321,41 @@ def kernel_times(ws: DecodeStep, reps: int):
         evs["hca_attend"].append(e)
     torch.cuda.synchronize()
     return {k: statistics.mean(a.elapsed_time(b) for a, b in v) for k, v in evs.items()}
+
+
+def paged_measure(ws: DecodeStep, args, ms4_contiguous):
+    """The 4-sequence 1M CSA step with paged caches (64 entries = 256 tokens per page): step time
+    and the two kernels' times next to the contiguous ones, and a check that both layouts give
+    the same indices and outputs."""
+    P = 64
+    ws.make_paged(P)
+    g = None if args.no_graph else capture(ws.csa4_paged_step)
+    ms = time_replays(g, ws.csa4_paged_step, args.steps)
+    c = ws.csa_slice(B_CSA4)
+    ws.csa4_step()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ws.paged["idx"], c["idx"]) and torch.equal(ws.paged["out"], c["out"]))
+    ev = {"index_scan": [], "csa_attend": [], "index_scan_paged": [], "csa_attend_paged": []}
+    for _ in range(args.kernel_reps):
+        for name, fn in (("index_scan", lambda e: ws.index(c, ev=e)),
+                         ("csa_attend", lambda e: ws.csa_attend(c, ev=e)),
+                         ("index_scan_paged", lambda e: ws.index_paged(ev=e)),
+                         ("csa_attend_paged", lambda e: ws.csa_attend_paged(ev=e))):
+            e = event_pair()
+            fn(e)
+            ev[name].append(e)
+    torch.cuda.synchronize()
+    kt = {k: statistics.mean(a.elapsed_time(b) for a, b in v) * 1e3 for k, v in ev.items()}
+    log(f"  paged CSA step (P={P}): {ms * 1e3:.1f} us; kernels (us): "
+        + ", ".join(f"{k} {v:.2f}" for k, v in kt.items()) + f"; same results: {same}")
+    return {
+        "what": f"csa_decode_1m_b4 with both caches paged: {P} entries ({4 * P} tokens) per page, "
+                "pages in shuffled order, int32 block table",
+        "page_entries": P, "us_per_step": ms * 1e3,
+        "us_per_step_contiguous": None if ms4_contiguous is None else ms4_contiguous * 1e3,
+        "achieved_GBps": CSA4_BYTES / (ms * 1e-3) / 1e9,
+        "kernel_us": kt, "identical_to_contiguous": same,
+    }
 
 
 def capture(fn):
@@ -687,6 +763,8 @@ def main():
             "frac_of_hbm_peak": CSA4_BYTES / (ms4 * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "queries_per_s": B_CSA4 / (ms4 * 1e-3),
         }
+    if not args.no_csa4:
+        line["csa_decode_1m_b4_paged"] = paged_measure(ws, args, ms4)
     if not args.no_prefill:
         log("prefill chunk (4096 tokens on a 1M cache)...")
         del ws, graph, g4

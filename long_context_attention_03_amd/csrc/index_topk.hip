@@ -40,7 +40,7 @@ namespace csah {
 // Scan launch shape: workgroups per launch (the key range is split evenly among them) and load
 // groups in flight per lane (each double-buffered).
 #ifndef CSAH_SCAN_WGS
-#define CSAH_SCAN_WGS 1024
+#define CSAH_SCAN_WGS 512
 #endif
 #ifndef CSAH_SCAN_U
 #define CSAH_SCAN_U 4
@@ -161,11 +161,16 @@ template <int NB, bool PAGED>
 __global__ __launch_bounds__(256) void index_scan_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
     int64_t N, const int64_t* __restrict__ pos, int m, int Q, int chunk, IdxWs ws) {
-  constexpr int EPR = 256 / NB;  // entries per workgroup-wide group of lanes
+  constexpr int EPW = 64 / NB;   // entries per wavefront per group of lanes
   constexpr int U = CSAH_SCAN_U;  // groups whose loads are in flight together
-  constexpr int STEP = EPR * U;
+  constexpr int STEP = 4 * EPW * U;
+  static_assert(U % NB == 0, "each lane stores U / NB scores");
   const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
-  const int tid = threadIdx.x, sub = tid % NB, ent = tid / NB;
+  const int tid = threadIdx.x, sub = tid % NB;
+  // wavefront w takes the STEP / 4 consecutive entries [w * EPW * U, ...) of each step, group u
+  // the EPW entries from u * EPW on (lane q * NB + sub: entry q, block sub), so that after the
+  // quad reduction the wavefront can store its U * EPW scores as U / NB fully coalesced stores
+  const int ent = (tid >> 6) * (EPW * U) + (tid & 63) / NB;
   __shared__ uint32_t hist[kBins];
   __shared__ int32_t pages[PAGED ? kPageList : 1];
   for (int j = tid; j < kBins; j += 256) hist[j] = 0u;
@@ -193,7 +198,7 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
     auto load = [&](int r0, u32x4* c, uint32_t* e, bool clamp) {
 #pragma unroll
       for (int u = 0; u < U; u++) {
-        int r = r0 + u * EPR + ent;
+        int r = r0 + u * EPW + ent;
         if (clamp) r = r < n ? r : n - 1;
         if constexpr (PAGED) {
           const uint64_t row = page_row(pages, off0 + (uint32_t)r, kmap.shift);
@@ -206,13 +211,19 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
       }
     };
     auto score = [&](int r0, const u32x4* c, const uint32_t* e) {
+      float s[U];
 #pragma unroll
-      for (int u = 0; u < U; u++) {
-        const int r = r0 + u * EPR + ent;
-        const float s = block_score<NB>(c[u], e[u], qv);
-        if (sub == 0 && r < n) {
-          sc[r] = s;
-          atomicAdd(&hist[order_key(s) >> kBinShift], 1u);
+      for (int u = 0; u < U; u++) s[u] = block_score<NB>(c[u], e[u], qv);  // in all NB lanes
+#pragma unroll
+      for (int j = 0; j < U / NB; j++) {
+        // lane (q, sub) stores group j * NB + sub's score of its entry q
+        float v = s[j * NB];
+#pragma unroll
+        for (int t = 1; t < NB; t++) v = sub == t ? s[j * NB + t] : v;
+        const int r = r0 + (j * NB + sub) * EPW + ent;
+        if (r < n) {
+          sc[r] = v;
+          atomicAdd(&hist[order_key(v) >> kBinShift], 1u);
         }
       }
     };
