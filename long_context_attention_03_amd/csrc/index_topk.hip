@@ -79,6 +79,10 @@ static IdxWs make_ws(void* base, int64_t N, int k, bool with_scores) {
 // Queries of one sequence share its keys; from 16 of them on (one MFMA tile) with 128-dim keys and
 // at most 16 indexer heads the scores come from the scaled FP4 MFMA (see index_mfma_hist_kernel).
 static bool use_mfma_path(int Q, int HI, int dI) { return dI == 128 && Q >= 16 && HI <= 16; }
+// From 3 to 15 queries per sequence the scores come from the same MFMA tiles in one pass over the
+// keys and are stored, then selected and ranked as in the one-query scan (with 2, scanning the
+// keys once per query on the VALU is still faster).
+static bool use_mfma_scan(int Q, int HI, int dI) { return dI == 128 && Q >= 3 && Q < 16 && HI <= 16; }
 
 size_t index_workspace_bytes(int B, int Q, int64_t N, int k, int HI, int dI) {
   IdxWs w = make_ws(nullptr, N, k, !use_mfma_path(Q, HI, dI));
@@ -414,6 +418,8 @@ __device__ void finalize_slot(int slot, int64_t N, int k, int kk, int32_t* __res
   }
 }
 
+// BINS / SHIFT: the histogram the scan wrote (the top log2(BINS) bits of the order key)
+template <int BINS, int SHIFT>
 __global__ __launch_bounds__(kSelThreads) void index_select_kernel(
     const int64_t* __restrict__ pos, int m, int Q, int64_t N, int k, IdxWs ws) {
   const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
@@ -421,7 +427,7 @@ __global__ __launch_bounds__(kSelThreads) void index_select_kernel(
   const int64_t nv = visible_entries(pos, b, i, m, N);
   const int kk = (int)(nv < k ? nv : k);
   if (kk == 0 || (int64_t)blockIdx.x * kSelChunk >= nv) return;
-  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t h[BINS];
   __shared__ uint32_t suf[256];
   __shared__ uint32_t s_bin, s_above;
   __shared__ uint32_t wsum[kSelThreads / 64];
@@ -438,13 +444,13 @@ __global__ __launch_bounds__(kSelThreads) void index_select_kernel(
 #pragma unroll
     for (int e = 0; e < kSelPerThread; e++) v[e] = g0 + e < nv ? sc[g0 + e] : -INFINITY;
   }
-  find_threshold_bin<kBins>(ws.hist(slot), kk, h, suf, &s_bin, &s_above);
+  find_threshold_bin<BINS>(ws.hist(slot), kk, h, suf, &s_bin, &s_above);
   const uint32_t bstar = s_bin;
   uint32_t cls[kSelPerThread];  // 0 drop, 1 sure, 2 tie
   uint32_t cnt = 0;             // sure count | tie count << 16
 #pragma unroll
   for (int e = 0; e < kSelPerThread; e++) {
-    const uint32_t bin = order_key(v[e]) >> kBinShift;
+    const uint32_t bin = order_key(v[e]) >> SHIFT;
     cls[e] = (g0 + e < nv) ? (bin > bstar ? 1u : (bin == bstar ? 2u : 0u)) : 0u;
     cnt += cls[e] == 1u ? 1u : (cls[e] == 2u ? 0x10000u : 0u);
   }
@@ -497,7 +503,7 @@ constexpr int kRankPerWG = kRankThreads / kRankLanes;
 
 __global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
     const int64_t* __restrict__ pos, int m, int Q, int64_t N, int k,
-    int32_t* __restrict__ idx_out, float* __restrict__ score_out, IdxWs ws) {
+    int32_t* __restrict__ idx_out, float* __restrict__ score_out, IdxWs ws, int bin_bits) {
   const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
   const int t = threadIdx.x;
   const int64_t nv = visible_entries(pos, b, i, m, N);
@@ -515,7 +521,7 @@ __global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
   const uint32_t n = ns + nt;
   if (kk == 0 || n > (uint32_t)kSortCap) {
     if (blockIdx.x == 0)
-      finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh, 32 - kBinShift);
+      finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh, bin_bits);
     return;
   }
   int32_t* io = idx_out + (int64_t)slot * k;
@@ -606,7 +612,8 @@ __device__ __forceinline__ f32x4 tile_scores(const u32x4 kc, uint32_t ke, const 
 
 // Shared walk over the workgroup's keys: each wavefront takes every 4th tile of 16 keys. Loads go
 // in rounds of U tiles, double-buffered, so one round's loads are in flight while the previous
-// round is scored; `visit(key, score)` sees every visible (key, query) pair of the lane.
+// round is scored; `visit(key, scores, n)` sees the lane's query scored against the four
+// consecutive keys from `key` on, of which the first n (n >= 1) are visible.
 // Work split: the keys are cut into nkr ranges (a multiple of 8, at most kPKeys keys each) and the
 // queries into blocks of 16. Workgroups are dispatched round-robin over the 8 XCDs (id % 8), so
 // XCD x takes the key ranges x, x+8, ... for every query block: its few ranges stay resident in
@@ -681,11 +688,12 @@ __device__ __forceinline__ void mfma_walk(const uint8_t* __restrict__ q_codes,
 #pragma unroll
     for (int u = 0; u < U; u++) {
       if (j0 + u >= my_tiles) break;
-      const f32x4 sc = tile_scores<HP>(c[u], e[u], qo);
+      f32x4 sc = tile_scores<HP>(c[u], e[u], qo);
       const int kr0 = 16 * (wave + 4 * (j0 + u)) + 4 * blk;
+      const int nvis = lim - kr0 < 0 ? 0 : (lim - kr0 > 4 ? 4 : lim - kr0);
 #pragma unroll
-      for (int i = 0; i < 4; i++)
-        if (kr0 + i < lim) visit(g0 + kr0 + i, sc[i] + 0.0f);  // fold -0 into +0
+      for (int i = 0; i < 4; i++) sc[i] += 0.0f;  // fold -0 into +0
+      if (nvis > 0) visit(g0 + kr0, sc, nvis);
     }
   };
   u32x4 ca[U], cb[U];
@@ -720,10 +728,14 @@ __global__ __launch_bounds__(256, 2) void index_mfma_hist_kernel(
   const int n = threadIdx.x & 15;
   uint32_t* hq = hist + n * (kPBins / 2);
   mfma_walk<HP, PAGED>(q_codes, q_scales, HI, k_codes, k_scales, kmap, N, pos, m, Q, sp, b, qb,
-                       kr, pages, [&](int64_t, float s) {
-                  const uint32_t bin = order_key(s) >> kPBinShift;
-                  atomicAdd(&hq[bin >> 1], 1u << (16 * (bin & 1)));
-                });
+                       kr, pages, [&](int64_t, const f32x4& sc, int nvis) {
+#pragma unroll
+                         for (int i = 0; i < 4; i++) {
+                           if (i >= nvis) break;
+                           const uint32_t bin = order_key(sc[i]) >> kPBinShift;
+                           atomicAdd(&hq[bin >> 1], 1u << (16 * (bin & 1)));
+                         }
+                       });
   __syncthreads();
   const int q0 = qb * 16;
   for (int j = threadIdx.x; j < 16 * kPBins / 2; j += 256) {
@@ -779,22 +791,28 @@ __global__ __launch_bounds__(256) void index_mfma_select_kernel(
   uint64_t* sure = ws.sure((int)slot);
   uint64_t* tie = ws.tie((int)slot);
   mfma_walk<HP, PAGED>(q_codes, q_scales, HI, k_codes, k_scales, kmap, N, pos, m, Q, sp, b, qb,
-                       kr, pages, [&](int64_t key, float s) {
-                  if (!(s >= smin)) return;
-                  const uint32_t ok = order_key(s), bin = ok >> kPBinShift;
-                  const uint64_t x = ((uint64_t)ok << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)key);
-                  const int list = bin > thr ? 0 : 1;
-                  const uint32_t at = atomicAdd(&scount[list][n], 1u);
-                  if (at < (uint32_t)kPStage) {
-                    stage[list][n][at] = x;
-                  } else if (list == 0) {
-                    const uint32_t g = atomicAdd(&ctr[0], 1u);
-                    if (g < (uint32_t)k) sure[g] = x;
-                  } else {
-                    const uint32_t g = atomicAdd(&ctr[1], 1u);
-                    if ((int64_t)g < N) tie[g] = x;
-                  }
-                });
+                       kr, pages, [&](int64_t key0, const f32x4& sc, int nvis) {
+#pragma unroll
+                         for (int i = 0; i < 4; i++) {
+                           if (i >= nvis) break;
+                           const float s = sc[i];
+                           if (!(s >= smin)) continue;
+                           const uint32_t ok = order_key(s), bin = ok >> kPBinShift;
+                           const uint64_t x = ((uint64_t)ok << 32) |
+                                              (uint64_t)(0xFFFFFFFFu - (uint32_t)(key0 + i));
+                           const int list = bin > thr ? 0 : 1;
+                           const uint32_t at = atomicAdd(&scount[list][n], 1u);
+                           if (at < (uint32_t)kPStage) {
+                             stage[list][n][at] = x;
+                           } else if (list == 0) {
+                             const uint32_t g = atomicAdd(&ctr[0], 1u);
+                             if (g < (uint32_t)k) sure[g] = x;
+                           } else {
+                             const uint32_t g = atomicAdd(&ctr[1], 1u);
+                             if ((int64_t)g < N) tie[g] = x;
+                           }
+                         }
+                       });
   __syncthreads();
   if (threadIdx.x < 32) {
     const int list = threadIdx.x >> 4, qn = threadIdx.x & 15;
@@ -819,6 +837,52 @@ __global__ __launch_bounds__(256) void index_mfma_select_kernel(
   }
 }
 
+// A few queries per sequence (multi-token decode): one pass over the keys. The MFMA tiles give
+// the scores of all the workgroup's queries at once; each is stored and counted in the query's
+// 2048-bin histogram, and index_select_kernel / index_rank_kernel finish as in the one-query scan.
+template <int HP, bool PAGED>
+__global__ __launch_bounds__(256, 2) void index_mfma_scan_kernel(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
+    int64_t N, const int64_t* __restrict__ pos, int m, int Q, MfmaSplit sp, IdxWs ws) {
+  __shared__ uint32_t hist[16 * kPBins / 2];  // two 16-bit counters per word
+  __shared__ int32_t pages[PAGED ? kPageList : 1];
+  int b, qb, kr;
+  mfma_unit(sp, b, qb, kr);
+  const int n = threadIdx.x & 15, q0 = qb * 16;
+  const int words = (Q - q0 < 16 ? Q - q0 : 16) * (kPBins / 2);  // the block's queries only
+  for (int j = threadIdx.x; j < words; j += 256) hist[j] = 0u;
+  __syncthreads();
+  uint32_t* hq = hist + n * (kPBins / 2);
+  // lanes of queries past Q visit nothing; point them at a valid slot all the same
+  float* sc = ws.scores((int)((int64_t)b * Q + (q0 + n < Q ? q0 + n : Q - 1)));
+  mfma_walk<HP, PAGED>(q_codes, q_scales, HI, k_codes, k_scales, kmap, N, pos, m, Q, sp, b, qb,
+                       kr, pages, [&](int64_t key0, const f32x4& s4, int nvis) {
+                         if (nvis == 4) {
+                           *(f32x4*)(sc + key0) = s4;  // key0 is a multiple of 4
+                         } else {
+#pragma unroll
+                           for (int i = 0; i < 4; i++)
+                             if (i < nvis) sc[key0 + i] = s4[i];
+                         }
+#pragma unroll
+                         for (int i = 0; i < 4; i++) {
+                           if (i >= nvis) break;
+                           const uint32_t bin = order_key(s4[i]) >> kPBinShift;
+                           atomicAdd(&hq[bin >> 1], 1u << (16 * (bin & 1)));
+                         }
+                       });
+  __syncthreads();
+  for (int j = threadIdx.x; j < words; j += 256) {
+    const int qn = j / (kPBins / 2), wd = j - qn * (kPBins / 2);
+    const uint32_t v = hist[j];
+    if (v == 0u || q0 + qn >= Q) continue;
+    uint32_t* gh = ws.hist((int)((int64_t)b * Q + q0 + qn));
+    if (v & 0xFFFFu) atomicAdd(&gh[2 * wd], v & 0xFFFFu);
+    if (v >> 16) atomicAdd(&gh[2 * wd + 1], v >> 16);
+  }
+}
+
 __global__ __launch_bounds__(1024) void index_sort_kernel(const int64_t* __restrict__ pos, int m,
                                                           int Q, int64_t N, int k,
                                                           int32_t* __restrict__ idx_out,
@@ -832,19 +896,33 @@ __global__ __launch_bounds__(1024) void index_sort_kernel(const int64_t* __restr
   finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh, bin_bits);
 }
 
+// Key ranges of at most kPKeys keys (for paged keys also at most 1024 pages, +2 partial ones, so
+// that the page list fits); while the grid would be small (few sequences x query blocks), more
+// and shorter ranges, down to 1024 keys, bring it to about CSAH_MFMA_WGS workgroups.
+#ifndef CSAH_MFMA_WGS
+#define CSAH_MFMA_WGS 512
+#endif
+static MfmaSplit mfma_split(const IndexArgs& a, bool paged) {
+  const int64_t range_cap =
+      paged ? (kPKeys < ((int64_t)1024 << a.kmap.shift) ? kPKeys : ((int64_t)1024 << a.kmap.shift))
+            : kPKeys;
+  MfmaSplit sp;
+  sp.nqb = (a.Q + 15) / 16;
+  sp.B = a.B;
+  sp.nkr = 8 * (int)((a.N + 8 * range_cap - 1) / (8 * range_cap));
+  if (sp.nkr < 8) sp.nkr = 8;
+  int64_t want = 8 * ((CSAH_MFMA_WGS + 8LL * sp.nqb * a.B - 1) / (8LL * sp.nqb * a.B));
+  const int64_t most = 8 * ((a.N + 8 * 1024 - 1) / (8 * 1024));
+  if (want > most) want = most;
+  if (want > sp.nkr) sp.nkr = (int)want;
+  sp.keys_per_range = ((a.N + sp.nkr - 1) / sp.nkr + 15) / 16 * 16;
+  return sp;
+}
+
 template <int HP, bool PAGED>
 static hipError_t launch_mfma_hp(const IndexArgs& a, const IdxWs& w, hipStream_t s) {
   const int slots = a.B * a.Q;
-  // paged keys: a range spans at most 1024 pages (+2 partial ones), which fits the page list
-  const int64_t range_cap =
-      PAGED ? (kPKeys < ((int64_t)1024 << a.kmap.shift) ? kPKeys : ((int64_t)1024 << a.kmap.shift))
-            : kPKeys;
-  MfmaSplit sp;
-  sp.nkr = 8 * (int)((a.N + 8 * range_cap - 1) / (8 * range_cap));
-  if (sp.nkr < 8) sp.nkr = 8;
-  sp.keys_per_range = ((a.N + sp.nkr - 1) / sp.nkr + 15) / 16 * 16;
-  sp.nqb = (a.Q + 15) / 16;
-  sp.B = a.B;
+  const MfmaSplit sp = mfma_split(a, PAGED);
   const dim3 grid((unsigned)((int64_t)sp.nkr * sp.nqb * a.B));
   index_clear_kernel<<<slots, 256, 0, s>>>(w);
   a.prof.launch(index_mfma_hist_kernel<HP, PAGED>, grid, dim3(256), s, a.q_codes, a.q_scales,
@@ -871,6 +949,26 @@ static hipError_t launch_index_mfma(const IndexArgs& a) {
   return launch_mfma_hp<16, false>(a, w, s);
 }
 
+template <int HP, bool PAGED>
+static void launch_mfma_scan_hp(const IndexArgs& a, const IdxWs& w, hipStream_t s) {
+  const MfmaSplit sp = mfma_split(a, PAGED);
+  const dim3 grid((unsigned)((int64_t)sp.nkr * sp.nqb * a.B));
+  a.prof.launch(index_mfma_scan_kernel<HP, PAGED>, grid, dim3(256), s, a.q_codes, a.q_scales,
+                a.HI, a.k_codes, a.k_scales, a.kmap, a.N, a.pos, a.m, a.Q, sp, w);
+}
+
+static void launch_mfma_scan(const IndexArgs& a, const IdxWs& w, hipStream_t s) {
+  if (a.kmap.table) {
+    if (a.HI <= 4) launch_mfma_scan_hp<4, true>(a, w, s);
+    else if (a.HI <= 8) launch_mfma_scan_hp<8, true>(a, w, s);
+    else launch_mfma_scan_hp<16, true>(a, w, s);
+  } else {
+    if (a.HI <= 4) launch_mfma_scan_hp<4, false>(a, w, s);
+    else if (a.HI <= 8) launch_mfma_scan_hp<8, false>(a, w, s);
+    else launch_mfma_scan_hp<16, false>(a, w, s);
+  }
+}
+
 template <int NB>
 static void launch_scan(const IndexArgs& a, const IdxWs& w, int chunk, dim3 grid, hipStream_t s) {
   if (a.kmap.table)
@@ -887,6 +985,10 @@ hipError_t launch_index_topk(const IndexArgs& a) {
   if (use_mfma_path(a.Q, a.HI, a.dI)) return launch_index_mfma(a);
   IdxWs w = make_ws(a.ws, a.N, a.k, true);
   index_prep_kernel<<<slots, 256, 0, s>>>(a.q_codes, a.q_scales, a.HI, a.dI, w);
+  const bool mq = use_mfma_scan(a.Q, a.HI, a.dI);
+  if (mq) {
+    launch_mfma_scan(a, w, s);
+  } else {
   // scan: about CSAH_SCAN_WGS workgroups in total, each streaming a contiguous range
   const int64_t total = (int64_t)slots * (a.N > 0 ? a.N : 1);
   int64_t chunk = (total + CSAH_SCAN_WGS - 1) / CSAH_SCAN_WGS;
@@ -902,13 +1004,19 @@ hipError_t launch_index_topk(const IndexArgs& a) {
     case 64: launch_scan<2>(a, w, (int)chunk, gs, s); break;
     default: launch_scan<4>(a, w, (int)chunk, gs, s); break;
   }
+  }
   const int64_t nsel = a.N > 0 ? (a.N + kSelChunk - 1) / kSelChunk : 1;
-  index_select_kernel<<<dim3((unsigned)nsel, (unsigned)slots), kSelThreads, 0, s>>>(
-      a.pos, a.m, a.Q, a.N, a.k, w);
+  const dim3 gsel((unsigned)nsel, (unsigned)slots);
+  if (mq)
+    index_select_kernel<kPBins, kPBinShift><<<gsel, kSelThreads, 0, s>>>(a.pos, a.m, a.Q, a.N,
+                                                                        a.k, w);
+  else
+    index_select_kernel<kBins, kBinShift><<<gsel, kSelThreads, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k,
+                                                                      w);
   const int64_t cand = (a.N < kSortCap ? a.N : kSortCap);
-  const unsigned nrank = (unsigned)((cand + kRankPerWG - 1) / kRankPerWG);
-  index_rank_kernel<<<dim3(nrank > 0 ? nrank : 1, (unsigned)slots), kRankThreads, 0, s>>>(
-      a.pos, a.m, a.Q, a.N, a.k, a.idx_out, a.score_out, w);
+  const int64_t nrank = (cand + kRankPerWG - 1) / kRankPerWG;
+  index_rank_kernel<<<dim3(nrank > 0 ? (unsigned)nrank : 1u, (unsigned)slots), kRankThreads, 0, s>>>(
+      a.pos, a.m, a.Q, a.N, a.k, a.idx_out, a.score_out, w, 32 - (mq ? kPBinShift : kBinShift));
   return hipGetLastError();
 }
 

@@ -163,6 +163,33 @@ def test_prefill_chunk_full_size_sampled_queries():
     say(f"  {len(sample)} sampled queries bit-exact")
 
 
+@pytest.mark.parametrize("HI,Q", [(4, 2), (8, 7), (16, 15), (3, 5)])
+def test_multi_query_scan_shapes(HI, Q):
+    """2 to 15 queries per sequence (one MFMA pass, stored scores): head counts that pad the MFMA
+    operands, a ragged key count, and visibility that changes inside the query block (sequence 1's
+    queries see 4,000..4,003 entries, fewer than k for none; sequence 2's see 50..53 < k)."""
+    rng = np.random.default_rng(50 + HI + Q)
+    B, N, m, k = 3, 30011, 4, 512
+    kc, ks, qc, qs = _fp4_inputs(rng, B, Q, N, HI)
+    pos = np.array([N * m - Q, 4 * 4000 - 2, 4 * 50 - 1], np.int64)
+    _compare(f"multi-query HI={HI} Q={Q}", kc, ks, qc, qs, pos, m, k)
+
+
+def test_multi_query_scan_ties():
+    """Coarse keys (many equal scores) with 4 queries per sequence, and all-zero keys (every score
+    ties: more candidates than the sort buffer)."""
+    rng = np.random.default_rng(57)
+    B, Q, N, m, k = 2, 4, 12000, 4, 1000
+    kc, ks, qc, qs = _fp4_inputs(rng, B, Q, N, 4, coarse=True)
+    pos = np.array([N * m - Q, 4 * 3000], np.int64)
+    _compare("multi-query ties", kc, ks, qc, qs, pos, m, k)
+    kz = np.zeros_like(kc)
+    kzs = np.full_like(ks, 127)
+    _compare("multi-query all-equal", kz, kzs, qc, qs, pos, m, k)
+    gi, _ = _run(kz, kzs, qc, qs, pos, m, k)
+    assert (gi[0] == np.arange(k)).all()
+
+
 def test_multi_query_decode_1m_five_drafts():
     """Speculative verification: 5 query tokens per sequence at the end of a 1M context
     (positions L-5 .. L-1), 262,144 FP4 keys, top-1024 each; every query on the oracle."""

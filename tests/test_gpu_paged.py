@@ -51,6 +51,17 @@ def test_index_decode_page_sizes(P):
     _check_index("decode", kc, ks, qc, qs, pos, m, k, P, seed=P)
 
 
+@pytest.mark.parametrize("P", [4, 128])
+def test_index_multi_query_page_sizes(P):
+    """5 queries per sequence (one MFMA pass over paged keys, scores stored)."""
+    rng = np.random.default_rng(70 + P)
+    B, Q, N, m, k = 2, 5, 20000, 4, 256
+    kc, ks = O.encode_rows(rng.normal(size=(B, N, 128)), O.FMT_FP4_E8M0)
+    qc, qs = O.encode_rows(rng.normal(size=(B, Q, 4, 128)), O.FMT_FP4_E8M0)
+    pos = np.array([N * m - Q, 4 * 9000 - 3], np.int64)
+    _check_index("multi-query", kc, ks, qc, qs, pos, m, k, P, seed=P)
+
+
 @pytest.mark.parametrize("P", [8, 256])
 def test_index_prefill_schedule_page_sizes(P):
     """40 queries per sequence (the scaled-FP4-MFMA schedule); P = 8 shrinks the key ranges to
