@@ -258,27 +258,32 @@ template <int BINS>
 __device__ void find_threshold_bin(const uint32_t* __restrict__ gh, int64_t kk, uint32_t* h,
                                    uint32_t* suf, uint32_t* out_bin, uint32_t* out_above) {
   constexpr int PER = BINS / 256;
+  __shared__ uint32_t wave_total[4];
   // threads >= 256 only take part in the barriers
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63;
+  uint32_t v = 0;
   if (t < 256) {
-    uint32_t local = 0;
 #pragma unroll
     for (int j = 0; j < PER; j++) {
       const uint32_t c = gh[t * PER + j];
       h[t * PER + j] = c;
-      local += c;
+      v += c;
     }
-    suf[t] = local;
+  }
+  // inclusive suffix sum over the 256 groups: within each wavefront by shuffles, then across the
+  // four wavefronts through LDS
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_down((int)v, o, 64);
+    if (lane + o < 64) v += y;
+  }
+  if (t < 256 && lane == 0) wave_total[t >> 6] = v;
+  __syncthreads();
+  if (t < 256) {
+    for (int w = (t >> 6) + 1; w < 4; w++) v += wave_total[w];
+    suf[t] = v;
   }
   __syncthreads();
-  // inclusive suffix sum over the 256 groups (Hillis-Steele)
-  for (int o = 1; o < 256; o <<= 1) {
-    uint32_t add = 0;
-    if (t < 256) add = (t + o < 256) ? suf[t + o] : 0u;
-    __syncthreads();
-    if (t < 256) suf[t] += add;
-    __syncthreads();
-  }
   if (t < 256) {
     const uint32_t mine = suf[t];
     const uint32_t next = t < 255 ? suf[t + 1] : 0u;

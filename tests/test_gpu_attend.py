@@ -136,6 +136,21 @@ def test_head_count_not_multiple_of_16_fp32_rows():
     assert_close(o, ro, "H=20 out")
 
 
+@pytest.mark.parametrize("H", [40, 80])
+def test_bf16_head_counts_not_multiple_of_64(H):
+    """bf16 queries on E4M3 rows take the shared-tile kernel, which works on blocks of 64 heads:
+    a partial first block (40) and a full block plus a partial one (80), CSA and HCA."""
+    c = DecodeCase("csa128k", B=2, N=700, H=H, Q=2, pos=[4 * 700 - 2, 1000])
+    say(f"[attend] H={H} bf16 queries")
+    idx = _idx_random(c.B, 2, c.N, 300, 8 + H)
+    o, l, ro, rl = _csa(c, idx)
+    assert_close(o, ro, f"csa H={H} out")
+    assert_close(l, rl, f"csa H={H} lse")
+    o, l, ro, rl = _hca(c, 4)
+    assert_close(o, ro, f"hca H={H} out")
+    assert_close(l, rl, f"hca H={H} lse")
+
+
 def test_fp32_query_on_e4m3_rows():
     c = DecodeCase("csa128k", B=2, N=400, H=32)
     c.q = torch.from_numpy(c.q.view(np.int16)).view(torch.bfloat16).float().numpy() * 1.25
