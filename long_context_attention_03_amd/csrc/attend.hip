@@ -471,18 +471,18 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttendK p) {
 // ================================================================================================
 // E4M3 + bf16 rows (D = 512) with bf16 queries: workgroups that share converted row tiles.
 //
-// A workgroup of 8 wavefronts owns one (query, row split, block of 64 heads). Wavefront w works on
-// row stream w/4 and head group w%4 (16 heads). The two streams take alternate 32-row tiles of the
-// split. The 256 threads of a stream load each tile once: thread t takes row t/8, bytes 64i+8(t%8)
-// (i < 7) of the E4M3 part and 448+16(t%8) of the bf16 part, so every load instruction reads
-// 64 contiguous bytes per row. The tile is converted exactly to bf16 and stored row-major (1056-byte
-// LDS rows, the stride measured conflict-free for both read patterns) in a double-buffered tile
-// that the stream's four head groups share: 16-byte reads give the A-fragments of S^T = Y Q^T, the
-// transposing read gives the Y^T fragments of O^T += Y^T P^T, as in attend_kernel. One workgroup
-// barrier per tile orders the buffer reuse (a buffer is rewritten two tiles later, after every
-// wavefront has passed the barrier of the tile in between). The next tile's loads are issued after
-// the S^T phase and land during the softmax and P.Y phases. At the end the two streams' (max, sum,
-// accumulator) states are merged in LDS.
+// A workgroup of 4 wavefronts owns one (query, row split, block of 64 heads); wavefront w takes
+// head group w (16 heads). The 256 threads load each 32-row tile once: thread t takes row t/8,
+// bytes 64i+8(t%8) (i < 7) of the E4M3 part and 448+16(t%8) of the bf16 part, so every load
+// instruction reads 64 contiguous bytes per row. The tile is converted exactly to bf16 and stored
+// row-major (1056-byte LDS rows, the stride measured conflict-free for both read patterns) in a
+// double-buffered tile that the four head groups share: 16-byte reads give the A-fragments of
+// S^T = Y Q^T, the transposing read gives the Y^T fragments of O^T += Y^T P^T, as in
+// attend_kernel. One workgroup barrier per tile orders the buffer reuse (a buffer is rewritten two
+// tiles later, after every wavefront has passed the barrier of the tile in between). The next
+// tile's loads are issued after the S^T phase and land during the softmax and P.Y phases. Two
+// workgroups share a CU (LDS 67.6 KB, 256 registers per lane each), so one's barrier and softmax
+// waits overlap the other's matrix work.
 constexpr int kXTile = 32, kXRS = 528, kXTileElems = kXTile * kXRS;
 
 struct TileRawX {
@@ -490,17 +490,16 @@ struct TileRawX {
   u32x4 r;     // bf16 dims 448 + 8(t%8) .. +8
 };
 
-template <bool DENSE, int NS, bool PAGED>
-__global__ __launch_bounds__(256 * NS, 3 - NS) void attend_x_kernel(AttendK p) {
+template <bool DENSE, bool PAGED>
+__global__ __launch_bounds__(256, 2) void attend_x_kernel(AttendK p) {
   constexpr int D = 512, NCH = 16, NT = 32, RB = 576;
-  __shared__ __attribute__((aligned(16))) __bf16 ytile[NS][2][kXTileElems];  // [stream][buffer]
-  __shared__ uint32_t s_mask[NS][2][4];  // [stream][buffer][head group]: 8 row bits each
-  __shared__ float s_ml[4][16][2];
+  __shared__ __attribute__((aligned(16))) __bf16 ytile[2][kXTileElems];  // double buffer
+  __shared__ uint32_t s_mask[2][4];  // [buffer][loading wavefront]: 8 row bits each
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int st = NS == 1 ? 0 : wave >> 2, hgl = wave & 3;
+  const int hgl = wave;  // head group
   const int g = lane >> 4, n = lane & 15;
-  const int lrow = (tid & 255) >> 3, lk = tid & 7;  // the tile row this thread loads, its slot
+  const int lrow = tid >> 3, lk = tid & 7;  // the tile row this thread loads, its slot
   // Workgroups are dispatched round-robin over the 8 XCDs; consecutive workgroups of one XCD take
   // the head blocks of one (query, split) unit so that its rows are fetched into one L2.
   const int64_t wg = blockIdx.x;
@@ -539,7 +538,7 @@ __global__ __launch_bounds__(256 * NS, 3 - NS) void attend_x_kernel(AttendK p) {
   const uint8_t* dummy = p.N > 0 ? p.cache + (PAGED ? p.cmap.paged(b, 0) : p.cmap.flat(b, 0)) * RB
                                  : p.win + (int64_t)b * p.wstride * RB;
   const int ntiles = r1 > r0 ? (int)((r1 - r0 + kXTile - 1) / kXTile) : 0;
-  const int iters = (ntiles + NS - 1) / NS;
+  const int iters = ntiles;
 
   // entry id of this thread's row in the tile starting at tbase (CSA only)
   auto fetch_id = [&](int64_t tbase) -> int32_t {
@@ -612,22 +611,22 @@ __global__ __launch_bounds__(256 * NS, 3 - NS) void attend_x_kernel(AttendK p) {
   int32_t e_next = -1;   // contiguous: id of this thread's row in the next tile; paged: two ahead
   int64_t prow_next = -1;  // paged: pool row of this thread's row in the next tile
   if (iters > 0) {
-    const int64_t t0 = r0 + (int64_t)st * kXTile;
+    const int64_t t0 = r0;
     const int32_t e0 = fetch_id(t0);
     if constexpr (PAGED) {
-      const int32_t e1 = fetch_id(t0 + NS * kXTile);
-      e_next = fetch_id(t0 + 2 * NS * kXTile);
+      const int32_t e1 = fetch_id(t0 + kXTile);
+      e_next = fetch_id(t0 + 2 * kXTile);
       const int64_t prow0 = pool_row(t0 + lrow, e0);
-      prow_next = pool_row(t0 + NS * kXTile + lrow, e1);
+      prow_next = pool_row(t0 + kXTile + lrow, e1);
       load_rows(resolve_row(t0 + lrow, prow0, v_raw), raw);
     } else {
-      e_next = fetch_id(t0 + NS * kXTile);
+      e_next = fetch_id(t0 + kXTile);
       load_rows(resolve(t0 + lrow, e0, v_raw), raw);
     }
   }
   for (int it = 0; it < iters; it++) {
     const int buf = it & 1;
-    __bf16* yt = &ytile[st][buf][0];
+    __bf16* yt = &ytile[buf][0];
     {
       // convert and store this thread's share of the tile (masked rows become zeros)
       __bf16* dst = yt + lrow * kXRS;
@@ -650,12 +649,12 @@ __global__ __launch_bounds__(256 * NS, 3 - NS) void attend_x_kernel(AttendK p) {
         uint32_t m8 = 0;
 #pragma unroll
         for (int r = 0; r < 8; r++) m8 |= (uint32_t)((ball >> (8 * r)) & 1u) << r;
-        s_mask[st][buf][hgl] = m8;
+        s_mask[buf][hgl] = m8;
       }
     }
     __syncthreads();
-    const uint32_t mask = s_mask[st][buf][0] | (s_mask[st][buf][1] << 8) |
-                          (s_mask[st][buf][2] << 16) | (s_mask[st][buf][3] << 24);
+    const uint32_t mask = s_mask[buf][0] | (s_mask[buf][1] << 8) | (s_mask[buf][2] << 16) |
+                          (s_mask[buf][3] << 24);
     f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
     if (mask != 0u) {
       // S^T for rows tb..tb+15 (S0) and tb+16..tb+31 (S1)
@@ -667,17 +666,17 @@ __global__ __launch_bounds__(256 * NS, 3 - NS) void attend_x_kernel(AttendK p) {
         S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[c], S1, 0, 0, 0);
       }
     }
-    // the next tile of this stream: issue its loads now (and fetch the ids of the one after)
+    // the next tile: issue its loads now (and fetch the ids of the one after)
     v_raw = false;
     if (it + 1 < iters) {
-      const int64_t tn = r0 + (int64_t)(NS * (it + 1) + st) * kXTile;
+      const int64_t tn = r0 + (int64_t)(it + 1) * kXTile;
       if constexpr (PAGED) {
-        const int32_t e_after = fetch_id(tn + 2 * NS * kXTile);
+        const int32_t e_after = fetch_id(tn + 2 * kXTile);
         load_rows(resolve_row(tn + lrow, prow_next, v_raw), raw);
-        prow_next = pool_row(tn + NS * kXTile + lrow, e_next);
+        prow_next = pool_row(tn + kXTile + lrow, e_next);
         e_next = e_after;
       } else {
-        const int32_t e_after = fetch_id(tn + NS * kXTile);
+        const int32_t e_after = fetch_id(tn + kXTile);
         load_rows(resolve(tn + lrow, e_next, v_raw), raw);
         e_next = e_after;
       }
@@ -738,37 +737,11 @@ __global__ __launch_bounds__(256 * NS, 3 - NS) void attend_x_kernel(AttendK p) {
     }
   }
 
-  // ---- merge the streams, then write the output or this split's partial ----
+  // ---- write the output or this split's partial ----
   l_run += shfl_xor_f(l_run, 16);
   l_run += shfl_xor_f(l_run, 32);
-  constexpr int CS = D + 4;
-  static_assert(NS == 1 || 4 * 16 * CS * 4 <= (int)sizeof(ytile), "merge buffer fits the tiles");
-  float* comb = (float*)&ytile[0][0][0];  // [head group][16 heads][CS]
-  float m1 = -INFINITY, l1 = 0.0f;
-  if constexpr (NS == 2) {
-    __syncthreads();
-    if (st == 1) {
-#pragma unroll
-      for (int t = 0; t < NT; t++) *(f32x4*)(comb + (hgl * 16 + n) * CS + 16 * t + 4 * g) = O[t];
-      if (g == 0) {
-        s_ml[hgl][n][0] = m_run;
-        s_ml[hgl][n][1] = l_run;
-      }
-    }
-    __syncthreads();
-    m1 = s_ml[hgl][n][0];
-    l1 = s_ml[hgl][n][1];
-  }
-  if (st == 0 && head < p.H) {
-    const float M = fmaxf(m_run, m1);
-    const float w0 = m_run == -INFINITY ? 0.0f : exp2f(m_run - M);
-    const float w1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - M);
-    const float L = l_run * w0 + l1 * w1;
-    const float* cb = comb + (hgl * 16 + n) * CS + 4 * g;
-    auto combined = [&](int t) -> f32x4 {
-      if constexpr (NS == 2) return O[t] * w0 + *(const f32x4*)(cb + 16 * t) * w1;
-      else return O[t] * w0;
-    };
+  if (head < p.H) {
+    const float M = m_run, L = l_run;
     if (p.splits == 1) {
       float Mf = M, den = L, a = 1.0f;
       if (p.sink) {
@@ -780,14 +753,14 @@ __global__ __launch_bounds__(256 * NS, 3 - NS) void attend_x_kernel(AttendK p) {
       const float so = den > 0.0f ? a / den : 0.0f;
       float* op = p.out + ((int64_t)slot * p.H + head) * D + 4 * g;
 #pragma unroll
-      for (int t = 0; t < NT; t++) *(f32x4*)(op + 16 * t) = combined(t) * so;
+      for (int t = 0; t < NT; t++) *(f32x4*)(op + 16 * t) = O[t] * so;
       if (p.lse && g == 0)
         p.lse[(int64_t)slot * p.H + head] = den > 0.0f ? (Mf + log2f(den)) * kLn2 : -INFINITY;
     } else {
       // partial row: acc[D], max, sum, 2 pad floats (16-byte aligned rows)
       float* pp = p.part + (((int64_t)slot * p.splits + split) * p.H + head) * (D + 4);
 #pragma unroll
-      for (int t = 0; t < NT; t++) *(f32x4*)(pp + 16 * t + 4 * g) = combined(t);
+      for (int t = 0; t < NT; t++) *(f32x4*)(pp + 16 * t + 4 * g) = O[t];
       if (g == 0) {
         pp[D] = M;
         pp[D + 1] = L;
@@ -885,17 +858,15 @@ AttendPlan attend_plan(int B, int Q, int H, int D, int64_t max_rows) {
   return pl;
 }
 
-// attend_x_kernel: workgroups of 8 wavefronts over one block of 64 heads, two tiles per step;
-// one workgroup per CU, so about 256 of them.
-constexpr int kXStreams = 1;
+// attend_x_kernel: workgroups of 4 wavefronts over one block of 64 heads, two per CU (their LDS
+// and registers), so about 512 of them.
 static AttendPlan attend_x_plan(int B, int Q, int H, int64_t max_rows) {
   const int hb = (H + 63) / 64;
   const int64_t base = (int64_t)B * Q * hb;
   // each split writes a 64-head partial as large as 7 rows of input: with 16 or more queries
   // in flight, longer splits (fewer partials) win; with fewer, short splits keep the GPU busy
-  const int min_tiles = (base >= 16 ? 4 : 2) * kXStreams;
-  AttendPlan pl = make_plan(base, (max_rows + kXTile - 1) / kXTile, kXStreams == 1 ? 512 : 256,
-                            min_tiles);
+  const int min_tiles = base >= 16 ? 4 : 2;
+  AttendPlan pl = make_plan(base, (max_rows + kXTile - 1) / kXTile, 512, min_tiles);
   pl.head_groups = hb;
   return pl;
 }
@@ -955,13 +926,13 @@ hipError_t launch_attend(const AttendArgs& a) {
   dim3 grid((unsigned)(((units + 7) / 8) * per_round));
   hipError_t e;
   if (shared_tiles) {
-    const dim3 blk(256 * kXStreams);
+    const dim3 blk(256);
     if (a.cmap.table) {
-      if (a.idx) a.prof.launch(attend_x_kernel<false, kXStreams, true>, grid, blk, s, k);
-      else a.prof.launch(attend_x_kernel<true, kXStreams, true>, grid, blk, s, k);
+      if (a.idx) a.prof.launch(attend_x_kernel<false, true>, grid, blk, s, k);
+      else a.prof.launch(attend_x_kernel<true, true>, grid, blk, s, k);
     } else {
-      if (a.idx) a.prof.launch(attend_x_kernel<false, kXStreams, false>, grid, blk, s, k);
-      else a.prof.launch(attend_x_kernel<true, kXStreams, false>, grid, blk, s, k);
+      if (a.idx) a.prof.launch(attend_x_kernel<false, false>, grid, blk, s, k);
+      else a.prof.launch(attend_x_kernel<true, false>, grid, blk, s, k);
     }
     e = hipGetLastError();
   } else if (a.fmt == CSAH_FMT_ROW_E4M3_BF16)
