@@ -87,7 +87,9 @@ int64_t csah_row_bytes(int fmt, int D);
  * out_rows  [B][out_seq_stride] rows of out_fmt; entry g of sequence b is written to row
  *           b*out_seq_stride + g (point it at the cache's append position). out_seq_stride >= T/m.
  * out_scales FP4_E8M0 only: [B][out_seq_stride][D/32] scale bytes (NULL otherwise).
- * Supported: D % 64 == 0, 64 <= D <= 1024; D == 512 for ROW_E4M3_BF16; 1 <= m <= 65536.
+ * A call that writes no entry (B = 0 or T = 0) returns CSAH_OK after checking the scalar
+ * arguments and touches no buffer; its pointers may then be NULL.
+ * Supported: D in {64, 128, 256, 512, 1024}; D == 512 for ROW_E4M3_BF16; 1 <= m <= 65536.
  */
 int csah_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B, int64_t T,
                      int D, int m, const float* w, const float* beta, void* out_rows, int out_fmt,

@@ -98,8 +98,7 @@ static int kv_compress_impl(const void* raw, int raw_dtype, int64_t raw_seq_stri
                             const float* beta, void* out_rows, int out_fmt, EntryMap out_map,
                             int64_t first_entry, int64_t out_capacity, uint8_t* out_scales,
                             void* stream, ProfileHook prof) {
-  if (!raw || !w || !beta || !out_rows || B < 0 || T < 0 || D <= 0 || m <= 0)
-    return CSAH_ERR_INVALID_ARGUMENT;
+  if (B < 0 || T < 0 || D <= 0 || m <= 0) return CSAH_ERR_INVALID_ARGUMENT;
   if (raw_dtype != CSAH_DT_F32 && raw_dtype != CSAH_DT_BF16) return CSAH_ERR_INVALID_ARGUMENT;
   if (out_fmt != CSAH_FMT_ROW_F32 && out_fmt != CSAH_FMT_ROW_E4M3_BF16 &&
       out_fmt != CSAH_FMT_FP4_E8M0)
@@ -107,6 +106,8 @@ static int kv_compress_impl(const void* raw, int raw_dtype, int64_t raw_seq_stri
   if (T % m != 0 || span < m || skip < 0 || skip > T / m || raw_seq_stride < T ||
       out_capacity < T / m - skip)
     return CSAH_ERR_INVALID_ARGUMENT;
+  if (B == 0 || T / m - skip == 0) return CSAH_OK;  // no entry to write: nothing is touched
+  if (!raw || !w || !beta || !out_rows) return CSAH_ERR_INVALID_ARGUMENT;
   if ((out_fmt == CSAH_FMT_FP4_E8M0) != (out_scales != nullptr)) return CSAH_ERR_INVALID_ARGUMENT;
   if (!aligned(raw, 16) || !aligned(out_rows, 16)) return CSAH_ERR_INVALID_ARGUMENT;
   if (D != 64 && D != 128 && D != 256 && D != 512 && D != 1024) return CSAH_ERR_UNSUPPORTED;

@@ -78,6 +78,16 @@ def test_kv_compress_rejects_bad_arguments():
     assert f(FAKE, 0, 8, 1, 8, 96, 4, FAKE, FAKE, FAKE, 0, 2, None, None) == L.UNSUPPORTED
 
 
+def test_kv_compress_without_entries_touches_nothing():
+    """No complete group (T = 0) or no sequence (B = 0): OK without a device, NULL pointers
+    allowed; the scalar arguments are still checked."""
+    f = L.lib().csah_kv_compress
+    assert f(None, 0, 8, 1, 0, 512, 4, None, None, None, 1, 0, None, None) == L.OK
+    assert f(None, 0, 8, 0, 8, 512, 4, None, None, None, 1, 2, None, None) == L.OK
+    assert f(None, 0, 8, 1, 0, 512, 0, None, None, None, 1, 0, None, None) == L.INVALID_ARGUMENT
+    assert f(None, 7, 8, 1, 0, 512, 4, None, None, None, 1, 0, None, None) == L.INVALID_ARGUMENT
+
+
 def test_kv_compress_span_rejects_bad_arguments():
     f = L.lib().csah_kv_compress_span
     # span shorter than the stride

@@ -253,3 +253,32 @@ def test_multi_query_decode_1m_five_drafts():
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy(), ro, f"{name} Q=5 out")
         assert_close(lse.cpu().numpy(), rl, f"{name} Q=5 lse")
+
+
+def test_empty_cache_window_only_and_no_groups():
+    """N = 0 compressed entries (the cache pointer still valid): HCA attention is the window and
+    the sink alone, CSA with every slot empty equals it, the indexer returns only -1; and a
+    compression call with no complete group writes nothing."""
+    c = DecodeCase("csa128k", B=2, N=8, pos=[40, 500])
+    say("[attend] empty cache")
+    q, cache, win, pos, sink = c.gpu("q", "cache", "window", "pos", "sink")
+    o, l = L.hca_attend(q, cache, 4, win, c.wl.w, pos, sink, c.scale, N=0)
+    idx = torch.full((c.B, 1, 16), -1, dtype=torch.int32, device="cuda")
+    o2, l2 = L.csa_attend(q, cache, idx, win, c.wl.w, pos, sink, c.scale, N=0)
+    torch.cuda.synchronize()
+    ro, rl = O.hca_attend(c.q, c.cache, c.fmt, 4, c.window, c.wl.w, c.pos, c.sink, c.scale, N=0)
+    assert_close(o.cpu().numpy(), ro, "window-only out")
+    assert_close(l.cpu().numpy(), rl, "window-only lse")
+    assert_close(o2.cpu().numpy(), ro, "csa, all slots empty, out")
+    # indexer over no entries
+    gi, gs = L.index_topk(dev(c.qc), dev(c.qs), dev(c.kc), dev(c.ks), pos, 4, 32, N=0)
+    torch.cuda.synchronize()
+    assert (gi.cpu() == -1).all() and torch.isneginf(gs.cpu()).all()
+    # compression of a buffer with no complete group leaves the output untouched
+    x = torch.zeros((1, 8, 512), dtype=torch.bfloat16, device="cuda")
+    rows = torch.full((1, 4, 576), 0xAB, dtype=torch.uint8, device="cuda")
+    w = torch.zeros(512, device="cuda")
+    b = torch.zeros(4, device="cuda")
+    L.kv_compress(x[:, :0], 4, w, b, L.FMT_ROW_E4M3_BF16, out_rows=rows[:, 1:2])
+    torch.cuda.synchronize()
+    assert (rows.cpu() == 0xAB).all()
