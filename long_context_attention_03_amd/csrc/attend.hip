@@ -331,10 +331,18 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttendK p) {
     if (mask != 0u) {
       // online softmax (base 2); lane holds rows 4g+i (S0) and 16+4g+i (S1) of head n
       float v[8];
+      if (mask == 0xFFFFFFFFu) {  // every row valid (all but the edge tiles)
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        v[i] = ((mask >> (4 * g + i)) & 1u) ? S0[i] * p.scale_log2 : -INFINITY;
-        v[4 + i] = ((mask >> (16 + 4 * g + i)) & 1u) ? S1[i] * p.scale_log2 : -INFINITY;
+        for (int i = 0; i < 4; i++) {
+          v[i] = S0[i] * p.scale_log2;
+          v[4 + i] = S1[i] * p.scale_log2;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          v[i] = ((mask >> (4 * g + i)) & 1u) ? S0[i] * p.scale_log2 : -INFINITY;
+          v[4 + i] = ((mask >> (16 + 4 * g + i)) & 1u) ? S1[i] * p.scale_log2 : -INFINITY;
+        }
       }
       float tmax = v[0];
 #pragma unroll
@@ -356,7 +364,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttendK p) {
       float P[8], psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        P[i] = exp2f(v[i] - m_run);
+        P[i] = __builtin_amdgcn_exp2f(v[i] - m_run);  // v - m_run <= 8; -inf gives 0
         psum += P[i];
       }
       l_run += psum;
@@ -684,10 +692,18 @@ __global__ __launch_bounds__(256, 2) void attend_x_kernel(AttendK p) {
     if (mask != 0u) {
       // online softmax (base 2); lane holds rows 4g+i (S0) and 16+4g+i (S1) of head n
       float v[8];
+      if (mask == 0xFFFFFFFFu) {  // every row valid (all but the edge tiles)
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        v[i] = ((mask >> (4 * g + i)) & 1u) ? S0[i] * p.scale_log2 : -INFINITY;
-        v[4 + i] = ((mask >> (16 + 4 * g + i)) & 1u) ? S1[i] * p.scale_log2 : -INFINITY;
+        for (int i = 0; i < 4; i++) {
+          v[i] = S0[i] * p.scale_log2;
+          v[4 + i] = S1[i] * p.scale_log2;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          v[i] = ((mask >> (4 * g + i)) & 1u) ? S0[i] * p.scale_log2 : -INFINITY;
+          v[4 + i] = ((mask >> (16 + 4 * g + i)) & 1u) ? S1[i] * p.scale_log2 : -INFINITY;
+        }
       }
       float tmax = v[0];
 #pragma unroll
@@ -708,7 +724,7 @@ __global__ __launch_bounds__(256, 2) void attend_x_kernel(AttendK p) {
       float P[8], psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        P[i] = exp2f(v[i] - m_run);
+        P[i] = __builtin_amdgcn_exp2f(v[i] - m_run);  // v - m_run <= 8; -inf gives 0
         psum += P[i];
       }
       l_run += psum;
