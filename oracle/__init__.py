@@ -70,6 +70,9 @@ def lib():
             "oc_kv_compress": (I, [P, I, I64, I, I64, I, I, P, P, P, I, I64, P, P, P]),
             "oc_kv_compress_span": (I, [P, I, I64, I, I64, I, I, I, I64, P, P, P, I, I64, P, P,
                                         P]),
+            "oc_kv_compress_rope": (I, [P, I, I64, I, I64, I, I, I, I64, P, P, P, I, I64, P, P,
+                                        I, D, P, P]),
+            "oc_rope": (I, [P, I, I, I, I, I, I, P, D, I, P]),
             "oc_index_topk": (I, [P, P, I, I, P, P, I64, I64, P, I, I, I, I, P, P, P]),
             "oc_index_scores": (I, [P, P, I, I, P, P, I64, P, P]),
             "oc_csa_attend": (I, [P, I, I, I, P, I, I64, I64, P, I, P, I64, I, P, P, D, I, I, P, P]),
@@ -178,11 +181,14 @@ def decode_rows(rows, D: int, fmt: int, scales=None):
 
 # ------------------------------------------------------------------------------------ method
 def kv_compress(raw, raw_dtype: int, m: int, w, beta, out_fmt: int, span: int | None = None,
-                skip: int = 0):
+                skip: int = 0, tok_pos=None, rope_dims: int = 0, rope_base: float = 10000.0):
     """raw [B, T, D] (float32, or uint16 bf16 bits) -> dict(rows, scales, pre, pi).
 
     span (default m) tokens per entry at stride m; the first `skip` groups are context only.
-    pi is [B, T/m - skip, span] (0 for tokens before the buffer)."""
+    pi is [B, T/m - skip, span] (0 for tokens before the buffer).
+    rope_dims > 0: the last rope_dims dims of each pooled entry are turned by RoPE at the position
+    of its group's last token, tok_pos[b] + m(g+1) - 1 (tok_pos[b]: position of raw[b, 0]); pre
+    then holds the rotated values."""
     raw = _c(raw, np.float32 if raw_dtype == DT_F32 else np.uint16)
     B, T, D = raw.shape
     span = m if span is None else span
@@ -193,10 +199,33 @@ def kv_compress(raw, raw_dtype: int, m: int, w, beta, out_fmt: int, span: int | 
     scales = np.zeros((B, G, D // 32), np.uint8) if out_fmt == FMT_FP4_E8M0 else None
     pre = np.zeros((B, G, D), np.float64)
     pi = np.zeros((B, G, span), np.float64)
-    _check(lib().oc_kv_compress_span(_p(raw), raw_dtype, T, B, T, D, m, span, skip, _p(w),
-                                     _p(beta), _p(rows), out_fmt, G, _p(scales), _p(pre),
-                                     _p(pi)), "kv_compress")
+    if rope_dims:
+        tp = _c(tok_pos, np.int64)
+        _check(lib().oc_kv_compress_rope(_p(raw), raw_dtype, T, B, T, D, m, span, skip, _p(w),
+                                         _p(beta), _p(rows), out_fmt, G, _p(scales), _p(tp),
+                                         rope_dims, float(rope_base), _p(pre), _p(pi)),
+               "kv_compress_rope")
+    else:
+        _check(lib().oc_kv_compress_span(_p(raw), raw_dtype, T, B, T, D, m, span, skip, _p(w),
+                                         _p(beta), _p(rows), out_fmt, G, _p(scales), _p(pre),
+                                         _p(pi)), "kv_compress")
     return dict(rows=rows, scales=scales, pre=pre, pi=pi)
+
+
+def rope(x, pos, rope_dims: int, base: float = 10000.0, inverse: bool = False):
+    """RoPE of rows x [B, Q, H, D] (float32, or uint16 bf16 bits) -> fp64 [B, Q, H, D].
+
+    Row (b, i, h) sits at position pos[b] + i; its last rope_dims dims turn (inverse: turn back)
+    as RoFormer's general form prescribes (see oc_rope)."""
+    x = np.ascontiguousarray(x)
+    dt = DT_F32 if x.dtype == np.float32 else DT_BF16
+    x = _c(x, np.float32 if dt == DT_F32 else np.uint16)
+    B, Q, H, D = x.shape
+    pos = _c(pos, np.int64)
+    out = np.zeros((B, Q, H, D), np.float64)
+    _check(lib().oc_rope(_p(x), dt, B, Q, H, D, rope_dims, _p(pos), float(base), int(inverse),
+                         _p(out)), "rope")
+    return out
 
 
 def index_topk(q_codes, q_scales, k_codes, k_scales, pos, m: int, k: int, N: int | None = None):

@@ -34,6 +34,8 @@
  *   R10 the window is the w tokens [p-w+1, p] that have position >= 0.
  *   R12 the sink is one logit per head that enters the softmax denominator only.
  *   R13 the sparse / dense entries, the window and the sink share one softmax.
+ *   R25 RoPE follows RoFormer's general form on the last R dims; a compressed entry sits at the
+ *       position of the last token of its group (see oc_rope, oc_kv_compress_rope).
  */
 #include <math.h>
 #include <stdint.h>
@@ -282,12 +284,64 @@ static double load_elem(const void* base, int dtype, int64_t i) {
  * indexed by the token's place in the span, 0 .. span-1. span = m is the non-overlapping case.
  * The first `skip` groups only provide context: their entries are neither computed nor written,
  * and entry g (g >= skip) goes to output row g - skip. */
-int oc_kv_compress_span(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B, int64_t T,
-                        int D, int m, int span, int64_t skip, const float* w, const float* beta,
-                        unsigned char* out_rows, int out_fmt, int64_t out_seq_stride,
-                        unsigned char* out_scales, double* pre_out, double* pi_out) {
+/* ------------------------------------------------------------------------------------------ */
+/* RoPE on the rotary dims of one row (reading R25).                                            */
+/* [BSWEN] "Component 1: Shared Key-Value Vectors": keys and values are one shared vector and   */
+/* an inverse RoPE restores its positional information; [EXPL] "Architecture at a glance":      */
+/* each row keeps its rotary dims in BF16. The pages do not define the rotation. The definition */
+/* used is RoFormer's (Su et al., "RoFormer: Enhanced Transformer with Rotary Position          */
+/* Embedding", section 3.2, general form): the last R dims of the row form R/2 adjacent pairs   */
+/* (2j, 2j+1), and at position p pair j turns counter-clockwise by the angle p * theta_j,       */
+/* theta_j = base^(-2j/R):                                                                      */
+/*   (a, b) -> (a cos(p theta_j) - b sin(p theta_j),  a sin(p theta_j) + b cos(p theta_j)).    */
+/* The inverse turns each pair back by the same angle.                                          */
+/* ------------------------------------------------------------------------------------------ */
+static void rope_row(double* v, int D, int R, double p, double base, int inverse) {
+    for (int j = 0; j < R / 2; j++) {
+        double ang = p * pow(base, -2.0 * j / R);
+        if (inverse) ang = -ang;
+        double c = cos(ang), s = sin(ang);
+        double* a = v + (D - R) + 2 * j;
+        double x0 = a[0], x1 = a[1];
+        a[0] = x0 * c - x1 * s;
+        a[1] = x0 * s + x1 * c;
+    }
+}
+
+/* x: [B][Q][H][D] (F32 or BF16); row (b, i, h) is at position pos[b] + i (the position rule of  */
+/* the queries everywhere on the path). out: fp64 [B][Q][H][D], the rotated rows.               */
+int oc_rope(const void* x, int dtype, int B, int Q, int H, int D, int R, const int64_t* pos,
+            double base, int inverse, double* out) {
+    if (!x || !pos || !out || B < 0 || Q < 0 || H <= 0 || D <= 0 || R < 2 || R % 2 || R > D ||
+        !(base > 0.0) || isinf(base))
+        return OC_EINVAL;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; b++) {
+        for (int i = 0; i < Q; i++) {
+            for (int h = 0; h < H; h++) {
+                int64_t r = (((int64_t)b * Q + i) * H + h) * D;
+                for (int d = 0; d < D; d++) out[r + d] = load_elem(x, dtype, r + d);
+                rope_row(out + r, D, R, (double)(pos[b] + i), base, inverse);
+            }
+        }
+    }
+    return OC_OK;
+}
+
+/* Compression with RoPE (reading R25): the pooled entry c_g is rotated before it is encoded, at
+ * the position of the last token of its group, tok_pos[b] + m(g+1) - 1 when raw's token 0 of
+ * sequence b sits at tok_pos[b]. That is the token with which the group completes and the entry
+ * becomes visible (R9), and it does not depend on the span. R = 0: no rotation. */
+static int kv_compress_core(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B,
+                            int64_t T, int D, int m, int span, int64_t skip, const float* w,
+                            const float* beta, unsigned char* out_rows, int out_fmt,
+                            int64_t out_seq_stride, unsigned char* out_scales,
+                            const int64_t* tok_pos, int R, double base, double* pre_out,
+                            double* pi_out) {
     if (!raw || !w || !beta || !out_rows || B <= 0 || T < 0 || D <= 0 || m <= 0 || T % m ||
         span < m || skip < 0 || skip > T / m)
+        return OC_EINVAL;
+    if (R != 0 && (!tok_pos || R < 2 || R % 2 || R > D || !(base > 0.0) || isinf(base)))
         return OC_EINVAL;
     if (out_fmt == OC_FMT_FP4_E8M0 && (D % 32 || !out_scales)) return OC_EINVAL;
     if (out_fmt == OC_FMT_ROW_E4M3_BF16 && D < 64) return OC_EINVAL;
@@ -321,6 +375,7 @@ int oc_kv_compress_span(const void* raw, int raw_dtype, int64_t raw_seq_stride, 
                     if (first + j >= 0) s += z[j] * x[(int64_t)j * D + d];
                 c[d] = s;
             }
+            if (R) rope_row(c, D, R, (double)(tok_pos[b] + m * (g + 1) - 1), base, 0);
             int64_t orow = (int64_t)b * out_seq_stride + go;
             encode_row(c, out_fmt, D, out_rows + orow * rb,
                        out_fmt == OC_FMT_FP4_E8M0 ? out_scales + orow * (D / 32) : NULL);
@@ -330,6 +385,26 @@ int oc_kv_compress_span(const void* raw, int raw_dtype, int64_t raw_seq_stride, 
         }
     }
     return OC_OK;
+}
+
+int oc_kv_compress_span(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B, int64_t T,
+                        int D, int m, int span, int64_t skip, const float* w, const float* beta,
+                        unsigned char* out_rows, int out_fmt, int64_t out_seq_stride,
+                        unsigned char* out_scales, double* pre_out, double* pi_out) {
+    return kv_compress_core(raw, raw_dtype, raw_seq_stride, B, T, D, m, span, skip, w, beta,
+                            out_rows, out_fmt, out_seq_stride, out_scales, NULL, 0, 0.0, pre_out,
+                            pi_out);
+}
+
+int oc_kv_compress_rope(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B, int64_t T,
+                        int D, int m, int span, int64_t skip, const float* w, const float* beta,
+                        unsigned char* out_rows, int out_fmt, int64_t out_seq_stride,
+                        unsigned char* out_scales, const int64_t* tok_pos, int R, double base,
+                        double* pre_out, double* pi_out) {
+    if (R == 0) return OC_EINVAL;
+    return kv_compress_core(raw, raw_dtype, raw_seq_stride, B, T, D, m, span, skip, w, beta,
+                            out_rows, out_fmt, out_seq_stride, out_scales, tok_pos, R, base,
+                            pre_out, pi_out);
 }
 
 int oc_kv_compress(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B, int64_t T, int D,
