@@ -485,6 +485,45 @@ PF_N_HCA = N_HCA + PF_Q // 128      # 8,224
 PF_PEAK_BF16, PF_PEAK_FP4 = 2.5e15, 10.1e15
 
 
+def hooked_us(fn, reps: int):
+    """Average duration (us) of the dominant kernel of the library call fn(), from events attached
+    to its dispatch."""
+    evs = []
+    for _ in range(reps):
+        e = event_pair()
+        L.profile_next_call(*e)
+        fn()
+        evs.append(e)
+    torch.cuda.synchronize()
+    return statistics.mean(a.elapsed_time(b) for a, b in evs) * 1e3
+
+
+def rope_decode_measure(ws: DecodeStep, reps: int):
+    """RoPE at the decode step's sizes: the 16 queries' rotary dims (64 of 512, 64 heads, bf16),
+    the inverse on the f32 attention output, and the newest CSA group's compression with and
+    without RoPE."""
+    c = ws.csa
+    q_us = hooked_us(lambda: L.rope(c["q"], ws.pos, 64), reps)
+    o_us = hooked_us(lambda: L.rope(c["out"], ws.pos, 64, inverse=True), reps)
+    tok = ws.pos - 3  # the group's first token: its last token is the current position
+    comp = lambda: L.kv_compress(c["xt"], 4, ws.w_csa, ws.b_csa, L.FMT_ROW_E4M3_BF16,
+                                 out_rows=c["cache"][:, N_CSA - 1:])
+    comp_r = lambda: L.kv_compress_rope(c["xt"], 4, ws.w_csa, ws.b_csa, L.FMT_ROW_E4M3_BF16, tok,
+                                        64, out_rows=c["cache"][:, N_CSA - 1:])
+    cp_us, cr_us = hooked_us(comp, reps), hooked_us(comp_r, reps)
+    qb, ob = B_STEP * H * 64 * 2 * 2, B_STEP * H * 64 * 4 * 2
+    log(f"  RoPE at decode (us): queries {q_us:.2f}, output inverse {o_us:.2f}, "
+        f"compress m=4 {cp_us:.2f} -> with RoPE {cr_us:.2f}")
+    return {
+        "what": "RoPE at the decode step's sizes: 16 queries x 64 heads, the last 64 of 512 dims "
+                "(bf16, turned forward), the f32 attention output (turned back), and the newest "
+                "group's m=4 compression with RoPE at the group's last token",
+        "q_rope_us": q_us, "q_rope_bytes": qb,
+        "out_inverse_us": o_us, "out_inverse_bytes": ob,
+        "compress_m4_us": cp_us, "compress_m4_rope_us": cr_us,
+    }
+
+
 class PrefillStep:
     """One prefill chunk through one CSA and one HCA layer.
 
@@ -618,6 +657,26 @@ def prefill_measure(steps: int, warmup: int):
         span_ms.append(a.elapsed_time(e))
     span_bytes = (PF_Q + 4) * (D * 2 + DI * 4) + (PF_Q // 4) * (ROW + DI // 2 + DI // 32)
     t_span = statistics.median(span_ms[1:]) * 1e-3
+    # RoPE on the chunk: the 4096 queries' rotary dims (bf16), the inverse on the f32 output, and
+    # the chunk's m=4 compression with and without RoPE
+    reps = max(2, steps)
+    rq = hooked_us(lambda: L.rope(ps.q, ps.pos, 64), reps)
+    ro = hooked_us(lambda: L.rope(ps.out, ps.pos, 64, inverse=True), reps)
+    rc = hooked_us(lambda: L.kv_compress(ps.x, 4, ps.w_csa, ps.b_csa, L.FMT_ROW_E4M3_BF16,
+                                         out_rows=ps.cache[:, N_CSA:]), reps)
+    rcr = hooked_us(lambda: L.kv_compress_rope(ps.x, 4, ps.w_csa, ps.b_csa, L.FMT_ROW_E4M3_BF16,
+                                               ps.pos, 64, out_rows=ps.cache[:, N_CSA:]), reps)
+    qb, ob = PF_Q * H * 64 * 2 * 2, PF_Q * H * 64 * 4 * 2
+    log(f"  RoPE on the chunk (us): queries {rq:.1f} ({qb / rq / 1e3:.0f} GB/s), output inverse "
+        f"{ro:.1f} ({ob / ro / 1e3:.0f} GB/s), compress m=4 {rc:.1f} -> with RoPE {rcr:.1f}")
+    rope = {
+        "what": "RoPE on the chunk: 4096 queries x 64 heads, the last 64 of 512 dims (bf16, "
+                "turned forward), the f32 attention output (turned back), and the chunk's m=4 "
+                "compression with RoPE; bytes = the rotary dims read and written",
+        "q_rope_us": rq, "q_rope_bytes": qb, "q_rope_GBps": qb / rq / 1e3,
+        "out_inverse_us": ro, "out_inverse_bytes": ob, "out_inverse_GBps": ob / ro / 1e3,
+        "compress_m4_us": rc, "compress_m4_rope_us": rcr,
+    }
     kernels = {}
     for k, (fl, peak, dt) in ops.items():
         t = kt[k] * 1e-3
@@ -642,6 +701,7 @@ def prefill_measure(steps: int, warmup: int):
             "us": t_span * 1e6, "algorithmic_bytes": span_bytes,
             "achieved_GBps": span_bytes / t_span / 1e9,
         },
+        "rope": rope,
     }
 
 
@@ -765,6 +825,7 @@ def main():
         }
     if not args.no_csa4:
         line["csa_decode_1m_b4_paged"] = paged_measure(ws, args, ms4)
+    line["rope_decode"] = rope_decode_measure(ws, args.kernel_reps)
     if not args.no_prefill:
         log("prefill chunk (4096 tokens on a 1M cache)...")
         del ws, graph, g4

@@ -261,9 +261,67 @@ int csah_hca_attend_paged(const void* q, int q_dtype, int H, int D, const void* 
                           size_t ws_bytes, void* stream);
 
 /*
+ * RoPE on the rotary dims.
+ *   [BSWEN] "Component 1: Shared Key-Value Vectors": keys and values are one shared vector, and an
+ *   inverse RoPE restores its positional information; [EXPL] "Key numbers" (KV storage precision
+ *   row): a row's rotary dims are its BF16 part. The pages define neither the rotation nor its
+ *   frequencies; the library uses RoFormer's general form (Su et al., "RoFormer: Enhanced
+ *   Transformer with Rotary Position Embedding", section 3.2): the LAST R = rope_dims dims of a
+ *   D-wide row form R/2 adjacent pairs (2j, 2j+1), and at position p pair j turns
+ *   counter-clockwise by p * theta_j, theta_j = rope_base^(-2j/R):
+ *     (a, b) -> (a cos - b sin, a sin + b cos);   the inverse turns back by the same angle.
+ *   Angles, sines and cosines are computed in fp64, so positions of 2^20 and beyond keep their
+ *   accuracy. The use on the path: queries are turned at their positions before attention, each
+ *   compressed entry when it is written (csah_kv_compress_rope), and the attention output is
+ *   turned back at the query's position (inverse), which leaves every value's rotary part turned
+ *   by the entry's position relative to the query.
+ *   Constraints: D even, R even, 2 <= R <= D, rope_base finite and > 0, else
+ *   CSAH_ERR_INVALID_ARGUMENT.
+ */
+
+/*
+ * csah_rope -- turn the rotary dims of rows x [B][Q][H][D] in place. Row group (b, i) (all H
+ * heads) sits at position pos[b] + i (the queries' position rule of every call above).
+ * x         device array of dtype CSAH_DT_BF16 or CSAH_DT_F32, 16-byte aligned, contiguous.
+ *           bf16 rows are rounded once from the fp64 result (nearest, ties to even), f32 rows
+ *           likewise. Dims before D - R are not read or written.
+ * pos       [B] int64 device array, 8-byte aligned.
+ * inverse   0: turn forward; 1: turn back (the inverse RoPE of the attention output).
+ * Returns CSAH_OK without touching anything when B = 0 or Q = 0; CSAH_ERR_UNSUPPORTED for
+ * R > 1024 or B*Q > 2^31 - 1.
+ */
+int csah_rope(void* x, int dtype, int B, int Q, int H, int D, int rope_dims, const int64_t* pos,
+              double rope_base, int inverse, void* stream);
+
+/*
+ * csah_kv_compress_rope -- csah_kv_compress_span whose pooled entries are turned by RoPE before
+ * they are encoded. The entry of group g of raw (g counted from raw's token 0, context groups
+ * included) sits at the position of the group's last token, tok_pos[b] + m(g+1) - 1: the token
+ * that completes the group and makes the entry visible, whatever the span.
+ * tok_pos   [B] int64 device array (8-byte aligned): position of raw's token 0 of each sequence.
+ * rope_dims must be nonzero; other arguments and statuses as csah_kv_compress_span.
+ */
+int csah_kv_compress_rope(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B,
+                          int64_t T, int D, int m, int span, int64_t skip, const float* w,
+                          const float* beta, void* out_rows, int out_fmt, int64_t out_seq_stride,
+                          uint8_t* out_scales, const int64_t* tok_pos, int rope_dims,
+                          double rope_base, void* stream);
+
+/*
+ * csah_kv_compress_paged_rope -- csah_kv_compress_paged with the RoPE of csah_kv_compress_rope.
+ */
+int csah_kv_compress_paged_rope(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B,
+                                int64_t T, int D, int m, int span, int64_t skip, const float* w,
+                                const float* beta, void* out_pool, int out_fmt,
+                                uint8_t* out_scale_pool, const int32_t* block_table,
+                                int64_t table_stride, int page_size, int64_t first_entry,
+                                const int64_t* tok_pos, int rope_dims, double rope_base,
+                                void* stream);
+
+/*
  * csah_profile_next_call -- profiling aid (not part of the method). The next compression,
- * indexer or attention call (any of the calls above) made by the SAME host thread launches
- * its dominant kernel (the compressor; the indexer scan; the attention kernel) with `begin` and
+ * indexer, attention or RoPE call (any of the calls above) made by the SAME host thread launches
+ * its dominant kernel (the compressor; the indexer scan; the attention kernel; the rotation) with `begin` and
  * `end` attached to that dispatch, so that hipEventElapsedTime(begin, end) is the kernel's own
  * duration. Both are hipEvent_t passed as void*, created by the caller with timing enabled; NULL
  * for both cancels a pending request. The request is consumed by that

@@ -34,6 +34,7 @@ EXPORTS = ("csah_abi_version", "csah_status_string", "csah_row_bytes", "csah_kv_
            "csah_index_topk_workspace", "csah_index_topk", "csah_attend_workspace",
            "csah_csa_attend", "csah_hca_attend", "csah_kv_compress_paged",
            "csah_index_topk_paged", "csah_csa_attend_paged", "csah_hca_attend_paged",
+           "csah_rope", "csah_kv_compress_rope", "csah_kv_compress_paged_rope",
            "csah_profile_next_call")
 
 _lib = None
@@ -55,6 +56,7 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, I, I64, F, SZ = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
                             ctypes.c_size_t)
+        D = ctypes.c_double
         sig = {
             "csah_abi_version": (I, []),
             "csah_status_string": (ctypes.c_char_p, [I]),
@@ -77,6 +79,11 @@ def lib():
                                           P, F, I, I, P, P, P, SZ, P]),
             "csah_hca_attend_paged": (I, [P, I, I, I, P, I, P, I64, I, I64, I, P, I64, I, P, P,
                                           F, I, I, P, P, P, SZ, P]),
+            "csah_rope": (I, [P, I, I, I, I, I, I, P, D, I, P]),
+            "csah_kv_compress_rope": (I, [P, I, I64, I, I64, I, I, I, I64, P, P, P, I, I64, P,
+                                          P, I, D, P]),
+            "csah_kv_compress_paged_rope": (I, [P, I, I64, I, I64, I, I, I, I64, P, P, P, I, P,
+                                                P, I64, I, I64, P, I, D, P]),
             "csah_profile_next_call": (I, [P, P]),
         }
         for name, (res, args) in sig.items():
@@ -336,3 +343,53 @@ def hca_attend_paged(q, cache_pool, block_table, page_size: int, N: int, m: int,
                                      _ptr(lse), _ptr(ws), need, _stream(stream))
     _check("csah_hca_attend_paged", st)
     return out, lse
+
+
+# ----------------------------------------------------------------------------- RoPE
+def rope(x, pos, rope_dims: int = 64, base: float = 10000.0, inverse: bool = False, stream=None):
+    """Turn the last ``rope_dims`` dims of rows x [B, Q, H, D] (bfloat16 or float32, contiguous)
+    in place: row group (b, i) at position pos[b] + i; ``inverse`` turns back. Returns x."""
+    if not x.is_contiguous():
+        raise ValueError("rope needs a contiguous [B, Q, H, D] tensor")
+    B, Q, H, D = x.shape
+    st = lib().csah_rope(_ptr(x), _dt(x), B, Q, H, D, rope_dims, _ptr(pos), float(base),
+                         int(bool(inverse)), _stream(stream))
+    _check("csah_rope", st)
+    return x
+
+
+def kv_compress_rope(raw, m: int, w, beta, out_fmt: int, tok_pos, rope_dims: int = 64,
+                     rope_base: float = 10000.0, out_rows=None, out_scales=None,
+                     span: int | None = None, skip: int = 0, stream=None):
+    """kv_compress whose pooled entries are turned by RoPE before encoding: the entry of raw's
+    group g sits at tok_pos[b] + m(g+1) - 1 (tok_pos [B] int64: position of raw[b, 0])."""
+    B, T, D = raw.shape
+    G = T // m - skip
+    if out_rows is None:
+        out_rows = torch.empty((B, G, row_bytes(out_fmt, D)), dtype=torch.uint8, device=raw.device)
+        if out_fmt == FMT_FP4_E8M0:
+            out_scales = torch.empty((B, G, D // 32), dtype=torch.uint8, device=raw.device)
+    st = lib().csah_kv_compress_rope(_ptr(raw), _dt(raw), raw.stride(0) // raw.stride(1), B, T,
+                                     D, m, m if span is None else span, skip, _ptr(w),
+                                     _ptr(beta), _ptr(out_rows), out_fmt,
+                                     out_rows.stride(0) // out_rows.stride(1), _ptr(out_scales),
+                                     _ptr(tok_pos), rope_dims, float(rope_base), _stream(stream))
+    _check("csah_kv_compress_rope", st)
+    return out_rows, out_scales
+
+
+def kv_compress_paged_rope(raw, m: int, w, beta, out_fmt: int, pool, block_table,
+                           page_size: int, tok_pos, rope_dims: int = 64,
+                           rope_base: float = 10000.0, first_entry: int = 0, scale_pool=None,
+                           span: int | None = None, skip: int = 0, stream=None):
+    """kv_compress_paged with the RoPE of kv_compress_rope. Returns (pool, scale_pool)."""
+    B, T, D = raw.shape
+    tp, ts = _table(block_table)
+    st = lib().csah_kv_compress_paged_rope(_ptr(raw), _dt(raw), raw.stride(0) // raw.stride(1),
+                                           B, T, D, m, m if span is None else span, skip,
+                                           _ptr(w), _ptr(beta), _ptr(pool), out_fmt,
+                                           _ptr(scale_pool), tp, ts, page_size, first_entry,
+                                           _ptr(tok_pos), rope_dims, float(rope_base),
+                                           _stream(stream))
+    _check("csah_kv_compress_paged_rope", st)
+    return pool, scale_pool

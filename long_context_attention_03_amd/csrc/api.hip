@@ -1,5 +1,7 @@
 // api.hip -- the C ABI declared in include/csah.h: argument validation, workspace sizing, device
 // check and kernel launches. Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <stdint.h>
 #include <string.h>
 
 #include <mutex>
@@ -59,6 +61,12 @@ int paged_map(const int32_t* table, int64_t table_stride, int page_size, EntryMa
 
 EntryMap contiguous_map(int64_t seq_stride) { return EntryMap{nullptr, seq_stride, 0}; }
 
+// RoPE widths: an even number of rotary dims 2 <= R <= D, D even (pairs stay aligned), and a
+// finite positive base.
+bool rope_shape_ok(int D, int R, double base) {
+  return D % 2 == 0 && R >= 2 && R % 2 == 0 && R <= D && base > 0.0 && base < INFINITY;
+}
+
 int row_bytes(int fmt, int D) {
   if (fmt == CSAH_FMT_ROW_F32) return 4 * D;
   if (fmt == CSAH_FMT_ROW_E4M3_BF16) return D >= 64 ? D + 64 : -1;
@@ -97,8 +105,10 @@ static int kv_compress_impl(const void* raw, int raw_dtype, int64_t raw_seq_stri
                             int64_t T, int D, int m, int span, int64_t skip, const float* w,
                             const float* beta, void* out_rows, int out_fmt, EntryMap out_map,
                             int64_t first_entry, int64_t out_capacity, uint8_t* out_scales,
-                            void* stream, ProfileHook prof) {
+                            void* stream, ProfileHook prof, const int64_t* tok_pos = nullptr,
+                            int rope_dims = 0, double rope_base = 0.0) {
   if (B < 0 || T < 0 || D <= 0 || m <= 0) return CSAH_ERR_INVALID_ARGUMENT;
+  if (rope_dims != 0 && !rope_shape_ok(D, rope_dims, rope_base)) return CSAH_ERR_INVALID_ARGUMENT;
   if (raw_dtype != CSAH_DT_F32 && raw_dtype != CSAH_DT_BF16) return CSAH_ERR_INVALID_ARGUMENT;
   if (out_fmt != CSAH_FMT_ROW_F32 && out_fmt != CSAH_FMT_ROW_E4M3_BF16 &&
       out_fmt != CSAH_FMT_FP4_E8M0)
@@ -113,11 +123,15 @@ static int kv_compress_impl(const void* raw, int raw_dtype, int64_t raw_seq_stri
   if (D != 64 && D != 128 && D != 256 && D != 512 && D != 1024) return CSAH_ERR_UNSUPPORTED;
   if (out_fmt == CSAH_FMT_ROW_E4M3_BF16 && D != 512) return CSAH_ERR_UNSUPPORTED;
   if (span > 65536) return CSAH_ERR_UNSUPPORTED;
+  if (rope_dims != 0 && (!tok_pos || !aligned(tok_pos, 8))) return CSAH_ERR_INVALID_ARGUMENT;
   int st = check_device();
   if (st) return st;
   KvCompressArgs a{raw,  raw_dtype, raw_seq_stride, B,       T / m - skip, D,          m,
                    span, skip,      w,              beta,    out_rows,     out_fmt,    out_map,
                    first_entry,     out_scales,     stream,  prof};
+  a.tok_pos = tok_pos;
+  a.rope_dims = rope_dims;
+  a.rope_base = rope_base;
   return launch_status(launch_kv_compress(a));
 }
 
@@ -155,6 +169,54 @@ int csah_kv_compress_paged(const void* raw, int raw_dtype, int64_t raw_seq_strid
   return kv_compress_impl(raw, raw_dtype, raw_seq_stride, B, T, D, m, span, skip, w, beta,
                           out_pool, out_fmt, map, first_entry, cap - first_entry, out_scale_pool,
                           stream, prof);
+}
+
+int csah_kv_compress_rope(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B,
+                          int64_t T, int D, int m, int span, int64_t skip, const float* w,
+                          const float* beta, void* out_rows, int out_fmt, int64_t out_seq_stride,
+                          uint8_t* out_scales, const int64_t* tok_pos, int rope_dims,
+                          double rope_base, void* stream) {
+  const ProfileHook prof = take_profile();
+  if (rope_dims == 0) return CSAH_ERR_INVALID_ARGUMENT;
+  return kv_compress_impl(raw, raw_dtype, raw_seq_stride, B, T, D, m, span, skip, w, beta,
+                          out_rows, out_fmt, contiguous_map(out_seq_stride), 0, out_seq_stride,
+                          out_scales, stream, prof, tok_pos, rope_dims, rope_base);
+}
+
+int csah_kv_compress_paged_rope(const void* raw, int raw_dtype, int64_t raw_seq_stride, int B,
+                                int64_t T, int D, int m, int span, int64_t skip, const float* w,
+                                const float* beta, void* out_pool, int out_fmt,
+                                uint8_t* out_scale_pool, const int32_t* block_table,
+                                int64_t table_stride, int page_size, int64_t first_entry,
+                                const int64_t* tok_pos, int rope_dims, double rope_base,
+                                void* stream) {
+  const ProfileHook prof = take_profile();
+  if (rope_dims == 0) return CSAH_ERR_INVALID_ARGUMENT;
+  EntryMap map;
+  int64_t cap;
+  const int st = paged_map(block_table, table_stride, page_size, map, cap);
+  if (st) return st;
+  if (first_entry < 0 || first_entry > cap) return CSAH_ERR_INVALID_ARGUMENT;
+  return kv_compress_impl(raw, raw_dtype, raw_seq_stride, B, T, D, m, span, skip, w, beta,
+                          out_pool, out_fmt, map, first_entry, cap - first_entry, out_scale_pool,
+                          stream, prof, tok_pos, rope_dims, rope_base);
+}
+
+int csah_rope(void* x, int dtype, int B, int Q, int H, int D, int rope_dims, const int64_t* pos,
+              double rope_base, int inverse, void* stream) {
+  const ProfileHook prof = take_profile();
+  if (B < 0 || Q < 0 || H <= 0 || D <= 0 || (inverse != 0 && inverse != 1))
+    return CSAH_ERR_INVALID_ARGUMENT;
+  if (dtype != CSAH_DT_F32 && dtype != CSAH_DT_BF16) return CSAH_ERR_INVALID_ARGUMENT;
+  if (!rope_shape_ok(D, rope_dims, rope_base)) return CSAH_ERR_INVALID_ARGUMENT;
+  if (rope_dims > 2 * kRopeMaxPairs) return CSAH_ERR_UNSUPPORTED;
+  if ((int64_t)B * Q > INT32_MAX) return CSAH_ERR_UNSUPPORTED;
+  if (B == 0 || Q == 0) return CSAH_OK;  // no row: nothing is touched
+  if (!x || !pos || !aligned(x, 16) || !aligned(pos, 8)) return CSAH_ERR_INVALID_ARGUMENT;
+  int st = check_device();
+  if (st) return st;
+  RopeArgs a{x, dtype, B, Q, H, D, rope_dims, pos, rope_base, inverse, stream, prof};
+  return launch_status(launch_rope(a));
 }
 
 size_t csah_index_topk_workspace(int B, int Q, int64_t N, int k, int HI, int dI) {

@@ -15,7 +15,8 @@
 // groups take one wavefront each; long groups (m > 16) take a workgroup whose 4 wavefronts pool
 // a quarter of the tokens each and merge their states in LDS. The pooled row is encoded in the
 // output format and written with vector stores. HBM traffic is one read of the raw rows and one
-// write of the compressed rows.
+// write of the compressed rows. With RoPE (csah_kv_compress_rope) the pooled row's rotary pairs
+// are turned in fp64 before encoding, at the position of the last token of the entry's group.
 #include "csah_internal.h"
 #include "device_common.h"
 
@@ -64,12 +65,13 @@ constexpr int kTokBatch = 8;  // tokens whose loads and gate reductions are in f
 // WAVES = 1: one wavefront per entry, 4 entries per workgroup (short spans).
 // WAVES = 4: one workgroup per entry; wavefront w pools a quarter of the span and the four
 //            online-softmax states (max, sum, weighted sum) are merged in LDS.
-template <int DPL, bool RAW_BF16, int OUT_FMT, int WAVES>
+template <int DPL, bool RAW_BF16, int OUT_FMT, int WAVES, bool ROPE>
 __global__ __launch_bounds__(256) void kv_compress_kernel(
     const void* __restrict__ raw, int64_t raw_seq_stride, int B, int64_t G, int m, int span,
     int64_t skip, const float* __restrict__ w, const float* __restrict__ beta,
     uint8_t* __restrict__ out_rows, EntryMap omap, int64_t first_entry,
-    uint8_t* __restrict__ out_scales) {
+    uint8_t* __restrict__ out_scales, const int64_t* __restrict__ tok_pos, int rope_dims,
+    double rope_base) {
   constexpr int D = DPL * 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t gid = WAVES == 1 ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
@@ -162,7 +164,42 @@ __global__ __launch_bounds__(256) void kv_compress_kernel(
   float c[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; e++) c[e] = acc[e] / L;
-
+  if constexpr (ROPE) {
+    // RoPE before encoding: the rotary pairs (the last rope_dims dims) turn, in fp64, by the
+    // position of the last token of the entry's group. Lane l computes the (cos, sin) of pair
+    // jb + l of each round of 64 pairs, and the lanes holding a pair fetch them by shuffles, so a
+    // wavefront waits for one sine and cosine per round instead of one per pair it holds.
+    const double p = (double)(tok_pos[b] + (int64_t)m * (g + skip + 1) - 1);
+    const int r0 = D - rope_dims;  // even, so a pair never straddles two lanes when DPL >= 2
+    const int np = rope_dims / 2;
+    float other = 0.0f;
+    if constexpr (DPL == 1) other = __shfl_xor(c[0], 1, 64);  // the pair's other dim
+    for (int jb = 0; jb < np; jb += 64) {  // uniform: every lane takes part in the shuffles
+      double cl = 1.0, sl = 0.0;
+      if (jb + lane < np) rope_cos_sin(p, jb + lane, rope_dims, rope_base, false, cl, sl);
+      if constexpr (DPL == 1) {
+        const int src = ((lane - r0) >> 1) - jb;
+        const double cs = __shfl(cl, src & 63, 64), sn = __shfl(sl, src & 63, 64);
+        if (lane >= r0 && src >= 0 && src < 64) {
+          const bool odd = lane & 1;
+          const double x0 = odd ? other : c[0], x1 = odd ? c[0] : other;
+          c[0] = (float)(odd ? x0 * sn + x1 * cs : x0 * cs - x1 * sn);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < DPL; e += 2) {
+          const int d = lane * DPL + e;
+          const int src = ((d - r0) >> 1) - jb;
+          const double cs = __shfl(cl, src & 63, 64), sn = __shfl(sl, src & 63, 64);
+          if (d >= r0 && src >= 0 && src < 64) {
+            const double x0 = c[e], x1 = c[e + 1];
+            c[e] = (float)(x0 * cs - x1 * sn);
+            c[e + 1] = (float)(x0 * sn + x1 * cs);
+          }
+        }
+      }
+    }
+  }
   const int64_t orow = omap.row((int)b, first_entry + g);
   if constexpr (OUT_FMT == CSAH_FMT_ROW_F32) {
     float* o = (float*)out_rows + orow * D + lane * DPL;
@@ -220,29 +257,32 @@ __global__ __launch_bounds__(256) void kv_compress_kernel(
   }
 }
 
-template <int DPL, bool RAW_BF16, int WAVES>
+template <int DPL, bool RAW_BF16, int WAVES, bool ROPE>
 static hipError_t launch_waves(const KvCompressArgs& a) {
   const int64_t groups = (int64_t)a.B * a.G;
   dim3 grid((unsigned)(WAVES == 1 ? (groups + 3) / 4 : groups)), block(256);
   hipStream_t s = (hipStream_t)a.stream;
   switch (a.out_fmt) {
     case CSAH_FMT_ROW_F32:
-      a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_F32, WAVES>, grid, block, s,
+      a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_F32, WAVES, ROPE>, grid, block, s,
           a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.span, a.skip, a.w, a.beta, (uint8_t*)a.out_rows,
-          a.out_map, a.first_entry, a.out_scales);
+          a.out_map, a.first_entry, a.out_scales, a.tok_pos, a.rope_dims,
+          a.rope_base);
       break;
     case CSAH_FMT_ROW_E4M3_BF16:
       if constexpr (DPL == 8)
-        a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_E4M3_BF16, WAVES>, grid, block, s,
+        a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_ROW_E4M3_BF16, WAVES, ROPE>, grid, block, s,
             a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.span, a.skip, a.w, a.beta, (uint8_t*)a.out_rows,
-            a.out_map, a.first_entry, a.out_scales);
+            a.out_map, a.first_entry, a.out_scales, a.tok_pos, a.rope_dims,
+          a.rope_base);
       else
         return hipErrorInvalidValue;
       break;
     default:
-      a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_FP4_E8M0, WAVES>, grid, block, s,
+      a.prof.launch(kv_compress_kernel<DPL, RAW_BF16, CSAH_FMT_FP4_E8M0, WAVES, ROPE>, grid, block, s,
           a.raw, a.raw_seq_stride, a.B, a.G, a.m, a.span, a.skip, a.w, a.beta, (uint8_t*)a.out_rows,
-          a.out_map, a.first_entry, a.out_scales);
+          a.out_map, a.first_entry, a.out_scales, a.tok_pos, a.rope_dims,
+          a.rope_base);
   }
   return hipGetLastError();
 }
@@ -250,8 +290,11 @@ static hipError_t launch_waves(const KvCompressArgs& a) {
 template <int DPL, bool RAW_BF16>
 static hipError_t launch_dpl(const KvCompressArgs& a) {
   // a whole workgroup per entry once the span is long enough to keep 4 wavefronts busy
-  return a.span > 2 * kTokBatch ? launch_waves<DPL, RAW_BF16, 4>(a)
-                                : launch_waves<DPL, RAW_BF16, 1>(a);
+  if (a.rope_dims > 0)
+    return a.span > 2 * kTokBatch ? launch_waves<DPL, RAW_BF16, 4, true>(a)
+                                  : launch_waves<DPL, RAW_BF16, 1, true>(a);
+  return a.span > 2 * kTokBatch ? launch_waves<DPL, RAW_BF16, 4, false>(a)
+                                : launch_waves<DPL, RAW_BF16, 1, false>(a);
 }
 
 template <bool RAW_BF16>

@@ -60,8 +60,27 @@ struct KvCompressArgs {
   uint8_t* out_scales;
   void* stream;
   ProfileHook prof;
+  // RoPE of the pooled entry before encoding (rope_dims = 0: none): the last rope_dims dims turn
+  // at the position of the group's last token, tok_pos[b] + m (group + 1) - 1
+  const int64_t* tok_pos = nullptr;
+  int rope_dims = 0;
+  double rope_base = 0.0;
 };
 hipError_t launch_kv_compress(const KvCompressArgs& a);
+
+// ---- rope --------------------------------------------------------------------------------------
+constexpr int kRopeMaxPairs = 512;  // rotary dims per row: at most 1024
+struct RopeArgs {
+  void* x;  // [B][Q][H][D] of dtype, turned in place
+  int dtype;
+  int B, Q, H, D, R;
+  const int64_t* pos;  // [B]: row group (b, i) sits at pos[b] + i
+  double base;
+  int inverse;
+  void* stream;
+  ProfileHook prof;
+};
+hipError_t launch_rope(const RopeArgs& a);
 
 // ---- index_topk --------------------------------------------------------------------------------
 struct IndexArgs {

@@ -105,4 +105,14 @@ __device__ __forceinline__ uint32_t f32_to_e2m1(float r) {
   return sign | code;
 }
 
+// RoPE angle of rotary pair j (of R/2) at position p, as (cos, sin) in fp64: RoFormer's general
+// form turns pair j by p * base^(-2j/R); the inverse turns it back. fp64 keeps the angle exact
+// enough at positions of 2^20 and beyond (fp32 would lose the angle to within 0.1 radian).
+__device__ __forceinline__ void rope_cos_sin(double p, int j, int R, double base, bool inverse,
+                                             double& c, double& s) {
+  double ang = p * pow(base, -2.0 * j / R);
+  if (inverse) ang = -ang;
+  sincos(ang, &s, &c);
+}
+
 }  // namespace csah

@@ -287,8 +287,9 @@ static double load_elem(const void* base, int dtype, int64_t i) {
 /* ------------------------------------------------------------------------------------------ */
 /* RoPE on the rotary dims of one row (reading R25).                                            */
 /* [BSWEN] "Component 1: Shared Key-Value Vectors": keys and values are one shared vector and   */
-/* an inverse RoPE restores its positional information; [EXPL] "Architecture at a glance":      */
-/* each row keeps its rotary dims in BF16. The pages do not define the rotation. The definition */
+/* an inverse RoPE restores its positional information; [EXPL] "Key numbers" (KV storage       */
+/* precision row): each row keeps its rotary dims in BF16. The pages do not define the          */
+/* rotation. The definition                                                                     */
 /* used is RoFormer's (Su et al., "RoFormer: Enhanced Transformer with Rotary Position          */
 /* Embedding", section 3.2, general form): the last R dims of the row form R/2 adjacent pairs   */
 /* (2j, 2j+1), and at position p pair j turns counter-clockwise by the angle p * theta_j,       */

@@ -195,3 +195,51 @@ def test_valid_call_without_gpu_reports_unsupported():
     g = L.lib().csah_kv_compress_paged
     assert g(FAKE, 0, 8, 1, 8, 128, 4, 4, 0, FAKE, FAKE, FAKE, 0, None, FAKE, 1, 2, 0,
              None) == L.UNSUPPORTED
+
+
+def test_rope_rejects_bad_arguments():
+    f = L.lib().csah_rope
+    ok = dict(x=FAKE, dt=1, B=2, Q=1, H=64, D=512, R=64, pos=FAKE, base=10000.0, inv=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["x"], a["dt"], a["B"], a["Q"], a["H"], a["D"], a["R"], a["pos"], a["base"],
+                 a["inv"], None)
+
+    assert call(R=63) == L.INVALID_ARGUMENT          # odd rotary width
+    assert call(R=0) == L.INVALID_ARGUMENT
+    assert call(R=514) == L.INVALID_ARGUMENT         # wider than the row
+    assert call(D=511, R=64) == L.INVALID_ARGUMENT   # odd row width
+    assert call(base=0.0) == L.INVALID_ARGUMENT
+    assert call(base=float("inf")) == L.INVALID_ARGUMENT
+    assert call(base=float("nan")) == L.INVALID_ARGUMENT
+    assert call(inv=2) == L.INVALID_ARGUMENT
+    assert call(dt=7) == L.INVALID_ARGUMENT
+    assert call(H=0) == L.INVALID_ARGUMENT
+    assert call(x=None) == L.INVALID_ARGUMENT
+    assert call(pos=None) == L.INVALID_ARGUMENT
+    assert call(x=ctypes.c_void_p(4100)) == L.INVALID_ARGUMENT  # misaligned rows
+    assert call(D=2048, R=1026) == L.UNSUPPORTED     # more than 1024 rotary dims
+    # no rows: nothing is touched, null pointers allowed
+    assert call(B=0, x=None, pos=None) == L.OK
+    assert call(Q=0, x=None, pos=None) == L.OK
+
+
+def test_kv_compress_rope_rejects_bad_arguments():
+    f = L.lib().csah_kv_compress_rope
+    g = L.lib().csah_kv_compress_paged_rope
+
+    def comp(R=64, base=10000.0, tok=FAKE, D=512, T=8, B=1):
+        return f(FAKE, 0, T, B, T, D, 4, 4, 0, FAKE, FAKE, FAKE, 1, 2, None, tok, R, base, None)
+
+    assert comp(R=0) == L.INVALID_ARGUMENT           # use csah_kv_compress_span instead
+    assert comp(R=63) == L.INVALID_ARGUMENT
+    assert comp(R=576) == L.INVALID_ARGUMENT
+    assert comp(base=-1.0) == L.INVALID_ARGUMENT
+    assert comp(tok=None) == L.INVALID_ARGUMENT
+    assert comp(tok=ctypes.c_void_p(4100)) == L.INVALID_ARGUMENT  # tok_pos not 8-byte aligned
+    assert comp(T=0, tok=None) == L.OK               # no entry written: nothing touched
+    assert g(FAKE, 0, 8, 1, 8, 512, 4, 4, 0, FAKE, FAKE, FAKE, 1, None, FAKE, 4, 3, 0, FAKE, 64,
+             10000.0, None) == L.INVALID_ARGUMENT  # page size not a power of two
+    assert g(FAKE, 0, 8, 1, 8, 512, 4, 4, 0, FAKE, FAKE, FAKE, 1, None, FAKE, 4, 4, 0, FAKE, 0,
+             10000.0, None) == L.INVALID_ARGUMENT  # no rotary dims
