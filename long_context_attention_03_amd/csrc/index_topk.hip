@@ -47,6 +47,9 @@ namespace csah {
 #endif
 constexpr int kBins = 4096;
 constexpr int kBinShift = 20;  // top 12 bits of the order key
+// Scores of the decode scan are staged in LDS and written out a window at a time: stores mixed
+// into the key stream cost about 10% of the scan's time, one burst per window much less.
+constexpr int kScoreStage = 8192;
 constexpr int kSortCap = 4096;
 
 struct IdxWs {
@@ -173,10 +176,13 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
   const int tid = threadIdx.x, sub = tid % NB;
   // wavefront w takes the STEP / 4 consecutive entries [w * EPW * U, ...) of each step, group u
   // the EPW entries from u * EPW on (lane q * NB + sub: entry q, block sub), so that after the
-  // quad reduction the wavefront can store its U * EPW scores as U / NB fully coalesced stores
+  // quad reduction the wavefront writes its U * EPW scores to consecutive words of the LDS stage
+  // (U / NB conflict-free writes), from which whole windows go out as 16-byte stores
   const int ent = (tid >> 6) * (EPW * U) + (tid & 63) / NB;
+  static_assert(kScoreStage % (2 * STEP) == 0, "a stage window holds whole loop iterations");
   __shared__ uint32_t hist[kBins];
   __shared__ int32_t pages[PAGED ? kPageList : 1];
+  __shared__ float stage[kScoreStage];
   for (int j = tid; j < kBins; j += 256) hist[j] = 0u;
 
   const int64_t nv = visible_entries(pos, b, i, m, N);
@@ -226,15 +232,25 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
         for (int t = 1; t < NB; t++) v = sub == t ? s[j * NB + t] : v;
         const int r = r0 + (j * NB + sub) * EPW + ent;
         if (r < n) {
-          sc[r] = v;
+          stage[r & (kScoreStage - 1)] = v;
           atomicAdd(&hist[order_key(v) >> kBinShift], 1u);
         }
       }
+    };
+    // scores [w0, w1) of the stage window go out as coalesced 16-byte stores
+    auto flush = [&](int w0, int w1) {
+      __syncthreads();
+      int j = w0 + 4 * tid;
+      for (; j + 4 <= w1; j += 1024)
+        *(f32x4*)(sc + j) = *(const f32x4*)(stage + (j & (kScoreStage - 1)));
+      for (; j < w1; j++) sc[j] = stage[j & (kScoreStage - 1)];
+      __syncthreads();
     };
     // double-buffered groups; full groups need no clamping (control flow is workgroup-uniform)
     u32x4 ca[U], cb[U];
     uint32_t ea[U], eb[U];
     load(0, ca, ea, STEP > n);
+    int flushed = 0;
     for (int r0 = 0; r0 < n; r0 += 2 * STEP) {
       const bool has_b = r0 + STEP < n;
       if (has_b) load(r0 + STEP, cb, eb, r0 + 2 * STEP > n);
@@ -242,7 +258,12 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
       if (!has_b) break;
       if (r0 + 2 * STEP < n) load(r0 + 2 * STEP, ca, ea, r0 + 3 * STEP > n);
       score(r0 + STEP, cb, eb);
+      if (((r0 + 2 * STEP) & (kScoreStage - 1)) == 0 && r0 + 2 * STEP < n) {
+        flush(flushed, r0 + 2 * STEP);  // a full window, while the next loads are in flight
+        flushed = r0 + 2 * STEP;
+      }
     }
+    flush(flushed, n);
   }
   __syncthreads();
   uint32_t* gh = ws.hist(slot);

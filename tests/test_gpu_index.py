@@ -41,6 +41,21 @@ def test_csa1m_full_size():
     _compare("csa1m full", c.kc, c.ks, c.qc, c.qs, c.pos, c.m, c.wl.k)
 
 
+def test_long_key_ranges_several_stage_windows():
+    """2 x (2^22 + 777) keys: each scan workgroup's range holds more than two 8192-score stage
+    windows (two full flushes and a partial one), the last range of each sequence is ragged, and
+    the second sequence sees 999 groups fewer. Codes and scales are random bytes (scales in a
+    narrow band keep every score exact)."""
+    rng = np.random.default_rng(12)
+    B, N, HI, dI, m, k = 2, (1 << 22) + 777, 4, 128, 4, 1024
+    kc = rng.integers(0, 256, size=(B, N, dI // 2), dtype=np.uint8)
+    ks = rng.integers(124, 129, size=(B, N, dI // 32), dtype=np.uint8)
+    qc = rng.integers(0, 256, size=(B, 1, HI, dI // 2), dtype=np.uint8)
+    qs = rng.integers(125, 128, size=(B, 1, HI, dI // 32), dtype=np.uint8)
+    pos = np.array([N * m - 1, N * m - 1 - m * 999], np.int64)
+    _compare("long ranges", kc, ks, qc, qs, pos, m, k)
+
+
 def test_ties_multi_query_causal_and_ragged():
     """Coarse keys (many equal scores), 3 queries per sequence with causal visibility, ragged N."""
     rng = np.random.default_rng(7)
