@@ -202,3 +202,66 @@ def gather_pages(pool: np.ndarray, table: np.ndarray, S: int) -> np.ndarray:
     P = pool.shape[1]
     out = pool[table.reshape(-1)].reshape((B, per * P) + pool.shape[2:])
     return out[:, :S]
+
+
+# ----------------------------------------------------------------------------- RoPE checks
+def oracle_bf16(v):
+    """bf16 bits of fp64 values v (any shape), rounded by the oracle's own row encoder: chunks of
+    64 values become the bf16 part of E4M3+bf16 rows."""
+    v = np.asarray(v, np.float64)
+    flat = v.reshape(-1)
+    n = flat.size
+    pad = (-n) % 64
+    chunks = np.concatenate([flat, np.zeros(pad)]).reshape(-1, 64)
+    rows = np.zeros((chunks.shape[0], 512))
+    rows[:, 448:] = chunks
+    enc, _ = O.encode_rows(rows, O.FMT_ROW_E4M3_BF16)
+    bits = enc[:, 448:].copy().view(np.uint16).reshape(-1)[:n]
+    return bits.reshape(v.shape)
+
+
+def angle_bound(x_values, pos, R):
+    """Per rotary element: (p + 1) 2^-48 (|a| + |b|) for its pair (a, b) of row (b, i) at
+    p = pos[b] + i; x_values [B, Q, H, D] are the values before turning."""
+    x = np.abs(np.asarray(x_values, np.float64))
+    B, Q, H, D = x.shape
+    p = (np.asarray(pos, np.float64)[:, None] + np.arange(Q)[None, :])[:, :, None, None]
+    size = x[..., D - R::2] + x[..., D - R + 1::2]
+    t = np.empty(x.shape[:-1] + (R,))
+    t[..., 0::2] = t[..., 1::2] = (np.abs(p) + 1.0) * 2.0 ** -48 * size
+    return t
+
+
+def check_bf16(got_bits, ref, tol, what):
+    """got_bits (uint16) must be the oracle's rounding of ref, except where ref lies within tol
+    of a midpoint between two bf16 neighbours."""
+    want = oracle_bf16(ref)
+    bad = np.nonzero(got_bits != want)
+    for idx in zip(*bad):
+        a = O.bf16_value(int(got_bits[idx]))
+        b = O.bf16_value(int(want[idx]))
+        assert abs(ref[idx] - 0.5 * (a + b)) <= tol[idx], (what, idx, ref[idx], a, b, tol[idx])
+    say(f"  {what}: {len(bad[0])} of {got_bits.size} bf16 values off the oracle's rounding "
+        f"(each within the angle bound of a midpoint)")
+
+
+def check_f32(got, ref, tol, what):
+    """got (f32) must lie within half a binary32 ulp of ref plus tol."""
+    half_ulp = 0.5 * np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    err = np.abs(got.astype(np.float64) - ref)
+    worst = float(np.max(err / (half_ulp + tol))) if got.size else 0.0
+    say(f"  {what}: max err / (half ulp + angle bound) = {worst:.3g} over {got.size} values")
+    assert worst <= 1.0 + 1e-6, what
+
+
+def rope_tolerance(tol, pre, D, R):
+    """Pooling bound of a rotated dim: the bounds of both dims of its pair (a rotation moves an
+    error of (e_a, e_b) by at most |e_a| + |e_b| per dim) plus the binary32 rounding of the
+    turned value (2^-23 of the pair's size)."""
+    t = np.array(tol, np.float64, copy=True)
+    a, b = t[..., D - R::2], t[..., D - R + 1::2]
+    size = np.abs(pre[..., D - R::2]) + np.abs(pre[..., D - R + 1::2])
+    pair = a + b + 2.0 ** -23 * size
+    t[..., D - R::2] = pair
+    t[..., D - R + 1::2] = pair
+    return t

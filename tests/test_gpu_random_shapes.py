@@ -8,8 +8,9 @@ import torch
 
 import long_context_attention_03_amd as L
 import oracle as O
-from helpers import (assert_close, check_rows_e4m3_bf16, check_rows_fp4, dev, paginate,
-                     pooling_tolerance, say)
+from helpers import (angle_bound, assert_close, check_bf16, check_f32, check_rows_e4m3_bf16,
+                     check_rows_fp4, dev, gather_pages, paginate, pooling_tolerance,
+                     rope_tolerance, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -134,3 +135,98 @@ def test_kv_compress_random(seed):
         check_rows_e4m3_bf16(rows, ref["rows"], ref["pre"], tol)
     else:
         check_rows_fp4(rows, sc.cpu().numpy(), ref["rows"], ref["scales"], ref["pre"], tol)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_rope_random(seed):
+    """csah_rope on random widths (vector and one-pair-per-thread kernels), heads, positions up
+    to 2^31, bases, both directions and both row types."""
+    rng = np.random.default_rng(4000 + seed)
+    B, Q, H = int(rng.integers(1, 4)), int(rng.integers(1, 7)), int(rng.integers(1, 70))
+    D = int(rng.choice([64, 96, 128, 200, 256, 512, 1024]))
+    R = 2 * int(rng.integers(1, D // 2 + 1))
+    if rng.random() < 0.5:
+        R = min(D, 8 * int(rng.integers(1, 9)))  # whole 16-byte vectors
+    bf16 = rng.random() < 0.6
+    base = float(rng.choice([10000.0, 500000.0, 1e6, 2.5]))
+    inverse = bool(rng.random() < 0.4)
+    pos = rng.integers(0, 2 ** 31 - 64, size=B).astype(np.int64)
+    if rng.random() < 0.5:
+        pos = rng.integers(0, 1 << 21, size=B).astype(np.int64)
+    say(f"[random rope] seed={seed} B={B} Q={Q} H={H} D={D} R={R} bf16={bf16} base={base} "
+        f"inverse={inverse}")
+    if bf16:
+        x_t, x_np = _bf16(rng, (B, Q, H, D))
+    else:
+        x_np = rng.normal(size=(B, Q, H, D)).astype(np.float32)
+        x_t = torch.from_numpy(x_np)
+    xg = x_t.cuda()
+    L.rope(xg, torch.from_numpy(pos).cuda(), R, base, inverse)
+    torch.cuda.synchronize()
+    out = xg.cpu()
+    ref = O.rope(x_np, pos, R, base, inverse)
+    tol = angle_bound(x_t.float().numpy(), pos, R)
+    if bf16:
+        got = out.view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got[..., :D - R], x_np[..., :D - R])
+        check_bf16(got[..., D - R:], ref[..., D - R:], tol, "rotary dims")
+    else:
+        got = out.numpy()
+        assert np.array_equal(got[..., :D - R], x_np[..., :D - R])
+        check_f32(got[..., D - R:], ref[..., D - R:], tol, "rotary dims")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_kv_compress_rope_random(seed):
+    """csah_kv_compress_rope / csah_kv_compress_paged_rope on random group sizes, spans, context
+    groups, widths, rotary widths, positions and formats."""
+    rng = np.random.default_rng(5000 + seed)
+    B = int(rng.integers(1, 4))
+    m = int(rng.choice([1, 2, 4, 8, 128]))
+    span = m * int(rng.choice([1, 1, 2]))
+    skip = int(rng.integers(0, 3)) if span > m else 0
+    G = int(rng.integers(1, 30))
+    T = (G + skip) * m
+    fmt = int(rng.choice([O.FMT_ROW_F32, O.FMT_ROW_E4M3_BF16, O.FMT_FP4_E8M0]))
+    D = 512 if fmt == O.FMT_ROW_E4M3_BF16 else int(rng.choice([64, 128, 256, 512, 1024]))
+    R = 64 if fmt == O.FMT_ROW_E4M3_BF16 and rng.random() < 0.6 else 2 * int(rng.integers(1, D // 2 + 1))
+    base = float(rng.choice([10000.0, 1e6]))
+    tok = rng.integers(0, 1 << 22, size=B).astype(np.int64)
+    paged = rng.random() < 0.3
+    say(f"[random compress rope] seed={seed} B={B} T={T} D={D} m={m} span={span} skip={skip} "
+        f"fmt={fmt} R={R} paged={paged}")
+    w = rng.normal(0, 0.05, D).astype(np.float32)
+    beta = rng.normal(0, 0.3, span).astype(np.float32)
+    xf = rng.normal(size=(B, T, D)).astype(np.float32)
+    ref = O.kv_compress(xf, O.DT_F32, m, w, beta, fmt, span=span, skip=skip, tok_pos=tok,
+                        rope_dims=R, rope_base=base)
+    x_g, tok_g = torch.from_numpy(xf).cuda(), torch.from_numpy(tok).cuda()
+    if paged:
+        P = int(rng.choice([1, 4, 16]))
+        rb = L.row_bytes(fmt, D)
+        empty = np.zeros((B, G, rb), np.uint8)
+        pool, table = paginate(empty, P, rng)
+        spool = None
+        if fmt == O.FMT_FP4_E8M0:  # the scale pool shares the block table
+            spool = dev(np.zeros((pool.shape[0], P, D // 32), np.uint8))
+        pool_g = dev(pool)
+        L.kv_compress_paged_rope(x_g, m, dev(w), dev(beta), fmt, pool_g, dev(table), P, tok_g, R,
+                                 base, scale_pool=spool, span=span if span > m else None,
+                                 skip=skip)
+        torch.cuda.synchronize()
+        rows = gather_pages(pool_g.cpu().numpy(), table, G)
+        sc = None if spool is None else gather_pages(spool.cpu().numpy(), table, G)
+    else:
+        rows_t, sc_t = L.kv_compress_rope(x_g, m, dev(w), dev(beta), fmt, tok_g, R, base,
+                                          span=span if span > m else None, skip=skip)
+        torch.cuda.synchronize()
+        rows, sc = rows_t.cpu().numpy(), None if sc_t is None else sc_t.cpu().numpy()
+    tol = rope_tolerance(pooling_tolerance(xf, m, ref["pre"], span=span, skip=skip), ref["pre"],
+                         D, R)
+    if fmt == O.FMT_ROW_F32:
+        got = rows.view(np.float32).reshape(ref["pre"].shape)
+        assert_close(got, ref["pre"], "pooled and turned", atol=1e-4, rtol=1e-4)
+    elif fmt == O.FMT_ROW_E4M3_BF16:
+        check_rows_e4m3_bf16(rows, ref["rows"], ref["pre"], tol)
+    else:
+        check_rows_fp4(rows, sc, ref["rows"], ref["scales"], ref["pre"], tol)

@@ -16,59 +16,12 @@ import torch
 
 import long_context_attention_03_amd as L
 import oracle as O
-from helpers import (assert_close, bf16_bits, check_rows_e4m3_bf16, check_rows_fp4, dev,
-                     gather_pages, paginate, pooling_tolerance, say)
+from helpers import (angle_bound, assert_close, bf16_bits, check_bf16, check_f32,
+                     check_rows_e4m3_bf16, check_rows_fp4, dev, gather_pages, oracle_bf16,
+                     paginate, pooling_tolerance, rope_tolerance, say)
 from long_context_attention_03_amd import synth
 
 pytestmark = pytest.mark.gpu
-
-
-def _oracle_bf16(v):
-    """bf16 bits of fp64 values v (any shape), rounded by the oracle's own row encoder: chunks of
-    64 values become the bf16 part of E4M3+bf16 rows."""
-    v = np.asarray(v, np.float64)
-    flat = v.reshape(-1)
-    n = flat.size
-    pad = (-n) % 64
-    chunks = np.concatenate([flat, np.zeros(pad)]).reshape(-1, 64)
-    rows = np.zeros((chunks.shape[0], 512))
-    rows[:, 448:] = chunks
-    enc, _ = O.encode_rows(rows, O.FMT_ROW_E4M3_BF16)
-    bits = enc[:, 448:].copy().view(np.uint16).reshape(-1)[:n]
-    return bits.reshape(v.shape)
-
-
-def _angle_bound(x_values, pos, R):
-    """Per rotary element: (p + 1) 2^-48 (|a| + |b|) for its pair (a, b) of row (b, i) at
-    p = pos[b] + i; x_values [B, Q, H, D] are the values before turning."""
-    x = np.abs(np.asarray(x_values, np.float64))
-    B, Q, H, D = x.shape
-    p = (np.asarray(pos, np.float64)[:, None] + np.arange(Q)[None, :])[:, :, None, None]
-    size = x[..., D - R::2] + x[..., D - R + 1::2]
-    t = np.empty(x.shape[:-1] + (R,))
-    t[..., 0::2] = t[..., 1::2] = (np.abs(p) + 1.0) * 2.0 ** -48 * size
-    return t
-
-
-def _check_bf16(got_bits, ref, tol, what):
-    """got_bits (uint16) must be the oracle's rounding of ref, except where ref lies within tol
-    of a midpoint between two bf16 neighbours."""
-    want = _oracle_bf16(ref)
-    bad = np.nonzero(got_bits != want)
-    for idx in zip(*bad):
-        a = O.bf16_value(int(got_bits[idx]))
-        b = O.bf16_value(int(want[idx]))
-        assert abs(ref[idx] - 0.5 * (a + b)) <= tol[idx], (what, idx, ref[idx], a, b, tol[idx])
-    say(f"  {what}: {len(bad[0])} of {got_bits.size} bf16 values off the oracle's rounding "
-        f"(each within the angle bound of a midpoint)")
-
-
-def _check_f32(got, ref, tol, what):
-    half_ulp = 0.5 * np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
-    err = np.abs(got.astype(np.float64) - ref)
-    worst = float(np.max(err / (half_ulp + tol))) if got.size else 0.0
-    say(f"  {what}: max err / (half ulp + angle bound) = {worst:.3g} over {got.size} values")
-    assert worst <= 1.0 + 1e-6, what
 
 
 def _q(shape, seed, bf16=True):
@@ -92,7 +45,7 @@ def test_decode_queries_bf16_at_1m():
     got = bf16_bits(_run_rope(x, pos, 64))
     ref = O.rope(bf16_bits(x), pos, 64)
     np.testing.assert_array_equal(got[..., :448], bf16_bits(x)[..., :448])
-    _check_bf16(got[..., 448:], ref[..., 448:], _angle_bound(x.float().numpy(), pos, 64),
+    check_bf16(got[..., 448:], ref[..., 448:], angle_bound(x.float().numpy(), pos, 64),
                 "rotary dims")
 
 
@@ -104,7 +57,7 @@ def test_prefill_queries_bf16():
     got = bf16_bits(_run_rope(x, pos, 64))
     ref = O.rope(bf16_bits(x), pos, 64)
     np.testing.assert_array_equal(got[..., :448], bf16_bits(x)[..., :448])
-    _check_bf16(got[..., 448:], ref[..., 448:], _angle_bound(x.float().numpy(), pos, 64),
+    check_bf16(got[..., 448:], ref[..., 448:], angle_bound(x.float().numpy(), pos, 64),
                 "rotary dims")
 
 
@@ -115,7 +68,7 @@ def test_inverse_on_f32_attention_output():
     got = _run_rope(x, pos, 64, inverse=True).numpy()
     ref = O.rope(x.numpy(), pos, 64, inverse=True)
     np.testing.assert_array_equal(got[..., :448], x.numpy()[..., :448])
-    _check_f32(got[..., 448:], ref[..., 448:], _angle_bound(x.numpy(), pos, 64), "rotary dims")
+    check_f32(got[..., 448:], ref[..., 448:], angle_bound(x.numpy(), pos, 64), "rotary dims")
 
 
 def test_forward_then_inverse_restores_f32_rows():
@@ -142,17 +95,17 @@ def test_shapes(B, Q, H, D, R, bf16):
     say(f"[rope] shape B={B} Q={Q} H={H} D={D} R={R} bf16={bf16}")
     out = _run_rope(x, pos, R, base=500000.0)
     ref = O.rope(bf16_bits(x) if bf16 else x.numpy(), pos, R, base=500000.0)
-    tol = _angle_bound(x.float().numpy(), pos, R)
+    tol = angle_bound(x.float().numpy(), pos, R)
     if bf16:
         got = bf16_bits(out)
         np.testing.assert_array_equal(got[..., :D - R], bf16_bits(x)[..., :D - R])
-        _check_bf16(got[..., D - R:], ref[..., D - R:], tol, "rotary dims")
+        check_bf16(got[..., D - R:], ref[..., D - R:], tol, "rotary dims")
         # position 0 of sequence 0 is the identity rotation for query 0
         np.testing.assert_array_equal(got[0, 0], bf16_bits(x)[0, 0])
     else:
         got = out.numpy()
         np.testing.assert_array_equal(got[..., :D - R], x.numpy()[..., :D - R])
-        _check_f32(got[..., D - R:], ref[..., D - R:], tol, "rotary dims")
+        check_f32(got[..., D - R:], ref[..., D - R:], tol, "rotary dims")
 
 
 def test_bf16_special_values():
@@ -176,7 +129,7 @@ def test_bf16_special_values():
     say("[rope] bf16 special values")
     got = bf16_bits(_run_rope(x, pos, 64))
     ref = O.rope(bf16_bits(x), pos, 64)
-    want = _oracle_bf16(np.nan_to_num(ref, nan=0.0))
+    want = oracle_bf16(np.nan_to_num(ref, nan=0.0))
     nan_ref = np.isnan(ref)
     gv = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy()
     assert np.array_equal(np.isnan(gv), nan_ref)
@@ -190,19 +143,6 @@ def test_no_rows_is_a_no_op():
 
 
 # ----------------------------------------------------------------------------- compression
-def _rope_tolerance(tol, pre, D, R):
-    """Pooling bound of a rotated dim: the bounds of both dims of its pair (a rotation moves an
-    error of (e_a, e_b) by at most |e_a| + |e_b| per dim) plus the binary32 rounding of the
-    turned value (2^-23 of the pair's size)."""
-    t = np.array(tol, np.float64, copy=True)
-    a, b = t[..., D - R::2], t[..., D - R + 1::2]
-    size = np.abs(pre[..., D - R::2]) + np.abs(pre[..., D - R + 1::2])
-    pair = a + b + 2.0 ** -23 * size
-    t[..., D - R::2] = pair
-    t[..., D - R + 1::2] = pair
-    return t
-
-
 def _gpu_compress_rope(x, m, w, beta, fmt, tok, R, span=None, skip=0):
     rows, sc = L.kv_compress_rope(x.cuda(), m, dev(w), dev(beta), fmt,
                                   torch.from_numpy(np.asarray(tok, np.int64)).cuda(), R,
@@ -225,7 +165,7 @@ def test_compress_prefill_chunk_e4m3_bf16_rows(m):
     rows, _ = _gpu_compress_rope(x, m, w, beta, O.FMT_ROW_E4M3_BF16, tok, 64)
     ref = O.kv_compress(bf16_bits(x), O.DT_BF16, m, w, beta, O.FMT_ROW_E4M3_BF16, tok_pos=tok,
                         rope_dims=64)
-    tol = _rope_tolerance(pooling_tolerance(x.float().numpy(), m, ref["pre"]), ref["pre"], 512,
+    tol = rope_tolerance(pooling_tolerance(x.float().numpy(), m, ref["pre"]), ref["pre"], 512,
                           64)
     nd = check_rows_e4m3_bf16(rows, ref["rows"], ref["pre"], tol)
     say(f"  {nd} elements differ, all within fp32 round-off of a rounding midpoint")
@@ -241,7 +181,7 @@ def test_compress_indexer_keys_fp4():
     rows, sc = _gpu_compress_rope(xi, 4, w, beta, O.FMT_FP4_E8M0, tok, 64)
     ref = O.kv_compress(xi.numpy(), O.DT_F32, 4, w, beta, O.FMT_FP4_E8M0, tok_pos=tok,
                         rope_dims=64)
-    tol = _rope_tolerance(pooling_tolerance(xi.numpy(), 4, ref["pre"]), ref["pre"], 128, 64)
+    tol = rope_tolerance(pooling_tolerance(xi.numpy(), 4, ref["pre"]), ref["pre"], 128, 64)
     nd = check_rows_fp4(rows, sc, ref["rows"], ref["scales"], ref["pre"], tol)
     say(f"  {nd} codes differ, all at a rounding midpoint")
 
@@ -275,7 +215,7 @@ def test_compress_overlapping_span_with_context_groups():
     rows, _ = _gpu_compress_rope(x, 4, w, beta, O.FMT_ROW_E4M3_BF16, tok, 64, span=8, skip=1)
     ref = O.kv_compress(bf16_bits(x), O.DT_BF16, 4, w, beta, O.FMT_ROW_E4M3_BF16, span=8, skip=1,
                         tok_pos=tok, rope_dims=64)
-    tol = _rope_tolerance(pooling_tolerance(x.float().numpy(), 4, ref["pre"], span=8, skip=1),
+    tol = rope_tolerance(pooling_tolerance(x.float().numpy(), 4, ref["pre"], span=8, skip=1),
                           ref["pre"], 512, 64)
     check_rows_e4m3_bf16(rows, ref["rows"], ref["pre"], tol)
 
