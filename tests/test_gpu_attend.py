@@ -79,6 +79,16 @@ def test_hca1m_full_size():
     assert_close(l, rl, "hca1m lse")
 
 
+def test_csa_largest_k():
+    """4096 selected entries per query (the largest k the indexer returns), 10% empty slots."""
+    c = DecodeCase("csa128k", B=3)
+    idx = _idx_random(c.B, 1, c.N, 4096, 21, empty_frac=0.1)
+    say(f"[csa_attend] k=4096 B={c.B} N={c.N}")
+    o, l, ro, rl = _csa(c, idx)
+    assert_close(o, ro, "k=4096 out")
+    assert_close(l, rl, "k=4096 lse")
+
+
 def test_csa_empty_slots_no_sink_and_early_positions():
     """-1 slots, no sink, window rows before position 0, ragged k (not a tile multiple)."""
     c = DecodeCase("csa128k", B=3, N=700, pos=[5, 130, 2799])

@@ -56,6 +56,22 @@ def test_long_key_ranges_several_stage_windows():
     _compare("long ranges", kc, ks, qc, qs, pos, m, k)
 
 
+@pytest.mark.parametrize("Q,coarse", [(1, False), (1, True), (5, False), (16, False), (16, True)])
+def test_largest_k(Q, coarse):
+    """k = 4096, the largest supported: all three schedules (one query, the multi-query scan, the
+    prefill schedule), and coarse keys whose tie list pushes the candidates past the 4096-key
+    sort capacity onto the radix-select path."""
+    rng = np.random.default_rng(40 + Q)
+    B, N, HI, dI, m, k = 2, 70001, 4, 128, 4, 4096
+    kv = rng.normal(size=(B, N, dI))
+    if coarse:
+        kv = np.round(kv * 0.7)
+    kc, ks = O.encode_rows(kv, O.FMT_FP4_E8M0)
+    qc, qs = O.encode_rows(rng.normal(size=(B, Q, HI, dI)), O.FMT_FP4_E8M0)
+    pos = np.array([N * m - Q, 4 * 5000 + 3], np.int64)  # the second sees about 5000 entries
+    _compare(f"k=4096 Q={Q} coarse={coarse}", kc, ks, qc, qs, pos, m, k)
+
+
 def test_ties_multi_query_causal_and_ragged():
     """Coarse keys (many equal scores), 3 queries per sequence with causal visibility, ragged N."""
     rng = np.random.default_rng(7)
