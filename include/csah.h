@@ -288,7 +288,7 @@ int csah_hca_attend_paged(const void* q, int q_dtype, int H, int D, const void* 
  * pos       [B] int64 device array, 8-byte aligned.
  * inverse   0: turn forward; 1: turn back (the inverse RoPE of the attention output).
  * Returns CSAH_OK without touching anything when B = 0 or Q = 0; CSAH_ERR_UNSUPPORTED for
- * R > 1024 or B*Q > 2^31 - 1.
+ * R > 1024, B*Q > 2^31 - 1 or H*R > 2^28.
  */
 int csah_rope(void* x, int dtype, int B, int Q, int H, int D, int rope_dims, const int64_t* pos,
               double rope_base, int inverse, void* stream);

@@ -210,7 +210,8 @@ int csah_rope(void* x, int dtype, int B, int Q, int H, int D, int rope_dims, con
   if (dtype != CSAH_DT_F32 && dtype != CSAH_DT_BF16) return CSAH_ERR_INVALID_ARGUMENT;
   if (!rope_shape_ok(D, rope_dims, rope_base)) return CSAH_ERR_INVALID_ARGUMENT;
   if (rope_dims > 2 * kRopeMaxPairs) return CSAH_ERR_UNSUPPORTED;
-  if ((int64_t)B * Q > INT32_MAX) return CSAH_ERR_UNSUPPORTED;
+  // the kernels count a row group's pairs and vectors in 32-bit integers
+  if ((int64_t)B * Q > INT32_MAX || (int64_t)H * rope_dims > (1 << 28)) return CSAH_ERR_UNSUPPORTED;
   if (B == 0 || Q == 0) return CSAH_OK;  // no row: nothing is touched
   if (!x || !pos || !aligned(x, 16) || !aligned(pos, 8)) return CSAH_ERR_INVALID_ARGUMENT;
   int st = check_device();

@@ -220,6 +220,7 @@ def test_rope_rejects_bad_arguments():
     assert call(pos=None) == L.INVALID_ARGUMENT
     assert call(x=ctypes.c_void_p(4100)) == L.INVALID_ARGUMENT  # misaligned rows
     assert call(D=2048, R=1026) == L.UNSUPPORTED     # more than 1024 rotary dims
+    assert call(H=1 << 23, R=64) == L.UNSUPPORTED    # H * R beyond 2^28
     # no rows: nothing is touched, null pointers allowed
     assert call(B=0, x=None, pos=None) == L.OK
     assert call(Q=0, x=None, pos=None) == L.OK
