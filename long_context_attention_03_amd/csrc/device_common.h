@@ -52,22 +52,10 @@ __device__ __forceinline__ float quad_xor2_add(float v) {
   return v + __int_as_float(t);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 __device__ __forceinline__ float shfl_xor_f(float v, int o) { return __shfl_xor(v, o, 64); }
 
 // 64-bit lane mask of lanes whose predicate holds.
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
-
-// Number of set bits of `mask` below this lane.
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-  uint32_t lo = __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u);
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), lo);
-}
 
 // ---- encoders used by the compressor (independent of any host code) ------------------------
 
