@@ -51,7 +51,7 @@ constexpr int kBinShift = 20;  // top 12 bits of the order key
 // into the key stream cost about 10% of the scan's time, one burst per window much less. The
 // window is capped so that a CU holding two scan workgroups (16 KB histogram + 16 KB stage
 // each) still has LDS for an attention workgroup running concurrently on another stream; with
-// 32 KB windows that co-residency is lost and two-layer decode steps get 10-35% slower.
+// 32 KB windows that co-residency is lost and two-layer decode steps get about 10% slower.
 constexpr int kScoreStage = 4096;
 constexpr int kSortCap = 4096;
 
