@@ -129,22 +129,31 @@ class DecodeStep:
             hlse=torch.empty((BM, QM, H), dtype=torch.float32, device=dev),
             ws_idx=torch.empty(L.index_topk_workspace(BM, QM, N_CSA, K, HI, DI),
                                dtype=torch.uint8, device=dev),
-            ws_att=torch.empty(max(256, L.attend_workspace(BM, QM, H, D, N_HCA + W),
-                                   L.attend_workspace(BM, QM, H, D, K + W)),
-                               dtype=torch.uint8, device=dev))
+            ws_att=torch.empty(max(256, L.attend_workspace(BM, QM, H, D, K + W)),
+                               dtype=torch.uint8, device=dev),
+            ws_hatt=torch.empty(max(256, L.attend_workspace(BM, QM, H, D, N_HCA + W)),
+                                dtype=torch.uint8, device=dev))
         torch.cuda.synchronize()
 
-    def mtp_step(self):
-        """Verification of 5 draft tokens for 4 sequences: each query gets its own causal top-k,
-        sparse attention and dense HCA attention (the CSA and HCA caches of sequences 0-3)."""
+    def mtp_csa(self):
+        """Verification of 5 draft tokens for 4 sequences, CSA layer: each query gets its own
+        causal top-k and sparse attention (the CSA caches of sequences 0-3)."""
         c, t = self.csa_slice(B_CSA4), self.mtp
-        hc = self.hca["cache"][:B_CSA4]
         L.index_topk(t["iqc"], t["iqs"], c["kc"], c["ks"], self.pos_m, 4, K, want_scores=False,
                      ws=t["ws_idx"], idx_out=t["idx"])
         L.csa_attend(t["q"], c["cache"], t["idx"], t["win"], W, self.pos_m, self.sink, self.scale,
                      ws=t["ws_att"], out=t["out"], lse=t["lse"])
-        L.hca_attend(t["q"], hc, 128, t["hwin"], W, self.pos_m, self.sink, self.scale,
-                     ws=t["ws_att"], out=t["hout"], lse=t["hlse"])
+
+    def mtp_hca(self):
+        """The same 5 x 4 queries through the HCA layer: dense attention (own workspace, so that
+        the two layers can run on two streams)."""
+        t = self.mtp
+        L.hca_attend(t["q"], self.hca["cache"][:B_CSA4], 128, t["hwin"], W, self.pos_m, self.sink,
+                     self.scale, ws=t["ws_hatt"], out=t["hout"], lse=t["hlse"])
+
+    def mtp_step(self):
+        self.mtp_csa()
+        self.mtp_hca()
 
     def csa_slice(self, nb):
         """The first nb sequences of the CSA layer (views; nothing is copied)."""
@@ -253,13 +262,14 @@ class DecodeStep:
 class StepGraphs:
     """The step as two HIP graphs, one per layer, replayed on two streams so that the HCA branch
     (compress + dense attention, bound by the matrix cores) runs concurrently with the CSA branch
-    (compress + index scan, bound by HBM, then sparse attention). The layers are independent."""
+    (compress + index scan, bound by HBM, then sparse attention). The layers are independent.
+    (csa_fn, hca_fn) default to the decode step's branches; the multi-query step passes its own."""
 
-    def __init__(self, ws: "DecodeStep"):
+    def __init__(self, ws: "DecodeStep", csa_fn=None, hca_fn=None):
         self.ws = ws
-        self.g_csa = capture(ws.csa_branch)
+        self.g_csa = capture(csa_fn or ws.csa_branch)
         with torch.cuda.stream(ws.side):
-            self.g_hca = capture(ws.hca_branch)
+            self.g_hca = capture(hca_fn or ws.hca_branch)
         torch.cuda.synchronize()
 
     def replay(self):
@@ -800,8 +810,13 @@ def main():
         "kernels": kinfo,
     }
     if not args.no_csa4:
-        gm = None if args.no_graph else capture(ws.mtp_step)
-        msm = time_replays(gm, ws.mtp_step, args.steps)
+        if args.no_graph:
+            msm = time_replays(None, ws.mtp_step, args.steps)
+        else:
+            mg = StepGraphs(ws, ws.mtp_csa, ws.mtp_hca)
+            for _ in range(args.warmup):
+                mg.replay()
+            msm = time_replays(None, mg.replay, args.steps)
         log(f"  multi-query decode (4 sequences x {MTP_Q} queries): {msm * 1e3:.1f} us")
         # unique bytes: each sequence's keys and HCA rows once, each query's selected rows, the
         # windows, q and both outputs
