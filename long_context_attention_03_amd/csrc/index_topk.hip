@@ -522,13 +522,20 @@ __global__ __launch_bounds__(kSelThreads) void index_select_kernel(
 }
 
 // Ordered top-k by rank counting: keys are unique, so the output position of candidate x is the
-// number of candidates greater than x. A workgroup of 1024 lanes ranks 64 candidates; each group
-// of kRankLanes lanes splits the candidate list kRankLanes ways and sums the partial counts with
-// lane shuffles. Massive ties (more candidates than kSortCap) fall back to finalize_slot in
-// workgroup 0.
-constexpr int kRankThreads = 1024;
+// number of candidates greater than x. Every "sure" key lies in a higher histogram bin than every
+// "tie" key, so a group of candidates that are all sure counts over the sure keys only, and one
+// whose candidates are all tie counts over the tie keys and adds the sure count (counting over
+// both lists is right for either kind). A workgroup ranks 64 candidates and stages only the
+// list(s) they need in LDS. A group of kRankLanes lanes holds kRankCand consecutive candidates in
+// registers, splits the list kRankLanes ways, compares each key it reads with all of them (several
+// reads in flight per lane) and sums the partial counts with lane shuffles. Massive ties (more
+// candidates than kSortCap) fall back to finalize_slot in workgroup 0.
+constexpr int kRankThreads = 256;
 constexpr int kRankLanes = 16;
-constexpr int kRankPerWG = kRankThreads / kRankLanes;
+constexpr int kRankCand = 4;
+constexpr int kRankPerWG = kRankThreads / kRankLanes * kRankCand;
+static_assert(kRankCand == 4 && kSortCap < (1 << 16), "two 16-bit counts per shuffled word");
+constexpr int kRankStage = 8;  // staged keys in flight per thread
 
 __global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
     const int64_t* __restrict__ pos, int m, int Q, int64_t N, int k,
@@ -560,22 +567,69 @@ __global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
       io[j] = -1;
       if (so) so[j] = -INFINITY;
     }
-  const uint32_t e = (uint32_t)blockIdx.x * kRankPerWG + (t / kRankLanes);  // ranked here
-  if ((uint32_t)blockIdx.x * kRankPerWG >= n) return;
+  const uint32_t e0 = (uint32_t)blockIdx.x * kRankPerWG;  // the workgroup ranks [e0, e0 + 64)
+  if (e0 >= n) return;
   const uint64_t* sure = ws.sure(slot);
   const uint64_t* tie = ws.tie(slot);
-  for (uint32_t j = t; j < n; j += kRankThreads) keys[j] = j < ns ? sure[j] : tie[j - ns];
+  const uint32_t s0 = e0 < ns ? 0u : ns;                          // staged: [s0, s1)
+  const uint32_t s1 = e0 + kRankPerWG <= ns ? ns : n;
+  for (uint32_t j0 = s0 + t; j0 < s1; j0 += kRankStage * kRankThreads) {  // loads go out together
+    uint64_t v[kRankStage];
+#pragma unroll
+    for (int u = 0; u < kRankStage; u++) {
+      const uint32_t j = j0 + u * kRankThreads;
+      if (j < s1) v[u] = j < ns ? sure[j] : tie[j - ns];
+    }
+#pragma unroll
+    for (int u = 0; u < kRankStage; u++) {
+      const uint32_t j = j0 + u * kRankThreads;
+      if (j < s1) keys[j] = v[u];
+    }
+  }
   __syncthreads();
   const int part = t % kRankLanes;
-  const uint64_t x = e < n ? keys[e] : ~(uint64_t)0;
-  // lanes of a group read interleaved keys (j = part, part + kRankLanes, ...): no bank conflicts
-  uint32_t above = 0;
-  for (uint32_t j = part; j < n; j += kRankLanes) above += keys[j] > x ? 1u : 0u;
+  const uint32_t c0 = e0 + (uint32_t)(t / kRankLanes) * kRankCand;  // candidates c0 .. c0 + 3
+  uint64_t x[kRankCand];
 #pragma unroll
-  for (int o = 1; o < kRankLanes; o <<= 1) above += (uint32_t)__shfl_xor((int)above, o, 64);
-  if (part == 0 && e < n && above < (uint32_t)kk) {
-    io[above] = (int32_t)(0xFFFFFFFFu - (uint32_t)x);
-    if (so) so[above] = key_to_float((uint32_t)(x >> 32));
+  for (int c = 0; c < kRankCand; c++) x[c] = c0 + c < n ? keys[c0 + c] : ~(uint64_t)0;
+  // counted range [lo, hi): inside the staged range for every valid candidate of the group
+  uint32_t lo = 0, hi = 0;
+  if (c0 < n) {
+    const uint32_t clast = (c0 + kRankCand < n ? c0 + kRankCand : n) - 1;
+    lo = c0 >= ns ? ns : 0u;
+    hi = clast < ns ? ns : n;
+  }
+  uint32_t a[kRankCand] = {};
+  uint32_t j = lo + part;
+  for (; j + 3 * kRankLanes < hi; j += 4 * kRankLanes) {
+    const uint64_t y0 = keys[j], y1 = keys[j + kRankLanes], y2 = keys[j + 2 * kRankLanes],
+                   y3 = keys[j + 3 * kRankLanes];
+#pragma unroll
+    for (int c = 0; c < kRankCand; c++)
+      a[c] += (uint32_t)(y0 > x[c]) + (uint32_t)(y1 > x[c]) + (uint32_t)(y2 > x[c]) +
+              (uint32_t)(y3 > x[c]);
+  }
+  for (; j < hi; j += kRankLanes) {
+    const uint64_t y = keys[j];
+#pragma unroll
+    for (int c = 0; c < kRankCand; c++) a[c] += (uint32_t)(y > x[c]);
+  }
+  // counts stay below 2^16 (n <= kSortCap): two per word through the shuffles
+  uint32_t p01 = a[0] | a[1] << 16, p23 = a[2] | a[3] << 16;
+#pragma unroll
+  for (int o = 1; o < kRankLanes; o <<= 1) {
+    p01 += (uint32_t)__shfl_xor((int)p01, o, 64);
+    p23 += (uint32_t)__shfl_xor((int)p23, o, 64);
+  }
+  if (part < kRankCand) {  // lane `part` of the group writes candidate c0 + part
+    const uint32_t e = c0 + (uint32_t)part;
+    const uint32_t w = part < 2 ? p01 : p23;
+    const uint32_t above = ((part & 1) ? w >> 16 : w & 0xFFFFu) + lo;
+    const uint64_t xe = part == 0 ? x[0] : part == 1 ? x[1] : part == 2 ? x[2] : x[3];
+    if (e < n && above < (uint32_t)kk) {
+      io[above] = (int32_t)(0xFFFFFFFFu - (uint32_t)xe);
+      if (so) so[above] = key_to_float((uint32_t)(xe >> 32));
+    }
   }
 }
 
