@@ -229,3 +229,41 @@ def test_multi_query_decode_1m_five_drafts():
     kc, ks, qc, qs = _fp4_inputs(rng, B, Q, N, 4)
     pos = np.full(B, N * m - Q, np.int64)
     _compare("decode Q=5 at 1M", kc, ks, qc, qs, pos, m, k)
+
+
+def _sure_count(scores: np.ndarray, k: int, bin_shift: int = 20) -> tuple[int, int]:
+    """(entries in histogram bins above the k-th largest score's bin, entries in that bin) for
+    scores sorted descending; a bin is the top 32 - bin_shift bits of the score's order key."""
+    u = scores.astype(np.float32).view(np.uint32)
+    key = np.where(u & 0x80000000, ~u, u | 0x80000000).astype(np.uint32)
+    b = key >> bin_shift
+    t = b[k - 1]
+    return int((b > t).sum()), int((b == t).sum())
+
+
+def test_rank_sure_tie_boundaries():
+    """The ranking counts entries above the threshold bin ("sure") and in it ("tie") separately
+    and holds four candidates per lane group, 64 per workgroup. Cases put the sure/tie boundary
+    at every offset within a group of four, at 63, 0 and 1 past a multiple of 64, at 0 and 1, and
+    cut the tie bin at various points. The boundary is moved by raising the block scales of a few
+    low-ranked keys by 2^10, which lifts them above every threshold."""
+    rng = np.random.default_rng(21)
+    B, N, HI, dI, m = 1, 24000, 4, 128, 4
+    kc0, ks0 = O.encode_rows(rng.normal(size=(B, N, dI)), O.FMT_FP4_E8M0)
+    qc, qs = O.encode_rows(rng.normal(size=(B, 1, HI, dI)), O.FMT_FP4_E8M0)
+    pos = np.array([N * m - 1], np.int64)
+    order, _, _ = O.index_topk(qc, qs, kc0, ks0, pos, m, N)
+    seen = []
+    for lift, k in [(0, 1), (0, 3), (0, 20), (0, 100), (0, 500), (0, 1024), (51, 1075),
+                    (52, 1076), (53, 1077), (0, 2000), (0, 2200), (0, 3900)]:
+        ks = ks0.copy()
+        ks[0, order[0, 0, 5000:5000 + lift]] += 10  # positive scores, ranked far below k
+        _, rs, ex = O.index_topk(qc, qs, kc0, ks, pos, m, N)
+        assert ex.all()
+        ns, nt = _sure_count(rs[0, 0], k)
+        assert ns + nt <= 4096, "the counting path, not the radix-select fallback"
+        seen.append(ns)
+        _compare(f"boundary ns={ns} nt={nt} k={k}", kc0, ks, qc, qs, pos, m, k)
+    assert {s % 4 for s in seen} == {0, 1, 2, 3}
+    assert {s % 64 for s in seen if s >= 64} >= {63, 0, 1}
+    assert 0 in seen and 1 in seen
