@@ -30,8 +30,9 @@
 //             and one atomic per workgroup and list
 //   rank      the output position of each candidate is the number of candidates with a greater
 //             key (keys are unique; descending key = score descending, index ascending), counted
-//             by 16 lanes per candidate over many workgroups; when the candidates exceed LDS
-//             (massive ties) one workgroup radix-selects the tie list and sorts in LDS
+//             over the candidate's own list (sure or tie) by 16 lanes per group of 4 candidates
+//             over many workgroups; when the candidates exceed LDS (massive ties) one workgroup
+//             radix-selects the tie list and sorts in LDS
 #include "csah_internal.h"
 #include "device_common.h"
 
