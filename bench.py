@@ -291,15 +291,16 @@ def event_pair():
 
 # Algorithmic HBM bytes and flops per launch of each stage's dominant kernel: what the method must
 # move (selected rows, not the whole cache) and compute (QK and PV, 2 flops per MAC).
-#   index_scan: 16 sequences x 262,144 FP4 keys x (64 B codes + 4 B scales); 512 MAC per key.
+#   index_scan: 16 sequences x 262,144 FP4 keys x (64 B codes + 4 B scales); 512 MAC per key, on
+#               the scaled FP4 MFMA (4 heads as the columns of one 16 x 16 x 128 product).
 #   csa_attend: 16 x [(1024 + 128) rows x 576 B + 1024 ids x 4 B + q 64x512 bf16 + out 64x512 fp32
 #               + lse 64 fp32] + sink; 64 heads x 1152 rows x 512 x 4 flops.
 #   hca_attend: 16 x [(8192 + 128) rows x 576 B + q + out + lse] + sink; 64 x 8320 x 512 x 4 flops.
 CSA_SEQ_BYTES = (K + W) * ROW + K * 4 + H * D * 2 + H * D * 4 + H * 4
 KERNELS = {
     "index_scan": dict(per_step=1, bytes=B_STEP * SCAN_BYTES_PER_SEQ,
-                       flops=B_STEP * N_CSA * 512 * 2, peak_flops=157.3e12,
-                       name="index_scan_kernel (csah_index_topk)", source="index_topk.hip",
+                       flops=B_STEP * N_CSA * 512 * 2, peak_flops=10.1e15,
+                       name="index_scan_mx_kernel (csah_index_topk)", source="index_topk.hip",
                        profile="index_scan_csa1m_b16"),
     "csa_attend": dict(per_step=1, bytes=B_STEP * CSA_SEQ_BYTES + H * 4,
                        flops=B_STEP * H * (K + W) * D * 4, peak_flops=2.5e15,
@@ -771,7 +772,7 @@ def main():
         roof = {"bound": "hbm", "achieved": spec["bytes"] / t_dom / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma" if dom != "index_scan" else "alu",
+        roof = {"bound": "mfma",
                 "achieved": spec["flops"] / t_dom / 1e12, "peak": spec["peak_flops"] / 1e12,
                 "unit": "TFLOP/s"}
     queries = B_STEP

@@ -43,12 +43,14 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 }
 
 // Butterfly add across lanes lane ^ 1 and lane ^ 2 (DPP quad permutes).
+// Every lane reads a lane of its own quad, so bound_ctrl never applies; setting it lets the
+// compiler fold the move into the add (one DPP add instead of a DPP move and an add).
 __device__ __forceinline__ float quad_xor1_add(float v) {
-  int t = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  int t = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true);  // [1,0,3,2]
   return v + __int_as_float(t);
 }
 __device__ __forceinline__ float quad_xor2_add(float v) {
-  int t = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+  int t = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
   return v + __int_as_float(t);
 }
 

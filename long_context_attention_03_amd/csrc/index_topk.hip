@@ -46,6 +46,7 @@ namespace csah {
 #ifndef CSAH_SCAN_U
 #define CSAH_SCAN_U 4
 #endif
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 constexpr int kBins = 4096;
 constexpr int kBinShift = 20;  // top 12 bits of the order key
 // Scores of the decode scan are staged in LDS and written out a window at a time: stores mixed
@@ -206,10 +207,26 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
     const int64_t base_row = PAGED ? 0 : kmap.row(b, g0);
     const uint8_t* kc = k_codes + base_row * (16 * NB) + 16 * sub;
     const uint8_t* ks = k_scales + base_row * NB + sub;
+    // full steps of contiguous keys: a workgroup-uniform base per step plus a per-lane constant
+    // offset, so the loads take no per-step address arithmetic on the vector unit
+    const uint8_t* kcu = k_codes + base_row * (16 * NB);
+    const uint8_t* ksu = k_scales + base_row * NB;
+    const uint32_t lane_c = (uint32_t)ent * (16u * NB) + 16u * sub;
+    const uint32_t lane_s = (uint32_t)ent * NB + sub;
     const uint32_t off0 = PAGED ? (uint32_t)(g0 & (((int64_t)1 << kmap.shift) - 1)) : 0u;
     float* sc = ws.scores(slot) + g0;
     const int n = (int)(g1 - g0);
     auto load = [&](int r0, u32x4* c, uint32_t* e, bool clamp) {
+      if (!PAGED && !clamp) {
+        const uint8_t* pc = kcu + (size_t)(uint32_t)r0 * (16u * NB);
+        const uint8_t* ps = ksu + (size_t)(uint32_t)r0 * NB;
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+          c[u] = __builtin_nontemporal_load((const u32x4*)(pc + lane_c + u * (EPW * 16 * NB)));
+          e[u] = ps[lane_s + u * (EPW * NB)];
+        }
+        return;
+      }
 #pragma unroll
       for (int u = 0; u < U; u++) {
         int r = r0 + u * EPW + ent;
@@ -264,6 +281,147 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
       score(r0 + STEP, cb, eb);
       if (((r0 + 2 * STEP) & (kScoreStage - 1)) == 0 && r0 + 2 * STEP < n) {
         flush(flushed, r0 + 2 * STEP);  // a full window, while the next loads are in flight
+        flushed = r0 + 2 * STEP;
+      }
+    }
+    flush(flushed, n);
+  }
+  __syncthreads();
+  uint32_t* gh = ws.hist(slot);
+  for (int j = tid; j < kBins; j += 256) {
+    const uint32_t c = hist[j];
+    if (c) atomicAdd(&gh[j], c);
+  }
+}
+
+// The same scan on the matrix cores, for 128-dim keys and at most 4 indexer heads:
+// v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1 operands takes A = 16 keys (lane l: key l%16,
+// 32-element block l/16, with the block's E8M0 scale) and B = the query's heads as columns (lane l:
+// head l%16, block l/16; columns past the head count are zero codes), and leaves in register i of
+// lane l the head-(l%16) score of key 4(l/16)+i, every product exactly scaled. The 4 lanes of a
+// quad hold the 4 heads of the same 4 keys; a transposing quad reduction (two exchanges, each
+// sending the values the partner keeps) leaves lane c of the quad with key c's sum over the heads.
+// That sum is the score of the formula above regrouped (per head instead of head-summed first):
+// under the same precondition every partial sum is exact, so it is the same fp32 value. The rest
+// (contiguous ranges, LDS score stage, histogram, flushes) is the scan above; a tile of 16 keys
+// takes one MFMA and 26 vector instructions instead of about 65 (16 conversions, 32 FMAs and the
+// rest per block on the vector path). The kernel stays bound by HBM: taking the arithmetic off the
+// vector unit measured 16.7 against 18.4 us at 4 x 262,144 keys and 53.6 against 54.2 at 16.
+template <int CTRL>
+__device__ __forceinline__ float quad_read(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(256) void index_scan_mx_kernel(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
+    int64_t N, const int64_t* __restrict__ pos, int m, int Q, int chunk, IdxWs ws) {
+  constexpr int U = CSAH_SCAN_U;  // tiles of 16 keys per wavefront per step
+  constexpr int STEP = 4 * 16 * U;
+  static_assert(kScoreStage % (2 * STEP) == 0, "a stage window holds whole loop iterations");
+  const int slot = blockIdx.y, b = slot / Q, i = slot - b * Q;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, kb = lane >> 4;  // key of the tile (A) / head (B); 32-element block
+  __shared__ uint32_t hist[kBins];
+  __shared__ int32_t pages[PAGED ? kPageList : 1];
+  __shared__ float stage[kScoreStage];
+  for (int j = tid; j < kBins; j += 256) hist[j] = 0u;
+
+  const int64_t nv = visible_entries(pos, b, i, m, N);
+  const int64_t g0 = (int64_t)blockIdx.x * chunk;
+  const int64_t g1 = g0 + chunk < nv ? g0 + chunk : nv;
+  if constexpr (PAGED) {
+    if (g0 < nv) load_page_list(kmap, b, g0, g1, pages, tid, 256);
+  }
+  __syncthreads();
+  if (g0 < nv) {
+    i32x8 qb = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    int qe = 127;
+    if (col < HI) {
+      const int64_t qrow = (int64_t)slot * HI + col;
+      const u32x4 v = *(const u32x4*)(q_codes + qrow * 64 + 16 * kb);
+      qb[0] = (int)v[0];
+      qb[1] = (int)v[1];
+      qb[2] = (int)v[2];
+      qb[3] = (int)v[3];
+      qe = q_scales[qrow * 4 + kb];
+    }
+    const int64_t base_row = PAGED ? 0 : kmap.row(b, g0);
+    const uint8_t* kcu = k_codes + base_row * 64;
+    const uint8_t* ksu = k_scales + base_row * 4;
+    const uint32_t off0 = PAGED ? (uint32_t)(g0 & (((int64_t)1 << kmap.shift) - 1)) : 0u;
+    const int wkey = wave * 16 * U + col;  // this lane's key in tile 0 of a step
+    float* sc = ws.scores(slot) + g0;
+    const int n = (int)(g1 - g0);
+    auto load = [&](int r0, u32x4* c, uint32_t* e, bool clamp) {
+      if (!PAGED && !clamp) {  // uniform base per step, per-lane constant offsets
+        const uint8_t* pc = kcu + (size_t)(uint32_t)r0 * 64u;
+        const uint8_t* ps = ksu + (size_t)(uint32_t)r0 * 4u;
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+          c[u] = __builtin_nontemporal_load(
+              (const u32x4*)(pc + (uint32_t)wkey * 64u + 16u * kb + u * 1024));
+          e[u] = ps[(uint32_t)wkey * 4u + kb + u * 64];
+        }
+        return;
+      }
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        int r = r0 + wkey + 16 * u;
+        if (clamp) r = r < n ? r : n - 1;
+        if constexpr (PAGED) {
+          const uint64_t row = page_row(pages, off0 + (uint32_t)r, kmap.shift);
+          c[u] = __builtin_nontemporal_load((const u32x4*)(k_codes + row * 64u + 16u * kb));
+          e[u] = k_scales[row * 4u + kb];
+        } else {
+          c[u] = __builtin_nontemporal_load((const u32x4*)(kcu + (uint32_t)r * 64u + 16u * kb));
+          e[u] = ksu[(uint32_t)r * 4u + kb];
+        }
+      }
+    };
+    const bool hi2 = (col & 2) != 0, hi1 = (col & 1) != 0;
+    auto score = [&](int r0, const u32x4* c, const uint32_t* e) {
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const i32x8 a = i32x8{(int)c[u][0], (int)c[u][1], (int)c[u][2], (int)c[u][3], 0, 0, 0, 0};
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qb, z, 4, 4, 0,
+                                                                         (int)e[u], 0, qe);
+        // quad lane c: p[j] = head c of key j (of this lane's 4 keys); keep the keys whose bit 1
+        // is c's bit 1 and take the partner c^2's heads for them
+        const float s0 = (hi2 ? p[2] : p[0]) + quad_read<0x4E>(hi2 ? p[0] : p[2]);
+        const float s1 = (hi2 ? p[3] : p[1]) + quad_read<0x4E>(hi2 ? p[1] : p[3]);
+        // then key c itself, with the partner c^1's two heads of it
+        const float v = (hi1 ? s1 : s0) + quad_read<0xB1>(hi1 ? s0 : s1) + 0.0f;  // -0 -> +0
+        const int r = r0 + wave * 16 * U + 16 * u + 4 * kb + col;  // key c = col of the quad
+        if (col < 4 && r < n) {
+          stage[r & (kScoreStage - 1)] = v;
+          atomicAdd(&hist[order_key(v) >> kBinShift], 1u);
+        }
+      }
+    };
+    auto flush = [&](int w0, int w1) {
+      __syncthreads();
+      int j = w0 + 4 * tid;
+      for (; j + 4 <= w1; j += 1024)
+        *(f32x4*)(sc + j) = *(const f32x4*)(stage + (j & (kScoreStage - 1)));
+      for (; j < w1; j++) sc[j] = stage[j & (kScoreStage - 1)];
+      __syncthreads();
+    };
+    u32x4 ca[U], cb[U];
+    uint32_t ea[U], eb[U];
+    load(0, ca, ea, STEP > n);
+    int flushed = 0;
+    for (int r0 = 0; r0 < n; r0 += 2 * STEP) {
+      const bool has_b = r0 + STEP < n;
+      if (has_b) load(r0 + STEP, cb, eb, r0 + 2 * STEP > n);
+      score(r0, ca, ea);
+      if (!has_b) break;
+      if (r0 + 2 * STEP < n) load(r0 + 2 * STEP, ca, ea, r0 + 3 * STEP > n);
+      score(r0 + STEP, cb, eb);
+      if (((r0 + 2 * STEP) & (kScoreStage - 1)) == 0 && r0 + 2 * STEP < n) {
+        flush(flushed, r0 + 2 * STEP);
         flushed = r0 + 2 * STEP;
       }
     }
@@ -656,7 +814,6 @@ __global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
 constexpr int kPBins = 2048, kPBinShift = 21;
 constexpr int kPKeys = 16384;                // keys per workgroup: a 16-bit counter cannot overflow
 constexpr uint32_t kNoThreshold = 0xFFFFFFFFu;
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 template <int HP>  // HP >= HI: heads padded with zero codes contribute exactly 0
 struct QueryOps {
@@ -1055,6 +1212,15 @@ static void launch_mfma_scan(const IndexArgs& a, const IdxWs& w, hipStream_t s) 
 
 template <int NB>
 static void launch_scan(const IndexArgs& a, const IdxWs& w, int chunk, dim3 grid, hipStream_t s) {
+  if (NB == 4 && a.HI <= 4) {  // 128-dim keys, at most 4 heads: the MFMA scan
+    if (a.kmap.table)
+      a.prof.launch(index_scan_mx_kernel<true>, grid, dim3(256), s, a.q_codes, a.q_scales, a.HI,
+                    a.k_codes, a.k_scales, a.kmap, a.N, a.pos, a.m, a.Q, chunk, w);
+    else
+      a.prof.launch(index_scan_mx_kernel<false>, grid, dim3(256), s, a.q_codes, a.q_scales, a.HI,
+                    a.k_codes, a.k_scales, a.kmap, a.N, a.pos, a.m, a.Q, chunk, w);
+    return;
+  }
   if (a.kmap.table)
     a.prof.launch(index_scan_kernel<NB, true>, grid, dim3(256), s, a.k_codes, a.k_scales, a.kmap,
                   a.N, a.pos, a.m, a.Q, chunk, w);

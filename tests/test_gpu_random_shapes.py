@@ -55,6 +55,42 @@ def test_index_topk_random(seed):
     assert np.array_equal(gs, rs.astype(np.float32))
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_index_topk_random_mfma_scan(seed):
+    """One or two queries per sequence with 128-dim keys and 1-4 indexer heads: the scan whose
+    scores come from the scaled FP4 MFMA (heads as columns, zero columns past the head count)."""
+    rng = np.random.default_rng(3000 + seed)
+    Q = int(rng.choice([1, 2]))
+    HI = int(rng.integers(1, 5))
+    B = int(rng.integers(1, 5))
+    N = int(rng.integers(1, 40000))
+    k = int(rng.integers(1, 1500))
+    m = int(rng.choice([1, 4, 8]))
+    pos = rng.integers(0, N * m + 8, size=B).astype(np.int64)
+    pos[0] = N * m - Q
+    kv = rng.normal(size=(B, N, 128))
+    if rng.random() < 0.3:
+        kv = np.round(kv)
+    kc, ks = O.encode_rows(kv, O.FMT_FP4_E8M0)
+    qc, qs = O.encode_rows(rng.normal(size=(B, Q, HI, 128)), O.FMT_FP4_E8M0)
+    paged = rng.random() < 0.4
+    say(f"[random mfma scan] seed={seed} B={B} Q={Q} HI={HI} N={N} k={k} m={m} paged={paged}")
+    if paged:
+        P = int(rng.choice([1, 16, 64, 256]))
+        pc, table = paginate(kc, P, np.random.default_rng(seed))
+        ps, _ = paginate(ks, P, np.random.default_rng(seed))
+        gi, gs = L.index_topk_paged(dev(qc), dev(qs), dev(pc), dev(ps), dev(table), P, N, dev(pos),
+                                    m, k)
+    else:
+        gi, gs = L.index_topk(dev(qc), dev(qs), dev(kc), dev(ks), dev(pos), m, k)
+    torch.cuda.synchronize()
+    ri, rs, ex = O.index_topk(qc, qs, kc, ks, pos, m, k)
+    assert ex.all()
+    gi, gs = gi.cpu().numpy(), gs.cpu().numpy()
+    assert np.array_equal(gi, ri), f"{int((gi != ri).sum())} index mismatches"
+    assert np.array_equal(gs, rs.astype(np.float32))
+
+
 @pytest.mark.parametrize("seed", range(30))
 def test_attend_random(seed):
     rng = np.random.default_rng(2000 + seed)
