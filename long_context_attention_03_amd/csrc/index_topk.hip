@@ -21,9 +21,10 @@
 // launch):
 //   prep      qt (fp32, dI values) + clear the histogram / counters        (1 WG per slot)
 //   scan      stream the FP4 keys (coalesced 16-byte loads, one 32-element block per lane,
-//             dI/32 lanes per entry, 8 groups of loads in flight), write fp32 scores, build a 4096-bin
-//             histogram of the top 12 bits of each score's order key in LDS, flush it with
-//             global atomics
+//             8 groups of loads in flight), write fp32 scores, build a 4096-bin histogram of the
+//             top 12 bits of each score's order key in LDS, flush it with global atomics; the
+//             scores come from the scaled FP4 MFMA per head (128-dim keys, at most 4 heads:
+//             index_scan_mx_kernel) or from qt on the vector unit (index_scan_kernel)
 //   select    every workgroup finds the bin holding the k-th largest score from the histogram;
 //             entries above it ("sure") and in it ("tie") are appended as 64-bit keys
 //             (order_key(score) << 32 | ~g, unique per entry) at offsets from a block prefix sum
