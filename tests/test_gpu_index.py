@@ -267,3 +267,19 @@ def test_rank_sure_tie_boundaries():
     assert {s % 4 for s in seen} == {0, 1, 2, 3}
     assert {s % 64 for s in seen if s >= 64} >= {63, 0, 1}
     assert 0 in seen and 1 in seen
+
+
+@pytest.mark.parametrize("HI", [4, 5])
+def test_decode_scan_wide_exponent_range(HI):
+    """Each key's four block scales shifted by the same offset in [-90, 90]: key magnitudes span
+    2^-90 to 2^90, every score stays exact and in the fp32 normal range; k = N ranks (and
+    compares) every score, the smallest included. 4 heads take the MFMA scan (E8M0 scales as
+    MFMA operands), 5 the vector scan."""
+    rng = np.random.default_rng(31)
+    B, N, dI, m, k = 2, 4000, 128, 4, 4000
+    kc, ks = O.encode_rows(rng.normal(size=(B, N, dI)), O.FMT_FP4_E8M0)
+    off = rng.integers(-90, 91, size=(B, N, 1))
+    ks = np.clip(ks.astype(np.int64) + off, 1, 254).astype(np.uint8)
+    qc, qs = O.encode_rows(rng.normal(size=(B, 1, HI, dI)), O.FMT_FP4_E8M0)
+    pos = np.array([N * m - 1, N * m // 2], np.int64)
+    _compare(f"wide exponents HI={HI}", kc, ks, qc, qs, pos, m, k)
