@@ -70,6 +70,19 @@ def test_csa1m_full_size():
     assert_close(l, rl, "csa1m lse")
 
 
+def test_csa_decode_step_launch_shape_16_sequences():
+    """CSA attention as the decode step runs it: 16 sequences, top-1024 + 128-token window, 64
+    heads x 512 on E4M3+bf16 rows (9 row splits per sequence, 144 workgroups). The launch depends
+    on the sequence count and the row count, not on the cache length, so a 16,384-entry cache
+    stands in for the 262,144-entry one."""
+    c = DecodeCase("csa1m", B=16, N=16384)
+    say(f"[csa_attend] decode-step shape B={c.B} N={c.N} H={c.wl.H} k={c.wl.k}")
+    idx = _idx_random(c.B, 1, c.N, c.wl.k, 21)
+    o, l, ro, rl = _csa(c, idx)
+    assert_close(o, ro, "csa B=16 out")
+    assert_close(l, rl, "csa B=16 lse")
+
+
 def test_hca1m_full_size():
     """The 1M HCA decode at full size: 16 seqs x 8192 entries + window, 64 heads."""
     c = DecodeCase("hca1m")

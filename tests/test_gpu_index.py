@@ -41,6 +41,21 @@ def test_csa1m_full_size():
     _compare("csa1m full", c.kc, c.ks, c.qc, c.qs, c.pos, c.m, c.wl.k)
 
 
+def test_decode_step_launch_shape_16_sequences():
+    """The index call as the decode step runs it: 16 sequences x 262,144 entries, top-1024 (the
+    MFMA scan with 8192-key ranges over 512 workgroups, 32 select workgroups per sequence). Codes
+    are random bytes and scales a narrow band, which keeps every score exact."""
+    rng = np.random.default_rng(22)
+    B, N, HI, dI, m, k = 16, 262144, 4, 128, 4, 1024
+    kc = rng.integers(0, 256, size=(B, N, dI // 2), dtype=np.uint8)
+    ks = rng.integers(124, 129, size=(B, N, dI // 32), dtype=np.uint8)
+    qc = rng.integers(0, 256, size=(B, 1, HI, dI // 2), dtype=np.uint8)
+    qs = rng.integers(125, 128, size=(B, 1, HI, dI // 32), dtype=np.uint8)
+    pos = np.full(B, N * m - 1, np.int64)
+    pos[3] -= m * 5000  # one sequence sees fewer entries
+    _compare("decode-step shape", kc, ks, qc, qs, pos, m, k)
+
+
 def test_long_key_ranges_several_stage_windows():
     """2 x (2^22 + 777) keys: each scan workgroup's range holds more than two 8192-score stage
     windows (two full flushes and a partial one), the last range of each sequence is ragged, and
