@@ -298,3 +298,14 @@ def test_decode_scan_wide_exponent_range(HI):
     qc, qs = O.encode_rows(rng.normal(size=(B, 1, HI, dI)), O.FMT_FP4_E8M0)
     pos = np.array([N * m - 1, N * m // 2], np.int64)
     _compare(f"wide exponents HI={HI}", kc, ks, qc, qs, pos, m, k)
+
+
+def test_many_sequences_small_caches():
+    """700 sequences of 1,500 entries (one scan workgroup per sequence, 700 slots deep grids),
+    causal positions drawn per sequence, 4 heads x 128 (the MFMA scan)."""
+    rng = np.random.default_rng(41)
+    B, N, HI, dI, m, k = 700, 1500, 4, 128, 4, 100
+    kc, ks = O.encode_rows(rng.normal(size=(B, N, dI)), O.FMT_FP4_E8M0)
+    qc, qs = O.encode_rows(rng.normal(size=(B, 1, HI, dI)), O.FMT_FP4_E8M0)
+    pos = rng.integers(0, N * m, size=B).astype(np.int64)
+    _compare("many sequences", kc, ks, qc, qs, pos, m, k)
