@@ -103,6 +103,17 @@ struct IndexArgs {
 size_t index_workspace_bytes(int B, int Q, int64_t N, int k, int HI, int dI);
 hipError_t launch_index_topk(const IndexArgs& a);
 
+// One or two queries per sequence: certified per-range candidate lists and a top-k over their union
+// (index_cand.hip). The plan fixes the range length (chunk), the ranges per slot (R), the list
+// length (cap) and how many keys a range publishes at least (cmin).
+struct CandPlan {
+  int chunk, R, cap, cmin;
+};
+// false: more ranges than the top-k kernel holds (very long key ranges); page_shift < 0: contiguous
+bool index_cand_plan(int slots, int64_t N, int k, int page_shift, CandPlan* p);
+size_t index_cand_slot_bytes();
+hipError_t launch_index_cand(const IndexArgs& a, const CandPlan& p);
+
 // ---- attention ---------------------------------------------------------------------------------
 struct AttendPlan {
   int splits;          // row splits per (sequence, query, head group)

@@ -1,0 +1,858 @@
+// index_cand.hip -- decode indexer (one or two queries per sequence): a scan that leaves certified
+// per-range candidate lists, then one exact top-k over their union.
+//
+// [EXPL] "DeepSeek V4 Architecture Explained: CSA, HCA, mHC and Muon", section "How
+// compress-then-sparsify attention works": the indexer queries are scored against the compressed
+// indexer keys and each query keeps its top-k entries. [LLMB] "Inside DeepSeek-V4 ...", section
+// "1. Compressed Sparse Attention (CSA)": an FP4 indexer scores every compressed block and keeps
+// the top 1,024. [BSWEN] "How DeepSeek V4 Handles 1M Token Context with Hybrid Attention", section
+// "Component 3: DeepSeek Sparse Attention (DSA)": score all entries, keep the top k, attend.
+//
+// Key of entry g: order_key(score_g) << 32 | ~g. Keys are unique and a larger key means a higher
+// score, or an equal score and a lower index, so the output (score descending, index ascending) is
+// the kk = min(k, visible) largest keys in descending order.
+//
+// scan (grid: ranges x slots). A workgroup scores the visible keys of one range of at most 4096
+//   entries into LDS and counts a 4096-bin histogram of the top 12 bits of their keys. It then
+//   publishes a list P of its keys and a bound u that is at least every key it did not publish:
+//   P = the keys of the bins from b_pub up, where b_pub is the highest bin whose suffix count
+//   reaches cmin (one bin higher when that would overflow the list), and u = the largest key
+//   below b_pub (0 when none). Nothing else leaves the workgroup: no score array, no global
+//   histogram.
+// topk (grid: parts x slots). Every workgroup of a slot takes the union U of the slot's lists and
+//   T = the kk-th largest key of U (1 when U holds fewer than kk keys: then every key counts).
+//   U is a subset of all keys, so T is at most the true kk-th largest key. A range whose bound is
+//   below T therefore has no unpublished key in the top-kk: its part of the top-kk is in U. A range
+//   whose bound is at least T is scored again in full, its list replaced by all its keys >= T,
+//   and T recomputed (it can only rise, so the remaining ranges are checked against the new T).
+//   The keys >= T that remain are exactly the top-kk. Each workgroup ranks its share of them
+//   (the output position of a key is the number of larger keys in the set) and writes idx and
+//   score. With random keys a range holds about kk * range / visible of the top-kk and publishes
+//   several times that, so the re-scoring path is rare; it keeps the result exact when the
+//   relevant entries cluster (many of the top-kk in one range, or ties).
+#include <math.h>
+
+#include "index_common.h"
+
+namespace csah {
+
+constexpr int kUMax = 8192;           // union keys a top-k workgroup holds in LDS
+constexpr int kCandRange = 4096;      // keys per range at most: the LDS score array
+constexpr int kCandMaxRanges = 1024;  // ranges per slot at most (lists of at least 8 keys)
+constexpr int kCandThreads = 256;
+
+struct CandWs {
+  char* base;
+  size_t slot_bytes;
+  int R, cap;  // ranges per slot, keys per published list
+  __device__ uint64_t* keys(int s) const { return (uint64_t*)(base + (size_t)s * slot_bytes); }
+  __device__ uint64_t* bound(int s) const { return keys(s) + (size_t)R * cap; }
+};
+
+static inline size_t cand_al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// One slot's share of the workspace: every list and bound of the largest plan (R * cap <= kUMax).
+size_t index_cand_slot_bytes() { return cand_al256((size_t)(kUMax + kCandMaxRanges) * 8); }
+
+bool index_cand_plan(int slots, int64_t N, int k, int page_shift, CandPlan* p) {
+  const int64_t n = N > 0 ? N : 1;
+  // about 512 scan workgroups, ranges of 256..4096 keys
+  int64_t chunk = ((int64_t)slots * n + 511) / 512;
+  chunk = (chunk + 255) / 256 * 256;
+  if (chunk < 256) chunk = 256;
+  if (chunk > kCandRange) chunk = kCandRange;
+  // paged keys: a range spans at most 1024 pages (+1 partial one), which fits the page list
+  if (page_shift >= 0 && chunk > ((int64_t)1024 << page_shift)) chunk = (int64_t)1024 << page_shift;
+  const int64_t R = (n + chunk - 1) / chunk;
+  if (R > kCandMaxRanges) return false;
+  p->chunk = (int)chunk;
+  p->R = (int)R;
+  int cap = (int)(kUMax / R) & ~7;
+  if (cap > chunk) cap = (int)chunk;
+  p->cap = cap;
+  // a range holds about e of the top-kk; publishing e + 4 sqrt(e) + 8 makes a re-score rare
+  const int64_t kk = k < n ? k : n;
+  const double e = (double)kk * (double)chunk / (double)n;
+  int cmin = (int)ceil(e + 4.0 * sqrt(e) + 8.0);
+  if (cmin > cap) cmin = cap;
+  if (cmin < 1) cmin = 1;
+  p->cmin = cmin;
+  return true;
+}
+
+// ---- scoring a range ---------------------------------------------------------------------------
+// Scores of the keys [g0, g0 + n) of sequence b (1 <= n <= kCandRange) against query slot `slot`
+// into stage[0..n); with COUNT also a histogram of the top 12 bits of their order keys. Threads
+// 0..255 (four wavefronts) take part; `pages` holds the range's page list when PAGED. The scan
+// and the re-scoring in the top-k kernel run this same code, so they produce the same values.
+
+// 128-dim keys, at most 4 indexer heads: v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1 operands takes
+// A = 16 keys (lane l: key l%16, 32-element block l/16, with the block's E8M0 scale) and B = the
+// query's heads as columns (lane l: head l%16, block l/16; columns past the head count are zero
+// codes) and leaves in register i of lane l the head-(l%16) score of key 4(l/16)+i, every product
+// exactly scaled. A transposing quad reduction (two exchanges, each sending the values the partner
+// keeps) leaves lane c of a quad with key c's sum over the 4 heads. Per head the products are
+// exact; while the products' absolute sum spans fewer than 24 bits of the finest granularity every
+// partial sum is exact, so the score is the exact one, as in the head-summed form below.
+template <bool PAGED, bool COUNT, int U>
+__device__ __forceinline__ void score_range_mx(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
+    const EntryMap& kmap, int slot, int b, int64_t g0, int n, const int32_t* pages,
+    float* stage, uint32_t* hist) {
+  constexpr int STEP = 4 * 16 * U;  // U tiles of 16 keys per wavefront per step, double-buffered
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, kb = lane >> 4;
+  i32x8 qb = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  int qe = 127;
+  if (col < HI) {
+    const int64_t qrow = (int64_t)slot * HI + col;
+    const u32x4 v = *(const u32x4*)(q_codes + qrow * 64 + 16 * kb);
+    qb[0] = (int)v[0];
+    qb[1] = (int)v[1];
+    qb[2] = (int)v[2];
+    qb[3] = (int)v[3];
+    qe = q_scales[qrow * 4 + kb];
+  }
+  const int64_t base_row = PAGED ? 0 : kmap.row(b, g0);
+  const uint8_t* kcu = k_codes + base_row * 64;
+  const uint8_t* ksu = k_scales + base_row * 4;
+  const uint32_t off0 = PAGED ? (uint32_t)(g0 & (((int64_t)1 << kmap.shift) - 1)) : 0u;
+  const int wkey = wave * 16 * U + col;  // this lane's key in tile 0 of a step
+  auto load = [&](int r0, u32x4* c, uint32_t* e, bool clamp) {
+    if (!PAGED && !clamp) {  // workgroup-uniform base per step, per-lane constant offsets
+      const uint8_t* pc = kcu + (size_t)(uint32_t)r0 * 64u;
+      const uint8_t* ps = ksu + (size_t)(uint32_t)r0 * 4u;
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        c[u] = __builtin_nontemporal_load(
+            (const u32x4*)(pc + (uint32_t)wkey * 64u + 16u * kb + u * 1024));
+        e[u] = ps[(uint32_t)wkey * 4u + kb + u * 64];
+      }
+      return;
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      int r = r0 + wkey + 16 * u;
+      if (clamp) r = r < n ? r : n - 1;  // rows past the range read a valid row (masked below)
+      if constexpr (PAGED) {
+        const uint64_t row = page_row(pages, off0 + (uint32_t)r, kmap.shift);
+        c[u] = __builtin_nontemporal_load((const u32x4*)(k_codes + row * 64u + 16u * kb));
+        e[u] = k_scales[row * 4u + kb];
+      } else {
+        c[u] = __builtin_nontemporal_load((const u32x4*)(kcu + (uint32_t)r * 64u + 16u * kb));
+        e[u] = ksu[(uint32_t)r * 4u + kb];
+      }
+    }
+  };
+  const bool hi2 = (col & 2) != 0, hi1 = (col & 1) != 0;
+  auto score = [&](int r0, const u32x4* c, const uint32_t* e) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const i32x8 a = i32x8{(int)c[u][0], (int)c[u][1], (int)c[u][2], (int)c[u][3], 0, 0, 0, 0};
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qb, z, 4, 4, 0,
+                                                                       (int)e[u], 0, qe);
+      // quad lane c: p[j] = head c of key j (of this lane's 4 keys); keep the keys whose bit 1
+      // is c's bit 1 and take the partner c^2's heads for them
+      const float s0 = (hi2 ? p[2] : p[0]) + quad_read<0x4E>(hi2 ? p[0] : p[2]);
+      const float s1 = (hi2 ? p[3] : p[1]) + quad_read<0x4E>(hi2 ? p[1] : p[3]);
+      // then key c itself, with the partner c^1's two heads of it
+      const float v = (hi1 ? s1 : s0) + quad_read<0xB1>(hi1 ? s0 : s1) + 0.0f;  // -0 -> +0
+      const int r = r0 + wave * 16 * U + 16 * u + 4 * kb + col;  // key c = col of the quad
+      if (col < 4 && r < n) {
+        stage[r] = v;
+        if constexpr (COUNT) atomicAdd(&hist[order_key(v) >> kBinShift], 1u);
+      }
+    }
+  };
+  u32x4 ca[U], cb[U];
+  uint32_t ea[U], eb[U];
+  load(0, ca, ea, STEP > n);
+  for (int r0 = 0; r0 < n; r0 += 2 * STEP) {
+    const bool has_b = r0 + STEP < n;
+    if (has_b) load(r0 + STEP, cb, eb, r0 + 2 * STEP > n);
+    score(r0, ca, ea);
+    if (!has_b) break;
+    if (r0 + 2 * STEP < n) load(r0 + 2 * STEP, ca, ea, r0 + 3 * STEP > n);
+    score(r0 + STEP, cb, eb);
+  }
+}
+
+// Other key widths and head counts, on the vector unit. Because the heads are combined by a plain
+// sum, the score is one dot product of the key with the head-summed query
+// qt_i = sum_h 2^(Eq_h,b(i) - 127) e2m1(q_hi), scaled per key block by 2^(Ek - 127). NB = dI/32
+// consecutive lanes score one entry, one 32-element block each; a wavefront takes 64 consecutive
+// entries per step and its 16-byte loads cover one contiguous kilobyte of codes.
+template <int NB, bool PAGED, bool COUNT, int U>
+__device__ __forceinline__ void score_range_valu(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
+    const EntryMap& kmap, int slot, int b, int64_t g0, int n, const int32_t* pages,
+    float* stage, uint32_t* hist) {
+  constexpr int EPW = 64 / NB;  // entries per wavefront per group of lanes
+  constexpr int STEP = 4 * EPW * U;  // U groups whose loads are in flight together
+  static_assert(U % NB == 0, "each lane stores U / NB scores");
+  const int tid = threadIdx.x, sub = tid % NB;
+  // wavefront w takes the entries [w * EPW * U, ...) of each step, group u the EPW entries from
+  // u * EPW on (lane q * NB + sub: entry q, block sub)
+  const int ent = (tid >> 6) * (EPW * U) + (tid & 63) / NB;
+  float qv[32];
+#pragma unroll
+  for (int j = 0; j < 32; j++) qv[j] = 0.0f;
+  for (int h = 0; h < HI; h++) {
+    const int64_t qrow = (int64_t)slot * HI + h;
+    const u32x4 w = *(const u32x4*)(q_codes + qrow * (16 * NB) + 16 * sub);
+    const float s = e8m0_to_f32(q_scales[qrow * NB + sub]);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const f32x2 v0 = fp4x2_to_f32<0>(w[j]), v1 = fp4x2_to_f32<1>(w[j]);
+      const f32x2 v2 = fp4x2_to_f32<2>(w[j]), v3 = fp4x2_to_f32<3>(w[j]);
+      qv[8 * j + 0] += v0[0] * s;
+      qv[8 * j + 1] += v0[1] * s;
+      qv[8 * j + 2] += v1[0] * s;
+      qv[8 * j + 3] += v1[1] * s;
+      qv[8 * j + 4] += v2[0] * s;
+      qv[8 * j + 5] += v2[1] * s;
+      qv[8 * j + 6] += v3[0] * s;
+      qv[8 * j + 7] += v3[1] * s;
+    }
+  }
+  const int64_t base_row = PAGED ? 0 : kmap.row(b, g0);
+  const uint8_t* kc = k_codes + base_row * (16 * NB) + 16 * sub;
+  const uint8_t* ks = k_scales + base_row * NB + sub;
+  const uint8_t* kcu = k_codes + base_row * (16 * NB);
+  const uint8_t* ksu = k_scales + base_row * NB;
+  const uint32_t lane_c = (uint32_t)ent * (16u * NB) + 16u * sub;
+  const uint32_t lane_s = (uint32_t)ent * NB + sub;
+  const uint32_t off0 = PAGED ? (uint32_t)(g0 & (((int64_t)1 << kmap.shift) - 1)) : 0u;
+  auto load = [&](int r0, u32x4* c, uint32_t* e, bool clamp) {
+    if (!PAGED && !clamp) {
+      const uint8_t* pc = kcu + (size_t)(uint32_t)r0 * (16u * NB);
+      const uint8_t* ps = ksu + (size_t)(uint32_t)r0 * NB;
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        c[u] = __builtin_nontemporal_load((const u32x4*)(pc + lane_c + u * (EPW * 16 * NB)));
+        e[u] = ps[lane_s + u * (EPW * NB)];
+      }
+      return;
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      int r = r0 + u * EPW + ent;
+      if (clamp) r = r < n ? r : n - 1;
+      if constexpr (PAGED) {
+        const uint64_t row = page_row(pages, off0 + (uint32_t)r, kmap.shift);
+        c[u] = __builtin_nontemporal_load((const u32x4*)(kc + row * (16u * NB)));
+        e[u] = ks[row * NB];
+      } else {
+        c[u] = __builtin_nontemporal_load((const u32x4*)(kc + (uint32_t)r * (16u * NB)));
+        e[u] = ks[(uint32_t)r * NB];
+      }
+    }
+  };
+  auto score = [&](int r0, const u32x4* c, const uint32_t* e) {
+    float s[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) s[u] = block_score<NB>(c[u], e[u], qv);  // in all NB lanes
+#pragma unroll
+    for (int j = 0; j < U / NB; j++) {
+      // lane (q, sub) stores group j * NB + sub's score of its entry q
+      float v = s[j * NB];
+#pragma unroll
+      for (int t = 1; t < NB; t++) v = sub == t ? s[j * NB + t] : v;
+      const int r = r0 + (j * NB + sub) * EPW + ent;
+      if (r < n) {
+        stage[r] = v;
+        if constexpr (COUNT) atomicAdd(&hist[order_key(v) >> kBinShift], 1u);
+      }
+    }
+  };
+  u32x4 ca[U], cb[U];
+  uint32_t ea[U], eb[U];
+  load(0, ca, ea, STEP > n);
+  for (int r0 = 0; r0 < n; r0 += 2 * STEP) {
+    const bool has_b = r0 + STEP < n;
+    if (has_b) load(r0 + STEP, cb, eb, r0 + 2 * STEP > n);
+    score(r0, ca, ea);
+    if (!has_b) break;
+    if (r0 + 2 * STEP < n) load(r0 + 2 * STEP, ca, ea, r0 + 3 * STEP > n);
+    score(r0 + STEP, cb, eb);
+  }
+}
+
+// DEEP: four loads per lane in flight (the scan); otherwise as few as the lane layout allows (the
+// top-k kernel's re-scoring, which must stay within 128 registers). Each key's arithmetic is the
+// same either way.
+template <bool MX, int NB, bool PAGED, bool COUNT, bool DEEP>
+__device__ __forceinline__ void score_range(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales,
+    const EntryMap& kmap, int slot, int b, int64_t g0, int n, const int32_t* pages,
+    float* stage, uint32_t* hist) {
+  if constexpr (MX)
+    score_range_mx<PAGED, COUNT, DEEP ? 4 : 1>(q_codes, q_scales, HI, k_codes, k_scales, kmap,
+                                                slot, b, g0, n, pages, stage, hist);
+  else
+    score_range_valu<NB, PAGED, COUNT, DEEP ? 4 : NB>(q_codes, q_scales, HI, k_codes, k_scales,
+                                                       kmap, slot, b, g0, n, pages, stage, hist);
+}
+
+// The top-k kernel's re-scoring of one range, out of line: it runs rarely, and kept apart its
+// registers do not crowd the top-k kernel's own (1024 threads leave 128 per lane).
+template <bool MX, int NB, bool PAGED>
+__device__ __attribute__((noinline)) void rescore_range(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
+    int slot, int b, int64_t g0, int n, const int32_t* pages, float* stage) {
+  score_range<MX, NB, PAGED, false, false>(q_codes, q_scales, HI, k_codes, k_scales, kmap, slot, b,
+                                           g0, n, pages, stage, nullptr);
+}
+
+__device__ __forceinline__ uint64_t make_key(float s, int64_t g) {
+  return ((uint64_t)order_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)g);
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+// ---- wavefront scans on DPP -------------------------------------------------------------------
+// Row shifts by 1, 2, 4 and 8 give every lane the inclusive scan of its 16-lane row; broadcasting
+// lane 15 into rows 1 and 3, then lane 31 into rows 2 and 3, extends it to the whole wavefront.
+// Lanes whose source lies outside the row, and rows the mask leaves out, take the identity.
+__device__ __forceinline__ uint32_t wave_prefix_add(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);
+  return v;
+}
+
+// Inclusive scan within each 16-lane row (lane 15 of a row ends with the row's sum).
+__device__ __forceinline__ uint32_t row_prefix_add(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);
+  return v;
+}
+
+// Maximum over the wavefront (every lane gets it).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// 64-bit maximum over the wavefront: the high words first, then the low words of the lanes that
+// hold the largest high word.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  const uint32_t h = wave_max_u32((uint32_t)(v >> 32));
+  const uint32_t l = wave_max_u32((uint32_t)(v >> 32) == h ? (uint32_t)v : 0u);
+  return ((uint64_t)h << 32) | l;
+}
+
+// ---- block-wide helpers (all NT threads of the workgroup call them) ----------------------------
+template <int NT>
+struct Blk {
+  static constexpr int NW = NT / 64;
+  // lanes below this one in the wavefront whose bit of m is set
+  static __device__ __forceinline__ uint32_t below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  }
+  static __device__ __forceinline__ uint32_t sum(uint32_t v) {
+    __shared__ uint32_t s_w[NW];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_add(v), 63);
+    if (lane == 0) s_w[wave] = v;
+    __syncthreads();
+    uint32_t r = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) r += s_w[w];
+    __syncthreads();
+    return r;
+  }
+  static __device__ __forceinline__ uint64_t max64(uint64_t v) {
+    __shared__ uint64_t s_w[NW];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_max_u64(v);
+    if (lane == 0) s_w[wave] = v;
+    __syncthreads();
+    uint64_t r = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) r = max_u64(r, s_w[w]);
+    __syncthreads();
+    return r;
+  }
+  // (min of a, max of b) over the workgroup, one exchange
+  static __device__ __forceinline__ void minmax32(uint32_t a, uint32_t b, uint32_t* mn,
+                                                  uint32_t* mx) {
+    __shared__ uint32_t s_a[NW], s_b[NW];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    a = ~wave_max_u32(~a);
+    b = wave_max_u32(b);
+    if (lane == 0) {
+      s_a[wave] = a;
+      s_b[wave] = b;
+    }
+    __syncthreads();
+    uint32_t ra = 0xFFFFFFFFu, rb = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+      ra = min(ra, s_a[w]);
+      rb = max(rb, s_b[w]);
+    }
+    __syncthreads();
+    *mn = ra;
+    *mx = rb;
+  }
+  static __device__ __forceinline__ uint32_t max32(uint32_t v) {
+    __shared__ uint32_t s_w[NW];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_max_u32(v);
+    if (lane == 0) s_w[wave] = v;
+    __syncthreads();
+    uint32_t r = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) r = max(r, s_w[w]);
+    __syncthreads();
+    return r;
+  }
+  // The bin holding the r-th largest counted item of an nb-bin LDS histogram (bin order = item
+  // order): *bin, and *above = the count in the higher bins; returns the total count (when it is
+  // below r, *bin and *above are not set).
+  static __device__ __forceinline__ uint32_t find_bin(const uint32_t* hist, int nb, uint32_t r,
+                                                      uint32_t* bin, uint32_t* above) {
+    __shared__ uint32_t s_w[NW];
+    __shared__ uint32_t s_bin, s_above;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int per = (nb + NT - 1) / NT;
+    const int lo = t * per;
+    uint32_t v = 0;
+    for (int j = 0; j < per; j++) v += lo + j < nb ? hist[lo + j] : 0u;
+    const uint32_t pre = wave_prefix_add(v);
+    const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63);
+    if (lane == 0) s_w[wave] = wtot;
+    __syncthreads();
+    uint32_t above_w = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; w++) {
+      above_w += w > wave ? s_w[w] : 0u;
+      total += s_w[w];
+    }
+    const uint32_t suf = above_w + wtot - pre + v;  // items in this thread's bins and above
+    const uint32_t next = suf - v;                  // items above this thread's bins
+    if (suf >= r && next < r) {  // exactly one thread: the suffix count crosses r here
+      uint32_t acc = next, bsel = (uint32_t)lo;
+      for (int j = per - 1; j >= 0; j--) {
+        const uint32_t c = lo + j < nb ? hist[lo + j] : 0u;
+        if (acc + c >= r) {
+          bsel = (uint32_t)(lo + j);
+          break;
+        }
+        acc += c;
+      }
+      s_bin = bsel;
+      s_above = acc;
+    }
+    __syncthreads();
+    *bin = s_bin;
+    *above = s_above;
+    return total;
+  }
+  // Exclusive suffix sums of an nb-bin LDS histogram into out[b] = sum of cnt[b'] for b' > b
+  // (the start of bin b when the bins are laid out from the top down).
+  static __device__ __forceinline__ void suffix_starts(const uint32_t* cnt, int nb, uint32_t* out) {
+    __shared__ uint32_t s_w[NW];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int per = (nb + NT - 1) / NT;
+    const int lo = t * per;
+    uint32_t v = 0;
+    for (int j = 0; j < per; j++) v += lo + j < nb ? cnt[lo + j] : 0u;
+    const uint32_t pre = wave_prefix_add(v);
+    const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63);
+    if (lane == 0) s_w[wave] = wtot;
+    __syncthreads();
+    uint32_t above = wtot - pre;  // bins of the higher threads of this wavefront
+#pragma unroll
+    for (int w = 0; w < NW; w++) above += w > wave ? s_w[w] : 0u;
+    for (int j = per - 1; j >= 0; j--) {
+      if (lo + j < nb) {
+        out[lo + j] = above;
+        above += cnt[lo + j];
+      }
+    }
+    __syncthreads();
+  }
+};
+
+// Keys held in registers, KPT per thread: key j of thread t is item t + NT * j (0 = no key).
+
+// Stable compaction of the register-held keys (item t + NT * j, considered while below n) for
+// which keep(x) holds into out[base..), in item order. Returns how many were kept.
+template <int NT, int KPT, typename F>
+__device__ __forceinline__ int compact_regs(const uint64_t (&x)[KPT], int n, F keep,
+                                            uint64_t* out, int base) {
+  typedef Blk<NT> B;
+  constexpr int NW = NT / 64, NC = KPT * NW;
+  static_assert(NC <= 128, "one wavefront scans the counts, two per lane");
+  __shared__ uint32_t s_cnt[NC];
+  __shared__ uint32_t s_total;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  uint64_t m[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; j++) {
+    const bool f = t + NT * j < n && keep(x[j]);
+    m[j] = __ballot(f);
+    if (lane == 0) s_cnt[j * NW + wave] = (uint32_t)__popcll(m[j]);
+  }
+  __syncthreads();
+  if (wave == 0) {  // exclusive scan of the counts in (j, wavefront) order, which is item order
+    const uint32_t c0 = 2 * lane < NC ? s_cnt[2 * lane] : 0u;
+    const uint32_t c1 = 2 * lane + 1 < NC ? s_cnt[2 * lane + 1] : 0u;
+    const uint32_t incl = wave_prefix_add(c0 + c1);
+    const uint32_t ex = incl - c0 - c1;
+    if (2 * lane < NC) s_cnt[2 * lane] = ex;
+    if (2 * lane + 1 < NC) s_cnt[2 * lane + 1] = ex + c0;
+    if (lane == 63) s_total = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < KPT; j++)
+    if ((m[j] >> lane) & 1) out[base + (int)s_cnt[j * NW + wave] + (int)B::below(m[j])] = x[j];
+  const int total = (int)s_total;
+  __syncthreads();
+  return total;
+}
+
+// Load items [0, n) of an LDS key array into the register layout of compact_regs / top_sorted.
+template <int NT, int KPT>
+__device__ __forceinline__ void load_regs(const uint64_t* buf, int n, uint64_t (&x)[KPT]) {
+#pragma unroll
+  for (int j = 0; j < KPT; j++) {
+    const int at = (int)threadIdx.x + NT * j;
+    x[j] = at < n ? buf[at] : 0;
+  }
+}
+
+// ---- scan: score a range, publish its list and bound ------------------------------------------
+// stage[0..n): the range's scores (entry g0 + j), hist: their 4096-bin histogram. Writes the
+// published keys to out[0..cap) (in no particular order: the top-k ranks by value), zero padded,
+// and the largest unpublished key (0: none) to *bnd. Three barriers.
+__device__ void publish_candidates(const float* stage, const uint32_t* hist, int n, int64_t g0,
+                                   int cmin, int cap, uint64_t* __restrict__ out,
+                                   uint64_t* __restrict__ bnd) {
+  constexpr int NT = kCandThreads, NW = NT / 64, KPT = kCandRange / NT;
+  static_assert(kBins == 16 * NT, "each thread owns 16 bins");
+  __shared__ uint32_t s_w[NW];
+  __shared__ uint32_t s_bpub, s_cnt;
+  __shared__ uint64_t s_umax;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (t == 0) {
+    s_bpub = 0;  // publish every bin when the range fits the list
+    s_cnt = 0;
+    s_umax = 0;
+  }
+  if (n > cap) {  // uniform: b* = the highest bin whose suffix count reaches cmin
+    uint32_t h[16];
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) {
+      const u32x4 v4 = *(const u32x4*)(hist + 16 * t + j);
+      h[j] = v4[0];
+      h[j + 1] = v4[1];
+      h[j + 2] = v4[2];
+      h[j + 3] = v4[3];
+    }
+    uint32_t v = 0;
+#pragma unroll
+    for (int j = 0; j < 16; j++) v += h[j];
+    const uint32_t pre = wave_prefix_add(v);
+    const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)pre, 63);
+    if (lane == 0) s_w[wave] = wtot;
+    __syncthreads();
+    uint32_t above = wtot - pre;
+#pragma unroll
+    for (int w = 0; w < NW; w++) above += w > wave ? s_w[w] : 0u;
+    const uint32_t r = (uint32_t)cmin;
+    if (above < r && above + v >= r) {  // this thread's bins hold the cmin-th largest
+      uint32_t bsel = 16 * t, with_b = 0;
+#pragma unroll
+      for (int j = 15; j >= 0; j--) {
+        if (with_b == 0 && above + h[j] >= r) {
+          bsel = 16 * t + j;
+          with_b = above + h[j];  // keys in the bins from bsel up
+        }
+        above += h[j];
+      }
+      s_bpub = with_b <= (uint32_t)cap ? bsel : bsel + 1;  // the bins above hold < cmin <= cap
+    }
+  }
+  __syncthreads();
+  const uint32_t bpub = s_bpub;
+  uint64_t umax = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; j++) {  // item t + 256 j: conflict-free LDS reads
+    const int at = t + NT * j;
+    if (at >= n) break;
+    const float v = stage[at];
+    const uint64_t key = make_key(v, g0 + at);
+    if ((order_key(v) >> kBinShift) >= bpub) out[atomicAdd(&s_cnt, 1u)] = key;
+    else umax = max_u64(umax, key);
+  }
+  umax = wave_max_u64(umax);
+  if (lane == 0 && umax) atomicMax((unsigned long long*)&s_umax, (unsigned long long)umax);
+  __syncthreads();
+  for (int j = (int)s_cnt + t; j < cap; j += NT) out[j] = 0;
+  if (t == 0) *bnd = s_umax;
+}
+
+template <bool MX, int NB, bool PAGED>
+__global__ __launch_bounds__(kCandThreads) void index_cand_scan_kernel(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
+    int64_t N, const int64_t* __restrict__ pos, int m, int Q, int chunk, int cmin, CandWs cw) {
+  const int slot = blockIdx.y, r = blockIdx.x, b = slot / Q, i = slot - b * Q;
+  __shared__ uint32_t hist[kBins];
+  __shared__ __attribute__((aligned(16))) float stage[kCandRange];
+  __shared__ int32_t pages[PAGED ? kPageList : 1];
+  for (int j = threadIdx.x; j < kBins; j += kCandThreads) hist[j] = 0u;
+  const int64_t nv = visible_entries(pos, b, i, m, N);
+  const int64_t g0 = (int64_t)r * chunk;
+  const int n = g0 < nv ? (int)(nv - g0 < chunk ? nv - g0 : chunk) : 0;
+  if constexpr (PAGED) {
+    if (n > 0) load_page_list(kmap, b, g0, g0 + n, pages, threadIdx.x, kCandThreads);
+  }
+  __syncthreads();
+  if (n > 0)
+    score_range<MX, NB, PAGED, true, true>(q_codes, q_scales, HI, k_codes, k_scales, kmap, slot, b, g0,
+                                     n, pages, stage, hist);
+  __syncthreads();
+  publish_candidates(stage, hist, n, g0, cmin, cw.cap, cw.keys(slot) + (size_t)r * cw.cap,
+                     cw.bound(slot) + r);
+}
+
+// ---- top-k over the union ----------------------------------------------------------------------
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkKPT = kUMax / kTopkThreads;  // union keys per thread, in registers
+
+// Ranks the nonzero register-held keys (distinct) in descending order, writes the first kk of
+// them (io[rank], so[rank]) and returns the kk-th largest (1 when there are fewer than kk: then all
+// are written). A bucket sort from the top: bins fitted to the keys' range (whole high words), so
+// they spread over up to 4096 bins; a key's rank is its bin's start (the count in the higher bins)
+// plus the larger keys in its own bin, which holds few. cnt and cur are 4096-entry LDS arrays,
+// sorted an LDS array of kUMax keys.
+template <int NT, int KPT>
+__device__ uint64_t top_sorted(const uint64_t (&x)[KPT], uint32_t kk, uint32_t* cnt,
+                               uint32_t* cur, uint64_t* sorted, int32_t* __restrict__ io,
+                               float* __restrict__ so) {
+  typedef Blk<NT> B;
+  __shared__ uint64_t s_T;
+  const int t = threadIdx.x;
+  uint32_t lh = 0xFFFFFFFFu, hh = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; j++)
+    if (x[j] != 0) {
+      lh = min(lh, (uint32_t)(x[j] >> 32));
+      hh = max(hh, (uint32_t)(x[j] >> 32));
+    }
+  B::minmax32(lh, hh, &lh, &hh);
+  if (t == 0) s_T = 1;
+  if (lh > hh) {  // no key at all
+    __syncthreads();
+    return 1;
+  }
+  uint64_t base = (uint64_t)lh << 32;
+  uint64_t span = ((((uint64_t)hh) << 32) | 0xFFFFFFFFull) - base;
+  if (lh == hh) {  // one score (ties everywhere): fit the bins to the low words instead
+    uint32_t ll = 0xFFFFFFFFu, hl = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; j++)
+      if (x[j] != 0) {
+        ll = min(ll, (uint32_t)x[j]);
+        hl = max(hl, (uint32_t)x[j]);
+      }
+    B::minmax32(ll, hl, &ll, &hl);
+    base |= ll;
+    span = hl - ll;
+  }
+  const int bits = span ? 64 - __clzll((long long)span) : 0;
+  const int s = bits > 12 ? bits - 12 : 0;
+  const int nb = (int)(span >> s) + 1;
+  for (int j = t; j < nb; j += NT) cnt[j] = 0u;
+  __syncthreads();
+  uint32_t bn[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; j++) {
+    bn[j] = (uint32_t)((x[j] - base) >> s);
+    if (x[j] != 0) atomicAdd(&cnt[bn[j]], 1u);
+  }
+  __syncthreads();
+  B::suffix_starts(cnt, nb, cur);
+  uint32_t at[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; j++)
+    if (x[j] != 0) at[j] = atomicAdd(&cur[bn[j]], 1u);
+#pragma unroll
+  for (int j = 0; j < KPT; j++)
+    if (x[j] != 0) sorted[at[j]] = x[j];
+  __syncthreads();
+  // cur[b] is now the end of bin b, which starts at cur[b] - cnt[b]. The keys that can rank
+  // below kk sit at the positions before the end of the bin holding position kk - 1 (all of them,
+  // when there are fewer keys): one or two per thread.
+  const uint32_t total = cur[0];  // bin 0 ends at the last position
+  uint32_t lim = total;
+  if (kk < total) lim = cur[(uint32_t)((sorted[kk - 1] - base) >> s)];
+  for (uint32_t p = t; p < lim; p += NT) {
+    const uint64_t y = sorted[p];
+    const uint32_t b = (uint32_t)((y - base) >> s);
+    const uint32_t e = cur[b], st = e - cnt[b];
+    uint32_t rank = st;
+    for (uint32_t q = st; q < e; q++) rank += sorted[q] > y ? 1u : 0u;
+    if (rank < kk) {
+      io[rank] = (int32_t)(0xFFFFFFFFu - (uint32_t)y);
+      if (so) so[rank] = key_to_float((uint32_t)(y >> 32));
+      if (rank == kk - 1) s_T = y;
+    }
+  }
+  __syncthreads();
+  const uint64_t T = s_T;
+  __syncthreads();
+  return T;
+}
+
+// One workgroup per slot.
+template <bool MX, int NB, bool PAGED>
+__global__ __launch_bounds__(kTopkThreads) void index_cand_topk_kernel(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
+    int64_t N, const int64_t* __restrict__ pos, int m, int Q, int chunk, int k, CandWs cw,
+    int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+  constexpr int NT = kTopkThreads, KPT = kTopkKPT;
+  const int slot = blockIdx.x;
+  const int b = slot / Q, i = slot - b * Q, t = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) uint64_t buf[kUMax];
+  __shared__ uint32_t hist[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t stage_u[kCandRange];
+  __shared__ uint64_t bnd[kCandMaxRanges];
+  __shared__ int32_t pages[PAGED ? kPageList : 1];
+  __shared__ int s_next;
+  float* stage = (float*)stage_u;
+  const int R = cw.R, nU = R * cw.cap;  // nU <= kUMax
+  uint64_t x[KPT];
+  {  // the union straight into registers, 16-byte loads all in flight together (which key sits
+     // in which register does not matter: the ranking goes by value)
+    const u32x4* src = (const u32x4*)cw.keys(slot);
+#pragma unroll
+    for (int j = 0; j < KPT / 2; j++) {
+      const int at = t + NT * j;  // key pair at, nU even
+      const u32x4 v = 2 * at < nU ? __builtin_nontemporal_load(src + at) : u32x4{0u, 0u, 0u, 0u};
+      x[2 * j] = ((uint64_t)v[1] << 32) | v[0];
+      x[2 * j + 1] = ((uint64_t)v[3] << 32) | v[2];
+    }
+    const uint64_t* bs = cw.bound(slot);
+    for (int j = t; j < R; j += NT) bnd[j] = bs[j];
+    if (t == 0) s_next = 0x7FFFFFFF;
+  }
+  const int64_t nv = visible_entries(pos, b, i, m, N);
+  const uint32_t kk = (uint32_t)(nv < k ? nv : k);
+  int32_t* io = idx_out + (int64_t)slot * k;
+  float* so = score_out ? score_out + (int64_t)slot * k : nullptr;
+  for (int j = (int)kk + t; j < k; j += NT) {
+    io[j] = -1;
+    if (so) so[j] = -INFINITY;
+  }
+  if (kk == 0) return;
+  uint64_t T = top_sorted<NT, KPT>(x, kk, hist, stage_u, buf, io, so);
+  // a range whose bound reaches T holds unlisted keys that may rank below kk: those ranges are
+  // scored again, in index order, and the ranking redone over the result
+  for (int w = t; w < R; w += NT)
+    if (bnd[w] >= T) atomicMin(&s_next, w);
+  __syncthreads();
+  int w = s_next;
+  __syncthreads();
+  if (w >= R) return;
+  // every register slot is considered (the union's pair layout is not compact_regs' item order);
+  // empty slots hold 0 < T
+  int n = compact_regs<NT, KPT>(x, kUMax, [&](uint64_t y) { return y >= T; }, buf, 0);
+  for (;;) {
+    const int64_t g0 = (int64_t)w * chunk;
+    const int gn = (int)(nv - g0 < chunk ? nv - g0 : chunk);  // >= 1: a nonzero bound
+    const uint32_t lo = (uint32_t)g0, hi = (uint32_t)(g0 + gn);
+    load_regs<NT, KPT>(buf, n, x);
+    __syncthreads();
+    n = compact_regs<NT, KPT>(x, n, [&](uint64_t y) {
+      const uint32_t g = 0xFFFFFFFFu - (uint32_t)y;
+      return g < lo || g >= hi;
+    }, buf, 0);
+    if constexpr (PAGED) {
+      load_page_list(kmap, b, g0, g0 + gn, pages, t, NT);
+      __syncthreads();
+    }
+    if (t < kCandThreads)  // the scoring loop takes four wavefronts
+      rescore_range<MX, NB, PAGED>(q_codes, q_scales, HI, k_codes, k_scales, kmap, slot, b, g0, gn,
+                                   pages, stage);
+    __syncthreads();
+    {  // append the range's keys >= T (n <= kk <= 4096 before, gn <= 4096 more)
+      constexpr int SPT = kCandRange / NT;
+      uint64_t y[SPT];
+#pragma unroll
+      for (int j = 0; j < SPT; j++) {
+        const int at = t + NT * j;
+        y[j] = at < gn ? make_key(stage[at], g0 + at) : 0;
+      }
+      n += compact_regs<NT, SPT>(y, gn, [&](uint64_t z) { return z >= T; }, buf, n);
+    }
+    load_regs<NT, KPT>(buf, n, x);
+    __syncthreads();
+    T = top_sorted<NT, KPT>(x, kk, hist, stage_u, buf, io, so);
+    n = compact_regs<NT, KPT>(x, n, [&](uint64_t y) { return y >= T; }, buf, 0);
+    if (t == 0) s_next = 0x7FFFFFFF;
+    __syncthreads();
+    for (int v = w + 1 + t; v < R; v += NT)
+      if (bnd[v] >= T) atomicMin(&s_next, v);
+    __syncthreads();
+    w = s_next;
+    __syncthreads();
+    if (w >= R) break;
+  }
+}
+
+// ---- launch ------------------------------------------------------------------------------------
+template <bool MX, int NB, bool PAGED>
+static void launch_cand_t(const IndexArgs& a, const CandPlan& p, const CandWs& w, hipStream_t s) {
+  const int slots = a.B * a.Q;
+  a.prof.launch(index_cand_scan_kernel<MX, NB, PAGED>, dim3((unsigned)p.R, (unsigned)slots),
+                dim3(kCandThreads), s, a.q_codes, a.q_scales, a.HI, a.k_codes, a.k_scales, a.kmap,
+                a.N, a.pos, a.m, a.Q, p.chunk, p.cmin, w);
+  index_cand_topk_kernel<MX, NB, PAGED><<<dim3((unsigned)slots), kTopkThreads, 0, s>>>(
+      a.q_codes, a.q_scales, a.HI, a.k_codes, a.k_scales, a.kmap, a.N, a.pos, a.m, a.Q, p.chunk,
+      a.k, w, a.idx_out, a.score_out);
+}
+
+template <bool MX, int NB>
+static void launch_cand_p(const IndexArgs& a, const CandPlan& p, const CandWs& w, hipStream_t s) {
+  if (a.kmap.table) launch_cand_t<MX, NB, true>(a, p, w, s);
+  else launch_cand_t<MX, NB, false>(a, p, w, s);
+}
+
+hipError_t launch_index_cand(const IndexArgs& a, const CandPlan& p) {
+  hipStream_t s = (hipStream_t)a.stream;
+  CandWs w;
+  w.base = (char*)a.ws;
+  w.slot_bytes = index_cand_slot_bytes();
+  w.R = p.R;
+  w.cap = p.cap;
+  if (a.dI == 128 && a.HI <= 4) launch_cand_p<true, 4>(a, p, w, s);
+  else if (a.dI == 32) launch_cand_p<false, 1>(a, p, w, s);
+  else if (a.dI == 64) launch_cand_p<false, 2>(a, p, w, s);
+  else launch_cand_p<false, 4>(a, p, w, s);
+  return hipGetLastError();
+}
+
+}  // namespace csah

@@ -51,6 +51,17 @@ def test_index_decode_page_sizes(P):
     _check_index("decode", kc, ks, qc, qs, pos, m, k, P, seed=P)
 
 
+def test_index_decode_one_entry_pages_1m_keys():
+    """One entry per page over 1,048,576 keys: a scan range may span at most 1024 pages, so the
+    decode schedule runs its largest number of ranges (1024, with the shortest published lists)."""
+    rng = np.random.default_rng(83)
+    B, N, m, k = 1, 1 << 20, 4, 1024
+    kc, ks = O.encode_rows(rng.normal(size=(B, N, 128)), O.FMT_FP4_E8M0)
+    qc, qs = O.encode_rows(rng.normal(size=(B, 1, 4, 128)), O.FMT_FP4_E8M0)
+    pos = np.array([N * m - 1], np.int64)
+    _check_index("decode P=1 1M", kc, ks, qc, qs, pos, m, k, 1, seed=3)
+
+
 @pytest.mark.parametrize("P", [4, 128])
 def test_index_multi_query_page_sizes(P):
     """5 queries per sequence (one MFMA pass over paged keys, scores stored)."""
