@@ -23,6 +23,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# Per-file code generation options. attend.hip: matrix-core accumulators live in ordinary VGPRs
+# (the kernels rescale them with vector multiplies; held in AGPRs, every tile copied all of them
+# out and back around that rarely taken branch).
+FILE_FLAGS = {
+    "attend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _run(cmd):
@@ -42,7 +48,7 @@ def build(verbose: bool = False) -> str:
     procs = []
     for s in srcs:
         o = os.path.join(BUILD, os.path.basename(s) + ".o")
-        cmd = [HIPCC, *FLAGS, "-c", s, "-o", o]
+        cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(s), []), "-c", s, "-o", o]
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
                                             text=True)))
         objs.append(o)

@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttendK p) {
     int64_t nv = (pos_b + qi + 1) / p.m;
     Rc = nv < 0 ? 0 : (nv > p.N ? p.N : nv);
   } else {
-    Rc = p.k;
+    Rc = p.N > 0 ? p.k : 0;  // no compressed row can be valid without entries: none is read
   }
   const int64_t R = Rc + p.w;
   const int64_t r0 = (int64_t)split * p.rows_per_split;
@@ -493,14 +493,31 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttendK p) {
 // waits overlap the other's matrix work.
 constexpr int kXTile = 32, kXRS = 528, kXTileElems = kXTile * kXRS;
 
+// Max over the four 16-lane rows of a wavefront, in every lane: gfx950's permlane swaps exchange
+// rows 0<->1 and 2<->3 (16-lane swap), then the two halves (32-lane swap), so each lane ends up
+// holding the max of lanes l, l^16, l^32 and l^48.
+__device__ __forceinline__ float max_row_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+  x = fmaxf(u2f(a[0]), u2f(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return fmaxf(u2f(c[0]), u2f(c[1]));
+}
+
 struct TileRawX {
   u32x2 e[7];  // E4M3 bytes 64i + 8(t%8) .. +8
   u32x4 r;     // bf16 dims 448 + 8(t%8) .. +8
 };
 
-template <bool DENSE, bool PAGED>
-__global__ __launch_bounds__(256, 2) void attend_x_kernel(AttendK p) {
+// MINW: workgroups per CU the register budget is sized for. Grids of up to one workgroup per CU
+// (decode) take 1, so a wavefront may hold all 512 registers and nothing spills; larger grids
+// (prefill) take 2, so two workgroups overlap each other's waits.
+template <bool DENSE, bool PAGED, int MINW>
+__global__ __launch_bounds__(256, MINW) void attend_x_kernel(AttendK p) {
   constexpr int D = 512, NCH = 16, NT = 32, RB = 576;
+  // Tiles whose rows are in flight: with a CU's whole register file (MINW = 1) the rows of the
+  // next two tiles load while one is computed, which covers a gather's latency; with two
+  // workgroups per CU the other workgroup covers it and one tile ahead keeps registers free.
+  constexpr int PREF = MINW == 1 ? 2 : 1;
   __shared__ __attribute__((aligned(16))) __bf16 ytile[2][kXTileElems];  // double buffer
   __shared__ uint32_t s_mask[2][4];  // [buffer][loading wavefront]: 8 row bits each
 
@@ -510,25 +527,22 @@ __global__ __launch_bounds__(256, 2) void attend_x_kernel(AttendK p) {
   const int lrow = tid >> 3, lk = tid & 7;  // the tile row this thread loads, its slot
   // Workgroups are dispatched round-robin over the 8 XCDs; consecutive workgroups of one XCD take
   // the head blocks of one (query, split) unit so that its rows are fetched into one L2.
-  const int64_t wg = blockIdx.x;
-  const int64_t unit = (wg / (8 * p.hg)) * 8 + (wg & 7);
-  const int hb = (int)((wg >> 3) % p.hg);
-  if (unit >= (int64_t)p.splits * p.slots) return;
-  const int slot = (int)(unit / p.splits), split = (int)(unit - (int64_t)slot * p.splits);
-  const int b = slot / p.Q, qi = slot - b * p.Q;
+  // (32-bit workgroup arithmetic, kept in scalar registers: grids stay below 2^31)
+  // Every kernel argument in one round trip: left alone, the compiler loads each field where it
+  // is first used, and the chain of dependent scalar loads costs microseconds at start-up.
+  asm volatile("" ::"s"(p.q), "s"(p.H), "s"(p.cache), "s"(p.cmap.table), "s"(p.cmap.stride),
+               "s"(p.cmap.shift), "s"(p.N), "s"(p.idx), "s"(p.k), "s"(p.m), "s"(p.win),
+               "s"(p.wstride), "s"(p.w), "s"(p.pos), "s"(p.sink), "s"(p.scale_log2), "s"(p.Q),
+               "s"(p.splits), "s"(p.rows_per_split), "s"(p.hg), "s"(p.slots), "s"(p.out),
+               "s"(p.lse), "s"(p.part));
+  const int wg = blockIdx.x;
+  const int unit = (wg / (8 * p.hg)) * 8 + (wg & 7);
+  const int hb = (wg >> 3) % p.hg;
+  if (unit >= p.splits * p.slots) return;
+  const int slot = __builtin_amdgcn_readfirstlane(unit / p.splits);
+  const int split = unit - slot * p.splits;
+  const int b = __builtin_amdgcn_readfirstlane(slot / p.Q), qi = slot - b * p.Q;
   const int head = hb * 64 + hgl * 16 + n;
-
-  // query fragments: B operand of S^T = Y Q^T (k = dims 32c + 8g + e, n = head)
-  bf16x8 qf[NCH];
-#pragma unroll
-  for (int c = 0; c < NCH; c++) {
-    if (head < p.H)
-      qf[c] = __builtin_bit_cast(
-          bf16x8, *(const u32x4*)((const uint16_t*)p.q + ((int64_t)slot * p.H + head) * D +
-                                  32 * c + 8 * g));
-    else
-      qf[c] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-  }
 
   // the logical rows of this split: compressed rows [0, Rc), then the w window rows
   const int64_t pos_b = p.pos[b];
@@ -537,14 +551,20 @@ __global__ __launch_bounds__(256, 2) void attend_x_kernel(AttendK p) {
     int64_t nv = (pos_b + qi + 1) / p.m;
     Rc = nv < 0 ? 0 : (nv > p.N ? p.N : nv);
   } else {
-    Rc = p.k;
+    Rc = p.N > 0 ? p.k : 0;  // no compressed row can be valid without entries: none is read
   }
   const int64_t R = Rc + p.w;
   const int64_t r0 = (int64_t)split * p.rows_per_split;
   const int64_t r1 = r0 + p.rows_per_split < R ? r0 + p.rows_per_split : R;
   const int64_t rc_end = Rc < r1 ? Rc : r1;
-  const uint8_t* dummy = p.N > 0 ? p.cache + (PAGED ? p.cmap.paged(b, 0) : p.cmap.flat(b, 0)) * RB
-                                 : p.win + (int64_t)b * p.wstride * RB;
+  // Every tile issues the same loads whether its rows exist or not (absent rows read a dummy
+  // that is always mapped: a cache or window row, else the query), so the wait before a tile's
+  // rows are used covers only that tile: a skipped load would make the wait drain every load in
+  // flight. Index loads of absent rows read this sequence's position instead.
+  const uint8_t* dummy =
+      p.N > 0 ? p.cache + (PAGED ? p.cmap.paged(b, 0) : p.cmap.flat(b, 0)) * RB
+              : (p.w > 0 ? p.win + (int64_t)b * p.wstride * RB : (const uint8_t*)p.q);
+  const int32_t* dummy_i = (const int32_t*)(p.pos + b);
   const int ntiles = r1 > r0 ? (int)((r1 - r0 + kXTile - 1) / kXTile) : 0;
   const int iters = ntiles;
 
@@ -554,35 +574,23 @@ __global__ __launch_bounds__(256, 2) void attend_x_kernel(AttendK p) {
       return 0;
     } else {
       const int64_t j = tbase + lrow;
-      return j < rc_end ? p.idx[(int64_t)slot * p.k + j] : -1;
+      const int32_t e = *(j < rc_end ? p.idx + (int64_t)slot * p.k + j : dummy_i);
+      return j < rc_end ? e : -1;
     }
-  };
-  auto resolve = [&](int64_t j, int32_t e, bool& valid) -> const uint8_t* {
-    valid = false;
-    const uint8_t* ptr = dummy;
-    if (j < rc_end) {
-      const int64_t ent = DENSE ? j : (int64_t)e;
-      if (ent >= 0 && ent < p.N) {
-        valid = true;
-        ptr = p.cache + p.cmap.flat(b, ent) * RB;
-      }
-    } else if (j < r1) {
-      const int64_t r = qi + (j - Rc);   // window buffer row
-      if (pos_b - (p.w - 1) + r >= 0) {  // its token position is >= 0
-        valid = true;
-        ptr = p.win + ((int64_t)b * p.wstride + r) * RB;
-      }
-    }
-    return ptr;
   };
   // Paged caches: a row's pool row comes from the block table, a load that depends on the
   // entry id. Ids are fetched two tiles ahead and translated one tile ahead, so neither load
   // is waited for while the current tile's rows are in flight.
   auto pool_row = [&](int64_t j, int32_t e) -> int64_t {  // -1: not a valid compressed row
-    if (j >= rc_end) return -1;
     const int64_t ent = DENSE ? j : (int64_t)e;
-    if (ent < 0 || ent >= p.N) return -1;
-    return p.cmap.paged(b, ent);
+    const bool ok = j < rc_end && ent >= 0 && ent < p.N;
+    if constexpr (PAGED) {
+      const int64_t page = *(ok ? p.cmap.table + (int64_t)b * p.cmap.stride + (ent >> p.cmap.shift)
+                                : dummy_i);
+      return ok ? (page << p.cmap.shift) | (ent & (((int64_t)1 << p.cmap.shift) - 1)) : -1;
+    } else {
+      return ok ? p.cmap.flat(b, ent) : -1;
+    }
   };
   auto resolve_row = [&](int64_t j, int64_t prow, bool& valid) -> const uint8_t* {
     valid = false;
@@ -614,45 +622,77 @@ __global__ __launch_bounds__(256, 2) void attend_x_kernel(AttendK p) {
   for (int t = 0; t < NT; t++) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.0f;
 
-  TileRawX raw;
-  bool v_raw = false;
-  int32_t e_next = -1;   // contiguous: id of this thread's row in the next tile; paged: two ahead
-  int64_t prow_next = -1;  // paged: pool row of this thread's row in the next tile
-  if (iters > 0) {
-    const int64_t t0 = r0;
-    const int32_t e0 = fetch_id(t0);
-    if constexpr (PAGED) {
-      const int32_t e1 = fetch_id(t0 + kXTile);
-      e_next = fetch_id(t0 + 2 * kXTile);
-      const int64_t prow0 = pool_row(t0 + lrow, e0);
-      prow_next = pool_row(t0 + kXTile + lrow, e1);
-      load_rows(resolve_row(t0 + lrow, prow0, v_raw), raw);
-    } else {
-      e_next = fetch_id(t0 + kXTile);
-      load_rows(resolve(t0 + lrow, e0, v_raw), raw);
-    }
+  // Ring of PREF slots, one per tile in flight. Before iteration it (slot it % PREF) the slot holds
+  // the rows of tile it, the pool row of this thread's row of tile it + PREF and the entry id of
+  // tile it + 2 PREF: each load is issued a slot cycle before the one that depends on it.
+  // Start-up order: every id first (one wait covers them), then the first tile's rows, the query
+  // fragments and the other tiles' rows, so that the first tile and the query arrive together
+  // and neither waits behind the rest.
+  TileRawX raw[PREF];
+  bool v_raw[PREF];
+  int64_t pr[PREF];
+  int32_t ee[PREF], ea[PREF], eb[PREF];
+#pragma unroll
+  for (int k = 0; k < PREF; k++) {
+    const int64_t tk = r0 + (int64_t)k * kXTile;
+    ea[k] = fetch_id(tk);
+    eb[k] = fetch_id(tk + PREF * kXTile);
+    ee[k] = fetch_id(tk + 2 * PREF * kXTile);
   }
-  for (int it = 0; it < iters; it++) {
+  int64_t pa[PREF];
+#pragma unroll
+  for (int k = 0; k < PREF; k++) pa[k] = pool_row(r0 + (int64_t)k * kXTile + lrow, ea[k]);
+  load_rows(resolve_row(r0 + lrow, pa[0], v_raw[0]), raw[0]);
+  // query fragments: B operand of S^T = Y Q^T (k = dims 32c + 8g + e, n = head)
+  bf16x8 qf[NCH];
+  {
+    // Heads past H compute with head 0's query: their results are never stored, and nothing
+    // mixes heads, so no load sits in a branch and no select waits for the loaded values.
+    const uint16_t* qrow =
+        (const uint16_t*)p.q + ((int64_t)slot * p.H + (head < p.H ? head : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < NCH; c++)
+      qf[c] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 32 * c + 8 * g));
+  }
+#pragma unroll
+  for (int k = 1; k < PREF; k++)
+    load_rows(resolve_row(r0 + (int64_t)k * kXTile + lrow, pa[k], v_raw[k]), raw[k]);
+#pragma unroll
+  for (int k = 0; k < PREF; k++) pr[k] = pool_row(r0 + (int64_t)(k + PREF) * kXTile + lrow, eb[k]);
+  // refill a slot once its rows are consumed: rows of tile it + PREF, pool row of tile
+  // it + 2 PREF, id of tile it + 3 PREF (ids and pool rows past the split read nothing)
+  auto refill = [&](int it, TileRawX& rw, bool& vr, int64_t& prr, int32_t& er) {
+    const int64_t tn = r0 + (int64_t)(it + PREF) * kXTile;
+    load_rows(resolve_row(tn + lrow, prr, vr), rw);
+    prr = pool_row(tn + PREF * kXTile + lrow, er);
+    er = fetch_id(tn + 2 * PREF * kXTile);
+  };
+  auto tile_step = [&](int it, TileRawX& raw, bool& v_raw, int64_t& prr, int32_t& er) {
     const int buf = it & 1;
     __bf16* yt = &ytile[buf][0];
     {
-      // convert and store this thread's share of the tile (masked rows become zeros)
+      // convert and store this thread's share of the tile (absent rows become zeros; a
+      // wavefront whose rows all exist skips the masking)
       __bf16* dst = yt + lrow * kXRS;
-#pragma unroll
-      for (int i = 0; i < 7; i++) {
-        const uint32_t w0 = v_raw ? raw.e[i][0] : 0u, w1 = v_raw ? raw.e[i][1] : 0u;
-        const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
-        const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
-        const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
-        const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
-        *(bf16x8*)(dst + 64 * i + 8 * lk) =
-            bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-      }
-      u32x4 v = raw.r;
-#pragma unroll
-      for (int e = 0; e < 4; e++) v[e] = v_raw ? v[e] : 0u;
-      *(u32x4*)(dst + 448 + 8 * lk) = v;
       const uint64_t ball = ballot64(v_raw);
+      auto put = [&](bool keep) {
+#pragma unroll
+        for (int i = 0; i < 7; i++) {
+          const uint32_t w0 = keep ? raw.e[i][0] : 0u, w1 = keep ? raw.e[i][1] : 0u;
+          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+          *(bf16x8*)(dst + 64 * i + 8 * lk) =
+              bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        }
+        u32x4 v = raw.r;
+#pragma unroll
+        for (int e = 0; e < 4; e++) v[e] = keep ? v[e] : 0u;
+        *(u32x4*)(dst + 448 + 8 * lk) = v;
+      };
+      if (ball == ~0ull) put(true);
+      else put(v_raw);
       if (lane == 0) {
         uint32_t m8 = 0;
 #pragma unroll
@@ -660,65 +700,103 @@ __global__ __launch_bounds__(256, 2) void attend_x_kernel(AttendK p) {
         s_mask[buf][hgl] = m8;
       }
     }
+    if constexpr (PREF > 1) refill(it, raw, v_raw, prr, er);  // the slot's registers are free
     __syncthreads();
     const uint32_t mask = s_mask[buf][0] | (s_mask[buf][1] << 8) | (s_mask[buf][2] << 16) |
                           (s_mask[buf][3] << 24);
     f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
     if (mask != 0u) {
-      // S^T for rows tb..tb+15 (S0) and tb+16..tb+31 (S1)
+      // S^T for rows tb..tb+15 (S0) and tb+16..tb+31 (S1), even and odd chunks in separate
+      // accumulators: four independent chains issue back to back (a dependent product waits
+      // for its predecessor's result)
+      // (two chains with two workgroups per CU, which cover each other's waits and have no
+      // registers to spare)
+      if constexpr (MINW == 1) {
+        f32x4 S0e = S0, S0o = S0, S1e = S0, S1o = S0;
 #pragma unroll
-      for (int c = 0; c < NCH; c++) {
-        const bf16x8 a0 = *(const bf16x8*)(yt + n * kXRS + 32 * c + 8 * g);
-        const bf16x8 a1 = *(const bf16x8*)(yt + (16 + n) * kXRS + 32 * c + 8 * g);
-        S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[c], S0, 0, 0, 0);
-        S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[c], S1, 0, 0, 0);
+        for (int c = 0; c < NCH; c += 2) {
+          const bf16x8 a0 = *(const bf16x8*)(yt + n * kXRS + 32 * c + 8 * g);
+          const bf16x8 a1 = *(const bf16x8*)(yt + (16 + n) * kXRS + 32 * c + 8 * g);
+          const bf16x8 b0 = *(const bf16x8*)(yt + n * kXRS + 32 * (c + 1) + 8 * g);
+          const bf16x8 b1 = *(const bf16x8*)(yt + (16 + n) * kXRS + 32 * (c + 1) + 8 * g);
+          S0e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[c], S0e, 0, 0, 0);
+          S1e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[c], S1e, 0, 0, 0);
+          S0o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0, qf[c + 1], S0o, 0, 0, 0);
+          S1o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1, qf[c + 1], S1o, 0, 0, 0);
+        }
+        S0 = S0e + S0o;
+        S1 = S1e + S1o;
+      } else {
+#pragma unroll
+        for (int c = 0; c < NCH; c++) {
+          const bf16x8 a0 = *(const bf16x8*)(yt + n * kXRS + 32 * c + 8 * g);
+          const bf16x8 a1 = *(const bf16x8*)(yt + (16 + n) * kXRS + 32 * c + 8 * g);
+          S0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[c], S0, 0, 0, 0);
+          S1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[c], S1, 0, 0, 0);
+        }
       }
-      // scheduling groups: both reads of a chunk go out before its two products (left alone,
-      // the compiler waits for each read before the next one issues); 8% on long row ranges
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+      // Scheduling groups: the reads of QA chunks are in flight ahead of the products that use
+      // them, so the LDS latency hides behind QA chunks of matrix work (left alone, the compiler
+      // waits for each chunk's reads right before its products).
+      constexpr int QA = MINW == 1 ? 4 : 1;  // two workgroups per CU cover each other instead
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * QA, 0);  // LDS reads
 #pragma unroll
-      for (int c = 1; c < NCH; c++) {
+      for (int c = QA; c < NCH; c++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * QA, 0);
     }
-    // the next tile: issue its loads now (and fetch the ids of the one after)
-    v_raw = false;
-    if (it + 1 < iters) {
-      const int64_t tn = r0 + (int64_t)(it + 1) * kXTile;
-      if constexpr (PAGED) {
-        const int32_t e_after = fetch_id(tn + 2 * kXTile);
-        load_rows(resolve_row(tn + lrow, prow_next, v_raw), raw);
-        prow_next = pool_row(tn + kXTile + lrow, e_next);
-        e_next = e_after;
-      } else {
-        const int32_t e_after = fetch_id(tn + kXTile);
-        load_rows(resolve(tn + lrow, e_next, v_raw), raw);
-        e_next = e_after;
-      }
-    }
+    // one tile ahead: the next tile's loads go out now, after the products that needed the
+    // registers of the row fragments
+    if constexpr (PREF == 1) refill(it, raw, v_raw, prr, er);
+    auto ytr = [&](int t) -> bf16x8 {
+      const __bf16* base0 = yt + tr_row * kXRS + 16 * t + tr_col;
+      const short4_t y0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)base0);
+      const short4_t y1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(base0 + 16 * kXRS));
+      return __builtin_bit_cast(bf16x8,
+                                short8_t{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]});
+    };
     if (mask != 0u) {
-      // online softmax (base 2); lane holds rows 4g+i (S0) and 16+4g+i (S1) of head n
-      float v[8];
-      if (mask == 0xFFFFFFFFu) {  // every row valid (all but the edge tiles)
+      // Y^T fragments of the PV products, read from LDS into a ring of PA pairs of 16-dim
+      // tiles: the first PA pairs go out before the softmax, which hides their latency, and each
+      // later pair PA pairs ahead of its products.
+      constexpr int PA = MINW == 1 ? 4 : 1;
+      constexpr int RF = 2 * PA;              // fragments in the ring
+      constexpr int GRP = MINW == 1 ? 4 : 2;  // fragments per group of products
+      bf16x8 yf[RF];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          v[i] = S0[i] * p.scale_log2;
-          v[4 + i] = S1[i] * p.scale_log2;
+      for (int t = 0; t < RF; t++) yf[t] = ytr(t);
+      // online softmax (base 2); lane holds rows 4g+i (S0) and 16+4g+i (S1) of head n. With every
+      // row of the tile present (all but the edge tiles) the exponent is one fma of the raw score.
+      const bool full = mask == 0xFFFFFFFFu;
+      const float sc = p.scale_log2;
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        v[i] = S0[i];
+        v[4 + i] = S1[i];
+      }
+      float tmax;
+      if (full) {
+        float hi = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+        hi = fmaxf(hi, fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+        if (sc < 0.0f) {
+          hi = fminf(fminf(v[0], v[1]), fminf(v[2], v[3]));
+          hi = fminf(hi, fminf(fminf(v[4], v[5]), fminf(v[6], v[7])));
         }
+        tmax = hi * sc;
       } else {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          v[i] = ((mask >> (4 * g + i)) & 1u) ? S0[i] * p.scale_log2 : -INFINITY;
-          v[4 + i] = ((mask >> (16 + 4 * g + i)) & 1u) ? S1[i] * p.scale_log2 : -INFINITY;
+          v[i] = ((mask >> (4 * g + i)) & 1u) ? S0[i] * sc : -INFINITY;
+          v[4 + i] = ((mask >> (16 + 4 * g + i)) & 1u) ? S1[i] * sc : -INFINITY;
         }
-      }
-      float tmax = v[0];
+        tmax = v[0];
 #pragma unroll
-      for (int i = 1; i < 8; i++) tmax = fmaxf(tmax, v[i]);
-      tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-      tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+        for (int i = 1; i < 8; i++) tmax = fmaxf(tmax, v[i]);
+      }
+      tmax = max_row_groups(tmax);
       // lazy rescale: the reference max moves only when a head's max grows by more than 2^8
       const float m_new = fmaxf(m_run, tmax);
       if (__ballot(m_new > m_run + 8.0f)) {
@@ -733,7 +811,8 @@ __global__ __launch_bounds__(256, 2) void attend_x_kernel(AttendK p) {
       float P[8], psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; i++) {
-        P[i] = __builtin_amdgcn_exp2f(v[i] - m_run);  // v - m_run <= 8; -inf gives 0
+        // exponent <= 8; an absent row's -inf gives 0
+        P[i] = __builtin_amdgcn_exp2f(full ? __builtin_fmaf(v[i], sc, -m_run) : v[i] - m_run);
         psum += P[i];
       }
       l_run += psum;
@@ -743,24 +822,45 @@ __global__ __launch_bounds__(256, 2) void attend_x_kernel(AttendK p) {
         ph[e] = (__bf16)P[e];
         pl[e] = (__bf16)(P[e] - (float)ph[e]);
       }
-      auto ytr = [&](int t) -> bf16x8 {
-        const __bf16* base0 = yt + tr_row * kXRS + 16 * t + tr_col;
-        const short4_t y0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)base0);
-        const short4_t y1 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4_ptr)(base0 + 16 * kXRS));
-        return __builtin_bit_cast(
-            bf16x8, short8_t{y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]});
-      };
+      // a group's hi products, then its lo products: GRP independent chains
 #pragma unroll
-      for (int t = 0; t < NT; t += 2) {
-        const bf16x8 ya = ytr(t), yb = ytr(t + 1);
-        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya, ph, O[t], 0, 0, 0);
-        O[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yb, ph, O[t + 1], 0, 0, 0);
-        O[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ya, pl, O[t], 0, 0, 0);
-        O[t + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yb, pl, O[t + 1], 0, 0, 0);
+      for (int t = 0; t < NT; t += GRP) {
+        bf16x8 y[GRP];
+#pragma unroll
+        for (int j = 0; j < GRP; j++) y[j] = yf[(t + j) % RF];
+#pragma unroll
+        for (int j = 0; j < GRP; j++)
+          O[t + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(y[j], ph, O[t + j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < GRP; j++)
+          O[t + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(y[j], pl, O[t + j], 0, 0, 0);
+        if (t + RF < NT) {
+#pragma unroll
+          for (int j = 0; j < GRP; j++) yf[(t + j) % RF] = ytr(t + j + RF);
+        }
       }
+      // each group's products, then the reads of the group RF fragments ahead (2 transposing
+      // reads per 16-dim tile)
+#pragma unroll
+      for (int t = 0; t < NT - RF; t += GRP) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * GRP, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * GRP, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * RF, 1);
     }
+  };
+  // The ring slots are compile-time indices: the loop is unrolled by the ring depth and runs
+  // whole rounds of PREF tiles, where every step has the same loads in flight before it and so
+  // waits for its own rows only (a step skipped inside the loop would make every wait drain all
+  // loads). The last iters mod PREF tiles follow the loop.
+  int it0 = 0;
+  for (; it0 + PREF <= iters; it0 += PREF) {
+#pragma unroll
+    for (int k = 0; k < PREF; k++) tile_step(it0 + k, raw[k], v_raw[k], pr[k], ee[k]);
   }
+#pragma unroll
+  for (int k = 0; k < PREF - 1; k++)
+    if (it0 + k < iters) tile_step(it0 + k, raw[k], v_raw[k], pr[k], ee[k]);
 
   // ---- write the output or this split's partial ----
   l_run += shfl_xor_f(l_run, 16);
@@ -956,12 +1056,22 @@ hipError_t launch_attend(const AttendArgs& a) {
   hipError_t e;
   if (shared_tiles) {
     const dim3 blk(256);
-    if (a.cmap.table) {
-      if (a.idx) a.prof.launch(attend_x_kernel<false, true>, grid, blk, s, k);
-      else a.prof.launch(attend_x_kernel<true, true>, grid, blk, s, k);
+    if (grid.x <= 256) {
+      if (a.cmap.table) {
+        if (a.idx) a.prof.launch(attend_x_kernel<false, true, 1>, grid, blk, s, k);
+        else a.prof.launch(attend_x_kernel<true, true, 1>, grid, blk, s, k);
+      } else {
+        if (a.idx) a.prof.launch(attend_x_kernel<false, false, 1>, grid, blk, s, k);
+        else a.prof.launch(attend_x_kernel<true, false, 1>, grid, blk, s, k);
+      }
     } else {
-      if (a.idx) a.prof.launch(attend_x_kernel<false, false>, grid, blk, s, k);
-      else a.prof.launch(attend_x_kernel<true, false>, grid, blk, s, k);
+      if (a.cmap.table) {
+        if (a.idx) a.prof.launch(attend_x_kernel<false, true, 2>, grid, blk, s, k);
+        else a.prof.launch(attend_x_kernel<true, true, 2>, grid, blk, s, k);
+      } else {
+        if (a.idx) a.prof.launch(attend_x_kernel<false, false, 2>, grid, blk, s, k);
+        else a.prof.launch(attend_x_kernel<true, false, 2>, grid, blk, s, k);
+      }
     }
     e = hipGetLastError();
   } else if (a.fmt == CSAH_FMT_ROW_E4M3_BF16)

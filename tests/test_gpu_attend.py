@@ -305,3 +305,29 @@ def test_empty_cache_window_only_and_no_groups():
     L.kv_compress(x[:, :0], 4, w, b, L.FMT_ROW_E4M3_BF16, out_rows=rows[:, 1:2])
     torch.cuda.synchronize()
     assert (rows.cpu() == 0xAB).all()
+
+
+@pytest.mark.parametrize("with_sink", [True, False])
+def test_no_rows_and_no_window_buffer(with_sink):
+    """N = 0 and w = 0 with no window buffer at all (a null pointer) while the slots hold k > 0
+    ids (all -1): only the sink is visible, so the output is 0 and lse is the sink (or -inf).
+    Every row load of the kernels reads a mapped address even here (they never dereference the
+    null window)."""
+    c = DecodeCase("csa128k", B=2, N=8, pos=[40, 500])
+    say(f"[attend] no rows, no window buffer, sink={with_sink}")
+    q, cache, pos, sink = c.gpu("q", "cache", "pos", "sink")
+    s = sink if with_sink else None
+    idx = torch.full((c.B, 1, 16), -1, dtype=torch.int32, device="cuda")
+    o, l = L.csa_attend(q, cache, idx, None, 0, pos, s, c.scale, N=0)
+    o2, l2 = L.hca_attend(q, cache, 4, None, 0, pos, s, c.scale, N=0)
+    torch.cuda.synchronize()
+    empty = np.zeros((c.B, 0, c.window.shape[2]), np.uint8)
+    rs = c.sink if with_sink else None
+    ro, rl = O.csa_attend(c.q, c.cache, c.fmt, idx.cpu().numpy(), empty, 0, c.pos, rs, c.scale,
+                          N=0)
+    ro2, rl2 = O.hca_attend(c.q, c.cache, c.fmt, 4, empty, 0, c.pos, rs, c.scale, N=0)
+    assert not ro.any() and not ro2.any()
+    assert_close(o.cpu().numpy(), ro, "csa out")
+    assert_close(l.cpu().numpy(), rl, "csa lse")
+    assert_close(o2.cpu().numpy(), ro2, "hca out")
+    assert_close(l2.cpu().numpy(), rl2, "hca lse")
