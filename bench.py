@@ -12,7 +12,11 @@ and one HCA layer, i.e. every row of the decode hot path:
   3. HCA layer, the same 16 sequences: hca_attend over 8,192 entries + window + sink; it runs
      on a second stream, concurrently with the CSA layer (the two are independent).
 The CSA decode step of the 4-sequence 1M configuration (index_topk + csa_attend on 4 of the
-sequences) is timed separately and reported with its fraction of peak HBM bandwidth.
+sequences) is timed separately and reported with its fraction of peak HBM bandwidth, both on one
+replica (whose 71 MB of keys stay in the 256 MB last-level cache between replays) and rotating
+through 16 disjoint 4-sequence replicas (1.14 GB of keys). The 128K configuration (16 sequences x
+32,768 entries) is timed the same way over 8 disjoint slices of the 1M caches. Every figure is the
+median (with p10 / p90) of per-replay times over at least 200 replays.
 Inputs are seeded synthetic values (~N(0,1) before quantisation) generated and encoded on the
 GPU with the library's own kv_compress (m = 1 is its quantiser). The step's working set is
 ~2.8 GB, so consecutive steps stream from HBM rather than from the 256 MB last-level cache.
@@ -301,8 +305,8 @@ CSA_SEQ_BYTES = (K + W) * ROW + K * 4 + H * D * 2 + H * D * 4 + H * 4
 KERNELS = {
     "index_scan": dict(per_step=1, bytes=B_STEP * SCAN_BYTES_PER_SEQ,
                        flops=B_STEP * N_CSA * 512 * 2, peak_flops=10.1e15,
-                       name="index_scan_mx_kernel (csah_index_topk)", source="index_topk.hip",
-                       profile="index_scan_csa1m_b16"),
+                       name="index_cand_scan_kernel (csah_index_topk)", source="index_cand.hip",
+                       profile="index_cand_scan_csa1m_b16"),
     "csa_attend": dict(per_step=1, bytes=B_STEP * CSA_SEQ_BYTES + H * 4,
                        flops=B_STEP * H * (K + W) * D * 4, peak_flops=2.5e15,
                        name="attend_x_kernel (csah_csa_attend)", source="attend.hip",
@@ -316,6 +320,11 @@ KERNELS = {
 # The 1M-context CSA decode step of 4 sequences (index_topk + csa_attend): what the method must
 # move per sequence is its FP4 keys, the selected rows, the window, q and the output.
 CSA4_BYTES = B_CSA4 * (SCAN_BYTES_PER_SEQ + CSA_SEQ_BYTES) + H * 4
+# The 128K CSA decode configuration: 16 sequences x 32,768 entries (131,072 tokens, m = 4).
+N_128K = 32768
+CSA128K_BYTES = B_STEP * (N_128K * (DI // 2 + DI // 32) + CSA_SEQ_BYTES) + H * 4
+# All the decode step moves: every stage's algorithmic bytes (compression's few rows aside).
+STEP_BYTES = sum(k["bytes"] * k["per_step"] for k in KERNELS.values())
 
 
 def kernel_times(ws: DecodeStep, reps: int):
@@ -400,6 +409,94 @@ def time_replays(g, fn, steps):
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
+
+
+def replay_stats(replays, n: int):
+    """Per-replay times (us) of n calls: replays(i) runs replay i (graphs rotate by i). Events
+    bracket each replay on the current stream; returns median, p10, p90 and mean."""
+    evs = []
+    for i in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        replays(i)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    v = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    return {"median_us": v[n // 2], "p10_us": v[n // 10], "p90_us": v[(9 * n) // 10],
+            "mean_us": statistics.mean(v), "replays": n}
+
+
+class Replicas:
+    """Disjoint copies of a CSA decode configuration (index_topk + csa_attend), one HIP graph
+    each, replayed in rotation so that consecutive replays read different keys and rows and the
+    last-level cache holds none of them. make(r) -> dict(iqc, iqs, kc, ks, cache, win, q, pos)."""
+
+    def __init__(self, ws: "DecodeStep", make, count: int, k: int = K):
+        self.ws, self.graphs, self.keep = ws, [], []
+        for r in range(count):
+            c = make(r)
+            B = c["kc"].shape[0]
+            dev = c["kc"].device
+            c["idx"] = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+            c["out"] = torch.empty((B, 1, H, D), dtype=torch.float32, device=dev)
+            c["lse"] = torch.empty((B, 1, H), dtype=torch.float32, device=dev)
+            N = c["kc"].shape[1]
+            c["ws_idx"] = torch.empty(L.index_topk_workspace(B, 1, N, k, HI, DI),
+                                      dtype=torch.uint8, device=dev)
+            c["ws_att"] = torch.empty(max(256, L.attend_workspace(B, 1, H, D, k + W)),
+                                      dtype=torch.uint8, device=dev)
+
+            def fn(c=c):
+                L.index_topk(c["iqc"], c["iqs"], c["kc"], c["ks"], c["pos"], 4, k,
+                             want_scores=False, ws=c["ws_idx"], idx_out=c["idx"])
+                L.csa_attend(c["q"], c["cache"], c["idx"], c["win"], W, c["pos"], ws.sink,
+                             ws.scale, ws=c["ws_att"], out=c["out"], lse=c["lse"])
+            self.keep.append(c)
+            self.graphs.append(capture(fn))
+
+    def stats(self, n: int, rotate: bool):
+        return replay_stats(lambda i: self.graphs[i % len(self.graphs) if rotate else 0].replay(),
+                            n)
+
+
+def csa4_replicas(ws: "DecodeStep", count: int = 16, seed: int = 77):
+    """16 disjoint 4-sequence replicas of the 1M CSA decode step: sequences 4r..4r+3 of the
+    decode step's caches for r < 4, then 12 more sets of FP4 keys (N(0,1) before quantisation)
+    over the same rows (each replica's own keys select its own rows)."""
+    d = synth.Draws(seed, torch.device("cuda"))
+    extra = []
+    step = 1 << 16
+    for r in range(4, count):
+        kc = torch.empty((B_CSA4, N_CSA, DI // 2), dtype=torch.uint8, device="cuda")
+        ks = torch.empty((B_CSA4, N_CSA, DI // 32), dtype=torch.uint8, device="cuda")
+        for b in range(B_CSA4):
+            for r0 in range(0, N_CSA, step):
+                encode(d.normal((1, step, DI)), 1, L.FMT_FP4_E8M0,
+                       rows=kc[b:b + 1, r0:r0 + step], scales=ks[b:b + 1, r0:r0 + step])
+        extra.append((kc, ks))
+    c = ws.csa
+
+    def make(r):
+        g = r % 4
+        sl = slice(B_CSA4 * g, B_CSA4 * (g + 1))
+        kc, ks = (c["kc"][sl], c["ks"][sl]) if r < 4 else extra[r - 4]
+        return dict(iqc=c["iqc"][sl], iqs=c["iqs"][sl], kc=kc, ks=ks, cache=c["cache"][sl],
+                    win=c["win"][sl], q=c["q"][sl], pos=ws.pos[sl])
+    return Replicas(ws, make, count)
+
+
+def csa128k_replicas(ws: "DecodeStep", count: int = 8):
+    """The 128K configuration (16 sequences x 32,768 entries, 131,072 tokens at m = 4) as 8
+    disjoint 32,768-entry slices of the 1M caches: 8 x 35.7 MB of keys and 8 x 302 MB of rows."""
+    c = ws.csa
+    pos = torch.full((B_STEP,), 4 * N_128K - 1, dtype=torch.int64, device="cuda")
+
+    def make(r):
+        sl = slice(N_128K * r, N_128K * (r + 1))
+        return dict(iqc=c["iqc"], iqs=c["iqs"], kc=c["kc"][:, sl], ks=c["ks"][:, sl],
+                    cache=c["cache"][:, sl], win=c["win"], q=c["q"], pos=pos)
+    return Replicas(ws, make, count)
 
 
 def traffic_from_profile(kernel: str):
@@ -746,12 +843,27 @@ def main():
     graph = None if args.no_graph else StepGraphs(ws)
     log(f"timing {args.steps} steps ({'graph replay' if graph else 'eager'})...")
     ms = time_replays(graph, ws.step, args.steps)
-    log(f"  {ms * 1e3:.1f} us per step")
-    g4, ms4 = None, None
+    n_stats = max(200, args.steps)
+    step_stats = replay_stats(lambda i: graph.replay() if graph else ws.step(), n_stats)
+    log(f"  {ms * 1e3:.1f} us per step (median {step_stats['median_us']:.1f}, p10 "
+        f"{step_stats['p10_us']:.1f}, p90 {step_stats['p90_us']:.1f})")
+    g4, ms4, rot4, rot128 = None, None, None, None
     if not args.no_csa4:
         g4 = None if args.no_graph else capture(ws.csa4_step)
         ms4 = time_replays(g4, ws.csa4_step, args.steps)
         log(f"  CSA decode step, 4 sequences at 1M: {ms4 * 1e3:.1f} us")
+        if not args.no_graph:
+            log("  16 rotated 4-sequence replicas (1.14 GB of keys) and 8 rotated 128K slices...")
+            r4 = csa4_replicas(ws)
+            rot4 = {"one_replica": r4.stats(n_stats, False), "rotated_16": r4.stats(n_stats, True)}
+            del r4
+            r128 = csa128k_replicas(ws)
+            rot128 = {"one_replica": r128.stats(n_stats, False),
+                      "rotated_8": r128.stats(n_stats, True)}
+            del r128
+            log(f"  4 x 1M: median {rot4['one_replica']['median_us']:.1f} us on one replica, "
+                f"{rot4['rotated_16']['median_us']:.1f} us rotated; 16 x 128K: "
+                f"{rot128['one_replica']['median_us']:.1f} / {rot128['rotated_8']['median_us']:.1f} us")
     kt = kernel_times(ws, args.kernel_reps)
     log("  dominant kernels (us): " + ", ".join(f"{k} {v * 1e3:.2f}" for k, v in kt.items()))
     # the roofline object reports the kernel that moves most of the step's algorithmic HBM bytes
@@ -787,6 +899,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "step_replay_us": step_stats,
+        "step_algorithmic_bytes": STEP_BYTES,
+        "step_frac_of_hbm_peak": STEP_BYTES / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -841,6 +956,27 @@ def main():
             "achieved_GBps": CSA4_BYTES / (ms4 * 1e-3) / 1e9,
             "frac_of_hbm_peak": CSA4_BYTES / (ms4 * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "queries_per_s": B_CSA4 / (ms4 * 1e-3),
+        }
+        if rot4 is not None:
+            med = rot4["rotated_16"]["median_us"]
+            line["csa_decode_1m_b4"].update({
+                "replays": rot4,
+                "rotated_median_us": med,
+                "rotated_frac_of_hbm_peak": CSA4_BYTES / (med * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                "rotation": "16 disjoint 4-sequence replicas, 1.14 GB of FP4 keys; one_replica "
+                            "replays the same 71 MB of keys, which stay in the 256 MB last-level "
+                            "cache",
+            })
+    if rot128 is not None:
+        med = rot128["rotated_8"]["median_us"]
+        line["csa_decode_128k_b16"] = {
+            "what": "index_topk + csa_attend for 16 sequences at 131,072 tokens (32,768 FP4 keys "
+                    "each, top-1024, window 128, sink)",
+            "replays": rot128, "rotated_median_us": med, "algorithmic_bytes": CSA128K_BYTES,
+            "achieved_GBps": CSA128K_BYTES / (med * 1e-6) / 1e9,
+            "frac_of_hbm_peak": CSA128K_BYTES / (med * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "queries_per_s": B_STEP / (med * 1e-6),
+            "rotation": "8 disjoint 32,768-entry slices of the 1M caches (285 MB of keys)",
         }
     if not args.no_csa4:
         line["csa_decode_1m_b4_paged"] = paged_measure(ws, args, ms4)

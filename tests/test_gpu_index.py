@@ -328,3 +328,22 @@ def test_many_sequences_small_caches():
     qc, qs = O.encode_rows(rng.normal(size=(B, 1, HI, dI)), O.FMT_FP4_E8M0)
     pos = rng.integers(0, N * m, size=B).astype(np.int64)
     _compare("many sequences", kc, ks, qc, qs, pos, m, k)
+
+
+def test_csa128k_full_shape_index_then_attention():
+    """The 128K CSA decode configuration at its own shape: 16 sequences x 32,768 entries (131,072
+    tokens at m = 4), top-1024 over 4 x 128 FP4 indexer heads, then sparse attention of 64 heads
+    x 512 over the selected rows + 128-token window + sink. Indices and scores bit-exact, the
+    attention output and lse within 1e-3 of the oracle on the GPU's own selection."""
+    from helpers import assert_close
+    c = DecodeCase("csa128k")
+    assert (c.B, c.N, c.wl.k) == (16, 32768, 1024)
+    _compare("csa128k full", c.kc, c.ks, c.qc, c.qs, c.pos, c.m, c.wl.k)
+    gi, _ = _run(c.kc, c.ks, c.qc, c.qs, c.pos, c.m, c.wl.k)
+    say("[csa_attend] csa128k full: 16 x (1024 + 128) rows")
+    q, cache, win, pos, sink = c.gpu("q", "cache", "window", "pos", "sink")
+    out, lse = L.csa_attend(q, cache, dev(gi), win, c.wl.w, pos, sink, c.scale)
+    torch.cuda.synchronize()
+    ro, rl = O.csa_attend(c.q, c.cache, c.fmt, gi, c.window, c.wl.w, c.pos, c.sink, c.scale)
+    assert_close(out.cpu().numpy(), ro, "csa128k out")
+    assert_close(lse.cpu().numpy(), rl, "csa128k lse")

@@ -402,3 +402,80 @@ def test_tiny_workload_end_to_end_is_self_consistent():
     o, l = O.csa_attend(q, csa["rows"], O.FMT_ROW_F32, idx, win, wl.w, pos, sink, wl.scale)
     oh, lh = O.hca_attend(q, hca["rows"], O.FMT_ROW_F32, 128, win, wl.w, pos, sink, wl.scale)
     assert np.isfinite(o).all() and np.isfinite(oh).all()
+
+
+# ---- pins of the indexer's fp32-exactness flag --------------------------------------------------
+# A score is a sum of products q_i k_i 2^(Eq+Ek-254), each product an integer multiple of the
+# finest unit u = 2^(emin-256) (2*e2m1 values are the integers 0, 1, 2, 3, 4, 6, 8, 12). If the
+# absolute products total less than 2^24 units, every partial sum in any order is an integer
+# below 2^24 units and binary32 holds it exactly; one unit past 2^24 no longer fits in 24
+# significand bits. The cases below are built from that definition, with block sums chosen by
+# hand, and the score is checked against a direct fp64 sum of the decoded values.
+_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _key_block(pairs):
+    """32 (q code, k code) pairs -> (q codes, k codes) as 32-element code arrays."""
+    assert len(pairs) <= 32
+    q = np.zeros(32, np.uint8)
+    k = np.zeros(32, np.uint8)
+    for i, (a, b) in enumerate(pairs):
+        q[i], k[i] = a, b
+    return q, k
+
+
+def _pack(codes):
+    codes = np.asarray(codes, np.uint8)
+    return (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+
+
+def _two_block_case(pairs0, pairs1, qs, ks):
+    """One head, dI = 64: block 0 and block 1 with the given code pairs and E8M0 bytes."""
+    q0, k0 = _key_block(pairs0)
+    q1, k1 = _key_block(pairs1)
+    qc = _pack(np.concatenate([q0, q1]))[None, :]
+    kc = _pack(np.concatenate([k0, k1]))[None, :]
+    s, ok = O.index_scores(qc, np.array([qs], np.uint8), kc, np.array([ks], np.uint8))
+    # direct fp64 sum of decoded products (exact here: few terms, power-of-two scales)
+    ref = 0.0
+    for b, (qq, kk) in enumerate(((q0, k0), (q1, k1))):
+        blk = sum(_E2M1[a] * _E2M1[c] for a, c in zip(qq, kk))
+        ref += blk * 2.0 ** (int(qs[b]) + int(ks[b]) - 254)
+    return float(s[0]), bool(ok[0]), ref
+
+
+# absolute block sums in twice-value units (2q * 2k): 144 = 12 * 12 (6.0 x 6.0), 64 = 8 * 8,
+# 36 = 6 * 6, 18 = 6 * 3, 9 = 3 * 3, 1 = 1 * 1
+_S4095 = [(7, 7)] * 28 + [(5, 5), (5, 3), (3, 3)]  # 4032 + 36 + 18 + 9 = 4095
+_S4097 = [(7, 7)] * 28 + [(6, 6), (1, 1)]          # 4032 + 64 + 1 = 4097
+
+
+def test_exact_flag_just_under_two_to_the_24_units():
+    # block 1 is 2^12 units coarser: 4095 * 2^12 + 4095 = 2^24 - 1 units in all
+    s, ok, ref = _two_block_case(_S4095, _S4095, [127, 127], [127, 139])
+    assert ok and s == ref
+
+
+def test_exact_flag_just_over_two_to_the_24_units():
+    # 4095 * 2^12 + 4097 = 2^24 + 1 units: some summation order needs 25 significant bits
+    s, ok, ref = _two_block_case(_S4097, _S4095, [127, 127], [127, 139])
+    assert not ok and s == ref
+
+
+def test_exact_flag_blocks_2_to_the_30_apart():
+    s, ok, ref = _two_block_case(_S4095, _S4095, [127, 127], [127, 157])
+    assert not ok and s == ref
+
+
+@pytest.mark.parametrize("e_low,expect", [(130, True), (129, False)])
+def test_exact_flag_finest_unit_must_be_a_normal_binary32(e_low, expect):
+    # finest unit 2^(e_low - 256): 2^-126 is the smallest normal binary32 power of two
+    s, ok, ref = _two_block_case([(2, 2)], [(2, 2)], [e_low - 127, e_low - 127], [127, 127])
+    assert ok == expect and s == ref
+
+
+@pytest.mark.parametrize("e_high,expect", [(358, True), (359, False)])
+def test_exact_flag_largest_block_must_stay_below_binary32_overflow(e_high, expect):
+    # a block value below 2^24 units of 2^(e_high - 256) stays under 2^(e_high - 232) < 2^127
+    s, ok, ref = _two_block_case([(2, 2)], [(2, 2)], [e_high - 179, e_high - 179], [179, 179])
+    assert ok == expect and s == ref
