@@ -51,6 +51,7 @@ extern "C" {
 #define CSAH_ERR_UNSUPPORTED (-2)      /* shape/format combination not built, or no gfx950    */
 #define CSAH_ERR_WORKSPACE_TOO_SMALL (-3)
 #define CSAH_ERR_LAUNCH (-4)           /* the HIP runtime refused a launch                     */
+#define CSAH_ERR_SCRATCH_LIMIT (-5)    /* csah_csa_attend_noalloc: more than its static scratch */
 
 /* element types of raw rows and queries */
 #define CSAH_DT_F32 0
@@ -187,6 +188,26 @@ int csah_csa_attend(const void* q, int q_dtype, int H, int D, const void* cache,
  * ws        at least csah_attend_workspace(B, Q, H, D, N + w) bytes, 256-byte aligned.
  * Supported: as csah_csa_attend; m >= 1; N + w < 2^31.
  */
+/*
+ * csah_csa_attend_noalloc -- csah_csa_attend for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). It takes
+ * no workspace: the split partials go to a scratch array of CSAH_NOALLOC_SCRATCH_BYTES (32 MiB)
+ * that the library holds in every GPU it runs on until the process ends, so the call neither
+ * allocates nor frees anything. Same arguments, layouts, results and statuses as csah_csa_attend
+ * without ws / ws_bytes, plus CSAH_ERR_SCRATCH_LIMIT (nothing enqueued) when
+ * csah_attend_workspace(B, Q, H, D, k + w) exceeds the scratch; 16 sequences of one query at
+ * H = 64, D = 512, k = 1024, w = 128 need 19 MB. Every call on a GPU shares that GPU's scratch
+ * and nothing in it needs clearing (each call writes every partial it reads); calls that overlap
+ * on one GPU (on different streams, or from different threads) race on it and must be ordered by
+ * the caller. The first call on a device looks up the scratch's address there.
+ */
+#define CSAH_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int csah_csa_attend_noalloc(const void* q, int q_dtype, int H, int D, const void* cache, int fmt,
+                            int64_t cache_seq_stride, int64_t N, const int32_t* idx, int k,
+                            const void* win, int64_t win_seq_stride, int w, const int64_t* pos,
+                            const float* sink, float scale, int B, int Q, float* out, float* lse,
+                            void* stream);
+
 int csah_hca_attend(const void* q, int q_dtype, int H, int D, const void* cache, int fmt,
                     int64_t cache_seq_stride, int64_t N, int m, const void* win,
                     int64_t win_seq_stride, int w, const int64_t* pos, const float* sink,

@@ -26,13 +26,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsah.so")
 
 OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, LAUNCH = 0, -1, -2, -3, -4
+SCRATCH_LIMIT = -5
+NOALLOC_SCRATCH_BYTES = 32 << 20  # csah_csa_attend_noalloc's static scratch per GPU
 DT_F32, DT_BF16 = 0, 1
 FMT_ROW_F32, FMT_ROW_E4M3_BF16, FMT_FP4_E8M0 = 0, 1, 2
 
 EXPORTS = ("csah_abi_version", "csah_status_string", "csah_row_bytes", "csah_kv_compress",
            "csah_kv_compress_span",
            "csah_index_topk_workspace", "csah_index_topk", "csah_attend_workspace",
-           "csah_csa_attend", "csah_hca_attend", "csah_kv_compress_paged",
+           "csah_csa_attend", "csah_csa_attend_noalloc", "csah_hca_attend",
+           "csah_kv_compress_paged",
            "csah_index_topk_paged", "csah_csa_attend_paged", "csah_hca_attend_paged",
            "csah_rope", "csah_kv_compress_rope", "csah_kv_compress_paged_rope",
            "csah_profile_next_call")
@@ -71,6 +74,8 @@ def lib():
                                     P, P, P, SZ, P]),
             "csah_hca_attend": (I, [P, I, I, I, P, I, I64, I64, I, P, I64, I, P, P, F, I, I, P,
                                     P, P, SZ, P]),
+            "csah_csa_attend_noalloc": (I, [P, I, I, I, P, I, I64, I64, P, I, P, I64, I, P, P, F,
+                                            I, I, P, P, P]),
             "csah_kv_compress_paged": (I, [P, I, I64, I, I64, I, I, I, I64, P, P, P, I, P, P,
                                            I64, I, I64, P]),
             "csah_index_topk_paged": (I, [P, P, I, I, P, P, P, I64, I, I64, P, I, I, I, I, P, P,
@@ -235,6 +240,27 @@ def csa_attend(q, cache, idx, window, w: int, pos, sink, scale: float, N: int | 
                                float(scale), B, Q, _ptr(out), _ptr(lse), _ptr(ws), need,
                                _stream(stream))
     _check("csah_csa_attend", st)
+    return out, lse
+
+
+def csa_attend_noalloc(q, cache, idx, window, w: int, pos, sink, scale: float,
+                       N: int | None = None, out=None, lse=None, stream=None):
+    """csa_attend whose partials use the library's static scratch (no workspace, no allocation
+    inside the call); out / lse may be passed preallocated."""
+    B, Q, H, D = q.shape
+    fmt = _fmt_of(cache, D)
+    N = cache.shape[1] if N is None else N
+    k = idx.shape[-1]
+    dev = q.device
+    out = torch.empty((B, Q, H, D), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((B, Q, H), dtype=torch.float32, device=dev) if lse is None else lse
+    wstride = window.stride(0) // window.stride(1) if w > 0 else 0
+    st = lib().csah_csa_attend_noalloc(_ptr(q), _dt(q), H, D, _ptr(cache), fmt,
+                                       cache.stride(0) // cache.stride(1), N, _ptr(idx), k,
+                                       _ptr(window) if w > 0 else None, wstride, w, _ptr(pos),
+                                       _ptr(sink), float(scale), B, Q, _ptr(out), _ptr(lse),
+                                       _stream(stream))
+    _check("csah_csa_attend_noalloc", st)
     return out, lse
 
 

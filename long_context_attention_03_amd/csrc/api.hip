@@ -32,6 +32,28 @@ int check_device() {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? CSAH_OK : CSAH_ERR_LAUNCH; }
 
+// Scratch of csah_csa_attend_noalloc: the split partials live in this array instead of a caller
+// workspace. Every GPU the library runs on holds its own copy until the process ends. In host
+// code the name is only a stand-in: kernels get the device address that hipGetSymbolAddress
+// returns for the current device, looked up once per device on its first call.
+static __device__ __align__(256) unsigned char scratch[CSAH_NOALLOC_SCRATCH_BYTES];
+
+void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[64];
+  static bool done[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!done[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    addr[dev] = ptr;
+    done[dev] = true;
+  }
+  return addr[dev];
+}
+
 thread_local ProfileHook g_next_prof;
 
 // Take (and clear) this thread's pending profiling request.
@@ -87,6 +109,8 @@ const char* csah_status_string(int status) {
     case CSAH_ERR_UNSUPPORTED: return "unsupported shape, format or device";
     case CSAH_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case CSAH_ERR_LAUNCH: return "kernel launch failed";
+    case CSAH_ERR_SCRATCH_LIMIT:
+      return "the call needs more than the library's static scratch (CSAH_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -318,6 +342,25 @@ int csah_csa_attend(const void* q, int q_dtype, int H, int D, const void* cache,
                        cache_seq_stride, N, idx, k, 1, win,
                        win_seq_stride, w, pos, sink, scale, B, Q, out, lse, ws, ws_bytes, stream,
                        prof);
+}
+
+int csah_csa_attend_noalloc(const void* q, int q_dtype, int H, int D, const void* cache, int fmt,
+                            int64_t cache_seq_stride, int64_t N, const int32_t* idx, int k,
+                            const void* win, int64_t win_seq_stride, int w, const int64_t* pos,
+                            const float* sink, float scale, int B, int Q, float* out, float* lse,
+                            void* stream) {
+  const ProfileHook prof = take_profile();
+  if (!idx || k < 0 || w < 0 || H <= 0 || D <= 0 || B <= 0 || Q <= 0)
+    return CSAH_ERR_INVALID_ARGUMENT;
+  if (attend_workspace_bytes(B, Q, H, D, (int64_t)k + w) > CSAH_NOALLOC_SCRATCH_BYTES)
+    return CSAH_ERR_SCRATCH_LIMIT;
+  int st = check_device();
+  if (st) return st;
+  void* ws = scratch_address();
+  if (!ws) return CSAH_ERR_LAUNCH;
+  return attend_common(q, q_dtype, H, D, cache, fmt, contiguous_map(cache_seq_stride),
+                       cache_seq_stride, N, idx, k, 1, win, win_seq_stride, w, pos, sink, scale,
+                       B, Q, out, lse, ws, CSAH_NOALLOC_SCRATCH_BYTES, stream, prof);
 }
 
 int csah_hca_attend(const void* q, int q_dtype, int H, int D, const void* cache, int fmt,
