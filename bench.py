@@ -208,12 +208,13 @@ class DecodeStep:
         self.hca_attend()
 
     def step(self):
-        """Eager step: the HCA branch on a second stream beside the CSA branch."""
+        """Eager step: the HCA branch on a second stream beside the CSA branch. The CSA branch
+        (the longer chain) is enqueued first; the second stream forks from the point before it."""
         main = torch.cuda.current_stream()
         self.side.wait_stream(main)
+        self.csa_branch()
         with torch.cuda.stream(self.side):
             self.hca_branch()
-        self.csa_branch()
         main.wait_stream(self.side)
 
     def csa4_step(self):
@@ -278,11 +279,15 @@ class StepGraphs:
         torch.cuda.synchronize()
 
     def replay(self):
+        # The CSA graph (the longer chain: compress, scan, top-k, attention) is launched first:
+        # a graph launch costs the host tens of microseconds, and the chain launched second
+        # reaches the GPU that much later. The side stream forks from the point before it, so
+        # the HCA graph does not wait for the CSA graph.
         main, side = torch.cuda.current_stream(), self.ws.side
         side.wait_stream(main)
+        self.g_csa.replay()
         with torch.cuda.stream(side):
             self.g_hca.replay()
-        self.g_csa.replay()
         main.wait_stream(side)
 
 

@@ -894,10 +894,13 @@ __global__ __launch_bounds__(256, MINW) void attend_x_kernel(AttendK p) {
   }
 }
 
-// Combine the split partials of one (query, head) with the sink. The per-split weights are computed
-// once into LDS; each thread then owns D/128 consecutive dims and reads every split's values with
-// independent vector loads.
+// Combine the split partials of one (query, head) with the sink. Each thread owns D/128
+// consecutive dims. The rows of up to 16 splits are loaded at once, before their weights are
+// known (only the split maxima and sums wait for the weight computation), so one batch costs
+// one memory round trip; absent splits read split 0 again and get weight 0, which keeps every
+// load out of a branch.
 constexpr int kMaxSplits = 64;
+constexpr int kMergeBatch = 16;
 
 template <int D>
 __global__ __launch_bounds__(128) void attend_merge_kernel(const float* __restrict__ part,
@@ -906,27 +909,32 @@ __global__ __launch_bounds__(128) void attend_merge_kernel(const float* __restri
                                                            float* __restrict__ out,
                                                            float* __restrict__ lse) {
   constexpr int DPT = D / 128;
+  typedef float vecD __attribute__((ext_vector_type(DPT)));
   const int hh = blockIdx.x, slot = blockIdx.y, t = threadIdx.x;
   const float* base = part + ((int64_t)slot * splits * H + hh) * (D + 4);
   const int64_t sstride = (int64_t)H * (D + 4);
-  __shared__ float s_m[kMaxSplits], s_w[kMaxSplits];
+  __shared__ float s_w[kMaxSplits];
   __shared__ float s_den, s_mf;
   float ml = -INFINITY, ll = 0.0f;
-  if (t < splits) {
-    ml = base[t * sstride + D];
-    ll = base[t * sstride + D + 1];
-    s_m[t] = ml;
-  }
+  const float* mlp = base + (t < splits ? t : 0) * sstride + D;
+  ml = mlp[0];
+  ll = mlp[1];
+  // the first batch of rows, in flight while the weights are computed
+  vecD v[kMergeBatch];
+#pragma unroll
+  for (int j = 0; j < kMergeBatch; j++)
+    v[j] = *(const vecD*)(base + (j < splits ? j : 0) * sstride + t * DPT);
+  if (t >= splits) ml = -INFINITY, ll = 0.0f;
   // max over splits (and the sink) within the first wave
-  float M = ml;
   if (t < 64) {
+    float M = ml;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     float Mf = M;
     const float sg = sink ? sink[hh] * kLog2e : 0.0f;
     if (sink) Mf = fmaxf(M, sg);
     const float wgt = (t < splits && ml != -INFINITY) ? exp2f(ml - Mf) : 0.0f;
-    if (t < splits) s_w[t] = wgt;
+    s_w[t] = wgt;
     float den = ll * wgt;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
@@ -937,24 +945,26 @@ __global__ __launch_bounds__(128) void attend_merge_kernel(const float* __restri
   }
   __syncthreads();
   const float den = s_den;
-  float acc[DPT];
+  vecD acc = {};
+  for (int s0 = 0; s0 < splits; s0 += kMergeBatch) {
+    if (s0 > 0) {
 #pragma unroll
-  for (int e = 0; e < DPT; e++) acc[e] = 0.0f;
-  for (int s0 = 0; s0 < splits; s0++) {
-    const float wgt = s_w[s0];
-    const float* src = base + s0 * sstride + t * DPT;
-    if constexpr (DPT == 4) {
-      const f32x4 v = *(const f32x4*)src;
+      for (int j = 0; j < kMergeBatch; j++) {
+        const int sj = s0 + j < splits ? s0 + j : 0;
+        v[j] = *(const vecD*)(base + sj * sstride + t * DPT);
+      }
+    }
 #pragma unroll
-      for (int e = 0; e < 4; e++) acc[e] = fmaf(v[e], wgt, acc[e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < DPT; e++) acc[e] = fmaf(src[e], wgt, acc[e]);
+    for (int j = 0; j < kMergeBatch; j++) {
+      const float wgt = s0 + j < splits ? s_w[s0 + j] : 0.0f;
+      acc += v[j] * wgt;
     }
   }
   const int64_t oo = (int64_t)slot * H + hh;
+  vecD r;
 #pragma unroll
-  for (int e = 0; e < DPT; e++) out[oo * D + t * DPT + e] = den > 0.0f ? acc[e] / den : 0.0f;
+  for (int e = 0; e < DPT; e++) r[e] = den > 0.0f ? acc[e] / den : 0.0f;
+  *(vecD*)(out + oo * D + t * DPT) = r;
   if (t == 0 && lse) lse[oo] = den > 0.0f ? (s_mf + log2f(den)) * kLn2 : -INFINITY;
 }
 
@@ -988,14 +998,16 @@ AttendPlan attend_plan(int B, int Q, int H, int D, int64_t max_rows) {
 static AttendPlan attend_x_plan(int B, int Q, int H, int64_t max_rows) {
   const int hb = (H + 63) / 64;
   const int64_t base = (int64_t)B * Q * hb;
-  // each split writes a 64-head partial as large as 7 rows of input: with 16 or more queries
-  // in flight, longer splits (fewer partials) win; with fewer, short splits keep the GPU busy
-  const int min_tiles = base >= 16 ? 4 : 2;
-  // At most one workgroup per CU (256). Two fill a CU's whole register file, which shuts out
-  // any kernel running concurrently on another stream (the other layer of a decode step, the
-  // other micro-batch). One per CU makes a dense 16-sequence call 18% slower when it runs alone
-  // and a two-layer decode step (both layers on two streams) about 3% faster.
-  AttendPlan pl = make_plan(base, (max_rows + kXTile - 1) / kXTile, 256, min_tiles);
+  // Each split writes a 64-head partial (128 KB, as large as 228 rows of input), yet a 32-row
+  // tile costs about 1.7 us of matrix and vector issue, so parallelism wins over partial bytes:
+  // measured at 16 sequences, splits of 3 tiles (12 per sequence) beat 4 tiles by 9% and 6 tiles
+  // by 25%; at 4 sequences, 2 tiles beat 1, 3 and 4.
+  const int min_tiles = base >= 16 ? 3 : 2;
+  // At most 240 workgroups, one per CU: a workgroup takes a CU's whole register file, and the
+  // 16 CUs left over (two per XCD) keep room for a kernel running concurrently on another stream.
+  // In a decode step the CSA layer's top-k (16 workgroups of 1,024 threads) otherwise waits for
+  // the whole HCA attention to finish.
+  AttendPlan pl = make_plan(base, (max_rows + kXTile - 1) / kXTile, 240, min_tiles);
   pl.head_groups = hb;
   return pl;
 }

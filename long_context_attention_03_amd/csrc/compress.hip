@@ -59,14 +59,30 @@ __device__ __forceinline__ void load_token(const void* raw, int64_t row, int lan
 
 constexpr int kTokBatch = 8;  // tokens whose loads and gate reductions are in flight together
 
+// Sum over the 64 lanes, in every lane, by symmetric exchanges only (quad swaps, half-row and
+// row mirrors, gfx950's 16- and 32-lane swaps): both lanes of each pairing add the same two
+// values, so every lane ends with the bit-identical sum, and no step goes through LDS.
+__device__ __forceinline__ float wave_sum_all(float v) {
+  v += u2f(__builtin_amdgcn_mov_dpp(f2u(v), 0xB1, 0xF, 0xF, true));   // lanes i ^ 1
+  v += u2f(__builtin_amdgcn_mov_dpp(f2u(v), 0x4E, 0xF, 0xF, true));   // lanes i ^ 2
+  v += u2f(__builtin_amdgcn_mov_dpp(f2u(v), 0x141, 0xF, 0xF, true));  // half-row mirror
+  v += u2f(__builtin_amdgcn_mov_dpp(f2u(v), 0x140, 0xF, 0xF, true));  // row mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
+  v = u2f(a[0]) + u2f(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+  return u2f(c[0]) + u2f(c[1]);
+}
+
 // Entry g (after `skip` context-only groups) pools the `span` tokens that end with the last token
 // of group g, [m(g+1) - span, m(g+1)); tokens before the start of the buffer are left out and the
 // positional bias is indexed by the token's place in the span. span = m: one entry per group.
 // WAVES = 1: one wavefront per entry, 4 entries per workgroup (short spans).
-// WAVES = 4: one workgroup per entry; wavefront w pools a quarter of the span and the four
-//            online-softmax states (max, sum, weighted sum) are merged in LDS.
+// WAVES = 4 or 8: one workgroup per entry; wavefront w pools a share of the span and the
+//            online-softmax states (max, sum, weighted sum) are merged in LDS. With 8
+//            wavefronts (spans past 64 tokens) a wavefront loads two batches before it pools
+//            the first, so a 128-token group costs one memory round trip.
 template <int DPL, bool RAW_BF16, int OUT_FMT, int WAVES, bool ROPE>
-__global__ __launch_bounds__(256) void kv_compress_kernel(
+__global__ __launch_bounds__(64 * (WAVES == 1 ? 4 : WAVES)) void kv_compress_kernel(
     const void* __restrict__ raw, int64_t raw_seq_stride, int B, int64_t G, int m, int span,
     int64_t skip, const float* __restrict__ w, const float* __restrict__ beta,
     uint8_t* __restrict__ out_rows, EntryMap omap, int64_t first_entry,
@@ -75,7 +91,7 @@ __global__ __launch_bounds__(256) void kv_compress_kernel(
   constexpr int D = DPL * 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t gid = WAVES == 1 ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
-  if (gid >= (int64_t)B * G) return;  // uniform per wavefront (WAVES = 1) or workgroup (4)
+  if (gid >= (int64_t)B * G) return;  // uniform per wavefront (WAVES = 1) or workgroup
   const int64_t b = gid / G, g = gid - b * G;  // g: output row; group g + skip
 
   float wv[DPL];
@@ -96,13 +112,22 @@ __global__ __launch_bounds__(256) void kv_compress_kernel(
   for (int e = 0; e < DPL; e++) acc[e] = 0.0f;
   float M = -INFINITY, L = 0.0f;
   const int64_t row0 = b * raw_seq_stride + first;  // + j >= 0 for every position read
-  for (int t0 = t_begin; t0 < t_end; t0 += kTokBatch) {
-    float x[kTokBatch][DPL];
+  // NB batches of tokens are loaded before the first is pooled (their loads in flight together)
+  constexpr int NB = (WAVES >= 8 && DPL <= 8) ? 2 : 1;
+  for (int t00 = t_begin; t00 < t_end; t00 += NB * kTokBatch) {
+    float xb[NB][kTokBatch][DPL];
 #pragma unroll
-    for (int u = 0; u < kTokBatch; u++) {
-      const int t = t0 + u < t_end ? t0 + u : t_end - 1;  // clamped: loads stay unconditional
-      load_token<DPL, RAW_BF16>(raw, row0 + t, lane, x[u]);
-    }
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+      for (int u = 0; u < kTokBatch; u++) {
+        const int tt = t00 + nb * kTokBatch + u;
+        const int t = tt < t_end ? tt : t_end - 1;  // clamped: loads stay unconditional
+        load_token<DPL, RAW_BF16>(raw, row0 + t, lane, xb[nb][u]);
+      }
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+    const int t0 = t00 + nb * kTokBatch;
+    float (&x)[kTokBatch][DPL] = xb[nb];
     float z[kTokBatch];
 #pragma unroll
     for (int u = 0; u < kTokBatch; u++) {
@@ -112,9 +137,7 @@ __global__ __launch_bounds__(256) void kv_compress_kernel(
       z[u] = s;
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-#pragma unroll
-      for (int u = 0; u < kTokBatch; u++) z[u] += __shfl_xor(z[u], o, 64);
+    for (int u = 0; u < kTokBatch; u++) z[u] = wave_sum_all(z[u]);
     float bmax = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kTokBatch; u++) {
@@ -122,7 +145,8 @@ __global__ __launch_bounds__(256) void kv_compress_kernel(
       bmax = fmaxf(bmax, z[u]);
     }
     const float Mn = fmaxf(M, bmax);
-    const float sc = expf(M - Mn);  // 0 on the first batch (M = -inf)
+    // 0 on the first batch (M = -inf); a batch past the span end (Mn = M = -inf) changes nothing
+    const float sc = Mn == -INFINITY ? 1.0f : expf(M - Mn);
 #pragma unroll
     for (int e = 0; e < DPL; e++) acc[e] *= sc;
     L *= sc;
@@ -134,6 +158,7 @@ __global__ __launch_bounds__(256) void kv_compress_kernel(
       L += p;
     }
     M = Mn;
+    }
   }
   if constexpr (WAVES > 1) {
     __shared__ float s_acc[WAVES][D];
@@ -260,7 +285,7 @@ __global__ __launch_bounds__(256) void kv_compress_kernel(
 template <int DPL, bool RAW_BF16, int WAVES, bool ROPE>
 static hipError_t launch_waves(const KvCompressArgs& a) {
   const int64_t groups = (int64_t)a.B * a.G;
-  dim3 grid((unsigned)(WAVES == 1 ? (groups + 3) / 4 : groups)), block(256);
+  dim3 grid((unsigned)(WAVES == 1 ? (groups + 3) / 4 : groups)), block(64 * (WAVES == 1 ? 4 : WAVES));
   hipStream_t s = (hipStream_t)a.stream;
   switch (a.out_fmt) {
     case CSAH_FMT_ROW_F32:
@@ -289,12 +314,15 @@ static hipError_t launch_waves(const KvCompressArgs& a) {
 
 template <int DPL, bool RAW_BF16>
 static hipError_t launch_dpl(const KvCompressArgs& a) {
-  // a whole workgroup per entry once the span is long enough to keep 4 wavefronts busy
+  // a whole workgroup per entry once the span is long enough to keep 4 wavefronts busy, 8
+  // wavefronts (two batches each for 128 tokens) past 8 batches
   if (a.rope_dims > 0)
-    return a.span > 2 * kTokBatch ? launch_waves<DPL, RAW_BF16, 4, true>(a)
-                                  : launch_waves<DPL, RAW_BF16, 1, true>(a);
-  return a.span > 2 * kTokBatch ? launch_waves<DPL, RAW_BF16, 4, false>(a)
-                                : launch_waves<DPL, RAW_BF16, 1, false>(a);
+    return a.span > 8 * kTokBatch   ? launch_waves<DPL, RAW_BF16, 8, true>(a)
+           : a.span > 2 * kTokBatch ? launch_waves<DPL, RAW_BF16, 4, true>(a)
+                                    : launch_waves<DPL, RAW_BF16, 1, true>(a);
+  return a.span > 8 * kTokBatch   ? launch_waves<DPL, RAW_BF16, 8, false>(a)
+         : a.span > 2 * kTokBatch ? launch_waves<DPL, RAW_BF16, 4, false>(a)
+                                  : launch_waves<DPL, RAW_BF16, 1, false>(a);
 }
 
 template <bool RAW_BF16>
