@@ -504,14 +504,25 @@ def csa128k_replicas(ws: "DecodeStep", count: int = 8):
     return Replicas(ws, make, count)
 
 
+def source_hash(path: str) -> str:
+    """First 16 hex digits of the sha256 of a source file's code: comments and whitespace are
+    dropped first, so that documentation edits do not invalidate counters taken from the code."""
+    import hashlib
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
 def traffic_from_profile(kernel: str):
     """HBM bytes per launch from the committed counter summary, if it matches the kernel's source.
 
     profiles/<kernel>_<workload>_counters.txt holds `key = value` lines written from two rocprofv3 --pmc
-    runs (FETCH_SIZE, WRITE_SIZE) scaled by a copy-kernel calibration; its source_sha256_16 is the
-    hash of the .hip file the kernel was built from when the counters were taken.
+    runs (FETCH_SIZE, WRITE_SIZE) scaled by a copy-kernel calibration; its source_sha256_16 is
+    source_hash() of the .hip file the kernel was built from when the counters were taken.
     """
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"{KERNELS[kernel]['profile']}_counters.txt")
     try:
         rec = {}
@@ -521,8 +532,7 @@ def traffic_from_profile(kernel: str):
                     k, v = ln.split("=", 1)
                     rec[k.strip()] = v.strip()
         src = os.path.join(ROOT, "long_context_attention_03_amd", "csrc", KERNELS[kernel]["source"])
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        if rec.get("source_sha256_16") != h:
+        if rec.get("source_sha256_16") != source_hash(src):
             return None
         return float(rec["hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):

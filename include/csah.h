@@ -13,7 +13,9 @@
  *
  * Conventions shared by every entry point
  *  - Every array argument is a DEVICE pointer to memory owned by the caller. The library never
- *    allocates, frees or synchronises; it keeps no state between calls.
+ *    allocates, frees or synchronises. Between calls it keeps only a thread's pending profiling
+ *    request (csah_profile_next_call, consumed by that thread's next call) and, for
+ *    csah_csa_attend_noalloc, a scratch array in every GPU it runs on.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). A call only enqueues
  *    kernels on it and returns.
  *  - Arguments are validated on the host before anything is enqueued. On a nonzero status nothing
@@ -22,7 +24,8 @@
  *    derive from device data so that they stay inside the shapes passed, and the results are then
  *    unspecified.
  *  - Strides are counted in rows (tokens or entries) of the buffer's own row format.
- *  - Calls are reentrant; concurrent calls must use distinct workspaces.
+ *  - Calls are reentrant; concurrent calls must use distinct workspaces (concurrent
+ *    csah_csa_attend_noalloc calls on one GPU share its scratch and must be ordered).
  *
  * Row formats of one token's / one compressed entry's shared K=V vector (D values):
  *   CSAH_FMT_ROW_F32        D little-endian binary32 values (4*D bytes).
@@ -137,10 +140,15 @@ int csah_kv_compress_span(const void* raw, int raw_dtype, int64_t raw_seq_stride
  * ws        device workspace of at least csah_index_topk_workspace(B, Q, N, k, HI, dI) bytes,
  *           256-byte aligned; its contents need no initialisation and are clobbered.
  * Supported: 1 <= HI <= 16, dI in {32, 64, 128}, 1 <= k <= 4096, N < 2^31, m >= 1, B*Q < 65536.
- * Two schedules compute the same result. With dI = 128 and Q >= 16 (a prefill chunk: many
- * queries of one sequence share its keys) the scores come from the scaled FP4 MFMA and are
- * recomputed rather than stored; the workspace then holds, per query, a histogram, counters and
- * candidate lists of up to N 8-byte keys. Otherwise every score is stored (4 more bytes per entry).
+ * Several schedules compute the same result; the workspace size follows the one the shape takes.
+ *  - Decode (Q <= 2 queries per sequence, N <= 2^20): a scan leaves per-range candidate lists and
+ *    one top-k pass per query ranks their union; the workspace is a fixed 73,728 bytes per
+ *    (sequence, query) slot, whatever N.
+ *  - dI = 128 and Q >= 16 (a prefill chunk: many queries of one sequence share its keys): the
+ *    scores come from the scaled FP4 MFMA and are recomputed rather than stored; the workspace
+ *    holds, per query, a histogram, counters and candidate lists of up to N 8-byte keys.
+ *  - Otherwise (3 <= Q <= 15 with 128-dim keys, or N > 2^20) every score is stored: per slot
+ *    the head-summed query, a histogram, counters, 4 bytes per entry and two candidate lists.
  */
 size_t csah_index_topk_workspace(int B, int Q, int64_t N, int k, int HI, int dI);
 int csah_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int dI,
@@ -169,7 +177,9 @@ int csah_index_topk(const uint8_t* q_codes, const uint8_t* q_scales, int HI, int
  * sink      [H] fp32 logits or NULL. scale: softmax temperature applied to q.y.
  * out       [B][Q][H][D] fp32; lse [B][Q][H] fp32 or NULL.
  * ws        at least csah_attend_workspace(B, Q, H, D, k + w) bytes, 256-byte aligned.
- * Supported: H % 16 == 0; (fmt, D) = (ROW_E4M3_BF16, 512) or (ROW_F32, 128); k + w < 2^31.
+ * Supported: any H >= 1 (heads go in groups of 16 per wavefront; the heads that pad the last
+ *   group are computed and not stored); (fmt, D) = (ROW_E4M3_BF16, 512) or (ROW_F32, 128);
+ *   k + w < 2^31.
  */
 size_t csah_attend_workspace(int B, int Q, int H, int D, int64_t max_rows);
 int csah_csa_attend(const void* q, int q_dtype, int H, int D, const void* cache, int fmt,

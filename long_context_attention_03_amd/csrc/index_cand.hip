@@ -19,15 +19,16 @@
 //   reaches cmin (one bin higher when that would overflow the list), and u = the largest key
 //   below b_pub (0 when none). Nothing else leaves the workgroup: no score array, no global
 //   histogram.
-// topk (grid: parts x slots). Every workgroup of a slot takes the union U of the slot's lists and
-//   T = the kk-th largest key of U (1 when U holds fewer than kk keys: then every key counts).
+// topk (grid: one workgroup of 1024 threads per slot). The workgroup takes the union U of the
+//   slot's lists into registers and T = the kk-th largest key of U (1 when U holds fewer than kk
+//   keys: then every key counts).
 //   U is a subset of all keys, so T is at most the true kk-th largest key. A range whose bound is
 //   below T therefore has no unpublished key in the top-kk: its part of the top-kk is in U. A range
 //   whose bound is at least T is scored again in full, its list replaced by all its keys >= T,
 //   and T recomputed (it can only rise, so the remaining ranges are checked against the new T).
-//   The keys >= T that remain are exactly the top-kk. Each workgroup ranks its share of them
-//   (the output position of a key is the number of larger keys in the set) and writes idx and
-//   score. With random keys a range holds about kk * range / visible of the top-kk and publishes
+//   The keys >= T that remain are exactly the top-kk. They are bucket-sorted in LDS with bins
+//   fitted to their key range; a key's output position is its bin's start plus the number of
+//   larger keys in its bin, and idx and score are written from there. With random keys a range holds about kk * range / visible of the top-kk and publishes
 //   several times that, so the re-scoring path is rare; it keeps the result exact when the
 //   relevant entries cluster (many of the top-kk in one range, or ties).
 #include <math.h>

@@ -16,9 +16,14 @@
 // fewer than 24 bits of the finest granularity each fp32 operation is exact: the result is the
 // exact score in any order, and the selection below is bit-exact.
 //
-// Pipeline per (sequence, query) "slot", four kernels (kernel boundaries carry the cross-workgroup
-// dependencies; on multi-XCD gfx950 a device-scope release fence per workgroup costs more than a
-// launch):
+// Schedules. Decode calls (one or two queries per sequence) over at most 2^20 entries per
+// sequence take the candidate-list scan and top-k of index_cand.hip. A prefill chunk (16 or more
+// queries of one sequence, 128-dim keys) takes the MFMA histogram / select / sort passes at the
+// end of this file, 3 to 15 queries take the multi-query MFMA scan, and everything else takes the
+// pipeline below, per (sequence, query) "slot", four kernels. Kernel boundaries carry the
+// cross-workgroup dependencies: measured on MI355X, a dependent kernel costs about 1.7 us inside
+// a graph, an in-kernel ticket-ordered hand-off about 1.3 us with one workgroup per phase and far
+// more with many (same-address atomics serialize, about 8 ns each).
 //   prep      qt (fp32, dI values) + clear the histogram / counters        (1 WG per slot)
 //   scan      stream the FP4 keys (coalesced 16-byte loads, one 32-element block per lane,
 //             8 groups of loads in flight), write fp32 scores, build a 4096-bin histogram of the

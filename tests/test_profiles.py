@@ -3,11 +3,12 @@ traffic_over_algorithmic line): counted bytes (FETCH_SIZE + WRITE_SIZE scaled by
 size) over the bytes the method must move, per kernel, must stay under the stated limits, and
 each summary must have been taken from the kernel source as it is now (a summary of older code
 is no evidence; refresh it with the commands written in its header)."""
-import hashlib
 import os
 import re
 
 import pytest
+
+from bench import source_hash
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PROFILES = os.path.join(ROOT, "profiles")
@@ -29,7 +30,7 @@ def _read(name):
     rec, src = {}, None
     with open(os.path.join(PROFILES, f"{name}_counters.txt")) as f:
         for ln in f:
-            m = re.search(r"sha256 of (csrc/\S+\.hip)", ln)
+            m = re.search(r"source_sha256_16 is .*?(csrc/\S+\.hip)", ln)
             if m:
                 src = m.group(1)
             if "=" in ln and not ln.lstrip().startswith("#"):
@@ -43,8 +44,8 @@ def test_counted_traffic_within_limit_and_current(name):
     rec, src = _read(name)
     assert src, f"{name}: the summary does not name its source file"
     path = os.path.join(ROOT, "long_context_attention_03_amd", src)
-    h = hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
-    assert rec["source_sha256_16"] == h, f"{name}: counters were taken from another {src}"
+    assert rec["source_sha256_16"] == source_hash(path), \
+        f"{name}: counters were taken from another version of {src}"
     fetch = float(rec["fetch_size_kib_per_dispatch"]) * 1024 * float(rec["fetch_factor"])
     write = float(rec["write_size_kib_per_dispatch"]) * 1024 * float(rec["write_factor"])
     total = float(rec["hbm_bytes_per_launch"])
