@@ -140,6 +140,66 @@ def _dt(t):
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _rows_dense(t) -> bool:
+    """A [B, n, ...] tensor whose rows (the dims after the second) are densely packed, one after
+    another along dim 1, while dim 0 (the sequence) may have any stride that is a whole number of
+    rows: a sequence slice of a larger cache. The library takes that stride in rows."""
+    if t.dim() < 2:
+        return t.is_contiguous()
+    row = 1
+    for size, stride in zip(reversed(t.shape[2:]), reversed(t.stride()[2:])):
+        if size > 1 and stride != row:
+            return False
+        row *= size
+    if t.stride(1) != row:
+        return False
+    return t.shape[0] <= 1 or t.stride(0) % row == 0
+
+
+def _validate(dev, *items):
+    """Check arguments before their raw pointers are taken. items: (tensor or None, name, dtypes,
+    layout), layout "dense" (contiguous) or "rows" (see _rows_dense). Dtypes are checked for every
+    argument first, then the device, then the layout the kernels address."""
+    items = [it for it in items if it[0] is not None]
+    for t, name, dtypes, _ in items:
+        if t.dtype not in dtypes:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+    for t, name, _, _ in items:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: a GPU tensor is required (got {t.device})")
+        if t.device != dev:
+            raise ValueError(f"{name}: on {t.device}, the call runs on {dev}")
+    for t, name, _, layout in items:
+        if layout == "dense" and not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+        if layout == "rows" and not _rows_dense(t):
+            raise ValueError(f"{name}: rows must be packed (only the sequence dim may be strided)")
+
+
+_U8 = (torch.uint8,)
+_I32 = (torch.int32,)
+_I64 = (torch.int64,)
+_F32 = (torch.float32,)
+_QDT = (torch.bfloat16, torch.float32)
+
+
+def _check_attend_args(q, cache, cache_layout, idx, window, w, pos, sink, out, lse):
+    _validate(q.device, (q, "q", _QDT, "dense"), (cache, "cache", _U8, cache_layout),
+              (idx, "idx", _I32, "dense"), (window if w > 0 else None, "window", _U8, "rows"),
+              (pos, "pos", _I64, "dense"), (sink, "sink", _F32, "dense"),
+              (out, "out", _F32, "dense"), (lse, "lse", _F32, "dense"))
+
+
+def _check_index_args(q_codes, q_scales, k_codes, k_scales, k_layout, pos, idx_out, score_out):
+    _validate(q_codes.device, (q_codes, "q_codes", _U8, "dense"),
+              (q_scales, "q_scales", _U8, "dense"), (k_codes, "k_codes", _U8, k_layout),
+              (k_scales, "k_scales", _U8, k_layout), (pos, "pos", _I64, "dense"),
+              (idx_out, "idx_out", _I32, "dense"), (score_out, "score_out", _F32, "dense"))
+    if k_layout == "rows" and k_codes.dim() == 3 and k_scales.dim() == 3 and k_codes.shape[0] > 1 \
+            and k_codes.stride(0) // k_codes.stride(1) != k_scales.stride(0) // k_scales.stride(1):
+        raise ValueError("k_codes and k_scales must have the same sequence stride in rows")
+
+
 def _workspace(nbytes: int, device, ws=None):
     if nbytes == 0:
         return None
@@ -189,6 +249,7 @@ def index_topk_workspace(B: int, Q: int, N: int, k: int, HI: int, dI: int) -> in
 def index_topk(q_codes, q_scales, k_codes, k_scales, pos, m: int, k: int, N: int | None = None,
                want_scores: bool = True, ws=None, idx_out=None, score_out=None, stream=None):
     """Top-k entries per query -> (idx int32 [B, Q, k], scores fp32 [B, Q, k] or None)."""
+    _check_index_args(q_codes, q_scales, k_codes, k_scales, "rows", pos, idx_out, score_out)
     B, Q, HI, half = q_codes.shape
     dI = 2 * half
     kstride = k_codes.stride(0) // k_codes.stride(1)
@@ -224,6 +285,7 @@ def _fmt_of(rows, D):
 def csa_attend(q, cache, idx, window, w: int, pos, sink, scale: float, N: int | None = None,
                ws=None, out=None, lse=None, stream=None):
     """Sparse attention over cache rows idx + window + sink -> (out fp32 [B,Q,H,D], lse [B,Q,H])."""
+    _check_attend_args(q, cache, "rows", idx, window, w, pos, sink, out, lse)
     B, Q, H, D = q.shape
     fmt = _fmt_of(cache, D)
     N = cache.shape[1] if N is None else N
@@ -247,6 +309,7 @@ def csa_attend_noalloc(q, cache, idx, window, w: int, pos, sink, scale: float,
                        N: int | None = None, out=None, lse=None, stream=None):
     """csa_attend whose partials use the library's static scratch (no workspace, no allocation
     inside the call); out / lse may be passed preallocated."""
+    _check_attend_args(q, cache, "rows", idx, window, w, pos, sink, out, lse)
     B, Q, H, D = q.shape
     fmt = _fmt_of(cache, D)
     N = cache.shape[1] if N is None else N
@@ -267,6 +330,7 @@ def csa_attend_noalloc(q, cache, idx, window, w: int, pos, sink, scale: float,
 def hca_attend(q, cache, m: int, window, w: int, pos, sink, scale: float, N: int | None = None,
                ws=None, out=None, lse=None, stream=None):
     """Dense attention over every visible entry + window + sink -> (out, lse)."""
+    _check_attend_args(q, cache, "rows", None, window, w, pos, sink, out, lse)
     B, Q, H, D = q.shape
     fmt = _fmt_of(cache, D)
     N = cache.shape[1] if N is None else N
@@ -311,6 +375,8 @@ def index_topk_paged(q_codes, q_scales, k_pool_codes, k_pool_scales, block_table
                      page_size: int, N: int, pos, m: int, k: int, want_scores: bool = True,
                      ws=None, idx_out=None, score_out=None, stream=None):
     """index_topk over FP4 keys in a paged pool -> (logical idx [B, Q, k], scores or None)."""
+    _check_index_args(q_codes, q_scales, k_pool_codes, k_pool_scales, "dense", pos, idx_out,
+                      score_out)
     B, Q, HI, half = q_codes.shape
     dI = 2 * half
     dev = q_codes.device
@@ -332,6 +398,7 @@ def index_topk_paged(q_codes, q_scales, k_pool_codes, k_pool_scales, block_table
 def csa_attend_paged(q, cache_pool, block_table, page_size: int, N: int, idx, window, w: int,
                      pos, sink, scale: float, ws=None, out=None, lse=None, stream=None):
     """csa_attend with the compressed cache in a paged pool (idx: logical entries)."""
+    _check_attend_args(q, cache_pool, "dense", idx, window, w, pos, sink, out, lse)
     B, Q, H, D = q.shape
     fmt = _fmt_of(cache_pool, D)
     k = idx.shape[-1]
@@ -354,6 +421,7 @@ def csa_attend_paged(q, cache_pool, block_table, page_size: int, N: int, idx, wi
 def hca_attend_paged(q, cache_pool, block_table, page_size: int, N: int, m: int, window, w: int,
                      pos, sink, scale: float, ws=None, out=None, lse=None, stream=None):
     """hca_attend with the compressed cache in a paged pool."""
+    _check_attend_args(q, cache_pool, "dense", None, window, w, pos, sink, out, lse)
     B, Q, H, D = q.shape
     fmt = _fmt_of(cache_pool, D)
     dev = q.device

@@ -488,9 +488,10 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttendK p) {
 // S^T = Y Q^T, the transposing read gives the Y^T fragments of O^T += Y^T P^T, as in
 // attend_kernel. One workgroup barrier per tile orders the buffer reuse (a buffer is rewritten two
 // tiles later, after every wavefront has passed the barrier of the tile in between). The next
-// tile's loads are issued after the S^T phase and land during the softmax and P.Y phases. Two
-// workgroups share a CU (LDS 67.6 KB, 256 registers per lane each), so one's barrier and softmax
-// waits overlap the other's matrix work.
+// tile's loads are issued after the S^T phase and land during the softmax and P.Y phases. With
+// MINW = 2 two workgroups share a CU (LDS 67.6 KB, at most 256 registers per lane each), so one's
+// barrier and softmax waits overlap the other's matrix work; with MINW = 1 a workgroup keeps more
+// tiles in flight instead.
 constexpr int kXTile = 32, kXRS = 528, kXTileElems = kXTile * kXRS;
 
 // Max over the four 16-lane rows of a wavefront, in every lane: gfx950's permlane swaps exchange

@@ -10,12 +10,12 @@
 //
 // Lane l of a wavefront owns DPL = D/64 consecutive dimensions, so every token row is read with
 // one coalesced vector load per lane. Tokens go in batches of 8 whose loads and gate reductions
-// (wavefront butterflies) are in flight together. The softmax is evaluated online (running max,
+// (symmetric wavefront exchanges) are in flight together. The softmax is evaluated online (running max,
 // running denominator, running weighted sum), which keeps a group of any size in registers. Short
-// groups take one wavefront each; long groups (m > 16) take a workgroup whose 4 wavefronts pool
-// a quarter of the tokens each and merge their states in LDS. The pooled row is encoded in the
-// output format and written with vector stores. HBM traffic is one read of the raw rows and one
-// write of the compressed rows. With RoPE (csah_kv_compress_rope) the pooled row's rotary pairs
+// spans (up to 16 tokens) take one wavefront each; longer ones take a workgroup of 4 (up to 64)
+// or 8 wavefronts that pool a share of the tokens each and merge their states in LDS. The pooled
+// row is encoded in the output format and written with vector stores. HBM traffic is one read of
+// the raw rows and one write of the compressed rows. With RoPE (csah_kv_compress_rope) the pooled row's rotary pairs
 // are turned in fp64 before encoding, at the position of the last token of the entry's group.
 #include "csah_internal.h"
 #include "device_common.h"

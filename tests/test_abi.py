@@ -247,3 +247,39 @@ def test_kv_compress_rope_rejects_bad_arguments():
              10000.0, None) == L.INVALID_ARGUMENT  # page size not a power of two
     assert g(FAKE, 0, 8, 1, 8, 512, 4, 4, 0, FAKE, FAKE, FAKE, 1, None, FAKE, 4, 4, 0, FAKE, 0,
              10000.0, None) == L.INVALID_ARGUMENT  # no rotary dims
+
+
+def test_binding_checks_dtypes_devices_and_layouts_before_any_call():
+    """The Python binding refuses what the kernels would misread (an int32 pos, an int64 idx, a
+    strided code view, a host tensor) before it takes a raw pointer."""
+    import torch
+    qc = torch.zeros(1, 1, 4, 64, dtype=torch.uint8)
+    qs = torch.zeros(1, 1, 4, 4, dtype=torch.uint8)
+    kc = torch.zeros(2, 16, 64, dtype=torch.uint8)
+    ks = torch.zeros(2, 16, 4, dtype=torch.uint8)
+    pos64 = torch.zeros(2, dtype=torch.int64)
+    with pytest.raises(TypeError, match="pos"):
+        L.index_topk(qc, qs, kc, ks, pos64.to(torch.int32), 4, 8)
+    with pytest.raises(TypeError, match="k_codes"):
+        L.index_topk(qc, qs, kc.to(torch.int16), ks, pos64, 4, 8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        L.index_topk(qc, qs, kc, ks, pos64, 4, 8)
+    q = torch.zeros(1, 1, 64, 512, dtype=torch.bfloat16)
+    cache = torch.zeros(1, 8, 576, dtype=torch.uint8)
+    with pytest.raises(TypeError, match="idx"):
+        L.csa_attend(q, cache, torch.zeros(1, 1, 8, dtype=torch.int64), None, 0, pos64[:1], None,
+                     0.04)
+    with pytest.raises(TypeError, match="sink"):
+        L.hca_attend(q, cache, 4, None, 0, pos64[:1], torch.zeros(64, dtype=torch.float64), 0.04)
+    with pytest.raises(TypeError, match="q"):
+        L.hca_attend(q.to(torch.float16), cache, 4, None, 0, pos64[:1], None, 0.04)
+
+
+def test_row_layout_rule():
+    """Sequence slices of a larger cache pass; views whose rows are not packed do not."""
+    import torch
+    big = torch.zeros(4, 100, 64, dtype=torch.uint8)
+    assert L._rows_dense(big) and L._rows_dense(big[:, 10:50]) and L._rows_dense(big[1:3, 5:])
+    assert not L._rows_dense(big[:, :, :32])       # half of every row
+    assert not L._rows_dense(big.transpose(0, 1))  # sequences interleaved
+    assert not L._rows_dense(big[:, ::2])          # every other row

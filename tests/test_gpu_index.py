@@ -57,9 +57,10 @@ def test_decode_step_launch_shape_16_sequences():
 
 
 def test_long_key_ranges_several_stage_windows():
-    """2 x (2^22 + 777) keys: each scan workgroup's range holds more than two 8192-score stage
-    windows (two full flushes and a partial one), the last range of each sequence is ragged, and
-    the second sequence sees 999 groups fewer. Codes and scales are random bytes (scales in a
+    """2 x (2^22 + 777) keys, beyond the candidate-list schedule's 2^22 per sequence, so the
+    stored-score schedule runs: each scan workgroup streams 17,408 keys, four full 4096-score
+    stage windows and a partial one; the last range of each sequence is ragged,
+    and the second sequence sees 999 groups fewer. Codes and scales are random bytes (scales in a
     narrow band keep every score exact)."""
     rng = np.random.default_rng(12)
     B, N, HI, dI, m, k = 2, (1 << 22) + 777, 4, 128, 4, 1024
