@@ -819,6 +819,7 @@ def prefill_measure(steps: int, warmup: int):
                      "peak": kernels[dom]["peak_TFLOPs"], "unit": "TFLOP/s",
                      "frac": kernels[dom]["frac"]},
         "kernels": kernels,
+        "index_workspace_bytes": L.index_topk_workspace(1, PF_Q, PF_N_CSA, K, HI, DI),
         "compress_span8": {
             "what": "the chunk's overlapping entries: 8 tokens each at stride 4 (1024 E4M3+bf16 "
                     "rows and 1024 FP4 indexer keys, the 4 preceding tokens as context)",

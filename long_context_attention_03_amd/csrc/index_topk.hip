@@ -58,6 +58,7 @@ constexpr int kSortCap = 4096;
 struct IdxWs {
   char* base;
   size_t slot_bytes, off_hist, off_ctr, off_scores, off_sure, off_tie;
+  uint32_t tie_cap;  // keys the tie list holds
   __device__ char* slot(int s) const { return base + (size_t)s * slot_bytes; }
   __device__ float* qt(int s) const { return (float*)slot(s); }
   __device__ uint32_t* hist(int s) const { return (uint32_t*)(slot(s) + off_hist); }
@@ -69,16 +70,30 @@ struct IdxWs {
 
 static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Per-slot layout. The scan path stores every score; the MFMA path recomputes them instead.
+// Tie list of a prefill query (the MFMA path): its threshold bin holds about N/60 keys or fewer
+// when the scores spread like a sum of many products (the bin is a quarter of a binade at about
+// 2.7 standard deviations out for k = 1024 of 263,168), so N/32 keys, and at least twice the
+// LDS sort's capacity, take it; a query whose bin holds more is finished by index_rescan_kernel.
+// That keeps a 4096-query chunk's workspace at a few hundred MB instead of N keys per query.
+static uint32_t prefill_tie_cap(int64_t N) {
+  int64_t c = (N + 31) / 32;
+  if (c < 2 * kSortCap) c = 2 * kSortCap;
+  if (c > N) c = N;
+  return (uint32_t)c;
+}
+
+// Per-slot layout. The scan path stores every score and can take every key as a tie; the MFMA
+// path recomputes the scores instead and caps the tie list.
 static IdxWs make_ws(void* base, int64_t N, int k, bool with_scores) {
   IdxWs w;
   w.base = (char*)base;
+  w.tie_cap = with_scores ? (uint32_t)N : prefill_tie_cap(N);
   w.off_hist = al256(128 * sizeof(float));
   w.off_ctr = w.off_hist + al256(kBins * sizeof(uint32_t));
   w.off_scores = w.off_ctr + 256;
   w.off_sure = w.off_scores + (with_scores ? al256((size_t)N * sizeof(float)) : 0);
   w.off_tie = w.off_sure + al256((size_t)k * sizeof(uint64_t));
-  w.slot_bytes = w.off_tie + al256((size_t)N * sizeof(uint64_t));
+  w.slot_bytes = w.off_tie + al256((size_t)w.tie_cap * sizeof(uint64_t));
   return w;
 }
 
@@ -765,6 +780,8 @@ __global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
 //            lists, as index_select_kernel does from stored scores
 //   sort     per query: bitonic sort of the candidates in LDS (after a radix select when the tie
 //            list is longer than kSortCap), then the ordered top-k
+//   rescan   per query whose threshold bin held more keys than its tie list (capped at N/32, at
+//            least 8192): an exact radix select over fresh passes across its keys, then the sort
 constexpr int kPBins = 2048, kPBinShift = 21;
 constexpr int kPKeys = 16384;                // keys per workgroup: a 16-bit counter cannot overflow
 constexpr uint32_t kNoThreshold = 0xFFFFFFFFu;
@@ -1003,8 +1020,8 @@ __global__ __launch_bounds__(256) void index_mfma_select_kernel(
                              const uint32_t g = atomicAdd(&ctr[0], 1u);
                              if (g < (uint32_t)k) sure[g] = x;
                            } else {
-                             const uint32_t g = atomicAdd(&ctr[1], 1u);
-                             if ((int64_t)g < N) tie[g] = x;
+                             const uint32_t g = atomicAdd(&ctr[1], 1u);  // counts past the cap
+                             if (g < ws.tie_cap) tie[g] = x;
                            }
                          }
                        });
@@ -1027,7 +1044,7 @@ __global__ __launch_bounds__(256) void index_mfma_select_kernel(
     if (list == 0) {
       if (g < (uint32_t)k) ws.sure((int)sl)[g] = stage[0][qn][e];
     } else {
-      if ((int64_t)g < N) ws.tie((int)sl)[g] = stage[1][qn][e];
+      if (g < ws.tie_cap) ws.tie((int)sl)[g] = stage[1][qn][e];
     }
   }
 }
@@ -1086,9 +1103,158 @@ __global__ __launch_bounds__(1024) void index_sort_kernel(const int64_t* __restr
   const int slot = blockIdx.x, b = slot / Q, i = slot - b * Q;
   const int64_t nv = visible_entries(pos, b, i, m, N);
   const int kk = (int)(nv < k ? nv : k);
+  if (kk > 0 && ws.ctr(slot)[1] > ws.tie_cap) return;  // overflowed: index_rescan_kernel
   __shared__ uint64_t keys[kSortCap];
   __shared__ uint32_t dh[256];
   finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh, bin_bits);
+}
+
+// ---- prefill: a query whose threshold bin overflowed its tie list ------------------------------
+// One workgroup per slot; every slot whose tie list held its whole bin returns at once. For the
+// others (ties in bulk, or a score distribution far from the usual spread) the workgroup finds
+// the kk-th largest key T by a radix select over fresh passes across the query's visible keys,
+// 11 key bits a pass below the shared bin, and a last pass collects the bin's keys >= T: with the
+// sure list they are exactly the top-kk, sorted in LDS as index_sort_kernel does. The scores come
+// from the same MFMA tiles as the earlier passes (every column of the B operand holds this query,
+// and lanes 0..3 of each 16-lane group take keys 4 * group + 0..3), so they are the same values.
+constexpr int kPBinBits = 32 - kPBinShift;  // key bits of the shared bin
+constexpr int kRescanDigit = 11;
+constexpr int kRescanThreads = 256;
+
+template <int HP, typename F>
+__device__ __forceinline__ void rescan_keys(const QueryOps<HP>& qo,
+                                            const uint8_t* __restrict__ k_codes,
+                                            const uint8_t* __restrict__ k_scales,
+                                            const EntryMap& kmap, int b, int64_t nv, F visit) {
+  constexpr int U = 4, NW = kRescanThreads / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, blk = lane >> 4;
+  const int64_t ntile = (nv + 15) / 16;
+  for (int64_t t0 = wave; t0 < ntile; t0 += NW * U) {
+    u32x4 c[U];
+    uint32_t e[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      int64_t g = 16 * (t0 + NW * u) + n;
+      g = g < nv ? g : nv - 1;  // rows past the visible keys read a valid row (masked below)
+      const int64_t row = kmap.row(b, g);
+      c[u] = *(const u32x4*)(k_codes + row * 64 + 16 * blk);
+      e[u] = k_scales[row * 4 + blk];
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int64_t tile = t0 + NW * u;
+      f32x4 sc = tile_scores<HP>(c[u], e[u], qo);
+#pragma unroll
+      for (int j = 0; j < 4; j++) sc[j] += 0.0f;  // fold -0 into +0
+      const float s = n == 0 ? sc[0] : (n == 1 ? sc[1] : (n == 2 ? sc[2] : sc[3]));
+      const int64_t g = 16 * tile + 4 * blk + n;
+      if (n < 4 && g < nv)
+        visit(((uint64_t)order_key(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)g));
+    }
+  }
+}
+
+template <int HP, bool PAGED>
+__global__ __launch_bounds__(kRescanThreads) void index_rescan_kernel(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
+    int64_t N, const int64_t* __restrict__ pos, int m, int Q, int k,
+    int32_t* __restrict__ idx_out, float* __restrict__ score_out, IdxWs ws) {
+  const int slot = blockIdx.x, b = slot / Q, i = slot - b * Q, t = threadIdx.x;
+  const int64_t nv = visible_entries(pos, b, i, m, N);
+  const int kk = (int)(nv < k ? nv : k);
+  const uint32_t* ctr = ws.ctr(slot);
+  if (kk == 0 || ctr[1] <= ws.tie_cap) return;  // uniform over the workgroup
+  constexpr int kLow = 64 - kPBinBits;           // key bits below the bin
+  constexpr int kDBins = 1 << kRescanDigit;
+  constexpr int kPer = kDBins / kRescanThreads;  // digit bins per thread
+  __shared__ uint32_t hist[kDBins];
+  __shared__ uint32_t suf[kRescanThreads];
+  __shared__ uint64_t keys[kSortCap];
+  __shared__ uint64_t s_prefix, s_mask;
+  __shared__ uint32_t s_r, s_cnt;
+  const uint32_t thr = ctr[2];
+  const uint32_t ns = ctr[0] < (uint32_t)kk ? ctr[0] : (uint32_t)kk;  // < kk by the threshold
+  QueryOps<HP> qo;
+  load_query_ops<HP>(q_codes, q_scales, HI, (int64_t)b * Q + i, true, (t & 63) >> 4, qo);
+  if (t == 0) {
+    s_prefix = (uint64_t)thr << kLow;
+    s_mask = ~(uint64_t)0 << kLow;
+    s_r = (uint32_t)kk - ns;  // rank (from 1) of T among the bin's keys
+  }
+  __syncthreads();
+  for (int lo = kLow; lo > 0;) {
+    const int width = lo >= kRescanDigit ? kRescanDigit : lo;
+    const int shift = lo - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int j = t; j < kDBins; j += kRescanThreads) hist[j] = 0u;
+    __syncthreads();
+    // read before the barriers below; one thread rewrites them after the last of those
+    const uint64_t pm = s_mask, pv = s_prefix;
+    const uint32_t r = s_r;
+    rescan_keys<HP>(qo, k_codes, k_scales, kmap, b, nv, [&](uint64_t x) {
+      if ((x & pm) == pv) atomicAdd(&hist[(uint32_t)(x >> shift) & dmask], 1u);
+    });
+    __syncthreads();
+    // thread t owns digits [kPer t, kPer t + kPer); suf[t] = keys in digits >= kPer t
+    uint32_t own = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; j++) own += hist[kPer * t + j];
+    suf[t] = own;
+    __syncthreads();
+    for (int off = 1; off < kRescanThreads; off <<= 1) {
+      const uint32_t v = suf[t] + (t + off < kRescanThreads ? suf[t + off] : 0u);
+      __syncthreads();
+      suf[t] = v;
+      __syncthreads();
+    }
+    const uint32_t above = t + 1 < kRescanThreads ? suf[t + 1] : 0u;
+    if (above < r && r <= suf[t]) {  // exactly one thread: the r-th largest is in its digits
+      uint32_t cum = above;
+      int d = kPer * t + kPer - 1;
+      for (; d > kPer * t; d--) {
+        if (cum + hist[d] >= r) break;
+        cum += hist[d];
+      }
+      s_r = r - cum;
+      s_prefix = pv | ((uint64_t)d << shift);
+      s_mask = pm | ((uint64_t)dmask << shift);
+    }
+    __syncthreads();
+    lo = shift;
+  }
+  // s_prefix is now T itself (all 64 bits fixed); the bin's keys >= T are its top kk - ns
+  const uint64_t T = s_prefix;
+  if (t == 0) s_cnt = 0u;
+  const uint64_t* sure = ws.sure(slot);
+  for (int j = t; j < (int)ns; j += kRescanThreads) keys[j] = sure[j];
+  __syncthreads();
+  rescan_keys<HP>(qo, k_codes, k_scales, kmap, b, nv, [&](uint64_t x) {
+    if ((uint32_t)(x >> kLow) == thr && x >= T) {
+      const uint32_t at = atomicAdd(&s_cnt, 1u);
+      if (ns + at < (uint32_t)kSortCap) keys[ns + at] = x;
+    }
+  });
+  __syncthreads();
+  const uint32_t got = s_cnt < (uint32_t)kSortCap - ns ? s_cnt : (uint32_t)kSortCap - ns;
+  const int n = (int)(ns + got);
+  int p2 = 2;
+  while (p2 < n) p2 <<= 1;
+  for (int j = n + t; j < p2; j += kRescanThreads) keys[j] = 0;
+  __syncthreads();
+  bitonic_sort_desc(keys, p2);
+  int32_t* io = idx_out + (int64_t)slot * k;
+  float* so = score_out ? score_out + (int64_t)slot * k : nullptr;
+  for (int j = t; j < k; j += kRescanThreads) {
+    if (j < kk && j < n) {
+      const uint64_t x = keys[j];
+      io[j] = (int32_t)(0xFFFFFFFFu - (uint32_t)x);
+      if (so) so[j] = key_to_float((uint32_t)(x >> 32));
+    } else {
+      io[j] = -1;
+      if (so) so[j] = -INFINITY;
+    }
+  }
 }
 
 // Key ranges of at most kPKeys keys (for paged keys also at most 1024 pages, +2 partial ones, so
@@ -1127,7 +1293,11 @@ static hipError_t launch_mfma_hp(const IndexArgs& a, const IdxWs& w, hipStream_t
                                                            a.k_codes, a.k_scales, a.kmap, a.N,
                                                            a.pos, a.m, a.Q, a.k, sp, w);
   index_sort_kernel<<<slots, 1024, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, a.idx_out, a.score_out, w,
-                                           32 - kPBinShift);
+                                           kPBinBits);
+  if (w.tie_cap < (uint64_t)a.N)  // otherwise no tie list can overflow
+    index_rescan_kernel<HP, PAGED><<<slots, kRescanThreads, 0, s>>>(
+        a.q_codes, a.q_scales, a.HI, a.k_codes, a.k_scales, a.kmap, a.N, a.pos, a.m, a.Q, a.k,
+        a.idx_out, a.score_out, w);
   return hipGetLastError();
 }
 

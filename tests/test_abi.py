@@ -283,3 +283,13 @@ def test_row_layout_rule():
     assert not L._rows_dense(big[:, :, :32])       # half of every row
     assert not L._rows_dense(big.transpose(0, 1))  # sequences interleaved
     assert not L._rows_dense(big[:, ::2])          # every other row
+
+
+def test_prefill_index_workspace_is_bounded():
+    """The 4096-query prefill chunk over 263,168 FP4 keys: each query's tie list holds N/32 keys
+    (at least 8192) instead of N, so the workspace is a few hundred MB, not 8.7 GB; a query
+    whose threshold bin holds more is finished by the re-scan."""
+    ws = L.index_topk_workspace(1, 4096, 263168, 1024, 4, 128)
+    assert 0 < ws < (512 << 20), ws
+    # the decode schedules are unchanged: candidate lists of a fixed size per slot
+    assert L.index_topk_workspace(16, 1, 262144, 1024, 4, 128) == 16 * 73728

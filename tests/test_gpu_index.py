@@ -195,7 +195,8 @@ def test_prefill_schedule_ties_and_fewer_visible_than_k():
 
 
 def test_prefill_schedule_all_equal_scores():
-    """Zero keys: 20,000 tied candidates per query exceed the sort buffer (radix-select path)."""
+    """Zero keys: 20,000 tied candidates per query, more than the 8192-key tie list holds, so
+    every query is finished by the re-scan (radix select on the index bits alone)."""
     rng = np.random.default_rng(32)
     B, Q, N, m, k = 1, 16, 20000, 4, 1000
     kc = np.zeros((B, N, 64), np.uint8)
@@ -205,6 +206,49 @@ def test_prefill_schedule_all_equal_scores():
     _compare("prefill all-equal", kc, ks, qc, qs, pos, m, k)
     gi, _ = _run(kc, ks, qc, qs, pos, m, k)
     assert (gi[0, :, :] == np.arange(k)).all()
+
+
+def _one_bin_inputs(rng, B, Q, N, HI):
+    """Scores that differ but share one 11-bit histogram bin: key block 0 is all 4.0 and query
+    block 0 all 1.0, 128 per head, so each score starts at 128 HI (a power of two for HI = 4, 8);
+    the other blocks add a non-negative term below 36 * 96 * HI / 256, under a quarter of that
+    (positive codes, keys scaled by 2^-8), so every score lies in the first quarter of its
+    binade: one bin."""
+    kc = np.zeros((B, N, 64), np.uint8)
+    kc[:, :, :16] = 0x66
+    kc[:, :, 16:] = rng.integers(0, 8, size=(B, N, 48)) | (rng.integers(0, 8, size=(B, N, 48)) << 4)
+    ks = np.full((B, N, 4), 119, np.uint8)
+    ks[:, :, 0] = 127
+    qc = np.zeros((B, Q, HI, 64), np.uint8)
+    qc[..., :16] = 0x22
+    qc[..., 16:] = rng.integers(0, 8, size=(B, Q, HI, 48)) | (rng.integers(0, 8, size=(B, Q, HI, 48)) << 4)
+    qs = np.full((B, Q, HI, 4), 127, np.uint8)
+    return kc, ks, qc, qs
+
+
+@pytest.mark.parametrize("HI", [4, 8])
+def test_prefill_tie_list_overflow_distinct_scores_in_one_bin(HI):
+    """30,000 keys whose scores all fall in the threshold bin, mostly distinct (with some ties):
+    the bin overflows the 8192-key tie list of every query, and the re-scan's radix select has to
+    split the bin on score bits, then on index bits. 20 queries (a partial second block) with
+    causal visibility changing inside the blocks."""
+    rng = np.random.default_rng(40 + HI)
+    B, Q, N, m, k = 1, 20, 30000, 4, 1024
+    kc, ks, qc, qs = _one_bin_inputs(rng, B, Q, N, HI)
+    pos = np.array([N * m - Q - 37], np.int64)
+    _compare(f"prefill one-bin HI={HI}", kc, ks, qc, qs, pos, m, k)
+
+
+def test_prefill_tie_list_overflow_mixed_with_normal_queries():
+    """Two sequences x 32 queries over 20,000 normal keys; in each sequence queries 16..31 have
+    zero codes (every score 0: the whole visible range ties and overflows the tie list) while
+    queries 0..15 take the ordinary path, so both finishers run in one call."""
+    rng = np.random.default_rng(43)
+    B, Q, N, m, k = 2, 32, 20000, 4, 777
+    kc, ks, qc, qs = _fp4_inputs(rng, B, Q, N, 4)
+    qc[:, 16:] = 0
+    pos = np.array([N * m - Q, 4 * 15000 - 1], np.int64)
+    _compare("prefill overflow mixed", kc, ks, qc, qs, pos, m, k)
 
 
 def test_prefill_chunk_full_size_sampled_queries():

@@ -85,6 +85,18 @@ def test_index_prefill_schedule_page_sizes(P):
     _check_index("prefill", kc, ks, qc, qs, pos, m, k, P, seed=P)
 
 
+def test_index_prefill_tie_list_overflow_paged():
+    """Prefill queries whose threshold bin overflows the tie list (zero query codes: every score
+    ties), finished by the re-scan through the block table, next to ordinary queries."""
+    rng = np.random.default_rng(97)
+    B, Q, N, m, k = 2, 32, 20000, 4, 500
+    kc, ks = O.encode_rows(rng.normal(size=(B, N, 128)), O.FMT_FP4_E8M0)
+    qc, qs = O.encode_rows(rng.normal(size=(B, Q, 4, 128)), O.FMT_FP4_E8M0)
+    qc[:, 20:] = 0
+    pos = np.array([N * m - Q, 4 * 12000 - 1], np.int64)
+    _check_index("prefill overflow", kc, ks, qc, qs, pos, m, k, 16, seed=97)
+
+
 # ---- attention -----------------------------------------------------------------------------
 def _pages(c, P, seed):
     pool, table = paginate(c.cache, P, np.random.default_rng(seed))
