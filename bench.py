@@ -279,10 +279,10 @@ class StepGraphs:
         torch.cuda.synchronize()
 
     def replay(self):
-        # The CSA graph (the longer chain: compress, scan, top-k, attention) is launched first:
-        # a graph launch costs the host tens of microseconds, and the chain launched second
-        # reaches the GPU that much later. The side stream forks from the point before it, so
-        # the HCA graph does not wait for the CSA graph.
+        # The CSA graph (the longer chain: compress, scan, top-k, attention) is launched first,
+        # since a graph launch costs the host tens of microseconds (with the current kernels the
+        # other order measures the same). The side stream forks from the point before it, so the
+        # HCA graph does not wait for the CSA graph.
         main, side = torch.cuda.current_stream(), self.ws.side
         side.wait_stream(main)
         self.g_csa.replay()
