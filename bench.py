@@ -504,6 +504,76 @@ def csa128k_replicas(ws: "DecodeStep", count: int = 8):
     return Replicas(ws, make, count)
 
 
+HCA_BYTES = KERNELS["hca_attend"]["bytes"]
+
+
+class HcaReplicas:
+    """The 1M HCA decode configuration (16 sequences x 8,192 entries + window + sink) as one HIP
+    graph per replica: replica 0 is the decode step's own HCA cache, the others are disjoint
+    8,192-entry slices of the CSA cache (rows of the same format and distribution), so that the
+    rotation reads 15 x 75.5 MB = 1.13 GB of rows and the last-level cache holds none of them.
+    Replays are serialized on one stream, so the replicas share the workspace and outputs."""
+
+    def __init__(self, ws: "DecodeStep", count: int = 15):
+        h, c = ws.hca, ws.csa
+        self.out = torch.empty((B_STEP, 1, H, D), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((B_STEP, 1, H), dtype=torch.float32, device="cuda")
+        self.ws_att = torch.empty(max(256, L.attend_workspace(B_STEP, 1, H, D, N_HCA + W)),
+                                  dtype=torch.uint8, device="cuda")
+        self.graphs = []
+        for r in range(count):
+            cache = h["cache"] if r == 0 else c["cache"][:, N_HCA * (r - 1):N_HCA * r]
+
+            def fn(cache=cache):
+                L.hca_attend(h["q"], cache, 128, h["win"], W, ws.pos, ws.sink, ws.scale,
+                             N=N_HCA, ws=self.ws_att, out=self.out, lse=self.lse)
+            self.graphs.append(capture(fn))
+
+    def stats(self, n: int, rotate: bool):
+        return replay_stats(lambda i: self.graphs[i % len(self.graphs) if rotate else 0].replay(),
+                            n)
+
+
+def tiny_measure(steps: int):
+    """The tiny configuration (1 sequence, 4,096 tokens, 8 heads x 128, fp32 rows and queries,
+    indexer 4 x 64, top-64, window 128): its caches compressed from raw tokens by the library
+    (m = 4 rows and FP4 indexer keys, m = 128 rows), then one decode step (index_topk,
+    csa_attend, hca_attend) as a HIP graph. The whole working set is a few MB and stays in L2,
+    so this line measures launch and latency, not bandwidth."""
+    wl = synth.WORKLOADS["tiny"]
+    dev = torch.device("cuda")
+    raw = synth.raw_tokens(wl, wl.L, dev)
+    v = synth.decode_inputs(wl, dev)
+    rows4, _ = L.kv_compress(raw["x"], 4, raw["w_csa"], raw["b_csa"], L.FMT_ROW_F32)
+    rows128, _ = L.kv_compress(raw["x"], 128, raw["w_hca"], raw["b_hca"], L.FMT_ROW_F32)
+    kc, ks = L.kv_compress(raw["xi"], 4, raw["w_idx"], raw["b_idx"], L.FMT_FP4_E8M0)
+    iqc, iqs = encode(v["iq"].view(1, wl.HI, wl.dI), 1, L.FMT_FP4_E8M0)
+    iqc, iqs = iqc.view(1, 1, wl.HI, wl.dI // 2), iqs.view(1, 1, wl.HI, wl.dI // 32)
+    win, _ = encode(v["window"], 1, L.FMT_ROW_F32)
+    q, sink = v["q"], v["sink"]
+    pos = torch.full((1,), wl.L - 1, dtype=torch.int64, device=dev)
+    idx = torch.empty((1, 1, wl.k), dtype=torch.int32, device=dev)
+    o1, l1 = torch.empty((1, 1, wl.H, wl.D), device=dev), torch.empty((1, 1, wl.H), device=dev)
+    o2, l2 = torch.empty_like(o1), torch.empty_like(l1)
+    wsi = torch.empty(L.index_topk_workspace(1, 1, kc.shape[1], wl.k, wl.HI, wl.dI),
+                      dtype=torch.uint8, device=dev)
+    wsa = torch.empty(max(256, L.attend_workspace(1, 1, wl.H, wl.D, wl.k + wl.w)),
+                      dtype=torch.uint8, device=dev)
+    wsh = torch.empty(max(256, L.attend_workspace(1, 1, wl.H, wl.D, rows128.shape[1] + wl.w)),
+                      dtype=torch.uint8, device=dev)
+
+    def step():
+        L.index_topk(iqc, iqs, kc, ks, pos, 4, wl.k, want_scores=False, ws=wsi, idx_out=idx)
+        L.csa_attend(q, rows4, idx, win, wl.w, pos, sink, wl.scale, ws=wsa, out=o1, lse=l1)
+        L.hca_attend(q, rows128, 128, win, wl.w, pos, sink, wl.scale, ws=wsh, out=o2, lse=l2)
+    g = capture(step)
+    st = replay_stats(lambda i: g.replay(), max(200, steps))
+    return {"what": "tiny configuration: 1 sequence at 4,096 tokens, 8 heads x 128 (fp32), "
+                    "index_topk over 1,024 FP4 keys (4 x 64) -> top-64, csa_attend, hca_attend "
+                    "over 32 entries, window 128, sink; one graph per step",
+            "replays": st, "queries_per_s": 1e6 / st["median_us"]}
+
+
 def source_hash(path: str) -> str:
     """First 16 hex digits of the sha256 of a source file's code: comments and whitespace are
     dropped first, so that documentation edits do not invalidate counters taken from the code."""
@@ -863,7 +933,7 @@ def main():
     step_stats = replay_stats(lambda i: graph.replay() if graph else ws.step(), n_stats)
     log(f"  {ms * 1e3:.1f} us per step (median {step_stats['median_us']:.1f}, p10 "
         f"{step_stats['p10_us']:.1f}, p90 {step_stats['p90_us']:.1f})")
-    g4, ms4, rot4, rot128 = None, None, None, None
+    g4, ms4, rot4, rot128, roth = None, None, None, None, None
     if not args.no_csa4:
         g4 = None if args.no_graph else capture(ws.csa4_step)
         ms4 = time_replays(g4, ws.csa4_step, args.steps)
@@ -877,9 +947,14 @@ def main():
             rot128 = {"one_replica": r128.stats(n_stats, False),
                       "rotated_8": r128.stats(n_stats, True)}
             del r128
+            rh = HcaReplicas(ws)
+            roth = {"one_replica": rh.stats(n_stats, False), "rotated_15": rh.stats(n_stats, True)}
+            del rh
             log(f"  4 x 1M: median {rot4['one_replica']['median_us']:.1f} us on one replica, "
                 f"{rot4['rotated_16']['median_us']:.1f} us rotated; 16 x 128K: "
-                f"{rot128['one_replica']['median_us']:.1f} / {rot128['rotated_8']['median_us']:.1f} us")
+                f"{rot128['one_replica']['median_us']:.1f} / {rot128['rotated_8']['median_us']:.1f} us; "
+                f"HCA 16 x 1M: {roth['one_replica']['median_us']:.1f} / "
+                f"{roth['rotated_15']['median_us']:.1f} us")
     kt = kernel_times(ws, args.kernel_reps)
     log("  dominant kernels (us): " + ", ".join(f"{k} {v * 1e3:.2f}" for k, v in kt.items()))
     # the roofline object reports the kernel that moves most of the step's algorithmic HBM bytes
@@ -994,8 +1069,29 @@ def main():
             "queries_per_s": B_STEP / (med * 1e-6),
             "rotation": "8 disjoint 32,768-entry slices of the 1M caches (285 MB of keys)",
         }
+    if roth is not None:
+        med = roth["rotated_15"]["median_us"]
+        line["hca_decode_1m_b16"] = {
+            "what": "hca_attend for 16 sequences at 1,048,576 tokens (8,192 entries each, window "
+                    "128, sink)",
+            "replays": roth, "rotated_median_us": med, "algorithmic_bytes": HCA_BYTES,
+            "achieved_GBps": HCA_BYTES / (med * 1e-6) / 1e9,
+            "frac_of_hbm_peak": HCA_BYTES / (med * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "queries_per_s": B_STEP / (med * 1e-6),
+            "rotation": "15 replicas: the HCA cache and 14 disjoint 8,192-entry slices of the CSA "
+                        "cache (1.13 GB of rows)",
+        }
+        if rot4 is not None:
+            t4, t3 = rot4["rotated_16"]["median_us"], med
+            line["one_csa_plus_one_hca_layer_1m"] = {
+                "what": "queries/s through one CSA and one HCA layer at 1M context from the two "
+                        "rotated configurations timed apart: 1 / (t_csa_4seq / 4 + t_hca_16seq / 16)",
+                "t_csa_decode_1m_b4_us": t4, "t_hca_decode_1m_b16_us": t3,
+                "queries_per_s": 1e6 / (t4 / B_CSA4 + t3 / B_STEP),
+            }
     if not args.no_csa4:
         line["csa_decode_1m_b4_paged"] = paged_measure(ws, args, ms4)
+        line["tiny_decode"] = tiny_measure(args.steps)
     line["rope_decode"] = rope_decode_measure(ws, args.kernel_reps)
     if not args.no_prefill:
         log("prefill chunk (4096 tokens on a 1M cache)...")
