@@ -57,11 +57,19 @@ size_t index_cand_slot_bytes() { return cand_al256((size_t)(kUMax + kCandMaxRang
 
 bool index_cand_plan(int slots, int64_t N, int k, int page_shift, CandPlan* p) {
   const int64_t n = N > 0 ? N : 1;
-  // about 512 scan workgroups, ranges of 256..4096 keys
+  // about 512 scan workgroups, ranges of 256..4096 keys. Where that would need longer ranges
+  // (many keys in all) the ranges shrink towards 2048 keys instead: 16 x 262,144 keys then run as
+  // 2048 workgroups, two rounds per CU, so one round's publication overlaps the other's loads
+  // (measured 45.8 against 47.6 us; the 4-sequence launch, 512 ranges of 2048, is unchanged)
   int64_t chunk = ((int64_t)slots * n + 511) / 512;
   chunk = (chunk + 255) / 256 * 256;
   if (chunk < 256) chunk = 256;
-  if (chunk > kCandRange) chunk = kCandRange;
+  if (chunk > kCandRange) {
+    chunk = ((int64_t)slots * n + 2047) / 2048;
+    chunk = (chunk + 255) / 256 * 256;
+    if (chunk < kCandRange / 2) chunk = kCandRange / 2;
+    if (chunk > kCandRange) chunk = kCandRange;
+  }
   // paged keys: a range spans at most 1024 pages (+1 partial one), which fits the page list
   if (page_shift >= 0 && chunk > ((int64_t)1024 << page_shift)) chunk = (int64_t)1024 << page_shift;
   const int64_t R = (n + chunk - 1) / chunk;
