@@ -575,15 +575,34 @@ def tiny_measure(steps: int):
 
 
 def source_hash(path: str) -> str:
-    """First 16 hex digits of the sha256 of a source file's code: comments and whitespace are
-    dropped first, so that documentation edits do not invalidate counters taken from the code."""
+    """First 16 hex digits of the sha256 of a kernel source's code together with the local headers
+    it includes (recursively, looked up beside it and in include/): comments and whitespace are
+    dropped first, so that documentation edits do not invalidate counters taken from the code,
+    while a change in any header the kernels are built from does."""
     import hashlib
     import re
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    text = " ".join(text.split())
-    return hashlib.sha256(text.encode()).hexdigest()[:16]
+    dirs = [os.path.dirname(os.path.abspath(path)), os.path.join(ROOT, "include")]
+    order = []
+
+    def visit(p):
+        if p in order:
+            return
+        order.append(p)
+        for inc in re.findall(r'#include\s+"([^"]+)"', open(p).read()):
+            for d in dirs:
+                q = os.path.join(d, inc)
+                if os.path.exists(q):
+                    visit(q)
+                    break
+
+    visit(os.path.abspath(path))
+    h = hashlib.sha256()
+    for p in order:
+        text = open(p).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(kernel: str):

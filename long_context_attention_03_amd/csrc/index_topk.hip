@@ -42,6 +42,7 @@
 #include "csah_internal.h"
 #include "device_common.h"
 #include "index_common.h"
+#include "index_rank.h"
 
 namespace csah {
 
@@ -481,10 +482,14 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelPerThread = 8;
 constexpr int kSelChunk = kSelThreads * kSelPerThread;
 
-// bin_bits: width of the histogram bin (top bits of the order key) shared by every tie candidate
+// bin_bits: width of the histogram bin (top bits of the order key) shared by every tie candidate.
+// The candidates (at most kSortCap) are ordered by a bucket ranking in LDS when cnt and cur
+// (kBins-entry LDS arrays) are given, else by a bitonic sort.
+template <int NT>
 __device__ void finalize_slot(int slot, int64_t N, int k, int kk, int32_t* __restrict__ idx_out,
                               float* __restrict__ score_out, IdxWs ws, uint64_t* keys,
-                              uint32_t* dh, int bin_bits) {
+                              uint32_t* dh, int bin_bits, uint32_t* cnt = nullptr,
+                              uint32_t* cur = nullptr) {
   __shared__ uint64_t s_prefix, s_pmask;
   __shared__ uint32_t s_r, s_cnt;
   const int t = threadIdx.x;
@@ -557,6 +562,22 @@ __device__ void finalize_slot(int slot, int64_t N, int k, int kk, int32_t* __res
     }
     __syncthreads();
     n = (int)(ns + (s_cnt < (uint32_t)kSortCap - ns ? s_cnt : (uint32_t)kSortCap - ns));
+  }
+  if (cnt) {
+    // keys are unique: rank them from the top through buckets fitted to their range (a key's
+    // position is its bucket's start plus the larger keys in its bucket) and write the first kk
+    constexpr int KPT = kSortCap / NT;
+    __syncthreads();
+    uint64_t x[KPT];
+    load_regs<NT, KPT>(keys, n, x);
+    __syncthreads();  // keys now serves as the ranked array
+    const int kw = n < kk ? n : kk;
+    for (int j = kw + t; j < k; j += NT) {
+      io[j] = -1;
+      if (so) so[j] = -INFINITY;
+    }
+    top_sorted<NT, KPT>(x, (uint32_t)kw, cnt, cur, keys, io, so);
+    return;
   }
   int p2 = 2;
   while (p2 < n) p2 <<= 1;
@@ -685,7 +706,7 @@ __global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
   const uint32_t n = ns + nt;
   if (kk == 0 || n > (uint32_t)kSortCap) {
     if (blockIdx.x == 0)
-      finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh, bin_bits);
+      finalize_slot<kRankThreads>(slot, N, k, kk, idx_out, score_out, ws, keys, dh, bin_bits);
     return;
   }
   int32_t* io = idx_out + (int64_t)slot * k;
@@ -1106,7 +1127,8 @@ __global__ __launch_bounds__(1024) void index_sort_kernel(const int64_t* __restr
   if (kk > 0 && ws.ctr(slot)[1] > ws.tie_cap) return;  // overflowed: index_rescan_kernel
   __shared__ uint64_t keys[kSortCap];
   __shared__ uint32_t dh[256];
-  finalize_slot(slot, N, k, kk, idx_out, score_out, ws, keys, dh, bin_bits);
+  __shared__ uint32_t cnt[kBins], cur[kBins];
+  finalize_slot<1024>(slot, N, k, kk, idx_out, score_out, ws, keys, dh, bin_bits, cnt, cur);
 }
 
 // ---- prefill: a query whose threshold bin overflowed its tie list ------------------------------
