@@ -43,8 +43,8 @@ def test_csa1m_full_size():
 
 def test_decode_step_launch_shape_16_sequences():
     """The index call as the decode step runs it: 16 sequences x 262,144 entries, top-1024 (the
-    MFMA scan with 8192-key ranges over 512 workgroups, 32 select workgroups per sequence). Codes
-    are random bytes and scales a narrow band, which keeps every score exact."""
+    candidate-list scan with 2048-key ranges over 2048 workgroups, then one top-k workgroup per
+    sequence). Codes are random bytes and scales a narrow band, which keeps every score exact."""
     rng = np.random.default_rng(22)
     B, N, HI, dI, m, k = 16, 262144, 4, 128, 4, 1024
     kc = rng.integers(0, 256, size=(B, N, dI // 2), dtype=np.uint8)
@@ -94,8 +94,8 @@ def test_clustered_top_entries_are_scored_again(HI):
 @pytest.mark.parametrize("Q,coarse", [(1, False), (1, True), (5, False), (16, False), (16, True)])
 def test_largest_k(Q, coarse):
     """k = 4096, the largest supported: all three schedules (one query, the multi-query scan, the
-    prefill schedule), and coarse keys whose tie list pushes the candidates past the 4096-key
-    sort capacity onto the radix-select path."""
+    prefill schedule), and coarse keys whose tie list pushes the candidates of the last two past
+    the 4096-key sort capacity onto the radix-select path."""
     rng = np.random.default_rng(40 + Q)
     B, N, HI, dI, m, k = 2, 70001, 4, 128, 4, 4096
     kv = rng.normal(size=(B, N, dI))
@@ -118,7 +118,8 @@ def test_ties_multi_query_causal_and_ragged():
 
 
 def test_all_equal_scores_take_lowest_indices():
-    """Zero keys: every score ties, so the top-k is the k lowest indices (radix-select path)."""
+    """Zero keys: every score ties, so the top-k is the k lowest indices. No range can publish
+    its one full bin, so every range's bound reaches the threshold and is scored again."""
     B, N, dI = 1, 50000, 64
     kc = np.zeros((B, N, dI // 2), np.uint8)
     ks = np.full((B, N, dI // 32), 127, np.uint8)
@@ -321,11 +322,11 @@ def _sure_count(scores: np.ndarray, k: int, bin_shift: int = 20) -> tuple[int, i
 
 
 def test_rank_sure_tie_boundaries():
-    """The ranking counts entries above the threshold bin ("sure") and in it ("tie") separately
-    and holds four candidates per lane group, 64 per workgroup. Cases put the sure/tie boundary
-    at every offset within a group of four, at 63, 0 and 1 past a multiple of 64, at 0 and 1, and
-    cut the tie bin at various points. The boundary is moved by raising the block scales of a few
-    low-ranked keys by 2^10, which lifts them above every threshold."""
+    """One query per sequence (the candidate-list schedule) around the sure/tie boundaries of the
+    stored-score ranking: cases put the boundary at every offset within a group of four, at 63, 0
+    and 1 past a multiple of 64, at 0 and 1, and cut the tie bin at various points. The boundary
+    is moved by raising the block scales of a few low-ranked keys by 2^10, which lifts them above
+    every threshold. The multi-query test below reaches the ranking kernel itself."""
     rng = np.random.default_rng(21)
     B, N, HI, dI, m = 1, 24000, 4, 128, 4
     kc0, ks0 = O.encode_rows(rng.normal(size=(B, N, dI)), O.FMT_FP4_E8M0)
@@ -343,6 +344,56 @@ def test_rank_sure_tie_boundaries():
         assert ns + nt <= 4096, "the counting path, not the radix-select fallback"
         seen.append(ns)
         _compare(f"boundary ns={ns} nt={nt} k={k}", kc0, ks, qc, qs, pos, m, k)
+    assert {s % 4 for s in seen} == {0, 1, 2, 3}
+    assert {s % 64 for s in seen if s >= 64} >= {63, 0, 1}
+    assert 0 in seen and 1 in seen
+
+
+def test_multi_query_rank_sure_tie_boundaries():
+    """The ranking kernel of the 3-15-query schedule counts entries above the threshold bin
+    ("sure") and in it ("tie") separately and holds four candidates per lane group, 64 per
+    workgroup. Three copies of one query (the last sees all 24,000 entries); cases are chosen from
+    the oracle's own ranking so that the sure count lands on every offset within a group of four,
+    on 63, 0 and 1 past a multiple of 64, and on 0 and 1 (2048-bin histogram: 11-bit bins). Lifting
+    L low-ranked keys by 2^10 puts them above every threshold, so with k the sure count is L plus
+    the original sure count at k - L."""
+    rng = np.random.default_rng(23)
+    B, Q, N, HI, dI, m = 1, 3, 24000, 4, 128, 4
+    kc0, ks0 = O.encode_rows(rng.normal(size=(B, N, dI)), O.FMT_FP4_E8M0)
+    q1c, q1s = O.encode_rows(rng.normal(size=(B, 1, HI, dI)), O.FMT_FP4_E8M0)
+    qc, qs = np.repeat(q1c, Q, axis=1), np.repeat(q1s, Q, axis=1)
+    pos = np.array([N * m - Q], np.int64)  # query 2 sees every entry, queries 0 and 1 one fewer
+    last = np.array([N * m - 1], np.int64)
+    order, rs0, _ = O.index_topk(q1c, q1s, kc0, ks0, last, m, 4096)
+    u = rs0[0, 0].astype(np.float32).view(np.uint32)
+    bins = (np.where(u & 0x80000000, ~u, u | 0x80000000).astype(np.uint32) >> 21).astype(np.int64)
+    sure = np.array([int((bins > bins[j]).sum()) for j in range(4096)])  # sure count at k = j + 1
+    ties = np.array([int((bins == bins[j]).sum()) for j in range(4096)])
+    want = {("mod4", r) for r in range(4)} | {("mod64", r) for r in (63, 0, 1)} | {("abs", 0), ("abs", 1)}
+    cases = {}
+    for k in range(1, 3000):
+        for L in range(0, 64):
+            j = k - L - 1
+            if j < 0 or L + sure[j] + ties[j] > 4000:
+                continue
+            ns = L + int(sure[j])
+            for tag in (("mod4", ns % 4), ("abs", ns)) + ((("mod64", ns % 64),) if ns >= 64 else ()):
+                if tag in want and tag not in cases:
+                    cases[tag] = (L, k)
+        if len(cases) == len(want):
+            break
+    assert len(cases) == len(want), sorted(want - set(cases))
+    # and wide tie bins cut at various points
+    wide = [(0, k) for k in (500, 1024, 2000, 3500) if sure[k - 1] + ties[k - 1] <= 4000]
+    seen = []
+    for L, k in sorted(set(cases.values()) | set(wide)):
+        ks = ks0.copy()
+        ks[0, order[0, 0, 3000:3000 + L]] += 10  # positive scores, ranked far below k
+        _, rs, ex = O.index_topk(q1c, q1s, kc0, ks, last, m, k)
+        assert ex.all()
+        ns, nt = _sure_count(rs[0, 0], k, bin_shift=21) if k < 4096 else (None, None)
+        seen.append(ns)
+        _compare(f"multi-query boundary L={L} k={k} ns={ns} nt={nt}", kc0, ks, qc, qs, pos, m, k)
     assert {s % 4 for s in seen} == {0, 1, 2, 3}
     assert {s % 64 for s in seen if s >= 64} >= {63, 0, 1}
     assert 0 in seen and 1 in seen
