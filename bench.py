@@ -829,12 +829,12 @@ def prefill_measure(steps: int, warmup: int):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
-    ev = {"index_hist": [], "csa_attend": [], "hca_attend": []}
+    ev = {"index_select": [], "csa_attend": [], "hca_attend": []}
     for _ in range(max(1, steps // 2)):
         ps.compress()
         e = event_pair()
         ps.index(e)
-        ev["index_hist"].append(e)
+        ev["index_select"].append(e)
         e = event_pair()
         ps.csa(e)
         ev["csa_attend"].append(e)
@@ -847,7 +847,7 @@ def prefill_measure(steps: int, warmup: int):
     # QK + PV flops of the attention over each query's rows (1152 CSA, 8192 + (i+1)//128 + 128 HCA)
     n_vis = sum(min(PF_N_CSA, (PF_POS0 + i + 1) // 4) for i in range(PF_Q))
     hca_rows = sum(min(PF_N_HCA, (PF_POS0 + i + 1) // 128) + W for i in range(PF_Q))
-    ops = {"index_hist": (2.0 * 512 * n_vis, PF_PEAK_FP4, "fp4"),
+    ops = {"index_select": (2.0 * 512 * n_vis, PF_PEAK_FP4, "fp4"),
            "csa_attend": (4.0 * H * D * PF_Q * (K + W), PF_PEAK_BF16, "bf16"),
            "hca_attend": (4.0 * H * D * hca_rows, PF_PEAK_BF16, "bf16")}
     # overlapping entries (8 tokens each at stride 4) for the chunk: the 4 tokens before it are

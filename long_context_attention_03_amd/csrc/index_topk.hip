@@ -16,10 +16,10 @@
 // fewer than 24 bits of the finest granularity each fp32 operation is exact: the result is the
 // exact score in any order, and the selection below is bit-exact.
 //
-// Schedules. Decode calls (one or two queries per sequence) over at most 2^20 entries per
+// Schedules. Decode calls (one or two queries per sequence) over at most 2^22 entries per
 // sequence take the candidate-list scan and top-k of index_cand.hip. A prefill chunk (16 or more
-// queries of one sequence, 128-dim keys) takes the MFMA histogram / select / sort passes at the
-// end of this file, 3 to 15 queries take the multi-query MFMA scan, and everything else takes the
+// queries of one sequence, 128-dim keys) takes the sampled-threshold MFMA passes at the end of
+// this file, 3 to 15 queries take the multi-query MFMA scan, and everything else takes the
 // pipeline below, per (sequence, query) "slot", four kernels. Kernel boundaries carry the
 // cross-workgroup dependencies: measured on MI355X, a dependent kernel costs about 1.7 us inside
 // a graph, an in-kernel ticket-ordered hand-off about 1.3 us with one workgroup per phase and far
@@ -71,11 +71,10 @@ struct IdxWs {
 
 static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Tie list of a prefill query (the MFMA path): its threshold bin holds about N/60 keys or fewer
-// when the scores spread like a sum of many products (the bin is a quarter of a binade at about
-// 2.7 standard deviations out for k = 1024 of 263,168), so N/32 keys, and at least twice the
-// LDS sort's capacity, take it; a query whose bin holds more is finished by index_rescan_kernel.
-// That keeps a 4096-query chunk's workspace at a few hundred MB instead of N keys per query.
+// Candidate list of a prefill query (the MFMA path): the keys at or above its sampled threshold
+// estimate, a few kk (see index_sample_thresh_kernel); N/32 keys and at least twice the LDS
+// ranking's capacity hold them, and a query with more is finished by index_rescan_kernel. That
+// keeps a 4096-query chunk's workspace at a few hundred MB instead of N keys per query.
 static uint32_t prefill_tie_cap(int64_t N) {
   int64_t c = (N + 31) / 32;
   if (c < 2 * kSortCap) c = 2 * kSortCap;
@@ -99,7 +98,7 @@ static IdxWs make_ws(void* base, int64_t N, int k, bool with_scores) {
 }
 
 // Queries of one sequence share its keys; from 16 of them on (one MFMA tile) with 128-dim keys and
-// at most 16 indexer heads the scores come from the scaled FP4 MFMA (see index_mfma_hist_kernel).
+// at most 16 indexer heads the scores come from the scaled FP4 MFMA (see index_mfma_select_kernel).
 static bool use_mfma_path(int Q, int HI, int dI) { return dI == 128 && Q >= 16 && HI <= 16; }
 // From 3 to 15 queries per sequence the scores come from the same MFMA tiles in one pass over the
 // keys and are stored, then selected and ranked as in the one-query scan (with 2, scanning the
@@ -548,7 +547,7 @@ __device__ void finalize_slot(int slot, int64_t N, int k, int kk, int32_t* __res
       hi = shift;
     }
     // bits above kLowBits are the (shared) bin: compare the low bits only
-    const uint64_t low = ((uint64_t)1 << kLowBits) - 1;
+    const uint64_t low = kLowBits >= 64 ? ~(uint64_t)0 : ((uint64_t)1 << kLowBits) - 1;
     const uint64_t thr = s_prefix;
     if (t == 0) s_cnt = 0;
     __syncthreads();
@@ -792,17 +791,15 @@ __global__ __launch_bounds__(kRankThreads) void index_rank_kernel(
 // one instruction per head into the same accumulator leaves score(key 4*(l/16)+i, query l%16) in
 // register i of lane l. Every product is exact, so under the same precondition as the scan (the
 // absolute sum spans fewer than 24 bits of the finest granularity) the scores are the exact ones in
-// any accumulation order, and the two passes below recompute bit-identical values.
-//   clear    zero the per-query histograms and counters
-//   hist     scores -> per-query histogram of the top 11 bits of the order key (16-bit LDS counters
-//            for the workgroup's 16 queries x 16,384 keys, flushed with global atomics)
-//   thresh   per query: the bin holding its kk-th largest score and the count above it
-//   select   scores again -> keys above the bin ("sure") and in it ("tie") appended to the query's
-//            lists, as index_select_kernel does from stored scores
-//   sort     per query: bitonic sort of the candidates in LDS (after a radix select when the tie
-//            list is longer than kSortCap), then the ordered top-k
-//   rescan   per query whose threshold bin held more keys than its tie list (capped at N/32, at
-//            least 8192): an exact radix select over fresh passes across its keys, then the sort
+// any accumulation order, and every pass below computes bit-identical values.
+//   clear    zero the per-query counters
+//   sample   score kSampleSegs segments of kSampleSeg keys spread over each query block's keys
+//   thresh   per query: an exact order statistic of its sampled scores as the threshold estimate
+//   select   the one full pass: keys at or above the estimate appended to the query's list
+//   sort     per query: the list ranked in LDS (after a radix select when it exceeds kSortCap),
+//            then the ordered top-k
+//   rescan   per query whose list holds fewer than kk keys or more than its capacity: an exact
+//            radix select over fresh passes across its keys, then the ranking
 constexpr int kPBins = 2048, kPBinShift = 21;
 constexpr int kPKeys = 16384;                // keys per workgroup: a 16-bit counter cannot overflow
 constexpr uint32_t kNoThreshold = 0xFFFFFFFFu;
@@ -867,15 +864,16 @@ __device__ __forceinline__ void mfma_unit(const MfmaSplit& sp, int& b, int& qb, 
 
 // Paged keys: `pages` (LDS, kPageList entries) receives the range's block-table entries; the
 // walk's early return is uniform over the workgroup, so the barrier after filling it is safe.
+// The keys [g0, gend) of sequence b (cut at the block's visible keys) against query block qb.
 template <int HP, bool PAGED, typename F>
-__device__ __forceinline__ void mfma_walk(const uint8_t* __restrict__ q_codes,
-                                          const uint8_t* __restrict__ q_scales, int HI,
-                                          const uint8_t* __restrict__ k_codes,
-                                          const uint8_t* __restrict__ k_scales,
-                                          const EntryMap& kmap, int64_t N,
-                                          const int64_t* __restrict__ pos, int m, int Q,
-                                          const MfmaSplit& sp, int b, int qb, int kr,
-                                          int32_t* pages, F visit) {
+__device__ __forceinline__ void mfma_walk_keys(const uint8_t* __restrict__ q_codes,
+                                               const uint8_t* __restrict__ q_scales, int HI,
+                                               const uint8_t* __restrict__ k_codes,
+                                               const uint8_t* __restrict__ k_scales,
+                                               const EntryMap& kmap, int64_t N,
+                                               const int64_t* __restrict__ pos, int m, int Q,
+                                               int b, int qb, int64_t g0, int64_t gend,
+                                               int32_t* pages, F visit) {
   constexpr int U = 4;
   const int q0 = qb * 16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, blk = lane >> 4;
@@ -884,8 +882,7 @@ __device__ __forceinline__ void mfma_walk(const uint8_t* __restrict__ q_codes,
   const int64_t nv = qv ? visible_entries(pos, b, qi, m, N) : 0;
   // visibility is nondecreasing in the query index: the block's last query sees the most
   const int64_t nvmax = visible_entries(pos, b, (q0 + 15 < Q ? q0 + 15 : Q - 1), m, N);
-  const int64_t g0 = (int64_t)kr * sp.keys_per_range;
-  const int64_t g1 = g0 + sp.keys_per_range < nvmax ? g0 + sp.keys_per_range : nvmax;
+  const int64_t g1 = gend < nvmax ? gend : nvmax;
   if (g0 >= g1) return;
   if constexpr (PAGED) {
     load_page_list(kmap, b, g0, g1, pages, threadIdx.x, 256);
@@ -941,88 +938,158 @@ __device__ __forceinline__ void mfma_walk(const uint8_t* __restrict__ q_codes,
   }
 }
 
+// Key range kr of the split.
+template <int HP, bool PAGED, typename F>
+__device__ __forceinline__ void mfma_walk(const uint8_t* __restrict__ q_codes,
+                                          const uint8_t* __restrict__ q_scales, int HI,
+                                          const uint8_t* __restrict__ k_codes,
+                                          const uint8_t* __restrict__ k_scales,
+                                          const EntryMap& kmap, int64_t N,
+                                          const int64_t* __restrict__ pos, int m, int Q,
+                                          const MfmaSplit& sp, int b, int qb, int kr,
+                                          int32_t* pages, F visit) {
+  const int64_t g0 = (int64_t)kr * sp.keys_per_range;
+  mfma_walk_keys<HP, PAGED>(q_codes, q_scales, HI, k_codes, k_scales, kmap, N, pos, m, Q, b, qb,
+                            g0, g0 + sp.keys_per_range, pages, visit);
+}
+
 __global__ __launch_bounds__(256) void index_clear_kernel(IdxWs ws) {
-  uint32_t* h = ws.hist(blockIdx.x);
-  for (int j = threadIdx.x; j < kPBins; j += 256) h[j] = 0u;
   if (threadIdx.x < 64) ws.ctr(blockIdx.x)[threadIdx.x] = 0u;
 }
 
+// ---- prefill: a sampled threshold, one pass, an exact finish ---------------------------------
+// kSampleSegs segments of kSampleSeg keys spread evenly over the keys every query of a block sees
+// (all of them, contiguous, when those are at most kSampleSegs * kSampleSeg): their scores give
+// each query an estimate of its top-k threshold.
+constexpr int kSampleSegs = 64, kSampleSeg = 128, kSampleMax = kSampleSegs * kSampleSeg;
+
+__device__ __forceinline__ int64_t sample_seg_start(int64_t nvmin, int s) {
+  return nvmin <= kSampleMax ? (int64_t)s * kSampleSeg : (int64_t)s * (nvmin / kSampleSegs);
+}
+__device__ __forceinline__ int sample_count(int64_t nvmin) {
+  return nvmin <= kSampleMax ? (int)nvmin : kSampleMax;
+}
+
+// One workgroup per (sequence, block of 16 queries): the sampled keys' scores of each query go to
+// the start of its tie list (sample position s * kSampleSeg + offset), which the select pass
+// later overwrites with candidates.
 template <int HP, bool PAGED>
-__global__ __launch_bounds__(256, 2) void index_mfma_hist_kernel(
+__global__ __launch_bounds__(256) void index_mfma_sample_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
-    int64_t N, const int64_t* __restrict__ pos, int m, int Q, MfmaSplit sp, IdxWs ws) {
-  __shared__ uint32_t hist[16 * kPBins / 2];  // two 16-bit counters per word
+    int64_t N, const int64_t* __restrict__ pos, int m, int Q, int nqb, IdxWs ws) {
   __shared__ int32_t pages[PAGED ? kPageList : 1];
-  int b, qb, kr;
-  mfma_unit(sp, b, qb, kr);
-  for (int j = threadIdx.x; j < 16 * kPBins / 2; j += 256) hist[j] = 0u;
-  __syncthreads();
+  const int qb = blockIdx.x % nqb, b = blockIdx.x / nqb, q0 = qb * 16;
   const int n = threadIdx.x & 15;
-  uint32_t* hq = hist + n * (kPBins / 2);
-  mfma_walk<HP, PAGED>(q_codes, q_scales, HI, k_codes, k_scales, kmap, N, pos, m, Q, sp, b, qb,
-                       kr, pages, [&](int64_t, const f32x4& sc, int nvis) {
+  // the block's first query sees the fewest keys
+  const int64_t nvmin = visible_entries(pos, b, q0, m, N);
+  float* samp = (float*)ws.tie((int)((int64_t)b * Q + (q0 + n < Q ? q0 + n : Q - 1)));
+  for (int sg = 0; sg < kSampleSegs; sg++) {
+    const int64_t g0 = sample_seg_start(nvmin, sg);
+    int64_t g1 = g0 + kSampleSeg;
+    if (g1 > nvmin) g1 = nvmin;
+    if (g0 >= g1) break;  // uniform
+    float* dst = samp + sg * kSampleSeg - g0;
+    mfma_walk_keys<HP, PAGED>(q_codes, q_scales, HI, k_codes, k_scales, kmap, N, pos, m, Q, b, qb,
+                              g0, g1, pages, [&](int64_t key0, const f32x4& sc, int nvis) {
 #pragma unroll
-                         for (int i = 0; i < 4; i++) {
-                           if (i >= nvis) break;
-                           const uint32_t bin = order_key(sc[i]) >> kPBinShift;
-                           atomicAdd(&hq[bin >> 1], 1u << (16 * (bin & 1)));
-                         }
-                       });
-  __syncthreads();
-  const int q0 = qb * 16;
-  for (int j = threadIdx.x; j < 16 * kPBins / 2; j += 256) {
-    const int qn = j / (kPBins / 2), wd = j - qn * (kPBins / 2);
-    const uint32_t v = hist[j];
-    if (v == 0u || q0 + qn >= Q) continue;
-    uint32_t* gh = ws.hist((int64_t)b * Q + q0 + qn);
-    if (v & 0xFFFFu) atomicAdd(&gh[2 * wd], v & 0xFFFFu);
-    if (v >> 16) atomicAdd(&gh[2 * wd + 1], v >> 16);
+                                for (int i = 0; i < 4; i++)
+                                  if (i < nvis) dst[key0 + i] = sc[i];
+                              });
+    if constexpr (PAGED) __syncthreads();  // the next segment refills the page list
   }
 }
 
-__global__ __launch_bounds__(256) void index_thresh_kernel(const int64_t* __restrict__ pos, int m,
-                                                           int Q, int64_t N, int k, IdxWs ws) {
-  const int slot = blockIdx.x, b = slot / Q, i = slot - b * Q;
+// Per query: the threshold estimate, an order key, in ctr[2]. With mu = kk S / nv the expected
+// number of the S sampled keys among the true top kk, the estimate is the m-th largest sampled key
+// for m = mu + 6 sqrt(mu) + 8: it lies above the true kk-th largest key only when m or more
+// sampled keys do, far in the tail of their distribution, and every key at or above the estimate
+// then numbers about kk m / mu, a few kk. Queries that see at most kSortCap keys take every key
+// (estimate 0). A wrong estimate costs time only: the select pass counts the keys at or above it,
+// and a query with fewer than kk or more than its list holds is finished by index_rescan_kernel.
+__global__ __launch_bounds__(256) void index_sample_thresh_kernel(const int64_t* __restrict__ pos,
+                                                                  int m, int Q, int64_t N, int k,
+                                                                  IdxWs ws) {
+  constexpr int NT = 256, KPT = kSampleMax / NT;
+  const int slot = blockIdx.x, b = slot / Q, i = slot - b * Q, t = threadIdx.x;
   const int64_t nv = visible_entries(pos, b, i, m, N);
   const int64_t kk = nv < k ? nv : k;
-  __shared__ uint32_t h[kPBins];
-  __shared__ uint32_t suf[256];
-  __shared__ uint32_t s_bin, s_above;
   uint32_t* ctr = ws.ctr(slot);
-  if (kk == 0) {
-    if (threadIdx.x == 0) ctr[2] = kNoThreshold;
+  if (kk == 0 || nv <= kSortCap) {
+    if (t == 0) ctr[2] = kk == 0 ? kNoThreshold : 0u;
     return;
   }
-  find_threshold_bin<kPBins>(ws.hist(slot), kk, h, suf, &s_bin, &s_above);
-  if (threadIdx.x == 0) ctr[2] = s_bin;
+  const int S = sample_count(visible_entries(pos, b, i - i % 16, m, N));
+  const double mu = (double)kk * (double)S / (double)nv;
+  int64_t mt = (int64_t)ceil(mu + 6.0 * sqrt(mu) + 8.0);
+  if (mt >= S) {  // the sample cannot bound it: take every key
+    if (t == 0) ctr[2] = 0u;
+    return;
+  }
+  // the mt-th largest of the S sampled order keys, 8 bits at a time
+  __shared__ uint32_t h[256];
+  __shared__ uint32_t s_prefix, s_mask, s_r;
+  const float* samp = (const float*)ws.tie(slot);
+  uint32_t x[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; j++) {
+    const int at = t + NT * j;
+    x[j] = at < S ? order_key(samp[at] + 0.0f) : 0u;
+  }
+  if (t == 0) {
+    s_prefix = 0u;
+    s_mask = 0u;
+    s_r = (uint32_t)mt;
+  }
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    h[t] = 0u;
+    __syncthreads();
+    const uint32_t pm = s_mask, pv = s_prefix, r = s_r;
+#pragma unroll
+    for (int j = 0; j < KPT; j++)
+      if (t + NT * j < S && (x[j] & pm) == pv) atomicAdd(&h[(x[j] >> shift) & 0xFFu], 1u);
+    __syncthreads();
+    if (t == 0) {  // the digit holding the r-th largest, from the top
+      uint32_t cum = 0;
+      int d = 255;
+      for (; d > 0; d--) {
+        if (cum + h[d] >= r) break;
+        cum += h[d];
+      }
+      s_r = r - cum;
+      s_prefix = pv | ((uint32_t)d << shift);
+      s_mask = pm | (0xFFu << shift);
+    }
+    __syncthreads();
+  }
+  if (t == 0) ctr[2] = s_prefix;
 }
 
-// Candidates are staged per query in LDS and appended to the global lists with one atomic per
-// list per query per workgroup; a staging list that fills up spills straight to the global list.
-constexpr int kPStage = 128;
+// The one full pass: every key whose score reaches the query's estimate goes to its candidate
+// list (the tie list; ctr[1] counts past the list's end). Candidates are staged per query in LDS
+// and appended with one atomic per query and workgroup; a full stage spills straight to the list.
+constexpr int kPStage = 256;
 
 template <int HP, bool PAGED>
 __global__ __launch_bounds__(256) void index_mfma_select_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
-    int64_t N, const int64_t* __restrict__ pos, int m, int Q, int k, MfmaSplit sp, IdxWs ws) {
-  __shared__ uint64_t stage[2][16][kPStage];  // [sure / tie][query][slot]
+    int64_t N, const int64_t* __restrict__ pos, int m, int Q, MfmaSplit sp, IdxWs ws) {
+  __shared__ uint64_t stage[16][kPStage];
   __shared__ int32_t pages[PAGED ? kPageList : 1];
-  __shared__ uint32_t scount[2][16], sbase[2][16];
+  __shared__ uint32_t scount[16], sbase[16];
   int b, qb, kr;
   mfma_unit(sp, b, qb, kr);
   const int q0 = qb * 16, n = threadIdx.x & 15;
-  if (threadIdx.x < 32) scount[threadIdx.x >> 4][threadIdx.x & 15] = 0u;
+  if (threadIdx.x < 16) scount[threadIdx.x] = 0u;
   __syncthreads();
   const int qi = q0 + n;
   const int64_t slot = (int64_t)b * Q + (qi < Q ? qi : Q - 1);
   uint32_t* ctr = ws.ctr((int)slot);
-  const uint32_t thr = qi < Q ? ctr[2] : kNoThreshold;
-  // the smallest score of the threshold bin: scores below it are dropped with one compare
-  const float smin = thr == kNoThreshold ? INFINITY : key_to_float(thr << kPBinShift);
-  uint64_t* sure = ws.sure((int)slot);
-  uint64_t* tie = ws.tie((int)slot);
+  const uint32_t est = qi < Q ? ctr[2] : kNoThreshold;
+  // scores below the estimate are dropped with one compare (estimate 0: every key)
+  const float smin = est == kNoThreshold ? INFINITY : (est == 0u ? -INFINITY : key_to_float(est));
+  uint64_t* cand = ws.tie((int)slot);
   mfma_walk<HP, PAGED>(q_codes, q_scales, HI, k_codes, k_scales, kmap, N, pos, m, Q, sp, b, qb,
                        kr, pages, [&](int64_t key0, const f32x4& sc, int nvis) {
 #pragma unroll
@@ -1030,43 +1097,33 @@ __global__ __launch_bounds__(256) void index_mfma_select_kernel(
                            if (i >= nvis) break;
                            const float s = sc[i];
                            if (!(s >= smin)) continue;
-                           const uint32_t ok = order_key(s), bin = ok >> kPBinShift;
-                           const uint64_t x = ((uint64_t)ok << 32) |
+                           const uint64_t x = ((uint64_t)order_key(s) << 32) |
                                               (uint64_t)(0xFFFFFFFFu - (uint32_t)(key0 + i));
-                           const int list = bin > thr ? 0 : 1;
-                           const uint32_t at = atomicAdd(&scount[list][n], 1u);
+                           const uint32_t at = atomicAdd(&scount[n], 1u);
                            if (at < (uint32_t)kPStage) {
-                             stage[list][n][at] = x;
-                           } else if (list == 0) {
-                             const uint32_t g = atomicAdd(&ctr[0], 1u);
-                             if (g < (uint32_t)k) sure[g] = x;
+                             stage[n][at] = x;
                            } else {
                              const uint32_t g = atomicAdd(&ctr[1], 1u);  // counts past the cap
-                             if (g < ws.tie_cap) tie[g] = x;
+                             if (g < ws.tie_cap) cand[g] = x;
                            }
                          }
                        });
   __syncthreads();
-  if (threadIdx.x < 32) {
-    const int list = threadIdx.x >> 4, qn = threadIdx.x & 15;
-    const uint32_t c = scount[list][qn];
+  if (threadIdx.x < 16) {
+    const int qn = threadIdx.x;
+    const uint32_t c = scount[qn];
     const uint32_t staged = c < (uint32_t)kPStage ? c : (uint32_t)kPStage;
-    sbase[list][qn] = (staged && q0 + qn < Q)
-                          ? atomicAdd(&ws.ctr((int)((int64_t)b * Q + q0 + qn))[list], staged)
-                          : 0u;
+    sbase[qn] = (staged && q0 + qn < Q)
+                    ? atomicAdd(&ws.ctr((int)((int64_t)b * Q + q0 + qn))[1], staged)
+                    : 0u;
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < 2 * 16 * kPStage; j += 256) {
-    const int list = j / (16 * kPStage), qn = (j / kPStage) % 16, e = j % kPStage;
-    const uint32_t c = scount[list][qn];
+  for (int j = threadIdx.x; j < 16 * kPStage; j += 256) {
+    const int qn = j / kPStage, e = j % kPStage;
+    const uint32_t c = scount[qn];
     if ((uint32_t)e >= (c < (uint32_t)kPStage ? c : (uint32_t)kPStage) || q0 + qn >= Q) continue;
-    const int64_t sl = (int64_t)b * Q + q0 + qn;
-    const uint32_t g = sbase[list][qn] + e;
-    if (list == 0) {
-      if (g < (uint32_t)k) ws.sure((int)sl)[g] = stage[0][qn][e];
-    } else {
-      if (g < ws.tie_cap) ws.tie((int)sl)[g] = stage[1][qn][e];
-    }
+    const uint32_t g = sbase[qn] + e;
+    if (g < ws.tie_cap) ws.tie((int)((int64_t)b * Q + q0 + qn))[g] = stage[qn][e];
   }
 }
 
@@ -1124,22 +1181,24 @@ __global__ __launch_bounds__(1024) void index_sort_kernel(const int64_t* __restr
   const int slot = blockIdx.x, b = slot / Q, i = slot - b * Q;
   const int64_t nv = visible_entries(pos, b, i, m, N);
   const int kk = (int)(nv < k ? nv : k);
-  if (kk > 0 && ws.ctr(slot)[1] > ws.tie_cap) return;  // overflowed: index_rescan_kernel
+  // fewer candidates than kk (the estimate was above the kk-th key) or more than the list holds:
+  // index_rescan_kernel finishes the query
+  const uint32_t nc = ws.ctr(slot)[1];
+  if (kk > 0 && (nc < (uint32_t)kk || nc > ws.tie_cap)) return;
   __shared__ uint64_t keys[kSortCap];
   __shared__ uint32_t dh[256];
   __shared__ uint32_t cnt[kBins], cur[kBins];
   finalize_slot<1024>(slot, N, k, kk, idx_out, score_out, ws, keys, dh, bin_bits, cnt, cur);
 }
 
-// ---- prefill: a query whose threshold bin overflowed its tie list ------------------------------
-// One workgroup per slot; every slot whose tie list held its whole bin returns at once. For the
-// others (ties in bulk, or a score distribution far from the usual spread) the workgroup finds
+// ---- prefill: a query the estimate did not serve ---------------------------------------------
+// One workgroup per slot; every slot whose candidate list holds between kk keys and the list's
+// capacity returns at once (index_sort_kernel finished it). For the others the workgroup finds
 // the kk-th largest key T by a radix select over fresh passes across the query's visible keys,
-// 11 key bits a pass below the shared bin, and a last pass collects the bin's keys >= T: with the
-// sure list they are exactly the top-kk, sorted in LDS as index_sort_kernel does. The scores come
-// from the same MFMA tiles as the earlier passes (every column of the B operand holds this query,
-// and lanes 0..3 of each 16-lane group take keys 4 * group + 0..3), so they are the same values.
-constexpr int kPBinBits = 32 - kPBinShift;  // key bits of the shared bin
+// 11 key bits a pass, and a last pass collects the keys >= T: exactly the top-kk, sorted in LDS.
+// The scores come from the same MFMA tiles as the select pass (every column of the B operand holds
+// this query, and lanes 0..3 of each 16-lane group take keys 4 * group + 0..3), so they are the
+// same values.
 constexpr int kRescanDigit = 11;
 constexpr int kRescanThreads = 256;
 
@@ -1186,8 +1245,8 @@ __global__ __launch_bounds__(kRescanThreads) void index_rescan_kernel(
   const int64_t nv = visible_entries(pos, b, i, m, N);
   const int kk = (int)(nv < k ? nv : k);
   const uint32_t* ctr = ws.ctr(slot);
-  if (kk == 0 || ctr[1] <= ws.tie_cap) return;  // uniform over the workgroup
-  constexpr int kLow = 64 - kPBinBits;           // key bits below the bin
+  const uint32_t nc = ctr[1];
+  if (kk == 0 || (nc >= (uint32_t)kk && nc <= ws.tie_cap)) return;  // uniform over the workgroup
   constexpr int kDBins = 1 << kRescanDigit;
   constexpr int kPer = kDBins / kRescanThreads;  // digit bins per thread
   __shared__ uint32_t hist[kDBins];
@@ -1195,17 +1254,15 @@ __global__ __launch_bounds__(kRescanThreads) void index_rescan_kernel(
   __shared__ uint64_t keys[kSortCap];
   __shared__ uint64_t s_prefix, s_mask;
   __shared__ uint32_t s_r, s_cnt;
-  const uint32_t thr = ctr[2];
-  const uint32_t ns = ctr[0] < (uint32_t)kk ? ctr[0] : (uint32_t)kk;  // < kk by the threshold
   QueryOps<HP> qo;
   load_query_ops<HP>(q_codes, q_scales, HI, (int64_t)b * Q + i, true, (t & 63) >> 4, qo);
   if (t == 0) {
-    s_prefix = (uint64_t)thr << kLow;
-    s_mask = ~(uint64_t)0 << kLow;
-    s_r = (uint32_t)kk - ns;  // rank (from 1) of T among the bin's keys
+    s_prefix = 0;
+    s_mask = 0;
+    s_r = (uint32_t)kk;  // rank (from 1) of T among all the visible keys
   }
   __syncthreads();
-  for (int lo = kLow; lo > 0;) {
+  for (int lo = 64; lo > 0;) {
     const int width = lo >= kRescanDigit ? kRescanDigit : lo;
     const int shift = lo - width;
     const uint32_t dmask = (1u << width) - 1u;
@@ -1245,21 +1302,18 @@ __global__ __launch_bounds__(kRescanThreads) void index_rescan_kernel(
     __syncthreads();
     lo = shift;
   }
-  // s_prefix is now T itself (all 64 bits fixed); the bin's keys >= T are its top kk - ns
+  // s_prefix is now T itself (all 64 bits fixed); the keys >= T are the top kk
   const uint64_t T = s_prefix;
   if (t == 0) s_cnt = 0u;
-  const uint64_t* sure = ws.sure(slot);
-  for (int j = t; j < (int)ns; j += kRescanThreads) keys[j] = sure[j];
   __syncthreads();
   rescan_keys<HP>(qo, k_codes, k_scales, kmap, b, nv, [&](uint64_t x) {
-    if ((uint32_t)(x >> kLow) == thr && x >= T) {
+    if (x >= T) {
       const uint32_t at = atomicAdd(&s_cnt, 1u);
-      if (ns + at < (uint32_t)kSortCap) keys[ns + at] = x;
+      if (at < (uint32_t)kSortCap) keys[at] = x;
     }
   });
   __syncthreads();
-  const uint32_t got = s_cnt < (uint32_t)kSortCap - ns ? s_cnt : (uint32_t)kSortCap - ns;
-  const int n = (int)(ns + got);
+  const int n = (int)(s_cnt < (uint32_t)kSortCap ? s_cnt : (uint32_t)kSortCap);
   int p2 = 2;
   while (p2 < n) p2 <<= 1;
   for (int j = n + t; j < p2; j += kRescanThreads) keys[j] = 0;
@@ -1308,15 +1362,13 @@ static hipError_t launch_mfma_hp(const IndexArgs& a, const IdxWs& w, hipStream_t
   const MfmaSplit sp = mfma_split(a, PAGED);
   const dim3 grid((unsigned)((int64_t)sp.nkr * sp.nqb * a.B));
   index_clear_kernel<<<slots, 256, 0, s>>>(w);
-  a.prof.launch(index_mfma_hist_kernel<HP, PAGED>, grid, dim3(256), s, a.q_codes, a.q_scales,
+  index_mfma_sample_kernel<HP, PAGED><<<(unsigned)(sp.nqb * a.B), 256, 0, s>>>(
+      a.q_codes, a.q_scales, a.HI, a.k_codes, a.k_scales, a.kmap, a.N, a.pos, a.m, a.Q, sp.nqb, w);
+  index_sample_thresh_kernel<<<slots, 256, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, w);
+  a.prof.launch(index_mfma_select_kernel<HP, PAGED>, grid, dim3(256), s, a.q_codes, a.q_scales,
                 a.HI, a.k_codes, a.k_scales, a.kmap, a.N, a.pos, a.m, a.Q, sp, w);
-  index_thresh_kernel<<<slots, 256, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, w);
-  index_mfma_select_kernel<HP, PAGED><<<grid, 256, 0, s>>>(a.q_codes, a.q_scales, a.HI,
-                                                           a.k_codes, a.k_scales, a.kmap, a.N,
-                                                           a.pos, a.m, a.Q, a.k, sp, w);
-  index_sort_kernel<<<slots, 1024, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, a.idx_out, a.score_out, w,
-                                           kPBinBits);
-  if (w.tie_cap < (uint64_t)a.N)  // otherwise no tie list can overflow
+  index_sort_kernel<<<slots, 1024, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, a.idx_out, a.score_out, w, 0);
+  if (a.N > kSortCap)  // otherwise every query takes all its keys and no list can fall short
     index_rescan_kernel<HP, PAGED><<<slots, kRescanThreads, 0, s>>>(
         a.q_codes, a.q_scales, a.HI, a.k_codes, a.k_scales, a.kmap, a.N, a.pos, a.m, a.Q, a.k,
         a.idx_out, a.score_out, w);

@@ -196,8 +196,8 @@ def test_prefill_schedule_ties_and_fewer_visible_than_k():
 
 
 def test_prefill_schedule_all_equal_scores():
-    """Zero keys: 20,000 tied candidates per query, more than the 8192-key tie list holds, so
-    every query is finished by the re-scan (radix select on the index bits alone)."""
+    """Zero keys: every one of the 20,000 keys reaches the estimate, more than the 8192-key list
+    holds, so every query is finished by the re-scan (radix select on the index bits alone)."""
     rng = np.random.default_rng(32)
     B, Q, N, m, k = 1, 16, 20000, 4, 1000
     kc = np.zeros((B, N, 64), np.uint8)
@@ -229,10 +229,10 @@ def _one_bin_inputs(rng, B, Q, N, HI):
 
 @pytest.mark.parametrize("HI", [4, 8])
 def test_prefill_tie_list_overflow_distinct_scores_in_one_bin(HI):
-    """30,000 keys whose scores all fall in the threshold bin, mostly distinct (with some ties):
-    the bin overflows the 8192-key tie list of every query, and the re-scan's radix select has to
-    split the bin on score bits, then on index bits. 20 queries (a partial second block) with
-    causal visibility changing inside the blocks."""
+    """30,000 keys whose scores all fall in one 11-bit histogram bin, mostly distinct (with some
+    ties): the threshold estimate and the ranking must split them on score bits, then on index
+    bits. 20 queries (a partial second block) with causal visibility changing inside the
+    blocks."""
     rng = np.random.default_rng(40 + HI)
     B, Q, N, m, k = 1, 20, 30000, 4, 1024
     kc, ks, qc, qs = _one_bin_inputs(rng, B, Q, N, HI)
@@ -242,7 +242,7 @@ def test_prefill_tie_list_overflow_distinct_scores_in_one_bin(HI):
 
 def test_prefill_tie_list_overflow_mixed_with_normal_queries():
     """Two sequences x 32 queries over 20,000 normal keys; in each sequence queries 16..31 have
-    zero codes (every score 0: the whole visible range ties and overflows the tie list) while
+    zero codes (every score 0: every key reaches the estimate and the list overflows) while
     queries 0..15 take the ordinary path, so both finishers run in one call."""
     rng = np.random.default_rng(43)
     B, Q, N, m, k = 2, 32, 20000, 4, 777
@@ -250,6 +250,34 @@ def test_prefill_tie_list_overflow_mixed_with_normal_queries():
     qc[:, 16:] = 0
     pos = np.array([N * m - Q, 4 * 15000 - 1], np.int64)
     _compare("prefill overflow mixed", kc, ks, qc, qs, pos, m, k)
+
+
+def _sampled_positions(nvmin: int) -> np.ndarray:
+    """The keys the prefill schedule samples for a query block whose first query sees nvmin keys:
+    64 segments of 128 keys spread evenly (all of them, contiguous, up to 8192)."""
+    if nvmin <= 8192:
+        return np.arange(nvmin)
+    stride = nvmin // 64
+    return (np.arange(64)[:, None] * stride + np.arange(128)[None, :]).ravel()
+
+
+@pytest.mark.parametrize("sampled", ["high", "low"])
+def test_prefill_estimate_misled_by_the_sample(sampled):
+    """The threshold estimate comes from a sample of each query block's keys. Here the sampled
+    keys are built to mislead it: scored above every other key ("high": the estimate lands far
+    above the true kk-th key, too few candidates reach it) or below every other key ("low": nearly
+    all keys reach it, more than the list holds). Either way the re-scan must finish every query
+    exactly. 16 queries over 40,000 keys, 4 heads."""
+    rng = np.random.default_rng(50 if sampled == "high" else 51)
+    B, Q, N, m, k, HI = 1, 16, 40000, 4, 1024, 4
+    kc, ks, qc, qs = _fp4_inputs(rng, B, Q, N, HI)
+    pos = np.array([N * m - Q], np.int64)
+    smp = _sampled_positions((N * m - Q + 1) // m)
+    qc[..., :16] = 0x22  # query block 0 all 1.0: key block 0 decides the sampled keys' scores
+    qs[..., 0] = 127
+    kc[0, smp, :16] = 0x66 if sampled == "high" else 0xEE  # +4.0 or -4.0 throughout block 0
+    ks[0, smp, 0] = 127
+    _compare(f"prefill sample {sampled}", kc, ks, qc, qs, pos, m, k)
 
 
 def test_prefill_chunk_full_size_sampled_queries():
