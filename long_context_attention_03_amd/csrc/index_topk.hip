@@ -970,99 +970,121 @@ __device__ __forceinline__ int sample_count(int64_t nvmin) {
   return nvmin <= kSampleMax ? (int)nvmin : kSampleMax;
 }
 
-// One workgroup per (sequence, block of 16 queries): the sampled keys' scores of each query go to
-// the start of its tie list (sample position s * kSampleSeg + offset), which the select pass
-// later overwrites with candidates.
+// One workgroup per (sequence, block of 16 queries, group of kSampleTilesPerWG tiles of 16 sampled
+// keys): the sampled keys' scores of each query go to the start of its tie list (sample position
+// p = segment * kSampleSeg + offset), which the select pass later overwrites with candidates. A
+// tile lies inside one segment (kSampleSeg is a multiple of 16), and each wavefront loads all its
+// tiles at once.
+constexpr int kSampleTilesPerWG = 32, kSampleWaveTiles = kSampleTilesPerWG / 4;
+constexpr int kSampleGroups = kSampleMax / 16 / kSampleTilesPerWG;
+
 template <int HP, bool PAGED>
 __global__ __launch_bounds__(256) void index_mfma_sample_kernel(
     const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
     int64_t N, const int64_t* __restrict__ pos, int m, int Q, int nqb, IdxWs ws) {
-  __shared__ int32_t pages[PAGED ? kPageList : 1];
-  const int qb = blockIdx.x % nqb, b = blockIdx.x / nqb, q0 = qb * 16;
-  const int n = threadIdx.x & 15;
-  // the block's first query sees the fewest keys
+  const int grp = blockIdx.x % kSampleGroups, rest = blockIdx.x / kSampleGroups;
+  const int qb = rest % nqb, b = rest / nqb, q0 = qb * 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, n = lane & 15, blk = lane >> 4;
+  // the block's first query sees the fewest keys: the sample lies below that
   const int64_t nvmin = visible_entries(pos, b, q0, m, N);
-  float* samp = (float*)ws.tie((int)((int64_t)b * Q + (q0 + n < Q ? q0 + n : Q - 1)));
-  for (int sg = 0; sg < kSampleSegs; sg++) {
-    const int64_t g0 = sample_seg_start(nvmin, sg);
-    int64_t g1 = g0 + kSampleSeg;
-    if (g1 > nvmin) g1 = nvmin;
-    if (g0 >= g1) break;  // uniform
-    float* dst = samp + sg * kSampleSeg - g0;
-    mfma_walk_keys<HP, PAGED>(q_codes, q_scales, HI, k_codes, k_scales, kmap, N, pos, m, Q, b, qb,
-                              g0, g1, pages, [&](int64_t key0, const f32x4& sc, int nvis) {
+  const int S = sample_count(nvmin);
+  const int ntile = (S + 15) / 16;
+  const int t0 = grp * kSampleTilesPerWG + wave;  // this wavefront's tiles: t0 + 4 u
+  if (t0 >= ntile) return;                        // per wavefront: no barriers below
+  const int qi = q0 + n;
+  const bool qv = qi < Q;
+  QueryOps<HP> qo;
+  load_query_ops<HP>(q_codes, q_scales, HI, (int64_t)b * Q + qi, qv, blk, qo);
+  u32x4 c[kSampleWaveTiles];
+  uint32_t e[kSampleWaveTiles];
 #pragma unroll
-                                for (int i = 0; i < 4; i++)
-                                  if (i < nvis) dst[key0 + i] = sc[i];
-                              });
-    if constexpr (PAGED) __syncthreads();  // the next segment refills the page list
+  for (int u = 0; u < kSampleWaveTiles; u++) {
+    int p = 16 * (t0 + 4 * u) + n;  // sample position of this lane's key in the A operand
+    p = p < S ? p : S - 1;          // past the sample: a valid key, scored and dropped
+    const int64_t key = sample_seg_start(nvmin, p / kSampleSeg) + p % kSampleSeg;
+    const int64_t row = kmap.row(b, key);
+    c[u] = __builtin_nontemporal_load((const u32x4*)(k_codes + row * 64 + 16 * blk));
+    e[u] = k_scales[row * 4 + blk];
+  }
+  float* samp = (float*)ws.tie((int)((int64_t)b * Q + (qv ? qi : Q - 1)));
+#pragma unroll
+  for (int u = 0; u < kSampleWaveTiles; u++) {
+    const int tile = t0 + 4 * u;
+    if (tile >= ntile) break;  // uniform over the wavefront
+    f32x4 sc = tile_scores<HP>(c[u], e[u], qo);
+    const int p0 = 16 * tile + 4 * blk;  // positions of this lane's four scores
+    if (!qv) continue;
+    if (p0 + 4 <= S) {
+      *(f32x4*)(samp + p0) = sc;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        if (p0 + i < S) samp[p0 + i] = sc[i];
+    }
   }
 }
 
 // Per query: the threshold estimate, an order key, in ctr[2]. With mu = kk S / nv the expected
-// number of the S sampled keys among the true top kk, the estimate is the m-th largest sampled key
-// for m = mu + 6 sqrt(mu) + 8: it lies above the true kk-th largest key only when m or more
-// sampled keys do, far in the tail of their distribution, and every key at or above the estimate
-// then numbers about kk m / mu, a few kk. Queries that see at most kSortCap keys take every key
+// number of the S sampled keys among the true top kk, the estimate is (at most) the m-th largest
+// sampled key for m = mu + 6 sqrt(mu) + 8: it lies above the true kk-th largest key only when m or
+// more sampled keys do, far in the tail of their distribution, and the keys at or above it then
+// number about kk m / mu, a few kk. Queries that see at most kSortCap keys take every key
 // (estimate 0). A wrong estimate costs time only: the select pass counts the keys at or above it,
 // and a query with fewer than kk or more than its list holds is finished by index_rescan_kernel.
+// One wavefront per query, no barriers: where mu exceeds kEstMu only every r-th sampled key is
+// used (mu / r at most kEstMu, so m stays below 4 * 64); each lane keeps the 4 largest of its keys,
+// and the estimate is the m-th largest of those 256. They are sampled keys, so that value is at
+// most the m-th largest sampled key: the estimate can only come out lower, which keeps it safe.
+constexpr int kEstMu = 100, kEstKeep = 4;
+
 __global__ __launch_bounds__(256) void index_sample_thresh_kernel(const int64_t* __restrict__ pos,
                                                                   int m, int Q, int64_t N, int k,
-                                                                  IdxWs ws) {
-  constexpr int NT = 256, KPT = kSampleMax / NT;
-  const int slot = blockIdx.x, b = slot / Q, i = slot - b * Q, t = threadIdx.x;
+                                                                  int slots, IdxWs ws) {
+  const int lane = threadIdx.x & 63;
+  const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (slot >= slots) return;  // per wavefront: this kernel has no barriers
+  const int b = slot / Q, i = slot - b * Q;
   const int64_t nv = visible_entries(pos, b, i, m, N);
   const int64_t kk = nv < k ? nv : k;
   uint32_t* ctr = ws.ctr(slot);
   if (kk == 0 || nv <= kSortCap) {
-    if (t == 0) ctr[2] = kk == 0 ? kNoThreshold : 0u;
+    if (lane == 0) ctr[2] = kk == 0 ? kNoThreshold : 0u;
     return;
   }
   const int S = sample_count(visible_entries(pos, b, i - i % 16, m, N));
-  const double mu = (double)kk * (double)S / (double)nv;
-  int64_t mt = (int64_t)ceil(mu + 6.0 * sqrt(mu) + 8.0);
-  if (mt >= S) {  // the sample cannot bound it: take every key
-    if (t == 0) ctr[2] = 0u;
+  const double mu0 = (double)kk * (double)S / (double)nv;
+  const int r = mu0 > kEstMu ? (int)ceil(mu0 / kEstMu) : 1;  // use sampled keys 0, r, 2r, ...
+  const int S2 = (S + r - 1) / r;
+  const double mu = (double)kk * (double)S2 / (double)nv;
+  const int mt = (int)ceil(mu + 6.0 * sqrt(mu) + 8.0);
+  if (mt >= S2 || mt > kEstKeep * 64) {  // the sample cannot bound it: take every key
+    if (lane == 0) ctr[2] = 0u;
     return;
   }
-  // the mt-th largest of the S sampled order keys, 8 bits at a time
-  __shared__ uint32_t h[256];
-  __shared__ uint32_t s_prefix, s_mask, s_r;
   const float* samp = (const float*)ws.tie(slot);
-  uint32_t x[KPT];
+  uint32_t top[kEstKeep] = {0u, 0u, 0u, 0u};  // descending; 0: none
+  for (int q = lane; q < S2; q += 64) {
+    uint32_t x = order_key(samp[(size_t)q * r] + 0.0f);
 #pragma unroll
-  for (int j = 0; j < KPT; j++) {
-    const int at = t + NT * j;
-    x[j] = at < S ? order_key(samp[at] + 0.0f) : 0u;
-  }
-  if (t == 0) {
-    s_prefix = 0u;
-    s_mask = 0u;
-    s_r = (uint32_t)mt;
-  }
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    h[t] = 0u;
-    __syncthreads();
-    const uint32_t pm = s_mask, pv = s_prefix, r = s_r;
-#pragma unroll
-    for (int j = 0; j < KPT; j++)
-      if (t + NT * j < S && (x[j] & pm) == pv) atomicAdd(&h[(x[j] >> shift) & 0xFFu], 1u);
-    __syncthreads();
-    if (t == 0) {  // the digit holding the r-th largest, from the top
-      uint32_t cum = 0;
-      int d = 255;
-      for (; d > 0; d--) {
-        if (cum + h[d] >= r) break;
-        cum += h[d];
-      }
-      s_r = r - cum;
-      s_prefix = pv | ((uint32_t)d << shift);
-      s_mask = pm | (0xFFu << shift);
+    for (int j = 0; j < kEstKeep; j++) {  // insertion: x moves down past the smaller keys
+      const uint32_t hi = x > top[j] ? x : top[j], lo = x > top[j] ? top[j] : x;
+      top[j] = hi;
+      x = lo;
     }
-    __syncthreads();
   }
-  if (t == 0) ctr[2] = s_prefix;
+  // the mt-th largest of the 256 kept keys, one bit at a time from the top
+  uint32_t prefix = 0u, rr = (uint32_t)mt;
+  for (int bit = 31; bit >= 0; bit--) {
+    const uint32_t sel = ~0u << bit, want = prefix | (1u << bit);
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < kEstKeep; j++) c += (top[j] != 0u && (top[j] & sel) == want) ? 1u : 0u;
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)wave_prefix_add(c), 63);
+    if (total >= rr) prefix = want;
+    else rr -= total;
+  }
+  if (lane == 0) ctr[2] = prefix;
 }
 
 // The one full pass: every key whose score reaches the query's estimate goes to its candidate
@@ -1362,9 +1384,9 @@ static hipError_t launch_mfma_hp(const IndexArgs& a, const IdxWs& w, hipStream_t
   const MfmaSplit sp = mfma_split(a, PAGED);
   const dim3 grid((unsigned)((int64_t)sp.nkr * sp.nqb * a.B));
   index_clear_kernel<<<slots, 256, 0, s>>>(w);
-  index_mfma_sample_kernel<HP, PAGED><<<(unsigned)(sp.nqb * a.B), 256, 0, s>>>(
+  index_mfma_sample_kernel<HP, PAGED><<<(unsigned)(kSampleGroups * sp.nqb * a.B), 256, 0, s>>>(
       a.q_codes, a.q_scales, a.HI, a.k_codes, a.k_scales, a.kmap, a.N, a.pos, a.m, a.Q, sp.nqb, w);
-  index_sample_thresh_kernel<<<slots, 256, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, w);
+  index_sample_thresh_kernel<<<(slots + 3) / 4, 256, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, slots, w);
   a.prof.launch(index_mfma_select_kernel<HP, PAGED>, grid, dim3(256), s, a.q_codes, a.q_scales,
                 a.HI, a.k_codes, a.k_scales, a.kmap, a.N, a.pos, a.m, a.Q, sp, w);
   index_sort_kernel<<<slots, 1024, 0, s>>>(a.pos, a.m, a.Q, a.N, a.k, a.idx_out, a.score_out, w, 0);
