@@ -72,11 +72,12 @@ struct IdxWs {
 static inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Candidate list of a prefill query (the MFMA path): the keys at or above its sampled threshold
-// estimate, a few kk (see index_sample_thresh_kernel); N/32 keys and at least twice the LDS
-// ranking's capacity hold them, and a query with more is finished by index_rescan_kernel. That
-// keeps a 4096-query chunk's workspace at a few hundred MB instead of N keys per query.
-static uint32_t prefill_tie_cap(int64_t N) {
-  int64_t c = (N + 31) / 32;
+// estimate, about 2.3 kk whatever N is (see index_sample_thresh_kernel); 4 k keys and at least
+// twice the LDS ranking's capacity hold them, and a query with more is finished by
+// index_rescan_kernel. The list first holds the query's sampled scores (at most kSortCap * 2
+// floats). A 4096-query chunk's workspace is then a few hundred MB for any cache length.
+static uint32_t prefill_tie_cap(int64_t N, int k) {
+  int64_t c = 4 * (int64_t)k;
   if (c < 2 * kSortCap) c = 2 * kSortCap;
   if (c > N) c = N;
   return (uint32_t)c;
@@ -87,7 +88,7 @@ static uint32_t prefill_tie_cap(int64_t N) {
 static IdxWs make_ws(void* base, int64_t N, int k, bool with_scores) {
   IdxWs w;
   w.base = (char*)base;
-  w.tie_cap = with_scores ? (uint32_t)N : prefill_tie_cap(N);
+  w.tie_cap = with_scores ? (uint32_t)N : prefill_tie_cap(N, k);
   w.off_hist = al256(128 * sizeof(float));
   w.off_ctr = w.off_hist + al256(kBins * sizeof(uint32_t));
   w.off_scores = w.off_ctr + 256;

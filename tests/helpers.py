@@ -41,7 +41,8 @@ def assert_close(gpu, ref, what: str, atol=ATOL, rtol=RTOL):
     ref = np.asarray(ref, np.float64)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
     both_inf = np.isinf(gpu) & np.isinf(ref) & (np.sign(gpu) == np.sign(ref))
-    err = np.abs(gpu - ref)
+    with np.errstate(invalid="ignore"):  # inf - inf where both are the same infinity
+        err = np.abs(gpu - ref)
     lim = atol + rtol * np.abs(ref)
     bad = ~both_inf & ~(err <= lim)
     worst = float(np.max(np.where(both_inf, 0, err / lim))) if gpu.size else 0.0

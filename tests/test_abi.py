@@ -286,10 +286,16 @@ def test_row_layout_rule():
 
 
 def test_prefill_index_workspace_is_bounded():
-    """The 4096-query prefill chunk over 263,168 FP4 keys: each query's tie list holds N/32 keys
-    (at least 8192) instead of N, so the workspace is a few hundred MB, not 8.7 GB; a query
-    whose threshold bin holds more is finished by the re-scan."""
+    """The 4096-query prefill chunk over 263,168 FP4 keys: each query's candidate list holds
+    max(8192, 4 k) keys instead of N, so the workspace is a few hundred MB, not 8.7 GB, and it
+    does not grow with the cache length; a query whose list overflows is finished by the
+    re-scan."""
     ws = L.index_topk_workspace(1, 4096, 263168, 1024, 4, 128)
     assert 0 < ws < (512 << 20), ws
+    # a 4M-key cache (16M tokens at m = 4) needs no more per query than a 263K one
+    assert L.index_topk_workspace(1, 4096, 4 << 20, 1024, 4, 128) == ws
+    # a larger k widens the list: 4 k keys of 8 bytes per query beyond the 8192-key floor
+    big = L.index_topk_workspace(1, 4096, 4 << 20, 4096, 4, 128)
+    assert big >= 4096 * 4 * 4096 * 8, big
     # the decode schedules are unchanged: candidate lists of a fixed size per slot
     assert L.index_topk_workspace(16, 1, 262144, 1024, 4, 128) == 16 * 73728
