@@ -117,7 +117,14 @@ class DecodeStep:
                                   dtype=torch.uint8, device=dev)
         self.ws_hca = torch.empty(max(256, L.attend_workspace(B_STEP, 1, H, D, N_HCA + W)),
                                   dtype=torch.uint8, device=dev)
-        self.side = torch.cuda.Stream(device=dev)  # default priority
+        # The two layers' streams, created back to back (default priority); the step runs with
+        # `main` current. HIP maps streams onto the device's few hardware queues in turn, and two
+        # streams on one queue run one after the other: with the HCA layer on the queue of the
+        # stream that runs the CSA layer the step serializes (measured 179 against 137 us, for
+        # every fourth stream created beside the default stream). Two streams created in a row
+        # never share a queue.
+        self.main = torch.cuda.Stream(device=dev)
+        self.side = torch.cuda.Stream(device=dev)
         # speculative verification: 5 query tokens per sequence for the first 4 sequences
         QM, BM = MTP_Q, B_CSA4
         self.pos_m = torch.full((BM,), CTX - QM, dtype=torch.int64, device=dev)
@@ -208,8 +215,9 @@ class DecodeStep:
         self.hca_attend()
 
     def step(self):
-        """Eager step: the HCA branch on a second stream beside the CSA branch. The CSA branch
-        (the longer chain) is enqueued first; the second stream forks from the point before it."""
+        """Eager step: the HCA branch on the side stream beside the CSA branch on the current
+        stream (run it with `main` current). The CSA branch (the longer chain) is enqueued first;
+        the side stream forks from the point before it."""
         main = torch.cuda.current_stream()
         self.side.wait_stream(main)
         self.csa_branch()
@@ -279,10 +287,11 @@ class StepGraphs:
         torch.cuda.synchronize()
 
     def replay(self):
-        # The CSA graph (the longer chain: compress, scan, top-k, attention) is launched first,
-        # since a graph launch costs the host tens of microseconds (with the current kernels the
-        # other order measures the same). The side stream forks from the point before it, so the
-        # HCA graph does not wait for the CSA graph.
+        # Run with the step's `main` stream current (see DecodeStep). The CSA graph (the longer
+        # chain: compress, scan, top-k, attention) is launched first, since a graph launch costs
+        # the host tens of microseconds (with the current kernels the other order measures the
+        # same). The side stream forks from the point before it, so the HCA graph does not wait
+        # for the CSA graph. (Forking both layers off a third stream instead costs about 20 us.)
         main, side = torch.cuda.current_stream(), self.ws.side
         side.wait_stream(main)
         self.g_csa.replay()
@@ -941,6 +950,9 @@ def main():
     torch.cuda.set_device(0)
     log("building inputs (about 2.8 GB of encoded caches on the GPU)...")
     ws = DecodeStep()
+    # everything below runs on the step's main stream, which never shares a hardware queue with
+    # the side stream that the HCA layer takes
+    torch.cuda.set_stream(ws.main)
     log("warmup...")
     for _ in range(args.warmup):
         ws.step()
