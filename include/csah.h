@@ -146,7 +146,8 @@ int csah_kv_compress_span(const void* raw, int raw_dtype, int64_t raw_seq_stride
  *    (sequence, query) slot, whatever N.
  *  - dI = 128 and Q >= 16 (a prefill chunk: many queries of one sequence share its keys): the
  *    scores come from the scaled FP4 MFMA and are recomputed rather than stored; the workspace
- *    holds, per query, a histogram, counters and candidate lists of up to N 8-byte keys.
+ *    holds, per query, a histogram, counters and a candidate list of max(8192, 4k) 8-byte keys
+ *    (at most N), whatever N is.
  *  - Otherwise (3 <= Q <= 15 with 128-dim keys, or N > 2^20) every score is stored: per slot
  *    the head-summed query, a histogram, counters, 4 bytes per entry and two candidate lists.
  */
