@@ -207,7 +207,7 @@ int csah_csa_attend(const void* q, int q_dtype, int H, int D, const void* cache,
  * allocates nor frees anything. Same arguments, layouts, results and statuses as csah_csa_attend
  * without ws / ws_bytes, plus CSAH_ERR_SCRATCH_LIMIT (nothing enqueued) when
  * csah_attend_workspace(B, Q, H, D, k + w) exceeds the scratch; 16 sequences of one query at
- * H = 64, D = 512, k = 1024, w = 128 need 19 MB. Every call on a GPU shares that GPU's scratch
+ * H = 64, D = 512, k = 1024, w = 128 need 25.4 MB. Every call on a GPU shares that GPU's scratch
  * and nothing in it needs clearing (each call writes every partial it reads); calls that overlap
  * on one GPU (on different streams, or from different threads) race on it and must be ordered by
  * the caller. The first call on a device looks up the scratch's address there.

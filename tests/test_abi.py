@@ -299,3 +299,13 @@ def test_prefill_index_workspace_is_bounded():
     assert big >= 4096 * 4 * 4096 * 8, big
     # the decode schedules are unchanged: candidate lists of a fixed size per slot
     assert L.index_topk_workspace(16, 1, 262144, 1024, 4, 128) == 16 * 73728
+
+
+def test_noalloc_scratch_covers_the_decode_step():
+    """The no-allocation attention call's static scratch holds the split partials of the decode
+    step's CSA attention (16 sequences, 64 heads x 512, top-1024 + window 128) and of the
+    4-sequence step; the header states the 16-sequence figure."""
+    need16 = L.attend_workspace(16, 1, 64, 512, 1024 + 128)
+    need4 = L.attend_workspace(4, 1, 64, 512, 1024 + 128)
+    assert 0 < need4 < need16 <= L.NOALLOC_SCRATCH_BYTES, (need4, need16)
+    assert f"{need16 / 1e6:.1f} MB" in open(HEADER).read()
