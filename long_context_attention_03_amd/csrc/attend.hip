@@ -994,8 +994,8 @@ AttendPlan attend_plan(int B, int Q, int H, int D, int64_t max_rows) {
   return pl;
 }
 
-// attend_x_kernel: workgroups of 4 wavefronts over one block of 64 heads, two per CU (their LDS
-// and registers), so about 512 of them.
+// attend_x_kernel: workgroups of 4 wavefronts over one (query, row split, block of 64 heads). Grids
+// of up to 256 workgroups take the one-per-CU build, larger ones the two-per-CU build.
 static AttendPlan attend_x_plan(int B, int Q, int H, int64_t max_rows) {
   const int hb = (H + 63) / 64;
   const int64_t base = (int64_t)B * Q * hb;
@@ -1004,11 +1004,18 @@ static AttendPlan attend_x_plan(int B, int Q, int H, int64_t max_rows) {
   // measured at 16 sequences, splits of 3 tiles (12 per sequence) beat 4 tiles by 9% and 6 tiles
   // by 25%; at 4 sequences, 2 tiles beat 1, 3 and 4.
   const int min_tiles = base >= 16 ? 3 : 2;
-  // At most 240 workgroups, one per CU: a workgroup takes a CU's whole register file, and the
+  const int64_t tiles = (max_rows + kXTile - 1) / kXTile;
+  // Up to 240 workgroups, one per CU: a workgroup takes a CU's whole register file, and the
   // 16 CUs left over (two per XCD) keep room for a kernel running concurrently on another stream.
   // In a decode step the CSA layer's top-k (16 workgroups of 1,024 threads) otherwise waits for
-  // the whole HCA attention to finish.
-  AttendPlan pl = make_plan(base, (max_rows + kXTile - 1) / kXTile, 240, min_tiles);
+  // the whole HCA attention to finish. Dense attention over long row sets (64 tiles or more per
+  // query) for 20 or more (query, head block) units targets 480 workgroups instead, of the
+  // two-per-CU build: measured at 8,320 rows, 20 to 64 sequences ran 1.5-10% faster, and the
+  // 4 x 5-query decode step 142.5 against 151.3 us (its two attention grids then share CUs).
+  // Sparse attention (36 tiles) at 32 and 64 sequences ran 15-20% slower that way, and the
+  // 16-sequence step 139 against 133 us, so both keep 240.
+  const int64_t want = base >= 20 && tiles >= 64 ? 480 : 240;
+  AttendPlan pl = make_plan(base, tiles, want, min_tiles);
   pl.head_groups = hb;
   return pl;
 }
