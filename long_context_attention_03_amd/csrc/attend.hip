@@ -493,6 +493,8 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(AttendK p) {
 // barrier and softmax waits overlap the other's matrix work; with MINW = 1 a workgroup keeps more
 // tiles in flight instead.
 constexpr int kXTile = 32, kXRS = 528, kXTileElems = kXTile * kXRS;
+// a tile's lo term is left out when its largest weight is at most this share of the lane's sum
+constexpr float kLoSkipFrac = 0.0625f;
 
 // Max over the four 16-lane rows of a wavefront, in every lane: gfx950's permlane swaps exchange
 // rows 0<->1 and 2<->3 (16-lane swap), then the two halves (32-lane swap), so each lane ends up
@@ -512,7 +514,10 @@ struct TileRawX {
 // MINW: workgroups per CU the register budget is sized for. Grids of up to one workgroup per CU
 // (decode) take 1, so a wavefront may hold all 512 registers and nothing spills; larger grids
 // (prefill) take 2, so two workgroups overlap each other's waits.
-template <bool DENSE, bool PAGED, int MINW>
+// SKIPLO (two-per-CU build, splits of 64 tiles or more): tiles whose weights are all small next to
+// the weight already summed leave out the lo term of P (see the softmax below). Shorter splits
+// seldom reach that state and run faster with the hi and lo products interleaved.
+template <bool DENSE, bool PAGED, int MINW, bool SKIPLO>
 __global__ __launch_bounds__(256, MINW) void attend_x_kernel(AttendK p) {
   constexpr int D = 512, NCH = 16, NT = 32, RB = 576;
   // Tiles whose rows are in flight: with a CU's whole register file (MINW = 1) the rows of the
@@ -816,38 +821,89 @@ __global__ __launch_bounds__(256, MINW) void attend_x_kernel(AttendK p) {
         P[i] = __builtin_amdgcn_exp2f(full ? __builtin_fmaf(v[i], sc, -m_run) : v[i] - m_run);
         psum += P[i];
       }
-      l_run += psum;
-      bf16x8 ph, pl;
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        ph[e] = (__bf16)P[e];
-        pl[e] = (__bf16)(P[e] - (float)ph[e]);
+      // The lo term of P carries bits 9-16 of each weight. With SKIPLO a wavefront leaves it out
+      // of a tile when none of the tile's weights exceeds 1/16 of the weight its lane has already
+      // summed for the same head (that partial sum is at most the head's final normaliser):
+      // rows that small cannot dominate the output, and their rounding errors, of random sign and
+      // at most 2^-8 of each weight, add up to well under the 1e-3 tolerance. A softmax with a
+      // few dominant rows keeps the lo term on the tiles that hold them.
+      bool lo = true;
+      if constexpr (SKIPLO) {
+        float pmax = fmaxf(fmaxf(fmaxf(P[0], P[1]), fmaxf(P[2], P[3])),
+                           fmaxf(fmaxf(P[4], P[5]), fmaxf(P[6], P[7])));
+        lo = __ballot(pmax > kLoSkipFrac * l_run) != 0ull;
       }
-      // a group's hi products, then its lo products: GRP independent chains
+      l_run += psum;
+      if constexpr (!SKIPLO) {
+        bf16x8 ph, pl;
 #pragma unroll
-      for (int t = 0; t < NT; t += GRP) {
-        bf16x8 y[GRP];
+        for (int e = 0; e < 8; e++) {
+          ph[e] = (__bf16)P[e];
+          pl[e] = (__bf16)(P[e] - (float)ph[e]);
+        }
+        // a group's hi products, then its lo products: GRP independent chains
 #pragma unroll
-        for (int j = 0; j < GRP; j++) y[j] = yf[(t + j) % RF];
+        for (int t = 0; t < NT; t += GRP) {
+          bf16x8 y[GRP];
 #pragma unroll
-        for (int j = 0; j < GRP; j++)
-          O[t + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(y[j], ph, O[t + j], 0, 0, 0);
+          for (int j = 0; j < GRP; j++) y[j] = yf[(t + j) % RF];
 #pragma unroll
-        for (int j = 0; j < GRP; j++)
-          O[t + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(y[j], pl, O[t + j], 0, 0, 0);
-        if (t + RF < NT) {
+          for (int j = 0; j < GRP; j++)
+            O[t + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(y[j], ph, O[t + j], 0, 0, 0);
 #pragma unroll
-          for (int j = 0; j < GRP; j++) yf[(t + j) % RF] = ytr(t + j + RF);
+          for (int j = 0; j < GRP; j++)
+            O[t + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(y[j], pl, O[t + j], 0, 0, 0);
+          if (t + RF < NT) {
+#pragma unroll
+            for (int j = 0; j < GRP; j++) yf[(t + j) % RF] = ytr(t + j + RF);
+          }
+        }
+        // each group's products, then the reads of the group RF fragments ahead (2 transposing
+        // reads per 16-dim tile)
+#pragma unroll
+        for (int t = 0; t < NT - RF; t += GRP) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * GRP, 1);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * GRP, 1);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * RF, 1);
+      } else {
+        // the hi products over all dims, then (when kept) the lo products in a second pass that
+        // reads the Y^T fragments again: the pass is a block of its own after the first, so a
+        // tile without it runs exactly the hi pass, and neither pass holds the other's registers
+        auto pass = [&](const bf16x8& pw) {
+#pragma unroll
+          for (int t = 0; t < NT; t += GRP) {
+            bf16x8 y[GRP];
+#pragma unroll
+            for (int j = 0; j < GRP; j++) y[j] = yf[(t + j) % RF];
+#pragma unroll
+            for (int j = 0; j < GRP; j++)
+              O[t + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(y[j], pw, O[t + j], 0, 0, 0);
+            if (t + RF < NT) {
+#pragma unroll
+              for (int j = 0; j < GRP; j++) yf[(t + j) % RF] = ytr(t + j + RF);
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < NT - RF; t += GRP) {
+            __builtin_amdgcn_sched_group_barrier(0x008, GRP, 1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * GRP, 1);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, RF, 1);
+        };
+        bf16x8 ph;
+#pragma unroll
+        for (int e = 0; e < 8; e++) ph[e] = (__bf16)P[e];
+        pass(ph);
+        if (lo) {
+          bf16x8 pl;
+#pragma unroll
+          for (int e = 0; e < 8; e++) pl[e] = (__bf16)(P[e] - (float)ph[e]);
+#pragma unroll
+          for (int t = 0; t < RF; t++) yf[t] = ytr(t);
+          pass(pl);
         }
       }
-      // each group's products, then the reads of the group RF fragments ahead (2 transposing
-      // reads per 16-dim tile)
-#pragma unroll
-      for (int t = 0; t < NT - RF; t += GRP) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * GRP, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * GRP, 1);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * RF, 1);
     }
   };
   // The ring slots are compile-time indices: the loop is unrolled by the ring depth and runs
@@ -1076,21 +1132,30 @@ hipError_t launch_attend(const AttendArgs& a) {
   hipError_t e;
   if (shared_tiles) {
     const dim3 blk(256);
+    const bool paged = a.cmap.table != nullptr, dense = a.idx == nullptr;
     if (grid.x <= 256) {
-      if (a.cmap.table) {
-        if (a.idx) a.prof.launch(attend_x_kernel<false, true, 1>, grid, blk, s, k);
-        else a.prof.launch(attend_x_kernel<true, true, 1>, grid, blk, s, k);
+      if (paged) {
+        if (dense) a.prof.launch(attend_x_kernel<true, true, 1, false>, grid, blk, s, k);
+        else a.prof.launch(attend_x_kernel<false, true, 1, false>, grid, blk, s, k);
       } else {
-        if (a.idx) a.prof.launch(attend_x_kernel<false, false, 1>, grid, blk, s, k);
-        else a.prof.launch(attend_x_kernel<true, false, 1>, grid, blk, s, k);
+        if (dense) a.prof.launch(attend_x_kernel<true, false, 1, false>, grid, blk, s, k);
+        else a.prof.launch(attend_x_kernel<false, false, 1, false>, grid, blk, s, k);
+      }
+    } else if (pl.rows_per_split >= 64 * kXTile) {
+      if (paged) {
+        if (dense) a.prof.launch(attend_x_kernel<true, true, 2, true>, grid, blk, s, k);
+        else a.prof.launch(attend_x_kernel<false, true, 2, true>, grid, blk, s, k);
+      } else {
+        if (dense) a.prof.launch(attend_x_kernel<true, false, 2, true>, grid, blk, s, k);
+        else a.prof.launch(attend_x_kernel<false, false, 2, true>, grid, blk, s, k);
       }
     } else {
-      if (a.cmap.table) {
-        if (a.idx) a.prof.launch(attend_x_kernel<false, true, 2>, grid, blk, s, k);
-        else a.prof.launch(attend_x_kernel<true, true, 2>, grid, blk, s, k);
+      if (paged) {
+        if (dense) a.prof.launch(attend_x_kernel<true, true, 2, false>, grid, blk, s, k);
+        else a.prof.launch(attend_x_kernel<false, true, 2, false>, grid, blk, s, k);
       } else {
-        if (a.idx) a.prof.launch(attend_x_kernel<false, false, 2>, grid, blk, s, k);
-        else a.prof.launch(attend_x_kernel<true, false, 2>, grid, blk, s, k);
+        if (dense) a.prof.launch(attend_x_kernel<true, false, 2, false>, grid, blk, s, k);
+        else a.prof.launch(attend_x_kernel<false, false, 2, false>, grid, blk, s, k);
       }
     }
     e = hipGetLastError();

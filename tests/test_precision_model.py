@@ -1,0 +1,125 @@
+"""fp64 model of how the attention kernels round the softmax weights before the P.Y products.
+
+The kernels compute every score exactly (bf16 queries, rows exact in bf16) and accumulate in fp32,
+so the one rounding that matters is P's: a 16x16x32 bf16 product takes P in bf16. This models the
+three forms the kernels could use, on the parity tests' row and query distributions (E4M3 + bf16
+rows, bf16 queries, unit normal draws; scores of spread 1, 2, 4 and 8 through the query scale), and
+holds each to the atol = rtol = 1e-3 bar of the parity tests:
+
+- one bf16 term: fails the bar once a few rows carry most of the weight, even over thousands of
+  rows: this is why the kernels keep a second (lo) term;
+- hi + lo bf16 terms (about 16 significant bits): far inside the bar everywhere;
+- the lo term left out of a tile whose weights are all at most 1/16 of the weight the lane has
+  already summed for that head, as the two-per-CU build does on splits of 64 tiles or more: inside
+  half the bar at every spread, while it still leaves the lo term out of most tiles of a flat
+  softmax.
+
+The model follows the kernel's bookkeeping: 32-row tiles, a lane's running sum over its rows 4g..4g+3
+and 16+4g..16+4g+3 of each tile, a reference max that moves only when a head's max grows by more
+than 2^8, and the decision taken per wavefront of 16 heads.
+"""
+import numpy as np
+import pytest
+import torch
+
+TOL = 1e-3
+D = 512
+
+
+def _bf16(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def _e4m3(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).double().numpy()
+
+
+def _inputs(R, H, spread, seed):
+    rng = np.random.default_rng(seed)
+    y = rng.standard_normal((R, D))
+    y[:, :448] = _e4m3(y[:, :448])
+    y[:, 448:] = _bf16(y[:, 448:])
+    q = _bf16(rng.standard_normal((H, D)) * spread)
+    s2 = (q @ y.T) / np.sqrt(D) * np.log2(np.e)  # base-2 scores, exact products
+    sink = rng.standard_normal(H) * np.log2(np.e)
+    return y, s2, sink
+
+
+def _exact(y, s2, sink):
+    M = np.maximum(s2.max(1), sink)
+    p = np.exp2(s2 - M[:, None])
+    return (p @ y) / (p.sum(1) + np.exp2(sink - M))[:, None]
+
+
+def _kernel_model(y, s2, sink, mode, skip_frac=1 / 16):
+    """One split over all rows, as a prefill query's workgroup runs it. mode: 'hi', 'hilo' or
+    'skip'. Returns the output and the share of (tile, wavefront) steps without the lo term."""
+    H, R = s2.shape
+    m_run = np.full(H, -np.inf)
+    l_lane = np.zeros((H, 4))
+    O = np.zeros((H, D))
+    grp_of = (np.arange(32) % 16) // 4  # lane group holding each row of a tile
+    steps = skipped = 0
+    for t0 in range(0, R, 32):
+        st = s2[:, t0:t0 + 32]
+        g = grp_of[:st.shape[1]]
+        m_new = np.maximum(m_run, st.max(1))
+        move = m_new > m_run + 8
+        alpha = np.where(move & np.isfinite(m_run), np.exp2(m_run - m_new), 1.0)
+        alpha = np.where(move & ~np.isfinite(m_run), 0.0, alpha)
+        O *= alpha[:, None]
+        l_lane *= alpha[:, None]
+        m_run = np.where(move, m_new, m_run)
+        P = np.exp2(st - m_run[:, None])
+        hi = _bf16(P)
+        lo = _bf16(P - hi)
+        for w in range(0, H, 16):
+            hs = slice(w, w + 16)
+            if mode == "hi":
+                use_lo = False
+            elif mode == "hilo":
+                use_lo = True
+            else:
+                use_lo = any((P[hs][:, g == k].max(1) > skip_frac * l_lane[hs, k]).any()
+                             for k in range(4) if (g == k).any())
+            steps += 1
+            skipped += not use_lo
+            O[hs] += (hi[hs] + lo[hs] if use_lo else hi[hs]) @ y[t0:t0 + 32]
+        for k in range(4):
+            l_lane[:, k] += P[:, g == k].sum(1)
+    L = l_lane.sum(1) + np.exp2(sink - m_run)
+    return O / L[:, None], skipped / steps
+
+
+def _worst(got, ref):
+    return float((np.abs(got - ref) / (TOL + TOL * np.abs(ref))).max())
+
+
+@pytest.mark.parametrize("spread", [1.0, 2.0, 4.0, 8.0])
+def test_lo_term_skip_rule_stays_within_half_the_tolerance(spread):
+    worst, skip = 0.0, []
+    for seed in range(2):
+        y, s2, sink = _inputs(4160, 16, spread, seed)
+        got, sk = _kernel_model(y, s2, sink, "skip")
+        worst = max(worst, _worst(got, _exact(y, s2, sink)))
+        skip.append(sk)
+    assert worst < 0.5, f"spread {spread}: worst error {worst:.3f} of the tolerance"
+    if spread == 1.0:  # a flat softmax: most tiles go without the lo term
+        assert np.mean(skip) > 0.5, f"only {np.mean(skip):.2f} of the tiles skipped"
+
+
+@pytest.mark.parametrize("R", [32, 1152, 4160])
+def test_hi_lo_terms_far_inside_the_tolerance(R):
+    for spread in (1.0, 4.0):
+        y, s2, sink = _inputs(R, 16, spread, 5)
+        got, sk = _kernel_model(y, s2, sink, "hilo")
+        assert sk == 0.0
+        assert _worst(got, _exact(y, s2, sink)) < 0.05
+
+
+def test_one_bf16_term_fails_on_a_peaked_softmax():
+    """Why the kernels keep the lo term: with weights concentrated on a few rows, rounding P to
+    one bf16 term moves outputs by more than the tolerance even over 4,160 rows."""
+    y, s2, sink = _inputs(4160, 16, 4.0, 7)
+    got, _ = _kernel_model(y, s2, sink, "hi")
+    assert _worst(got, _exact(y, s2, sink)) > 1.0
