@@ -2,7 +2,7 @@
 
 The kernels compute every score exactly (bf16 queries, rows exact in bf16) and accumulate in fp32,
 so the one rounding that matters is P's: a 16x16x32 bf16 product takes P in bf16. This models the
-three forms the kernels could use, on the parity tests' row and query distributions (E4M3 + bf16
+forms the kernels could use, on the parity tests' row and query distributions (E4M3 + bf16
 rows, bf16 queries, unit normal draws; scores of spread 1, 2, 4 and 8 through the query scale), and
 holds each to the atol = rtol = 1e-3 bar of the parity tests:
 
@@ -12,7 +12,10 @@ holds each to the atol = rtol = 1e-3 bar of the parity tests:
 - the lo term left out of a tile whose weights are all at most 1/16 of the weight the lane has
   already summed for that head, as the two-per-CU build does on splits of 64 tiles or more: inside
   half the bar at every spread, while it still leaves the lo term out of most tiles of a flat
-  softmax.
+  softmax;
+- FP8 operands for the prefill contractions (OCP MX E4M3 with an E8M0 scale per 32 elements along
+  the contraction): P for P.Y, or the query for Q.Y (the rows' E4M3 dims are exact either way):
+  both miss the bar several times over, so the contractions stay on bf16.
 
 The model follows the kernel's bookkeeping: 32-row tiles, a lane's running sum over its rows 4g..4g+3
 and 16+4g..16+4g+3 of each tile, a reference max that moves only when a head's max grows by more
@@ -91,6 +94,18 @@ def _kernel_model(y, s2, sink, mode, skip_frac=1 / 16):
     return O / L[:, None], skipped / steps
 
 
+def _mx_e4m3(x, axis):
+    """OCP MX E4M3 along `axis`: blocks of 32 share the scale 2^(floor(log2 max|x|) - 8), the
+    scaled values round to E4M3 (saturating at 448, the format's largest finite value)."""
+    x = np.moveaxis(x, axis, -1)
+    sh, n = x.shape, x.shape[-1]
+    xp = np.concatenate([x, np.zeros(sh[:-1] + ((-n) % 32,))], -1).reshape(sh[:-1] + (-1, 32))
+    m = np.abs(xp).max(-1, keepdims=True)
+    E = np.where(m > 0, np.floor(np.log2(np.where(m > 0, m, 1.0))) - 8, 0.0)
+    q = _e4m3(np.clip(xp / 2.0 ** E, -448, 448)) * 2.0 ** E
+    return np.moveaxis(q.reshape(sh[:-1] + (-1,))[..., :n], -1, axis)
+
+
 def _worst(got, ref):
     return float((np.abs(got - ref) / (TOL + TOL * np.abs(ref))).max())
 
@@ -123,3 +138,25 @@ def test_one_bf16_term_fails_on_a_peaked_softmax():
     y, s2, sink = _inputs(4160, 16, 4.0, 7)
     got, _ = _kernel_model(y, s2, sink, "hi")
     assert _worst(got, _exact(y, s2, sink)) > 1.0
+
+
+@pytest.mark.parametrize("spread", [1.0, 4.0])
+def test_fp8_operands_fail_the_tolerance(spread):
+    """FP8 (MX E4M3) weights in P.Y, or an FP8 query in Q.Y, over 1,152 rows (a CSA query's
+    rows): each misses atol = rtol = 1e-3 by a wide margin (measured: P 6 and 27 x, the query 10 and
+    200 x the tolerance at spreads 1 and 4)."""
+    y, s2, sink = _inputs(1152, 16, spread, 3)
+    ref = _exact(y, s2, sink)
+    M = np.maximum(s2.max(1), sink)
+    p = np.exp2(s2 - M[:, None])
+    got = (_mx_e4m3(p, 1) @ y) / (p.sum(1) + np.exp2(sink - M))[:, None]
+    assert _worst(got, ref) > 3.0
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((1152, D))
+    y[:, :448] = _e4m3(y[:, :448])
+    y[:, 448:] = _bf16(y[:, 448:])
+    q = _bf16(rng.standard_normal((16, D)) * spread)
+    q8 = q.copy()
+    q8[:, :448] = _mx_e4m3(q[:, :448], 1)
+    sc = np.log2(np.e) / np.sqrt(D)
+    assert _worst(_exact(y, (q8 @ y.T) * sc, sink), _exact(y, (q @ y.T) * sc, sink)) > 5.0
