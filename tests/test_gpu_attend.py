@@ -102,6 +102,30 @@ def test_csa_largest_k():
     assert_close(l, rl, "k=4096 lse")
 
 
+@pytest.mark.parametrize("q_std", [1.0, 4.0])
+def test_csa_long_splits_two_per_cu_build(q_std):
+    """300 queries of one sequence with 4096 selected entries each (10% empty): two splits of 66
+    tiles per query on 600 workgroups, the two-per-CU build that leaves the lo term of P out of
+    tiles whose weights are all small. Scores of spread 1 and 4; sampled queries on the oracle."""
+    Q, k = 300, 4096
+    c = DecodeCase("csa128k", B=1, N=20000, Q=Q, pos=4 * 20000 - Q)
+    if q_std != 1.0:  # scale the bf16 queries (a power of two: exact)
+        qf = torch.from_numpy(c.q.view(np.int16)).view(torch.bfloat16).float() * q_std
+        c.q = bf16_bits(qf.to(torch.bfloat16))
+    idx = _idx_random(1, Q, c.N, k, 31, empty_frac=0.1)
+    say(f"[csa_attend] long splits Q={Q} k={k} N={c.N} q_std={q_std}")
+    q, cache, win, pos = c.gpu("q", "cache", "window", "pos")
+    out, lse = L.csa_attend(q, cache, dev(idx), win, c.wl.w, pos, dev(c.sink), c.scale)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    w = c.wl.w
+    for i in (0, 1, 150, Q - 1):
+        ro, rl = O.csa_attend(c.q[:, i:i + 1], c.cache, c.fmt, idx[:, i:i + 1],
+                              c.window[:, i:i + w], w, c.pos + i, c.sink, c.scale)
+        assert_close(out[:, i:i + 1], ro, f"long-split csa out, query {i}")
+        assert_close(lse[:, i:i + 1], rl, f"long-split csa lse, query {i}")
+
+
 def test_csa_empty_slots_no_sink_and_early_positions():
     """-1 slots, no sink, window rows before position 0, ragged k (not a tile multiple)."""
     c = DecodeCase("csa128k", B=3, N=700, pos=[5, 130, 2799])

@@ -157,6 +157,23 @@ def test_hca_attend_paged(P):
     assert_close(l, rl, "paged hca lse")
 
 
+@pytest.mark.parametrize("P", [16])
+def test_hca_attend_paged_prefill_grid(P):
+    """512 queries of one sequence over about 3,000 paged entries: one split of 98 tiles per
+    query on 512 workgroups, the two-per-CU build that leaves the lo term of P out of tiles whose
+    weights are all small. Paged equals contiguous bit for bit; sampled queries match the oracle."""
+    Q = 512
+    c = DecodeCase("hca1m", B=1, N=3000, Q=Q, pos=128 * 3000 - Q)
+    say(f"[hca_attend_paged] prefill grid B=1 Q={Q} N={c.N} P={P}")
+    o, l = _hca_both(c, 128, P, P)
+    w = c.wl.w
+    for i in (0, 1, 127, 128, 300, Q - 1):
+        ro, rl = O.hca_attend(c.q[:, i:i + 1], c.cache, c.fmt, 128, c.window[:, i:i + w], w,
+                              c.pos + i, c.sink, c.scale)
+        assert_close(o[:, i:i + 1], ro, f"paged hca prefill grid out, query {i}")
+        assert_close(l[:, i:i + 1], rl, f"paged hca prefill grid lse, query {i}")
+
+
 def test_fp32_rows_paged():
     """The tiny fp32-row configuration (D = 128) through both paged attention calls."""
     c = DecodeCase("tiny")
