@@ -113,6 +113,11 @@ struct CandPlan {
 bool index_cand_plan(int slots, int64_t N, int k, int page_shift, CandPlan* p);
 size_t index_cand_slot_bytes();
 hipError_t launch_index_cand(const IndexArgs& a, const CandPlan& p);
+// 3 to kCandMqMaxQ queries per sequence (128-dim keys): one MFMA pass per range scores all of a
+// sequence's queries and publishes a list per query; the same top-k finishes each query.
+constexpr int kCandMqMaxQ = 8;
+bool index_cand_plan_mq(int B, int Q, int64_t N, int k, int page_shift, CandPlan* p);
+hipError_t launch_index_cand_mq(const IndexArgs& a, const CandPlan& p);
 
 // ---- attention ---------------------------------------------------------------------------------
 struct AttendPlan {

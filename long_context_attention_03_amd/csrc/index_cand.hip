@@ -56,6 +56,8 @@ static inline size_t cand_al256(size_t x) { return (x + 255) & ~(size_t)255; }
 // One slot's share of the workspace: every list and bound of the largest plan (R * cap <= kUMax).
 size_t index_cand_slot_bytes() { return cand_al256((size_t)(kUMax + kCandMaxRanges) * 8); }
 
+static bool cand_plan_ranges(int64_t n, int64_t chunk, int k, CandPlan* p);
+
 bool index_cand_plan(int slots, int64_t N, int k, int page_shift, CandPlan* p) {
   const int64_t n = N > 0 ? N : 1;
   // about 512 scan workgroups, ranges of 256..4096 keys. Where that would need longer ranges
@@ -73,6 +75,11 @@ bool index_cand_plan(int slots, int64_t N, int k, int page_shift, CandPlan* p) {
   }
   // paged keys: a range spans at most 1024 pages (+1 partial one), which fits the page list
   if (page_shift >= 0 && chunk > ((int64_t)1024 << page_shift)) chunk = (int64_t)1024 << page_shift;
+  return cand_plan_ranges(n, chunk, k, p);
+}
+
+// Ranges of `chunk` keys over n: R, the list length and the published minimum.
+static bool cand_plan_ranges(int64_t n, int64_t chunk, int k, CandPlan* p) {
   const int64_t R = (n + chunk - 1) / chunk;
   if (R > kCandMaxRanges) return false;
   p->chunk = (int)chunk;
@@ -88,6 +95,17 @@ bool index_cand_plan(int slots, int64_t N, int k, int page_shift, CandPlan* p) {
   if (cmin < 1) cmin = 1;
   p->cmin = cmin;
   return true;
+}
+
+// Several queries per sequence: one scan workgroup per (range, sequence) stages every query's
+// scores of its range in LDS (Q x (chunk + 4) floats), so the range is capped by that array.
+constexpr int kMqStage = 12288;
+
+bool index_cand_plan_mq(int B, int Q, int64_t N, int k, int page_shift, CandPlan* p) {
+  if (Q < 1 || Q > kCandMqMaxQ || !index_cand_plan(B, N, k, page_shift, p)) return false;
+  const int64_t cmax = (int64_t)((kMqStage / Q - 4) / 256) * 256;
+  if (p->chunk <= cmax) return true;
+  return cand_plan_ranges(N > 0 ? N : 1, cmax, k, p);
 }
 
 // ---- scoring a range ---------------------------------------------------------------------------
@@ -519,6 +537,53 @@ __global__ __launch_bounds__(kTopkThreads) void index_cand_topk_kernel(
   }
 }
 
+// ---- several queries per sequence: one pass per range for all of them ----------------------------
+// The MFMA tiles of the multi-query walk score 16 keys against every query of sequence b (one
+// product per indexer head, the heads summed in the accumulator), so the keys are read once for
+// all Q queries. Lane n's query is n; its scores of the range go to its row of `stage` (rows
+// padded by 4 floats, so that the 16 queries' stores of one key fall in different banks). Then,
+// query by query, the row is counted into the 4096-bin histogram and published exactly as the
+// one-query scan publishes: a list and a bound for slot b * Q + q in range r. Every score is the
+// exact one, so it equals the one-query scoring's value bit for bit (the top-k re-scores a range
+// with that code).
+template <int HP, bool PAGED>
+__global__ __launch_bounds__(kCandThreads) void index_cand_mq_scan_kernel(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_scales, int HI,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_scales, EntryMap kmap,
+    int64_t N, const int64_t* __restrict__ pos, int m, int Q, int chunk, int cmin, CandWs cw) {
+  const int r = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) float stage[kMqStage];
+  __shared__ uint32_t hist[kBins];
+  __shared__ int32_t pages[PAGED ? kPageList : 1];
+  const int64_t g0 = (int64_t)r * chunk;
+  const int stride = chunk + 4;
+  mfma_walk_keys<HP, PAGED>(q_codes, q_scales, HI, k_codes, k_scales, kmap, N, pos, m, Q, b, 0,
+                            g0, g0 + chunk, pages, [&](int64_t key, const f32x4& sc, int nvis) {
+                              // only lanes of queries below Q get here (the others see no key)
+                              float* st = stage + (threadIdx.x & 15) * stride + (int)(key - g0);
+                              if (nvis == 4) {
+                                *(f32x4*)st = sc;  // key - g0 and the stride are multiples of 4
+                              } else {
+#pragma unroll
+                                for (int i = 0; i < 4; i++)
+                                  if (i < nvis) st[i] = sc[i];
+                              }
+                            });
+  for (int q = 0; q < Q; q++) {
+    __syncthreads();  // the stage is complete, the previous publication has read the histogram
+    for (int j = t; j < kBins; j += kCandThreads) hist[j] = 0u;
+    const int64_t nv = visible_entries(pos, b, q, m, N);
+    const int n = g0 < nv ? (int)(nv - g0 < chunk ? nv - g0 : chunk) : 0;
+    const float* sq = stage + q * stride;
+    __syncthreads();
+    for (int j = t; j < n; j += kCandThreads) atomicAdd(&hist[order_key(sq[j]) >> kBinShift], 1u);
+    __syncthreads();
+    const int slot = b * Q + q;
+    publish_candidates(sq, hist, n, g0, cmin, cw.cap, cw.keys(slot) + (size_t)r * cw.cap,
+                       cw.bound(slot) + r);
+  }
+}
+
 // ---- launch ------------------------------------------------------------------------------------
 template <bool MX, int NB, bool PAGED>
 static void launch_cand_t(const IndexArgs& a, const CandPlan& p, const CandWs& w, hipStream_t s) {
@@ -535,6 +600,51 @@ template <bool MX, int NB>
 static void launch_cand_p(const IndexArgs& a, const CandPlan& p, const CandWs& w, hipStream_t s) {
   if (a.kmap.table) launch_cand_t<MX, NB, true>(a, p, w, s);
   else launch_cand_t<MX, NB, false>(a, p, w, s);
+}
+
+template <int HP, bool PAGED>
+static void launch_cand_mq_scan(const IndexArgs& a, const CandPlan& p, const CandWs& w,
+                                hipStream_t s) {
+  a.prof.launch(index_cand_mq_scan_kernel<HP, PAGED>, dim3((unsigned)p.R, (unsigned)a.B),
+                dim3(kCandThreads), s, a.q_codes, a.q_scales, a.HI, a.k_codes, a.k_scales, a.kmap,
+                a.N, a.pos, a.m, a.Q, p.chunk, p.cmin, w);
+}
+
+template <bool MX, int NB, bool PAGED>
+static void launch_cand_topk(const IndexArgs& a, const CandPlan& p, const CandWs& w,
+                             hipStream_t s) {
+  index_cand_topk_kernel<MX, NB, PAGED><<<dim3((unsigned)(a.B * a.Q)), kTopkThreads, 0, s>>>(
+      a.q_codes, a.q_scales, a.HI, a.k_codes, a.k_scales, a.kmap, a.N, a.pos, a.m, a.Q, p.chunk,
+      a.k, w, a.idx_out, a.score_out);
+}
+
+hipError_t launch_index_cand_mq(const IndexArgs& a, const CandPlan& p) {
+  hipStream_t s = (hipStream_t)a.stream;
+  CandWs w;
+  w.base = (char*)a.ws;
+  w.slot_bytes = index_cand_slot_bytes();
+  w.R = p.R;
+  w.cap = p.cap;
+  const bool paged = a.kmap.table != nullptr;
+  if (a.HI <= 4) {
+    if (paged) launch_cand_mq_scan<4, true>(a, p, w, s);
+    else launch_cand_mq_scan<4, false>(a, p, w, s);
+  } else if (a.HI <= 8) {
+    if (paged) launch_cand_mq_scan<8, true>(a, p, w, s);
+    else launch_cand_mq_scan<8, false>(a, p, w, s);
+  } else {
+    if (paged) launch_cand_mq_scan<16, true>(a, p, w, s);
+    else launch_cand_mq_scan<16, false>(a, p, w, s);
+  }
+  // the top-k re-scores a range with the one-query code: the MFMA form for at most 4 heads
+  if (a.HI <= 4) {
+    if (paged) launch_cand_topk<true, 4, true>(a, p, w, s);
+    else launch_cand_topk<true, 4, false>(a, p, w, s);
+  } else {
+    if (paged) launch_cand_topk<false, 4, true>(a, p, w, s);
+    else launch_cand_topk<false, 4, false>(a, p, w, s);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_index_cand(const IndexArgs& a, const CandPlan& p) {

@@ -72,23 +72,25 @@ def test_long_key_ranges_several_stage_windows():
     _compare("long ranges", kc, ks, qc, qs, pos, m, k)
 
 
-@pytest.mark.parametrize("HI", [4, 5])
-def test_clustered_top_entries_are_scored_again(HI):
+@pytest.mark.parametrize("HI,Q", [(4, 1), (5, 1), (4, 5), (6, 5)])
+def test_clustered_top_entries_are_scored_again(HI, Q):
     """The relevant entries cluster. In sequence 0 the 1,500 entries from 30,000 on have every
     block scale raised by 2^4, so nearly all of the top-1024 lie in a few adjacent scan ranges,
     far more than any range publishes; sequence 1 has two such clusters, at the start and at the
-    ragged end. The top-k kernel must score those ranges again. 4 heads take the MFMA scan, 5
-    the vector scan; indices and scores stay bit-exact."""
-    rng = np.random.default_rng(61 + HI)
+    ragged end. The top-k kernel must score those ranges again. One query: 4 heads take the MFMA
+    scan, 5 the vector scan; five queries take the multi-query pass, whose per-query lists the
+    top-k re-scores with the one-query code (MFMA for 4 heads, vector for 6). Indices and scores
+    stay bit-exact."""
+    rng = np.random.default_rng(61 + HI + Q)
     B, N, dI, m, k = 2, 100003, 128, 4, 1024
     kc, ks = O.encode_rows(rng.normal(size=(B, N, dI)), O.FMT_FP4_E8M0)
     ks = ks.copy()
     ks[0, 30000:31500] += 4
     ks[1, :700] += 4
     ks[1, N - 800:] += 4
-    qc, qs = O.encode_rows(rng.normal(size=(B, 1, HI, dI)), O.FMT_FP4_E8M0)
-    pos = np.full(B, N * m - 1, np.int64)
-    _compare(f"clustered HI={HI}", kc, ks, qc, qs, pos, m, k)
+    qc, qs = O.encode_rows(rng.normal(size=(B, Q, HI, dI)), O.FMT_FP4_E8M0)
+    pos = np.full(B, N * m - Q, np.int64)
+    _compare(f"clustered HI={HI} Q={Q}", kc, ks, qc, qs, pos, m, k)
 
 
 @pytest.mark.parametrize("Q,coarse", [(1, False), (1, True), (5, False), (16, False), (16, True)])
