@@ -114,8 +114,11 @@ bool index_cand_plan(int slots, int64_t N, int k, int page_shift, CandPlan* p);
 size_t index_cand_slot_bytes();
 hipError_t launch_index_cand(const IndexArgs& a, const CandPlan& p);
 // 3 to kCandMqMaxQ queries per sequence (128-dim keys): one MFMA pass per range scores all of a
-// sequence's queries and publishes a list per query; the same top-k finishes each query.
-constexpr int kCandMqMaxQ = 8;
+// sequence's queries and publishes a list per query; the same top-k finishes each query. Measured
+// at 4 x 262,144 keys: 34.5 / 42.4 us against 49.3 / 58.3 us (stored scores) for 3 / 5 queries,
+// but 72.2 against 62.0 us for 6: the LDS stage then caps the ranges below 2048 keys, and the scan
+// needs more than one round of workgroups.
+constexpr int kCandMqMaxQ = 5;
 bool index_cand_plan_mq(int B, int Q, int64_t N, int k, int page_shift, CandPlan* p);
 hipError_t launch_index_cand_mq(const IndexArgs& a, const CandPlan& p);
 

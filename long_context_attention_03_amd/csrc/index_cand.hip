@@ -1,4 +1,4 @@
-// index_cand.hip -- decode indexer (one or two queries per sequence, and 3 to 8 with 128-dim keys):
+// index_cand.hip -- decode indexer (one or two queries per sequence, and 3 to 5 with 128-dim keys):
 // a scan that leaves certified per-range candidate lists, then one exact top-k over their union.
 // With several queries per sequence one scan workgroup scores its range for all of them at once
 // (the multi-query MFMA tiles) and publishes a list per query (index_cand_mq_scan_kernel).
