@@ -148,11 +148,11 @@ int csah_kv_compress_span(const void* raw, int raw_dtype, int64_t raw_seq_stride
  *    scores come from the scaled FP4 MFMA and are recomputed rather than stored; the workspace
  *    holds, per query, a histogram, counters and a candidate list of max(8192, 4k) 8-byte keys
  *    (at most N), whatever N is.
- *  - dI = 128 and 3 <= Q <= 5: one pass per key range scores all of a sequence's queries and
+ *  - dI = 128 and 3 <= Q <= 7: one pass per key range scores all of a sequence's queries and
  *    leaves a candidate list per query, ranked as in the decode schedule; the workspace is the
  *    larger of that schedule's 73,728 bytes per slot and the stored-score one below (which
  *    serves the call when the keys span more ranges than the lists allow).
- *  - Otherwise (6 <= Q <= 15 with 128-dim keys, or N > 2^20) every score is stored: per slot
+ *  - Otherwise (8 <= Q <= 15 with 128-dim keys, or N > 2^20) every score is stored: per slot
  *    the head-summed query, a histogram, counters, 4 bytes per entry and two candidate lists.
  */
 size_t csah_index_topk_workspace(int B, int Q, int64_t N, int k, int HI, int dI);

@@ -115,10 +115,10 @@ size_t index_cand_slot_bytes();
 hipError_t launch_index_cand(const IndexArgs& a, const CandPlan& p);
 // 3 to kCandMqMaxQ queries per sequence (128-dim keys): one MFMA pass per range scores all of a
 // sequence's queries and publishes a list per query; the same top-k finishes each query. Measured
-// at 4 x 262,144 keys: 34.5 / 42.4 us against 49.3 / 58.3 us (stored scores) for 3 / 5 queries,
-// but 72.2 against 62.0 us for 6: the LDS stage then caps the ranges below 2048 keys, and the scan
-// needs more than one round of workgroups.
-constexpr int kCandMqMaxQ = 5;
+// at 4 x 262,144 keys: 34.5 / 42.4 / 46.6 / 50.3 us against 49.3 / 58.3 / 61.3 / 63.5 us (stored
+// scores) for 3 / 5 / 6 / 7 queries; at 8 the LDS stage caps the ranges below 2048 keys and the
+// scan needs a second round of workgroups (79.0 against 64.7 us).
+constexpr int kCandMqMaxQ = 7;
 bool index_cand_plan_mq(int B, int Q, int64_t N, int k, int page_shift, CandPlan* p);
 hipError_t launch_index_cand_mq(const IndexArgs& a, const CandPlan& p);
 

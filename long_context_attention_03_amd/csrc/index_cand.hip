@@ -1,4 +1,4 @@
-// index_cand.hip -- decode indexer (one or two queries per sequence, and 3 to 5 with 128-dim keys):
+// index_cand.hip -- decode indexer (one or two queries per sequence, and 3 to 7 with 128-dim keys):
 // a scan that leaves certified per-range candidate lists, then one exact top-k over their union.
 // With several queries per sequence one scan workgroup scores its range for all of them at once
 // (the multi-query MFMA tiles) and publishes a list per query (index_cand_mq_scan_kernel).
@@ -100,8 +100,9 @@ static bool cand_plan_ranges(int64_t n, int64_t chunk, int k, CandPlan* p) {
 }
 
 // Several queries per sequence: one scan workgroup per (range, sequence) stages every query's
-// scores of its range in LDS (Q x (chunk + 4) floats), so the range is capped by that array.
-constexpr int kMqStage = 12288;
+// scores of its range in LDS (Q x (chunk + 4) floats), so the range is capped by that array: 7
+// queries of 2048 keys (56 KB; with the histogram and a page list two workgroups still share a CU).
+constexpr int kMqStage = 14364;
 
 bool index_cand_plan_mq(int B, int Q, int64_t N, int k, int page_shift, CandPlan* p) {
   if (Q < 1 || Q > kCandMqMaxQ || !index_cand_plan(B, N, k, page_shift, p)) return false;
